@@ -1,0 +1,156 @@
+"""GPU-vs-oracle acceptance rules (TEST INFRASTRUCTURE ONLY).
+
+The oracle is exact (double precision); the device computes in float32.  The
+rules below say when a device result counts as the oracle's result:
+
+1. Probe sets.  A device probe set may differ from the oracle's only by lists
+   whose oracle coarse distance lies within delta_c of the oracle's
+   nprobe-th smallest, delta_c(q) = 4 * gamma_{d+2} * (|x_q|^2 + max_l |c_l|^2),
+   gamma_n = n u / (1 - n u), u = 2^-24: a forward-error bound of any float32
+   evaluation of |x - c|^2 (direct or through the norm expansion), times two.
+   Where the sets differ the oracle is re-run on the device's probe set.
+2. Result ids.  The device id set may differ from the oracle's only by ids
+   whose oracle distance is within tau * D_o[k-1] of the oracle's k-th
+   distance; no duplicates; distances non-decreasing; the padding (+inf, -1)
+   matches.
+3. Distances.  Every returned id's distance is within tau relative of the
+   oracle's distance for that id (tau = 1e-4 float32 tables, 1e-2 fp16).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+from . import oracle as O
+
+TAU_F32 = 1e-4
+TAU_F16 = 1e-2
+
+
+def gamma(n: int) -> float:
+    u = 2.0 ** -24
+    return n * u / (1.0 - n * u)
+
+
+@dataclasses.dataclass
+class Report:
+    nq: int = 0
+    probe_flips: int = 0
+    queries_reprobed: int = 0
+    tie_swaps: int = 0
+    max_rel_err: float = 0.0
+    failures: list = dataclasses.field(default_factory=list)
+
+    def ok(self) -> bool:
+        return not self.failures
+
+    def summary(self) -> dict:
+        return dict(nq=self.nq, probe_flips=self.probe_flips, queries_reprobed=self.queries_reprobed,
+                    tie_swaps=self.tie_swaps, max_rel_err=self.max_rel_err,
+                    failures=len(self.failures))
+
+
+def _get(index, name):
+    return index[name] if isinstance(index, dict) else getattr(index, name)
+
+
+def check_probes(index, queries, gpu_probes, oracle_probes, report: Report):
+    """Rule 1.  Returns the list of query rows whose probe set differs."""
+    cent = np.asarray(_get(index, "centroids"), dtype=np.float32)
+    nlist, d = cent.shape
+    cmax = float(np.max(np.sum(cent.astype(np.float64) ** 2, axis=1)))
+    differ = []
+    for qi in range(len(queries)):
+        g = set(int(v) for v in gpu_probes[qi])
+        o = set(int(v) for v in oracle_probes[qi])
+        if len(g) != len(gpu_probes[qi]):
+            report.failures.append((qi, "duplicate probe"))
+            continue
+        if g == o:
+            continue
+        nprobe = len(oracle_probes[qi])
+        allp, alld = O.coarse(queries[qi], cent, nlist)
+        dist_of = {int(p): float(v) for p, v in zip(allp, alld)}
+        x2 = float(np.sum(np.asarray(queries[qi], dtype=np.float64) ** 2))
+        delta = 4.0 * gamma(d + 2) * (x2 + cmax)
+        edge = float(alld[nprobe - 1])
+        for lst in g ^ o:
+            if lst not in dist_of or abs(dist_of[lst] - edge) > delta:
+                report.failures.append((qi, f"probe {lst} outside the coarse tie band"))
+                break
+        report.probe_flips += len(g - o)
+        differ.append(qi)
+    return differ
+
+
+def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None):
+    """Rules 2 and 3 for each row; ora_* hold at least k columns (more give
+    the distances of ids just past the k-th)."""
+    rows = range(len(gpu_d)) if rows is None else rows
+    for r in rows:
+        gd = np.asarray(gpu_d[r], dtype=np.float64)
+        gi = np.asarray(gpu_i[r], dtype=np.int64)
+        od = np.asarray(ora_d[r], dtype=np.float64)
+        oi = np.asarray(ora_i[r], dtype=np.int64)
+        valid_o = int(np.sum(oi[:k] >= 0))
+        valid_g = int(np.sum(gi >= 0))
+        if valid_g != valid_o:
+            report.failures.append((r, f"valid count {valid_g} != {valid_o}"))
+            continue
+        if np.any(gi[valid_g:] != -1) or np.any(np.isfinite(gd[valid_g:])):
+            report.failures.append((r, "bad padding"))
+            continue
+        if np.any(gi[:valid_g] < 0):
+            report.failures.append((r, "sentinel inside the valid prefix"))
+            continue
+        if len(set(gi[:valid_g].tolist())) != valid_g:
+            report.failures.append((r, "duplicate ids"))
+            continue
+        if valid_g > 1 and np.any(np.diff(gd[:valid_g]) < 0):
+            report.failures.append((r, "distances not ascending"))
+            continue
+        if valid_g == 0:
+            continue
+        dist_of = {int(i): float(v) for i, v in zip(oi, od) if i >= 0}
+        kth = float(od[valid_o - 1])
+        band = tau * kth
+        gset, oset = set(gi[:valid_g].tolist()), set(oi[:valid_o].tolist())
+        bad = False
+        for i in gset ^ oset:
+            v = dist_of.get(int(i))
+            if v is None or abs(v - kth) > band:
+                report.failures.append((r, f"id {i} outside the k-th distance tie band"))
+                bad = True
+                break
+        if bad:
+            continue
+        report.tie_swaps += len(gset - oset)
+        for i, v in zip(gi[:valid_g], gd[:valid_g]):
+            ref = dist_of[int(i)]
+            err = abs(float(v) - ref)
+            if err > tau * abs(ref):
+                report.failures.append((r, f"id {i}: distance {v} vs oracle {ref}"))
+                break
+            if ref != 0:
+                report.max_rel_err = max(report.max_rel_err, err / abs(ref))
+
+
+def compare_search(index, queries, nprobe, k, gpu_d, gpu_i, gpu_probes=None, lut_mode=O.LUT_F64,
+                   tau=None, k_extra=32, nthreads=None) -> Report:
+    """Full acceptance check of a device IVF-PQ search against the oracle."""
+    tau = (TAU_F32 if lut_mode == O.LUT_F64 else TAU_F16) if tau is None else tau
+    queries = np.ascontiguousarray(queries, dtype=np.float32)
+    rep = Report(nq=len(queries))
+    kx = k + k_extra
+    od, oi, op = O.search(index, queries, nprobe, kx, lut_mode=lut_mode, nthreads=nthreads)
+    if gpu_probes is not None:
+        differ = check_probes(index, queries, gpu_probes, op, rep)
+        if differ:
+            rep.queries_reprobed = len(differ)
+            sub = np.asarray(differ)
+            d2, i2, _ = O.search(index, queries[sub], nprobe, kx, lut_mode=lut_mode,
+                                 probes=np.asarray(gpu_probes)[sub], nthreads=nthreads)
+            od[sub], oi[sub] = d2, i2
+    check_results(gpu_d, gpu_i, od, oi, k, tau, rep)
+    return rep

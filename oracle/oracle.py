@@ -1,0 +1,196 @@
+"""Python front of the CPU oracle (TEST INFRASTRUCTURE ONLY).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  It builds and loads ``liboracle.so`` (plain C, double
+precision, see ``ivfpq_oracle.c``) and wraps its entry points with ctypes.
+It has its own reader of the index file and imports nothing from the GPU
+package.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import struct
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "ivfpq_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+LUT_F64 = 0
+LUT_F16 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                               "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread", "-o", tmp, SRC,
+                               "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int, ctypes.c_int64
+        L.oracle_round_binary16.argtypes = [ctypes.c_float]
+        L.oracle_round_binary16.restype = ctypes.c_double
+        L.oracle_coarse.argtypes = [P, P, i32, i32, i32, P, P]
+        L.oracle_lut.argtypes = [P, P, P, i32, i32, i32, P]
+        L.oracle_search.argtypes = [P, P, P, P, P, i32, i32, i32, P, i64, i32, i32, i32, P, P, P,
+                                    P, i32]
+        L.oracle_bruteforce.argtypes = [P, P, i64, i32, P, i64, i32, P, P, i32]
+        L.oracle_bruteforce_bf16.argtypes = [P, i64, i32, P, i64, i32, P, P, i32]
+        for f in ("oracle_coarse", "oracle_lut", "oracle_search", "oracle_bruteforce",
+                  "oracle_bruteforce_bf16"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+# ---------------------------------------------------------------------------
+# the oracle's own index-file reader
+# ---------------------------------------------------------------------------
+
+def read_index_file(path: str) -> dict:
+    with open(path, "rb") as f:
+        head = f.read(32)
+        magic, d, nlist, m, nbits, ntotal = struct.unpack("<8sIIIIQ", head)
+        if magic != b"IVFPQ01\x00" or nbits != 8 or m < 1 or d % m:
+            raise ValueError("bad index file")
+        dsub = d // m
+        raw = np.fromfile(f, dtype=np.uint8)
+    o = 0
+    cent = raw[o:o + 4 * nlist * d].view("<f4").reshape(nlist, d)
+    o += 4 * nlist * d
+    books = raw[o:o + 4 * m * 256 * dsub].view("<f4").reshape(m, 256, dsub)
+    o += 4 * m * 256 * dsub
+    sizes = raw[o:o + 8 * nlist].view("<u8").astype(np.int64)
+    o += 8 * nlist
+    codes = raw[o:o + ntotal * m].reshape(ntotal, m)
+    o += ntotal * m
+    ids = raw[o:o + 8 * ntotal].view("<i8")
+    return dict(centroids=cent, codebooks=books, list_sizes=sizes, codes=codes, ids=ids)
+
+
+# ---------------------------------------------------------------------------
+# wrappers
+# ---------------------------------------------------------------------------
+
+def round_binary16(x: float) -> float:
+    return lib().oracle_round_binary16(float(x))
+
+
+def coarse(x, centroids, nprobe):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    c = np.ascontiguousarray(centroids, dtype=np.float32)
+    probes = np.empty(nprobe, dtype=np.int32)
+    dists = np.empty(nprobe, dtype=np.float64)
+    rc = lib().oracle_coarse(_p(x), _p(c), c.shape[1], c.shape[0], nprobe, _p(probes), _p(dists))
+    if rc:
+        raise ValueError(f"oracle_coarse failed ({rc})")
+    return probes, dists
+
+
+def lut(x, centroid, codebooks, lut_mode=LUT_F64):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    c = np.ascontiguousarray(centroid, dtype=np.float32)
+    b = np.ascontiguousarray(codebooks, dtype=np.float32)
+    m = b.shape[0]
+    out = np.empty((m, 256), dtype=np.float64)
+    rc = lib().oracle_lut(_p(x), _p(c), _p(b), x.shape[0], m, lut_mode, _p(out))
+    if rc:
+        raise ValueError(f"oracle_lut failed ({rc})")
+    return out
+
+
+def search(index, queries, nprobe, k, lut_mode=LUT_F64, probes=None, nthreads=None):
+    """Returns (distances float64 [nq,k], ids int64 [nq,k], probes int32 [nq,nprobe]).
+
+    ``index`` is any object with centroids, codebooks, list_sizes, codes and
+    ids attributes or keys."""
+    get = (lambda n: index[n]) if isinstance(index, dict) else (lambda n: getattr(index, n))
+    cent = np.ascontiguousarray(get("centroids"), dtype=np.float32)
+    books = np.ascontiguousarray(get("codebooks"), dtype=np.float32)
+    sizes = np.ascontiguousarray(get("list_sizes"), dtype=np.int64)
+    codes = np.ascontiguousarray(get("codes"), dtype=np.uint8)
+    ids = np.ascontiguousarray(get("ids"), dtype=np.int64)
+    q = np.ascontiguousarray(queries, dtype=np.float32)
+    nq, d = q.shape
+    nlist = cent.shape[0]
+    m = books.shape[0]
+    if probes is not None:
+        probes = np.ascontiguousarray(probes, dtype=np.int32)
+        assert probes.shape == (nq, nprobe)
+    od = np.empty((nq, k), dtype=np.float64)
+    oi = np.empty((nq, k), dtype=np.int64)
+    op = np.empty((nq, nprobe), dtype=np.int32)
+    rc = lib().oracle_search(_p(cent), _p(books), _p(sizes), _p(codes), _p(ids), d, nlist, m, _p(q),
+                             nq, nprobe, k, lut_mode, _p(probes), _p(od), _p(oi), _p(op),
+                             nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_search failed ({rc})")
+    return od, oi, op
+
+
+def bruteforce(db, queries, k, db_ids=None, nthreads=None):
+    db = np.ascontiguousarray(db, dtype=np.float32)
+    q = np.ascontiguousarray(queries, dtype=np.float32)
+    ids = None if db_ids is None else np.ascontiguousarray(db_ids, dtype=np.int64)
+    od = np.empty((q.shape[0], k), dtype=np.float64)
+    oi = np.empty((q.shape[0], k), dtype=np.int64)
+    rc = lib().oracle_bruteforce(_p(db), _p(ids), db.shape[0], db.shape[1], _p(q), q.shape[0], k,
+                                 _p(od), _p(oi), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_bruteforce failed ({rc})")
+    return od, oi
+
+
+def bruteforce_bf16(db_bits, query_bits, k, nthreads=None):
+    db = np.ascontiguousarray(db_bits, dtype=np.uint16)
+    q = np.ascontiguousarray(query_bits, dtype=np.uint16)
+    od = np.empty((q.shape[0], k), dtype=np.float64)
+    oi = np.empty((q.shape[0], k), dtype=np.int64)
+    rc = lib().oracle_bruteforce_bf16(_p(db), db.shape[0], db.shape[1], _p(q), q.shape[0], k,
+                                      _p(od), _p(oi), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_bruteforce_bf16 failed ({rc})")
+    return od, oi
+
+
+# ---------------------------------------------------------------------------
+# recall (two readings of the pages' measures)
+# ---------------------------------------------------------------------------
+
+def recall_1_at_k(found_ids, true_ids):
+    """Fraction of queries whose true nearest neighbour is among the k found."""
+    return float(np.mean([t[0] in set(f.tolist()) for f, t in zip(found_ids, true_ids)]))
+
+
+def recall_k_at_k(found_ids, true_ids):
+    """Mean fraction of the k found that are among the true k nearest."""
+    k = found_ids.shape[1]
+    return float(np.mean([len(set(f.tolist()) & set(t.tolist())) / k
+                          for f, t in zip(found_ids, true_ids)]))

@@ -1,0 +1,308 @@
+"""Pins of the CPU oracle against things other than itself.
+
+* a hand-worked case (tests/golden/hand_case.json);
+* the identity stated after Eq. (1) of the IVFPQ section of "Custom 8-bit
+  floating point value format for reducing shared memory bank conflict in
+  ANN search": the table sum R equals the squared L2 norm of the query minus
+  the reconstructed database vector (centroid + decoded residual);
+* PQ-exact integer data, where IVF-PQ with every list probed must equal exact
+  brute-force k-NN bit for bit;
+* textbook routines: numpy argsort for the coarse step, numpy float16 for
+  binary16 rounding, pure-Python loops for brute force.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from oracle import check
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def hand_index(extra=None):
+    g = json.load(open(os.path.join(GOLDEN, "hand_case.json")))
+    m, d = g["m"], g["d"]
+    books = np.empty((m, 256, d // m), dtype=np.float32)
+    books[:] = np.asarray(g["default_codeword"], dtype=np.float32)
+    for j, words in g["codewords"].items():
+        for v, w in words.items():
+            books[int(j), int(v)] = w
+    lists = [list(l) for l in g["lists"]]
+    if extra is not None:
+        lists[0] = lists[0] + [extra]
+    codes = np.array([c for l in lists for _, c in l], dtype=np.uint8).reshape(-1, m)
+    ids = np.array([i for l in lists for i, _ in l], dtype=np.int64)
+    sizes = np.array([len(l) for l in lists], dtype=np.int64)
+    idx = dict(centroids=np.asarray(g["centroids"], dtype=np.float32), codebooks=books,
+               list_sizes=sizes, codes=codes, ids=ids)
+    return g, idx
+
+
+def inf_list(v):
+    return [math.inf if x == "inf" else float(x) for x in v]
+
+
+def reconstruct(idx):
+    """Centroid of the entry's list plus the concatenated codewords."""
+    cent, books = idx["centroids"], idx["codebooks"]
+    m = books.shape[0]
+    lists = np.repeat(np.arange(len(idx["list_sizes"])), idx["list_sizes"])
+    dec = np.concatenate([books[j][idx["codes"][:, j]] for j in range(m)], axis=1)
+    return cent[lists].astype(np.float64) + dec.astype(np.float64)
+
+
+def numpy_knn(db, q, k, ids=None):
+    ids = np.arange(len(db)) if ids is None else ids
+    d = ((q[:, None, :].astype(np.float64) - db[None, :, :].astype(np.float64)) ** 2).sum(-1)
+    out_d = np.full((len(q), k), np.inf)
+    out_i = np.full((len(q), k), -1, dtype=np.int64)
+    for r in range(len(q)):
+        order = np.lexsort((ids, d[r]))[:k]
+        out_d[r, :len(order)] = d[r][order]
+        out_i[r, :len(order)] = ids[order]
+    return out_d, out_i
+
+
+# ---------------------------------------------------------------------------
+# hand-worked case
+# ---------------------------------------------------------------------------
+
+def test_hand_case_coarse_and_tables():
+    g, idx = hand_index()
+    x = np.asarray(g["query"], dtype=np.float32)
+    probes, dists = O.coarse(x, idx["centroids"], 2)
+    assert probes.tolist() == [0, 1]
+    assert dists.tolist() == g["coarse_distances"]
+    t0 = O.lut(x, idx["centroids"][0], idx["codebooks"])
+    assert t0[:, :3].tolist() == g["lut_list0_first3"]
+    t1 = O.lut(x, idx["centroids"][1], idx["codebooks"])
+    assert [t1[0, 0], t1[1, 0]] == g["lut_list1_code0"]
+
+
+@pytest.mark.parametrize("case", [0, 1])
+def test_hand_case_search(case):
+    g, idx = hand_index()
+    c = g["cases"][case]
+    d, i, p = O.search(idx, np.asarray([g["query"]], np.float32), c["nprobe"], c["k"])
+    assert i[0].tolist() == c["ids"]
+    assert d[0].tolist() == inf_list(c["dist"])
+
+
+def test_hand_case_tie_order():
+    g, _ = hand_index()
+    t = g["tie_case"]
+    _, idx = hand_index(extra=t["add_to_list0"])
+    d, i, _ = O.search(idx, np.asarray([g["query"]], np.float32), t["nprobe"], t["k"])
+    assert i[0].tolist() == t["ids"]
+    assert d[0].tolist() == inf_list(t["dist"])
+
+
+def test_coarse_tie_goes_to_lower_list_number():
+    cent = np.array([[1, 0], [0, 1], [-1, 0], [5, 5]], dtype=np.float32)
+    p, d = O.coarse(np.zeros(2, np.float32), cent, 3)
+    assert p.tolist() == [0, 1, 2] and d.tolist() == [1, 1, 1]
+
+
+# ---------------------------------------------------------------------------
+# the table-sum identity, random indexes of several shapes
+# ---------------------------------------------------------------------------
+
+def random_idx(seed, nlist, d, m, n):
+    rng = np.random.default_rng(seed)
+    sizes = rng.multinomial(n, np.ones(nlist) / nlist).astype(np.int64)
+    return dict(centroids=rng.standard_normal((nlist, d)).astype(np.float32),
+                codebooks=(0.5 * rng.standard_normal((m, 256, d // m))).astype(np.float32),
+                list_sizes=sizes, codes=rng.integers(0, 256, (n, m), dtype=np.uint8),
+                ids=rng.permutation(n).astype(np.int64)), rng
+
+
+@pytest.mark.parametrize("nlist,d,m,n", [(4, 8, 2, 300), (6, 12, 4, 500), (3, 24, 8, 257),
+                                         (5, 16, 16, 200)])
+def test_adc_equals_reconstruction_distance(nlist, d, m, n):
+    idx, rng = random_idx(1 + nlist * d, nlist, d, m, n)
+    q = rng.standard_normal((5, d)).astype(np.float32)
+    dist, ids, _ = O.search(idx, q, nlist, n)          # every list, every entry
+    recon = reconstruct(idx)
+    pos_of = np.empty(n, dtype=np.int64)
+    pos_of[idx["ids"]] = np.arange(n)
+    for r in range(len(q)):
+        expl = ((q[r].astype(np.float64) - recon[pos_of[ids[r]]]) ** 2).sum(1)
+        np.testing.assert_allclose(dist[r], expl, rtol=1e-5, atol=0)
+        assert np.max(np.abs(dist[r] - expl) / expl) < 1e-10
+
+
+def test_adc_single_list_matches_reconstruction():
+    idx, rng = random_idx(7, 3, 16, 4, 120)
+    q = rng.standard_normal((1, 16)).astype(np.float32)
+    probes, _ = O.coarse(q[0], idx["centroids"], 1)
+    dist, ids, p = O.search(idx, q, 1, 200)
+    assert p[0].tolist() == probes.tolist()
+    l = int(probes[0])
+    off = np.concatenate([[0], np.cumsum(idx["list_sizes"])])
+    in_list = set(idx["ids"][off[l]:off[l + 1]].tolist())
+    valid = ids[0] >= 0
+    assert set(ids[0][valid].tolist()) == in_list
+    assert valid.sum() == idx["list_sizes"][l]
+    assert np.all(np.isinf(dist[0][~valid])) and np.all(ids[0][~valid] == -1)
+
+
+# ---------------------------------------------------------------------------
+# coarse step against numpy's argsort
+# ---------------------------------------------------------------------------
+
+def test_coarse_matches_numpy_argsort():
+    rng = np.random.default_rng(11)
+    cent = rng.standard_normal((300, 24)).astype(np.float32)
+    for _ in range(10):
+        x = rng.standard_normal(24).astype(np.float32)
+        ref = ((x.astype(np.float64) - cent.astype(np.float64)) ** 2).sum(1)
+        order = np.argsort(ref, kind="stable")[:17]
+        p, d = O.coarse(x, cent, 17)
+        assert p.tolist() == order.tolist()
+        np.testing.assert_allclose(d, ref[order], rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# PQ-exact integer data: IVF-PQ (all lists) == exact k-NN, bit for bit
+# ---------------------------------------------------------------------------
+
+def pq_exact(seed, nlist=5, d=8, m=4, n=400, nq=6):
+    rng = np.random.default_rng(seed)
+    cent = rng.integers(-3, 4, (nlist, d)).astype(np.float32)
+    books = rng.integers(-3, 4, (m, 256, d // m)).astype(np.float32)
+    sizes = rng.multinomial(n, np.ones(nlist) / nlist).astype(np.int64)
+    codes = rng.integers(0, 256, (n, m), dtype=np.uint8)
+    ids = rng.permutation(n).astype(np.int64)
+    idx = dict(centroids=cent, codebooks=books, list_sizes=sizes, codes=codes, ids=ids)
+    db = reconstruct(idx).astype(np.float32)     # exact: small integers
+    q = rng.integers(-6, 7, (nq, d)).astype(np.float32)
+    return idx, db, q
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_pq_exact_integer_equals_bruteforce(seed):
+    idx, db, q = pq_exact(seed)
+    k = 25
+    d, i, _ = O.search(idx, q, 5, k)
+    bd, bi = numpy_knn(db, q, k, ids=idx["ids"])
+    assert np.array_equal(i, bi)
+    assert np.array_equal(d, bd)
+    cd, ci = O.bruteforce(db, q, k, db_ids=idx["ids"])
+    assert np.array_equal(ci, bi) and np.array_equal(cd, bd)
+    # heavy ties exist at these sizes: the (distance, id) order decides them
+    assert any(len(set(r.tolist())) < k for r in d)
+    assert O.recall_1_at_k(i, bi) == 1.0 and O.recall_k_at_k(i, bi) == 1.0
+
+
+# ---------------------------------------------------------------------------
+# brute force against pure-Python loops; bf16 widening against numpy
+# ---------------------------------------------------------------------------
+
+def test_bruteforce_pure_python():
+    rng = np.random.default_rng(5)
+    db = rng.standard_normal((40, 3)).astype(np.float32)
+    q = rng.standard_normal((4, 3)).astype(np.float32)
+    d, i = O.bruteforce(db, q, 7)
+    for r in range(4):
+        allp = sorted((sum((float(q[r][t]) - float(db[j][t])) ** 2 for t in range(3)), j)
+                      for j in range(40))
+        assert [j for _, j in allp[:7]] == i[r].tolist()
+        np.testing.assert_allclose(d[r], [v for v, _ in allp[:7]], rtol=1e-14)
+
+
+def test_bruteforce_bf16_widening():
+    rng = np.random.default_rng(6)
+    db = rng.integers(0, 1 << 16, (64, 8)).astype(np.uint16)
+    db &= ~np.uint16(0x7F80)            # keep exponents small: finite, no inf/nan
+    db |= np.uint16(0x3F00)
+    q = db[:3].copy()
+    d, i = O.bruteforce_bf16(db, q, 5)
+    dbf = (db.astype(np.uint32) << 16).view(np.float32)
+    qf = (q.astype(np.uint32) << 16).view(np.float32)
+    bd, bi = numpy_knn(dbf, qf, 5)
+    assert np.array_equal(i, bi) and np.allclose(d, bd, rtol=1e-14)
+    assert np.all(d[:, 0] == 0)
+
+
+def test_padding_when_fewer_candidates_than_k():
+    idx, rng = random_idx(3, 4, 8, 2, 30)
+    q = rng.standard_normal((3, 8)).astype(np.float32)
+    d, i, p = O.search(idx, q, 2, 64)
+    for r in range(3):
+        n = int(sum(idx["list_sizes"][l] for l in p[r]))
+        assert np.all(i[r, :n] >= 0) and np.all(i[r, n:] == -1)
+        assert np.all(np.isfinite(d[r, :n])) and np.all(np.isinf(d[r, n:]))
+
+
+def test_empty_lists_are_allowed():
+    idx, rng = random_idx(4, 6, 8, 2, 50)
+    idx["list_sizes"] = np.array([0, 20, 0, 30, 0, 0], dtype=np.int64)
+    q = rng.standard_normal((2, 8)).astype(np.float32)
+    d, i, _ = O.search(idx, q, 6, 60)
+    assert (i >= 0).sum(1).tolist() == [50, 50]
+
+
+# ---------------------------------------------------------------------------
+# binary16 rounding against numpy's float16
+# ---------------------------------------------------------------------------
+
+def test_round_binary16_matches_numpy():
+    rng = np.random.default_rng(9)
+    bits = rng.integers(0, 1 << 32, 20000, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    special = np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 65536.0, 2.0 ** -24, 2.0 ** -25,
+                        3 * 2.0 ** -25, 2.0 ** -26, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11,
+                        2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 6.1e-5, 1e-8, 1e6],
+                       dtype=np.float32)
+    # exponents spread over the binary16 range as well
+    spread = (rng.standard_normal(20000) * np.exp2(rng.uniform(-26, 17, 20000))).astype(np.float32)
+    for v in itertools.chain(special, -special, vals[:5000], spread):
+        with np.errstate(over="ignore"):
+            ref = float(np.float32(v).astype(np.float16))
+        got = O.round_binary16(float(v))
+        assert got == ref or (math.isnan(got) and math.isnan(ref)), (v, got, ref)
+
+
+def test_fp16_table_mode_rounds_each_entry():
+    idx, rng = random_idx(12, 2, 16, 4, 10)
+    x = rng.standard_normal(16).astype(np.float32)
+    full = O.lut(x, idx["centroids"][1], idx["codebooks"], O.LUT_F64)
+    half = O.lut(x, idx["centroids"][1], idx["codebooks"], O.LUT_F16)
+    # explicit table from the definition, then numpy's float32 -> float16
+    r = x.astype(np.float64) - idx["centroids"][1].astype(np.float64)
+    books = idx["codebooks"].astype(np.float64)
+    expl = np.stack([((r[j * 4:(j + 1) * 4][None, :] - books[j]) ** 2).sum(1) for j in range(4)])
+    np.testing.assert_allclose(full, expl, rtol=1e-14)
+    assert np.array_equal(half, expl.astype(np.float32).astype(np.float16).astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# the acceptance checker itself
+# ---------------------------------------------------------------------------
+
+def test_checker_accepts_oracle_and_rejects_perturbations():
+    idx, rng = random_idx(21, 8, 16, 4, 2000)
+    q = rng.standard_normal((8, 16)).astype(np.float32)
+    d, i, p = O.search(idx, q, 3, 20)
+    rep = check.compare_search(idx, q, 3, 20, d.astype(np.float32), i, p)
+    assert rep.ok(), rep.failures
+    far_d, far_i, _ = O.search(idx, q[:1], 3, 2000)
+    bad = i.copy()
+    bad[0, 5] = far_i[0][int(np.sum(far_i[0] >= 0)) - 1]     # the farthest probed entry
+    rep = check.compare_search(idx, q, 3, 20, d.astype(np.float32), bad, p)
+    assert not rep.ok()
+    dd = d.astype(np.float32).copy()
+    dd[1, 3] *= 1.001
+    dd[1] = np.sort(dd[1])
+    rep = check.compare_search(idx, q, 3, 20, dd, i, p)
+    assert not rep.ok()
+    pp = p.copy()
+    pp[2, 0] = [l for l in range(8) if l not in p[2]][0]
+    rep = check.compare_search(idx, q, 3, 20, d.astype(np.float32), i, pp)
+    assert not rep.ok()
