@@ -1,0 +1,291 @@
+"""Thin ctypes binding over ``libivfpq.so`` (declared in include/ivfpq.h).
+
+Argument marshalling only: every step of the search runs in the library's
+HIP kernels.  PyTorch supplies device memory and the HIP stream; it is
+imported before the library is loaded so both share one HIP runtime.  There
+is no fallback: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libivfpq.so")
+
+OK, E_INVALID_ARG, E_IO, E_FORMAT, E_NO_DEVICE, E_OUT_OF_MEMORY, E_DEVICE = range(7)
+LUT_F32, LUT_F16 = 0, 1
+MODE_NORMAL, MODE_SCAN_ONLY = 0, 1
+
+
+class IVFPQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class SearchParams(ctypes.Structure):
+    _fields_ = [("nprobe", ctypes.c_int32), ("k", ctypes.c_int32), ("lut", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("nlist", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("nbits", ctypes.c_int32), ("ntotal", ctypes.c_int64),
+                ("max_list", ctypes.c_int64), ("device", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("device_bytes", ctypes.c_int64)]
+
+
+class HostIndexStruct(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("nlist", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("nbits", ctypes.c_int32), ("ntotal", ctypes.c_int64),
+                ("centroids", ctypes.c_void_p), ("codebooks", ctypes.c_void_p),
+                ("list_sizes", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("ids", ctypes.c_void_p)]
+
+
+class Timings(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("coarse_ms", ctypes.c_double), ("worklist_ms", ctypes.c_double),
+                ("scan_ms", ctypes.c_double), ("merge_ms", ctypes.c_double),
+                ("total_ms", ctypes.c_double), ("scanned_entries", ctypes.c_int64),
+                ("work_items", ctypes.c_int64)]
+
+
+EXPORTS = ("ivfpq_validate_index_file", "ivfpq_validate_host_index", "ivfpq_load_index",
+           "ivfpq_load_index_host", "ivfpq_free_index", "ivfpq_index_info", "ivfpq_search",
+           "ivfpq_search_ex", "ivfpq_coarse_ex", "ivfpq_compute_luts_ex", "ivfpq_select_topk_ex",
+           "ivfpq_profile_begin",
+           "ivfpq_profile_end", "ivfpq_last_error", "ivfpq_status_string")
+
+_lib = None
+
+
+def lib():
+    """Load libivfpq.so (built in-tree by build_lib.py); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(the IVF-PQ search has no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        st = ctypes.c_int
+        sig = {
+            "ivfpq_validate_index_file": ([ctypes.c_char_p], st),
+            "ivfpq_validate_host_index": ([P], st),
+            "ivfpq_load_index": ([ctypes.c_char_p, i32, P], st),
+            "ivfpq_load_index_host": ([P, i32, P], st),
+            "ivfpq_free_index": ([P], None),
+            "ivfpq_index_info": ([P, P], st),
+            "ivfpq_search": ([P, P, i64, i32, i32, P, P], st),
+            "ivfpq_search_ex": ([P, P, P, i64, P, P, P, P], st),
+            "ivfpq_coarse_ex": ([P, P, i64, i32, P, P, P], st),
+            "ivfpq_compute_luts_ex": ([P, P, i64, P, i32, i32, P, P], st),
+            "ivfpq_select_topk_ex": ([P, i64, i64, i32, P, P, P], st),
+            "ivfpq_profile_begin": ([P, i32], st),
+            "ivfpq_profile_end": ([P, P], st),
+            "ivfpq_last_error": ([], ctypes.c_char_p),
+            "ivfpq_status_string": ([i32], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise IVFPQError(status, lib().ivfpq_last_error().decode())
+
+
+def ivfpq_last_error() -> str:
+    return lib().ivfpq_last_error().decode()
+
+
+def ivfpq_status_string(status: int) -> str:
+    return lib().ivfpq_status_string(status).decode()
+
+
+def ivfpq_validate_index_file(path: str) -> int:
+    """Host-only validation; returns the status code (0 = valid)."""
+    return lib().ivfpq_validate_index_file(os.fsencode(path))
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _host_struct(index, keep: list) -> HostIndexStruct:
+    get = (lambda n: index[n]) if isinstance(index, dict) else (lambda n: getattr(index, n))
+    cent = np.ascontiguousarray(get("centroids"), dtype=np.float32)
+    books = np.ascontiguousarray(get("codebooks"), dtype=np.float32)
+    sizes = np.ascontiguousarray(get("list_sizes"), dtype=np.int64)
+    codes = np.ascontiguousarray(get("codes"), dtype=np.uint8)
+    ids = np.ascontiguousarray(get("ids"), dtype=np.int64)
+    keep.extend([cent, books, sizes, codes, ids])
+    s = HostIndexStruct()
+    s.d, s.nlist = cent.shape[1], cent.shape[0]
+    s.m = books.shape[0]
+    s.nbits = 8
+    s.ntotal = codes.shape[0]
+    s.centroids, s.codebooks, s.list_sizes = _np_ptr(cent), _np_ptr(books), _np_ptr(sizes)
+    s.codes, s.ids = _np_ptr(codes), _np_ptr(ids)
+    return s
+
+
+def ivfpq_validate_host_index(index) -> int:
+    keep: list = []
+    s = _host_struct(index, keep)
+    return lib().ivfpq_validate_host_index(ctypes.byref(s))
+
+
+class Index:
+    """Owner of a device index handle."""
+
+    def __init__(self, handle: ctypes.c_void_p):
+        self._h = handle
+        self.info = ivfpq_index_info(self)
+
+    @property
+    def handle(self):
+        if not self._h:
+            raise ValueError("index is closed")
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().ivfpq_free_index(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def search(self, queries, nprobe, k, **kw):
+        return ivfpq_search_ex(self, queries, nprobe, k, **kw)
+
+
+def ivfpq_load_index(path: str, device: int = 0) -> Index:
+    h = ctypes.c_void_p()
+    _check(lib().ivfpq_load_index(os.fsencode(path), device, ctypes.byref(h)))
+    return Index(h)
+
+
+def ivfpq_load_index_host(index, device: int = 0) -> Index:
+    keep: list = []
+    s = _host_struct(index, keep)
+    h = ctypes.c_void_p()
+    _check(lib().ivfpq_load_index_host(ctypes.byref(s), device, ctypes.byref(h)))
+    return Index(h)
+
+
+def ivfpq_free_index(index: Index) -> None:
+    index.close()
+
+
+def ivfpq_index_info(index: Index) -> dict:
+    i = Info()
+    _check(lib().ivfpq_index_info(index.handle, ctypes.byref(i)))
+    return {f: getattr(i, f) for f, _ in Info._fields_ if f != "reserved"}
+
+
+def ivfpq_search(index: Index, queries: np.ndarray, nprobe: int, k: int):
+    """Blocking search on host arrays; returns (distances float32, ids int64)."""
+    q = np.ascontiguousarray(queries, dtype=np.float32)
+    nq = q.shape[0]
+    d = np.empty((nq, k), dtype=np.float32)
+    i = np.empty((nq, k), dtype=np.int64)
+    _check(lib().ivfpq_search(index.handle, _np_ptr(q), nq, nprobe, k, _np_ptr(d), _np_ptr(i)))
+    return d, i
+
+
+def _dev(t: torch.Tensor, dtype) -> torch.Tensor:
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"expected a contiguous {dtype} device tensor")
+    return t
+
+
+def _stream_ptr(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def ivfpq_search_ex(index: Index, queries: torch.Tensor, nprobe: int, k: int, lut: str = "f32",
+                    mode: int = MODE_NORMAL, chunk_len: int = 0, return_probes: bool = False,
+                    out=None, stream=None):
+    """Asynchronous device search on the current (or given) torch stream.
+
+    Returns (distances [nq,k] float32, ids [nq,k] int64[, probes [nq,nprobe] int32])."""
+    q = _dev(queries, torch.float32)
+    nq = q.shape[0]
+    if out is None:
+        dist = torch.empty((nq, k), dtype=torch.float32, device=q.device)
+        ids = torch.empty((nq, k), dtype=torch.int64, device=q.device)
+        probes = torch.empty((nq, nprobe), dtype=torch.int32, device=q.device) \
+            if return_probes else None
+    else:
+        dist, ids, probes = out
+    p = SearchParams(nprobe, k, LUT_F16 if lut == "f16" else LUT_F32, mode, chunk_len, 0)
+    _check(lib().ivfpq_search_ex(index.handle, ctypes.byref(p), ctypes.c_void_p(q.data_ptr()),
+                                 nq, ctypes.c_void_p(dist.data_ptr()),
+                                 ctypes.c_void_p(ids.data_ptr()),
+                                 ctypes.c_void_p(probes.data_ptr() if probes is not None else 0),
+                                 _stream_ptr(stream)))
+    return (dist, ids, probes) if return_probes else (dist, ids)
+
+
+def ivfpq_coarse_ex(index: Index, queries: torch.Tensor, nprobe: int, stream=None):
+    q = _dev(queries, torch.float32)
+    nq = q.shape[0]
+    probes = torch.empty((nq, nprobe), dtype=torch.int32, device=q.device)
+    dist = torch.empty((nq, nprobe), dtype=torch.float32, device=q.device)
+    _check(lib().ivfpq_coarse_ex(index.handle, ctypes.c_void_p(q.data_ptr()), nq, nprobe,
+                                 ctypes.c_void_p(probes.data_ptr()),
+                                 ctypes.c_void_p(dist.data_ptr()), _stream_ptr(stream)))
+    return probes, dist
+
+
+def ivfpq_compute_luts_ex(index: Index, queries: torch.Tensor, probes: torch.Tensor,
+                          lut: str = "f32", stream=None):
+    q = _dev(queries, torch.float32)
+    pr = _dev(probes, torch.int32)
+    nq, nprobe = pr.shape
+    m = index.info["m"]
+    out = torch.empty((nq, nprobe, m, 256), dtype=torch.float32, device=q.device)
+    _check(lib().ivfpq_compute_luts_ex(index.handle, ctypes.c_void_p(q.data_ptr()), nq,
+                                       ctypes.c_void_p(pr.data_ptr()), nprobe,
+                                       LUT_F16 if lut == "f16" else LUT_F32,
+                                       ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)))
+    return out
+
+
+def ivfpq_select_topk_ex(keys: torch.Tensor, k: int, stream=None):
+    """Row-wise k smallest of a [rows, n] float32 device tensor:
+    (values [rows,k] float32, column numbers [rows,k] int32)."""
+    x = _dev(keys, torch.float32)
+    rows, n = x.shape
+    d = torch.empty((rows, k), dtype=torch.float32, device=x.device)
+    p = torch.empty((rows, k), dtype=torch.int32, device=x.device)
+    _check(lib().ivfpq_select_topk_ex(ctypes.c_void_p(x.data_ptr()), rows, n, k,
+                                      ctypes.c_void_p(d.data_ptr()), ctypes.c_void_p(p.data_ptr()),
+                                      _stream_ptr(stream)))
+    return d, p
+
+
+def ivfpq_profile_begin(index: Index, max_calls: int) -> None:
+    _check(lib().ivfpq_profile_begin(index.handle, max_calls))
+
+
+def ivfpq_profile_end(index: Index) -> dict:
+    t = Timings()
+    _check(lib().ivfpq_profile_end(index.handle, ctypes.byref(t)))
+    return {f: getattr(t, f) for f, _ in Timings._fields_ if f != "reserved"}

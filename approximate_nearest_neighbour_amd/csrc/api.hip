@@ -1,0 +1,695 @@
+// C-ABI host side of the IVF-PQ library: argument and file validation (host
+// only), index upload, workspace, kernel sequencing on the caller's stream,
+// per-kernel event timing.  Declarations and conventions: include/ivfpq.h.
+#include "../../include/ivfpq.h"
+#include "internal.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+using namespace ivfpq;
+
+namespace {
+
+thread_local std::string g_err;
+
+ivfpq_status fail(ivfpq_status s, const std::string &msg)
+{
+    g_err = msg;
+    return s;
+}
+
+ivfpq_status ok()
+{
+    g_err.clear();
+    return IVFPQ_OK;
+}
+
+// Test hook: IVFPQ_TEST_FAIL_ALLOC=n makes the n-th device allocation of the
+// process fail (1-based), to exercise the out-of-memory paths.
+int g_alloc_count = 0;
+
+hipError_t dev_alloc(void **p, size_t bytes)
+{
+    const char *env = std::getenv("IVFPQ_TEST_FAIL_ALLOC");
+    ++g_alloc_count;
+    if (env && std::atoi(env) == g_alloc_count) {
+        *p = nullptr;
+        return hipErrorOutOfMemory;
+    }
+    return hipMalloc(p, bytes ? bytes : 1);
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) != hipSuccess)
+            prev = -1;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard()
+    {
+        if (prev >= 0)
+            (void)hipSetDevice(prev);
+    }
+};
+
+struct EventPair {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+constexpr int kStages = 4; // coarse, worklist, scan, merge
+
+} // namespace
+
+struct ivfpq_index {
+    int device = 0;
+    DeviceIndex dx;
+    int64_t device_bytes = 0;
+    // workspace
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    // profiling
+    bool profiling = false;
+    int prof_max = 0;
+    int prof_calls = 0;
+    int64_t prof_entries = 0;
+    int64_t prof_items = 0;
+    std::vector<EventPair> prof_events; // [call][stage]
+    std::vector<int> prof_used;         // [call][stage] 0/1
+    std::vector<uint32_t> host_off;     // list offsets (host copy)
+};
+
+namespace {
+
+ivfpq_status check_shape(int64_t d, int64_t nlist, int64_t m, int64_t nbits, int64_t ntotal)
+{
+    if (d < 1 || d > 1024)
+        return fail(IVFPQ_E_FORMAT, "d must be in [1, 1024]");
+    if (nlist < 1 || nlist > (1 << 30))
+        return fail(IVFPQ_E_FORMAT, "nlist must be in [1, 2^30]");
+    if (m < 1 || m > 64 || d % m)
+        return fail(IVFPQ_E_FORMAT, "m must be in [1, 64] and divide d");
+    if (nbits != 8)
+        return fail(IVFPQ_E_FORMAT, "only 8-bit sub-quantizer codes are supported");
+    if (ntotal < 0 || ntotal >= (int64_t)0xFFFFFFFFll)
+        return fail(IVFPQ_E_FORMAT, "ntotal must be below 2^32 - 1");
+    return IVFPQ_OK;
+}
+
+ivfpq_status check_sizes(const int64_t *sizes, int64_t nlist, int64_t ntotal, int64_t *max_list)
+{
+    int64_t sum = 0, mx = 0;
+    for (int64_t l = 0; l < nlist; ++l) {
+        if (sizes[l] < 0)
+            return fail(IVFPQ_E_FORMAT, "negative list size");
+        sum += sizes[l];
+        mx = sizes[l] > mx ? sizes[l] : mx;
+        if (sum > ntotal)
+            return fail(IVFPQ_E_FORMAT, "list sizes exceed ntotal");
+    }
+    if (sum != ntotal)
+        return fail(IVFPQ_E_FORMAT, "list sizes do not add up to ntotal");
+    if (max_list)
+        *max_list = mx;
+    return IVFPQ_OK;
+}
+
+struct FileHeader {
+    char magic[8];
+    uint32_t d, nlist, m, nbits;
+    uint64_t ntotal;
+};
+static_assert(sizeof(FileHeader) == 32, "header layout");
+
+size_t body_bytes(const FileHeader &h)
+{
+    const size_t dsub = h.d / h.m;
+    return (size_t)h.nlist * h.d * 4 + (size_t)h.m * 256 * dsub * 4 + (size_t)h.nlist * 8 +
+           (size_t)h.ntotal * h.m + (size_t)h.ntotal * 8;
+}
+
+ivfpq_status read_header(FILE *f, FileHeader *h)
+{
+    if (std::fread(h, sizeof *h, 1, f) != 1)
+        return fail(IVFPQ_E_FORMAT, "truncated header");
+    if (std::memcmp(h->magic, "IVFPQ01\0", 8) != 0)
+        return fail(IVFPQ_E_FORMAT, "bad magic");
+    ivfpq_status s = check_shape(h->d, h->nlist, h->m, h->nbits, (int64_t)h->ntotal);
+    if (s)
+        return s;
+    if (std::fseek(f, 0, SEEK_END) != 0)
+        return fail(IVFPQ_E_IO, "cannot seek");
+    const long end = std::ftell(f);
+    if (end < 0)
+        return fail(IVFPQ_E_IO, "cannot tell file size");
+    if ((size_t)end != sizeof *h + body_bytes(*h))
+        return fail(IVFPQ_E_FORMAT, (size_t)end < sizeof *h + body_bytes(*h)
+                                        ? "truncated index file"
+                                        : "trailing bytes after the index body");
+    if (std::fseek(f, sizeof *h, SEEK_SET) != 0)
+        return fail(IVFPQ_E_IO, "cannot seek");
+    return IVFPQ_OK;
+}
+
+void release(ivfpq_index *ix)
+{
+    if (!ix)
+        return;
+    DeviceGuard g(ix->device);
+    DeviceIndex &d = ix->dx;
+    (void)hipFree(d.centroids);
+    (void)hipFree(d.cnorms);
+    (void)hipFree(d.codebooks);
+    (void)hipFree(d.list_off);
+    (void)hipFree(d.codes);
+    (void)hipFree(d.ids);
+    (void)hipFree(ix->ws);
+    for (auto &e : ix->prof_events) {
+        if (e.start)
+            (void)hipEventDestroy(e.start);
+        if (e.stop)
+            (void)hipEventDestroy(e.stop);
+    }
+    delete ix;
+}
+
+ivfpq_status device_check(int device)
+{
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n < 1)
+        return fail(IVFPQ_E_NO_DEVICE, "no GPU available");
+    if (device < 0 || device >= n)
+        return fail(IVFPQ_E_NO_DEVICE, "device number out of range");
+    return IVFPQ_OK;
+}
+
+#define ALLOC_OR_FAIL(ptr, bytes)                                                              \
+    do {                                                                                       \
+        if (dev_alloc(reinterpret_cast<void **>(&(ptr)), (bytes)) != hipSuccess) {             \
+            (void)hipGetLastError();                                                           \
+            release(ix);                                                                       \
+            return fail(IVFPQ_E_OUT_OF_MEMORY, "device allocation failed");                    \
+        }                                                                                      \
+        ix->device_bytes += (int64_t)(bytes);                                                  \
+    } while (0)
+
+#define COPY_OR_FAIL(dst, src, bytes)                                                          \
+    do {                                                                                       \
+        if (hipMemcpy((dst), (src), (bytes), hipMemcpyHostToDevice) != hipSuccess) {           \
+            release(ix);                                                                       \
+            return fail(IVFPQ_E_DEVICE, "host to device copy failed");                         \
+        }                                                                                      \
+    } while (0)
+
+// Allocate the device index; the caller fills it.
+ivfpq_status alloc_index(int device, int d, int nlist, int m, int64_t ntotal,
+                         const int64_t *sizes, ivfpq_index **out)
+{
+    ivfpq_index *ix = new (std::nothrow) ivfpq_index();
+    if (!ix)
+        return fail(IVFPQ_E_OUT_OF_MEMORY, "host allocation failed");
+    ix->device = device;
+    DeviceIndex &dx = ix->dx;
+    dx.d = d;
+    dx.nlist = nlist;
+    dx.m = m;
+    dx.ntotal = ntotal;
+    ix->host_off.resize((size_t)nlist + 1);
+    ix->host_off[0] = 0;
+    int64_t mx = 0;
+    for (int l = 0; l < nlist; ++l) {
+        ix->host_off[l + 1] = ix->host_off[l] + (uint32_t)sizes[l];
+        mx = sizes[l] > mx ? sizes[l] : mx;
+    }
+    dx.max_list = mx;
+    ALLOC_OR_FAIL(dx.centroids, (size_t)nlist * d * 4);
+    ALLOC_OR_FAIL(dx.cnorms, (size_t)nlist * 4);
+    ALLOC_OR_FAIL(dx.codebooks, (size_t)d * 256 * 4);
+    ALLOC_OR_FAIL(dx.list_off, ((size_t)nlist + 1) * 4);
+    ALLOC_OR_FAIL(dx.codes, (size_t)ntotal * m);
+    ALLOC_OR_FAIL(dx.ids, (size_t)ntotal * 8);
+    COPY_OR_FAIL(dx.list_off, ix->host_off.data(), ((size_t)nlist + 1) * 4);
+    *out = ix;
+    return IVFPQ_OK;
+}
+
+ivfpq_status finish_load(ivfpq_index *ix)
+{
+    if (launch_cnorms(ix->dx, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        release(ix);
+        return fail(IVFPQ_E_DEVICE, "centroid norm kernel failed");
+    }
+    return IVFPQ_OK;
+}
+
+ivfpq_status ensure_ws(ivfpq_index *ix, size_t bytes)
+{
+    if (bytes <= ix->ws_bytes)
+        return IVFPQ_OK;
+    if (ix->ws) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(ix->ws);
+        ix->ws = nullptr;
+        ix->ws_bytes = 0;
+    }
+    if (dev_alloc(&ix->ws, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        ix->ws = nullptr;
+        return fail(IVFPQ_E_OUT_OF_MEMORY, "workspace allocation failed");
+    }
+    ix->ws_bytes = bytes;
+    return IVFPQ_OK;
+}
+
+ivfpq_status check_params(const ivfpq_index *ix, const ivfpq_search_params *p, int64_t nq)
+{
+    if (!ix)
+        return fail(IVFPQ_E_INVALID_ARG, "index handle is NULL");
+    if (!p)
+        return fail(IVFPQ_E_INVALID_ARG, "params is NULL");
+    if (nq < 0 || nq > (int64_t)0x7FFFFFFF)
+        return fail(IVFPQ_E_INVALID_ARG, "nq must be in [0, 2^31)");
+    if (p->nprobe < 1 || p->nprobe > ix->dx.nlist)
+        return fail(IVFPQ_E_INVALID_ARG, "nprobe must be in [1, nlist]");
+    if (p->nprobe > kMaxK)
+        return fail(IVFPQ_E_INVALID_ARG, "nprobe above 1024 is not supported");
+    if (p->k < 1 || p->k > kMaxK)
+        return fail(IVFPQ_E_INVALID_ARG, "k must be in [1, 1024]");
+    if (p->lut != IVFPQ_LUT_F32 && p->lut != IVFPQ_LUT_F16)
+        return fail(IVFPQ_E_INVALID_ARG, "unknown table type");
+    if (p->mode != IVFPQ_MODE_NORMAL && p->mode != IVFPQ_MODE_SCAN_ONLY)
+        return fail(IVFPQ_E_INVALID_ARG, "unknown mode");
+    if (p->chunk_len < 0)
+        return fail(IVFPQ_E_INVALID_ARG, "chunk_len must be >= 0");
+    return IVFPQ_OK;
+}
+
+void prof_record(ivfpq_index *ix, int stage, bool start, hipStream_t s)
+{
+    if (!ix->profiling || ix->prof_calls >= ix->prof_max)
+        return;
+    EventPair &e = ix->prof_events[(size_t)ix->prof_calls * kStages + stage];
+    (void)hipEventRecord(start ? e.start : e.stop, s);
+    if (!start)
+        ix->prof_used[(size_t)ix->prof_calls * kStages + stage] = 1;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *ivfpq_last_error(void) { return g_err.c_str(); }
+
+const char *ivfpq_status_string(ivfpq_status s)
+{
+    switch (s) {
+    case IVFPQ_OK: return "ok";
+    case IVFPQ_E_INVALID_ARG: return "invalid argument";
+    case IVFPQ_E_IO: return "i/o error";
+    case IVFPQ_E_FORMAT: return "malformed index";
+    case IVFPQ_E_NO_DEVICE: return "no device";
+    case IVFPQ_E_OUT_OF_MEMORY: return "out of memory";
+    case IVFPQ_E_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+ivfpq_status ivfpq_validate_index_file(const char *path)
+{
+    if (!path)
+        return fail(IVFPQ_E_INVALID_ARG, "path is NULL");
+    FILE *f = std::fopen(path, "rb");
+    if (!f)
+        return fail(IVFPQ_E_IO, std::string("cannot open ") + path);
+    FileHeader h;
+    ivfpq_status s = read_header(f, &h);
+    if (s) {
+        std::fclose(f);
+        return s;
+    }
+    // list sizes must add up to ntotal
+    const long sizes_at = (long)(sizeof h + (size_t)h.nlist * h.d * 4 + (size_t)h.d * 256 * 4);
+    std::vector<int64_t> sizes(h.nlist);
+    if (std::fseek(f, sizes_at, SEEK_SET) != 0 ||
+        std::fread(sizes.data(), 8, h.nlist, f) != h.nlist) {
+        std::fclose(f);
+        return fail(IVFPQ_E_IO, "cannot read list sizes");
+    }
+    std::fclose(f);
+    s = check_sizes(sizes.data(), h.nlist, (int64_t)h.ntotal, nullptr);
+    return s ? s : ok();
+}
+
+ivfpq_status ivfpq_validate_host_index(const ivfpq_host_index *src)
+{
+    if (!src)
+        return fail(IVFPQ_E_INVALID_ARG, "source is NULL");
+    ivfpq_status s = check_shape(src->d, src->nlist, src->m, src->nbits, src->ntotal);
+    if (s)
+        return s;
+    if (!src->centroids || !src->codebooks || !src->list_sizes ||
+        (src->ntotal > 0 && (!src->codes || !src->ids)))
+        return fail(IVFPQ_E_INVALID_ARG, "a required array is NULL");
+    s = check_sizes(src->list_sizes, src->nlist, src->ntotal, nullptr);
+    return s ? s : ok();
+}
+
+ivfpq_status ivfpq_load_index_host(const ivfpq_host_index *src, int device, ivfpq_index **out)
+{
+    if (!out)
+        return fail(IVFPQ_E_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    ivfpq_status s = ivfpq_validate_host_index(src);
+    if (s)
+        return s;
+    if ((s = device_check(device)))
+        return s;
+    DeviceGuard g(device);
+    if (!g.ok)
+        return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
+    ivfpq_index *ix = nullptr;
+    if ((s = alloc_index(device, src->d, src->nlist, src->m, src->ntotal, src->list_sizes, &ix)))
+        return s;
+    DeviceIndex &dx = ix->dx;
+    COPY_OR_FAIL(dx.centroids, src->centroids, (size_t)src->nlist * src->d * 4);
+    COPY_OR_FAIL(dx.codebooks, src->codebooks, (size_t)src->d * 256 * 4);
+    if (src->ntotal > 0) {
+        COPY_OR_FAIL(dx.codes, src->codes, (size_t)src->ntotal * src->m);
+        COPY_OR_FAIL(dx.ids, src->ids, (size_t)src->ntotal * 8);
+    }
+    if ((s = finish_load(ix)))
+        return s;
+    *out = ix;
+    return ok();
+}
+
+ivfpq_status ivfpq_load_index(const char *path, int device, ivfpq_index **out)
+{
+    if (!out)
+        return fail(IVFPQ_E_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    ivfpq_status s = ivfpq_validate_index_file(path);
+    if (s)
+        return s;
+    if ((s = device_check(device)))
+        return s;
+    FILE *f = std::fopen(path, "rb");
+    if (!f)
+        return fail(IVFPQ_E_IO, "cannot open index file");
+    FileHeader h;
+    if ((s = read_header(f, &h))) {
+        std::fclose(f);
+        return s;
+    }
+    const int d = (int)h.d, nlist = (int)h.nlist, m = (int)h.m;
+    const int64_t ntotal = (int64_t)h.ntotal;
+    std::vector<float> cent((size_t)nlist * d), books((size_t)d * 256);
+    std::vector<int64_t> sizes(nlist);
+    bool rd = std::fread(cent.data(), 4, cent.size(), f) == cent.size() &&
+              std::fread(books.data(), 4, books.size(), f) == books.size() &&
+              std::fread(sizes.data(), 8, sizes.size(), f) == sizes.size();
+    if (!rd) {
+        std::fclose(f);
+        return fail(IVFPQ_E_IO, "cannot read index header arrays");
+    }
+    DeviceGuard g(device);
+    if (!g.ok) {
+        std::fclose(f);
+        return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
+    }
+    ivfpq_index *ix = nullptr;
+    if ((s = alloc_index(device, d, nlist, m, ntotal, sizes.data(), &ix))) {
+        std::fclose(f);
+        return s;
+    }
+    DeviceIndex &dx = ix->dx;
+    COPY_OR_FAIL(dx.centroids, cent.data(), cent.size() * 4);
+    COPY_OR_FAIL(dx.codebooks, books.data(), books.size() * 4);
+    // stream codes and ids in chunks (the big arrays never sit whole in host memory)
+    const size_t chunk = (size_t)256 << 20;
+    std::vector<unsigned char> buf(chunk);
+    const size_t parts[2] = {(size_t)ntotal * m, (size_t)ntotal * 8};
+    unsigned char *dsts[2] = {dx.codes, reinterpret_cast<unsigned char *>(dx.ids)};
+    for (int a = 0; a < 2; ++a) {
+        for (size_t o = 0; o < parts[a]; o += chunk) {
+            const size_t n = parts[a] - o < chunk ? parts[a] - o : chunk;
+            if (std::fread(buf.data(), 1, n, f) != n) {
+                std::fclose(f);
+                release(ix);
+                return fail(IVFPQ_E_IO, "cannot read codes or ids");
+            }
+            if (hipMemcpy(dsts[a] + o, buf.data(), n, hipMemcpyHostToDevice) != hipSuccess) {
+                std::fclose(f);
+                release(ix);
+                return fail(IVFPQ_E_DEVICE, "host to device copy failed");
+            }
+        }
+    }
+    std::fclose(f);
+    if ((s = finish_load(ix)))
+        return s;
+    *out = ix;
+    return ok();
+}
+
+void ivfpq_free_index(ivfpq_index *idx) { release(idx); }
+
+ivfpq_status ivfpq_index_info(const ivfpq_index *idx, ivfpq_info *out)
+{
+    if (!idx || !out)
+        return fail(IVFPQ_E_INVALID_ARG, "NULL argument");
+    std::memset(out, 0, sizeof *out);
+    out->d = idx->dx.d;
+    out->nlist = idx->dx.nlist;
+    out->m = idx->dx.m;
+    out->nbits = 8;
+    out->ntotal = idx->dx.ntotal;
+    out->max_list = idx->dx.max_list;
+    out->device = idx->device;
+    out->device_bytes = idx->device_bytes;
+    return ok();
+}
+
+ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params *p,
+                             const float *queries_dev, int64_t nq, float *distances_dev,
+                             int64_t *ids_dev, int32_t *probes_dev, void *stream)
+{
+    ivfpq_index *idx = const_cast<ivfpq_index *>(cidx);
+    ivfpq_status s = check_params(idx, p, nq);
+    if (s)
+        return s;
+    if (nq == 0)
+        return ok();
+    if (!queries_dev || !distances_dev || (!ids_dev && p->mode == IVFPQ_MODE_NORMAL))
+        return fail(IVFPQ_E_INVALID_ARG, "a required device pointer is NULL");
+    DeviceGuard g(idx->device);
+    if (!g.ok)
+        return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    int32_t *probes = probes_dev;
+    if (!probes) {
+        if ((s = ensure_ws(idx, (size_t)nq * p->nprobe * 4)))
+            return s;
+        probes = reinterpret_cast<int32_t *>(idx->ws);
+    }
+    prof_record(idx, 0, true, st);
+    hipError_t e = launch_coarse(idx->dx, queries_dev, nq, p->nprobe, probes, nullptr, st);
+    prof_record(idx, 0, false, st);
+    if (e != hipSuccess)
+        return fail(IVFPQ_E_DEVICE, std::string("coarse kernel: ") + hipGetErrorString(e));
+    SearchArgs a;
+    a.queries = queries_dev;
+    a.nq = nq;
+    a.nprobe = p->nprobe;
+    a.k = p->k;
+    a.lut = p->lut;
+    a.mode = p->mode;
+    a.chunk_len = p->chunk_len;
+    a.out_d = distances_dev;
+    a.out_i = ids_dev;
+    a.probes = probes;
+    a.probe_d = nullptr;
+    prof_record(idx, 2, true, st);
+    e = launch_scan(idx->dx, a, st);
+    prof_record(idx, 2, false, st);
+    if (e != hipSuccess)
+        return fail(IVFPQ_E_DEVICE, std::string("scan kernel: ") + hipGetErrorString(e));
+    if (idx->profiling && idx->prof_calls < idx->prof_max) {
+        idx->prof_calls++;
+        idx->prof_items += nq;
+    }
+    return ok();
+}
+
+ivfpq_status ivfpq_search(const ivfpq_index *idx, const float *queries, int64_t nq, int nprobe,
+                          int k, float *distances, int64_t *ids)
+{
+    ivfpq_search_params p;
+    std::memset(&p, 0, sizeof p);
+    p.nprobe = nprobe;
+    p.k = k;
+    ivfpq_status s = check_params(idx, &p, nq);
+    if (s)
+        return s;
+    if (nq == 0)
+        return ok();
+    if (!queries || !distances || !ids)
+        return fail(IVFPQ_E_INVALID_ARG, "a required pointer is NULL");
+    DeviceGuard g(idx->device);
+    if (!g.ok)
+        return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
+    const size_t qb = (size_t)nq * idx->dx.d * 4, db = (size_t)nq * k * 4, ib = (size_t)nq * k * 8;
+    void *buf = nullptr;
+    if (dev_alloc(&buf, qb + db + ib) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(IVFPQ_E_OUT_OF_MEMORY, "device allocation failed");
+    }
+    unsigned char *b = static_cast<unsigned char *>(buf);
+    float *dq = reinterpret_cast<float *>(b);
+    int64_t *di = reinterpret_cast<int64_t *>(b + qb);
+    float *dd = reinterpret_cast<float *>(b + qb + ib);
+    if (hipMemcpy(dq, queries, qb, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(buf);
+        return fail(IVFPQ_E_DEVICE, "query upload failed");
+    }
+    s = ivfpq_search_ex(idx, &p, dq, nq, dd, di, nullptr, nullptr);
+    if (s == IVFPQ_OK) {
+        if (hipStreamSynchronize(nullptr) != hipSuccess ||
+            hipMemcpy(distances, dd, db, hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(ids, di, ib, hipMemcpyDeviceToHost) != hipSuccess)
+            s = fail(IVFPQ_E_DEVICE, "search failed on the device");
+    }
+    (void)hipFree(buf);
+    return s;
+}
+
+ivfpq_status ivfpq_coarse_ex(const ivfpq_index *idx, const float *queries_dev, int64_t nq,
+                             int nprobe, int32_t *probes_dev, float *coarse_dist_dev, void *stream)
+{
+    if (!idx)
+        return fail(IVFPQ_E_INVALID_ARG, "index handle is NULL");
+    if (nq < 0 || nq > (int64_t)0x7FFFFFFF)
+        return fail(IVFPQ_E_INVALID_ARG, "nq must be in [0, 2^31)");
+    if (nprobe < 1 || nprobe > idx->dx.nlist || nprobe > kMaxK)
+        return fail(IVFPQ_E_INVALID_ARG, "nprobe must be in [1, min(nlist, 1024)]");
+    if (nq == 0)
+        return ok();
+    if (!queries_dev || !probes_dev)
+        return fail(IVFPQ_E_INVALID_ARG, "a required device pointer is NULL");
+    DeviceGuard g(idx->device);
+    hipError_t e = launch_coarse(idx->dx, queries_dev, nq, nprobe, probes_dev, coarse_dist_dev,
+                                 reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(IVFPQ_E_DEVICE, std::string("coarse kernel: ") + hipGetErrorString(e));
+    return ok();
+}
+
+ivfpq_status ivfpq_compute_luts_ex(const ivfpq_index *idx, const float *queries_dev, int64_t nq,
+                                   const int32_t *probes_dev, int nprobe, int lut,
+                                   float *luts_dev, void *stream)
+{
+    if (!idx)
+        return fail(IVFPQ_E_INVALID_ARG, "index handle is NULL");
+    if (nq < 0 || nprobe < 1 || nprobe > idx->dx.nlist || nq * (int64_t)nprobe > 0x7FFFFFFF)
+        return fail(IVFPQ_E_INVALID_ARG, "bad nq or nprobe");
+    if (lut != IVFPQ_LUT_F32 && lut != IVFPQ_LUT_F16)
+        return fail(IVFPQ_E_INVALID_ARG, "unknown table type");
+    if (nq == 0)
+        return ok();
+    if (!queries_dev || !probes_dev || !luts_dev)
+        return fail(IVFPQ_E_INVALID_ARG, "a required device pointer is NULL");
+    DeviceGuard g(idx->device);
+    hipError_t e = launch_luts(idx->dx, queries_dev, nq, probes_dev, nprobe, lut, luts_dev,
+                               reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(IVFPQ_E_DEVICE, std::string("table kernel: ") + hipGetErrorString(e));
+    return ok();
+}
+
+ivfpq_status ivfpq_select_topk_ex(const float *keys_dev, int64_t rows, int64_t n, int k,
+                                  float *out_dist_dev, int32_t *out_pos_dev, void *stream)
+{
+    if (rows < 0 || rows > (int64_t)0x7FFFFFFF || n < 0 || n > (int64_t)0xFFFFFFFEll)
+        return fail(IVFPQ_E_INVALID_ARG, "rows must be in [0, 2^31) and n in [0, 2^32 - 1)");
+    if (k < 1 || k > kMaxK)
+        return fail(IVFPQ_E_INVALID_ARG, "k must be in [1, 1024]");
+    if (rows == 0)
+        return ok();
+    if ((!keys_dev && n > 0) || !out_dist_dev || !out_pos_dev)
+        return fail(IVFPQ_E_INVALID_ARG, "a required device pointer is NULL");
+    hipError_t e = launch_select(keys_dev, rows, n, k, out_dist_dev, out_pos_dev,
+                                 reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(IVFPQ_E_DEVICE, std::string("select kernel: ") + hipGetErrorString(e));
+    return ok();
+}
+
+ivfpq_status ivfpq_profile_begin(ivfpq_index *idx, int max_calls)
+{
+    if (!idx || max_calls < 1 || max_calls > 100000)
+        return fail(IVFPQ_E_INVALID_ARG, "bad profile arguments");
+    DeviceGuard g(idx->device);
+    const size_t need = (size_t)max_calls * kStages;
+    while (idx->prof_events.size() < need) {
+        EventPair e;
+        if (hipEventCreate(&e.start) != hipSuccess || hipEventCreate(&e.stop) != hipSuccess)
+            return fail(IVFPQ_E_DEVICE, "event creation failed");
+        idx->prof_events.push_back(e);
+    }
+    idx->prof_used.assign(need, 0);
+    idx->profiling = true;
+    idx->prof_max = max_calls;
+    idx->prof_calls = 0;
+    idx->prof_entries = 0;
+    idx->prof_items = 0;
+    return ok();
+}
+
+ivfpq_status ivfpq_profile_end(ivfpq_index *idx, ivfpq_timings *out)
+{
+    if (!idx || !out)
+        return fail(IVFPQ_E_INVALID_ARG, "NULL argument");
+    DeviceGuard g(idx->device);
+    std::memset(out, 0, sizeof *out);
+    double *slot[kStages] = {&out->coarse_ms, &out->worklist_ms, &out->scan_ms, &out->merge_ms};
+    for (int c = 0; c < idx->prof_calls; ++c) {
+        float first_start = -1.f;
+        hipEvent_t t0 = nullptr, t1 = nullptr;
+        for (int st = 0; st < kStages; ++st) {
+            const size_t i = (size_t)c * kStages + st;
+            if (!idx->prof_used[i])
+                continue;
+            if (hipEventSynchronize(idx->prof_events[i].stop) != hipSuccess)
+                return fail(IVFPQ_E_DEVICE, "event synchronisation failed");
+            float ms = 0.f;
+            (void)hipEventElapsedTime(&ms, idx->prof_events[i].start, idx->prof_events[i].stop);
+            *slot[st] += ms;
+            if (!t0)
+                t0 = idx->prof_events[i].start;
+            t1 = idx->prof_events[i].stop;
+            (void)first_start;
+        }
+        if (t0 && t1) {
+            float ms = 0.f;
+            (void)hipEventElapsedTime(&ms, t0, t1);
+            out->total_ms += ms;
+        }
+    }
+    out->calls = idx->prof_calls;
+    out->scanned_entries = idx->prof_entries;
+    out->work_items = idx->prof_items;
+    idx->profiling = false;
+    return ok();
+}
+
+} // extern "C"

@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI host code (api.hip) and the kernel
+// launchers (kernels_*.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ivfpq {
+
+// Device-resident index.  Positions (row numbers in the list-major code
+// array) are 32-bit: ntotal < 2^32, and 0xFFFFFFFF is the empty sentinel.
+struct DeviceIndex {
+    int d = 0, nlist = 0, m = 0;
+    int64_t ntotal = 0;
+    int64_t max_list = 0;
+    float *centroids = nullptr;  // [nlist][d]
+    float *cnorms = nullptr;     // [nlist] |c_l|^2
+    float *codebooks = nullptr;  // [m][256][dsub]
+    uint32_t *list_off = nullptr; // [nlist + 1]
+    uint8_t *codes = nullptr;    // [ntotal][m]
+    int64_t *ids = nullptr;      // [ntotal]
+};
+
+struct SearchArgs {
+    const float *queries;
+    int64_t nq;
+    int nprobe;
+    int k;
+    int lut;  // 0 = float32 table, 1 = binary16 table
+    int mode; // 0 normal, 1 scan only
+    int chunk_len;
+    float *out_d;
+    int64_t *out_i;
+    int32_t *probes; // [nq][nprobe] (workspace or caller buffer)
+    float *probe_d;  // [nq][nprobe] or nullptr
+};
+
+// Each launcher enqueues on `stream` and returns the launch status.
+hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
+                         int32_t *probes, float *probe_d, hipStream_t stream);
+hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &a, hipStream_t stream);
+hipError_t launch_luts(const DeviceIndex &ix, const float *queries, int64_t nq,
+                       const int32_t *probes, int nprobe, int lut, float *out, hipStream_t stream);
+hipError_t launch_cnorms(const DeviceIndex &ix, hipStream_t stream);
+hipError_t launch_select(const float *keys, int64_t rows, int64_t n, int k, float *out_d,
+                         int32_t *out_pos, hipStream_t stream);
+
+// Largest k / nprobe the selection supports.
+constexpr int kMaxK = 1024;
+
+} // namespace ivfpq

@@ -1,0 +1,185 @@
+// Wave64 register primitives for gfx950: cross-lane exchange and
+// data-independent sorting networks on lane-stride register arrays.
+//
+// Lane-stride array ("Billion-scale similarity search with GPUs", k-selection
+// section, register-array preliminaries): element e of an array of 64*R
+// elements lives in register e / 64 of lane e % 64.  The register index must
+// be a compile-time constant, the lane may be a run-time value.  A
+// compare-exchange between elements e and e ^ s happens inside one lane when
+// s >= 64 (two registers of the same lane) and across lanes otherwise.
+//
+// Cross-lane exchange by distance:
+//   s = 1, 2 : DPP quad_perm (a VALU operand modifier, no LDS traffic)
+//   s = 8    : DPP row_ror:8 (rotation by 8 inside a 16-lane row == xor 8)
+//   s = 4, 16: ds_swizzle bit-mask mode (xor inside 32-lane halves)
+//   s = 32   : ds_bpermute
+// The networks are bitonic: sort of 2^n elements in n(n+1)/2 steps, merge of
+// a bitonic sequence of 2^n elements in n steps.  Every lane executes the same
+// instruction stream whatever the data.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ivfpq {
+
+constexpr uint32_t kSentinel = 0xFFFFFFFFu;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v)
+{
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "lane distance");
+    if constexpr (S == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); // quad_perm 1,0,3,2
+    } else if constexpr (S == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); // quad_perm 2,3,0,1
+    } else if constexpr (S == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); // row_ror:8
+    } else if constexpr (S == 4 || S == 16) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (S << 10));
+    } else {
+        return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, (int)v);
+    }
+}
+
+template <int S>
+__device__ __forceinline__ float xor_lane(float v)
+{
+    return __uint_as_float(xor_lane<S>(__float_as_uint(v)));
+}
+
+// Compare-exchange of (k, v) with the partner lane at distance S.  keep_min
+// says whether this lane keeps the smaller key.  Equal keys never move, so
+// the two lanes always take consistent decisions.
+template <int S>
+__device__ __forceinline__ void cx_lane(float &k, uint32_t &v, bool keep_min)
+{
+    float pk = xor_lane<S>(k);
+    uint32_t pv = xor_lane<S>(v);
+    bool take = keep_min ? (pk < k) : (pk > k);
+    k = take ? pk : k;
+    v = take ? pv : v;
+}
+
+// In-lane compare-exchange between registers (a holds the lower element).
+__device__ __forceinline__ void cx_reg(float &ka, uint32_t &va, float &kb, uint32_t &vb, bool up)
+{
+    bool swap = up ? (kb < ka) : (ka < kb);
+    float tk = ka;
+    uint32_t tv = va;
+    ka = swap ? kb : ka;
+    va = swap ? vb : va;
+    kb = swap ? tk : kb;
+    vb = swap ? tv : vb;
+}
+
+template <int S>
+__device__ __forceinline__ void cx_lane_dispatch(float &k, uint32_t &v, bool keep_min)
+{
+    cx_lane<S>(k, v, keep_min);
+}
+
+__device__ __forceinline__ void cx_lane_rt(int s, float &k, uint32_t &v, bool keep_min)
+{
+    switch (s) {
+    case 1: cx_lane<1>(k, v, keep_min); break;
+    case 2: cx_lane<2>(k, v, keep_min); break;
+    case 4: cx_lane<4>(k, v, keep_min); break;
+    case 8: cx_lane<8>(k, v, keep_min); break;
+    case 16: cx_lane<16>(k, v, keep_min); break;
+    default: cx_lane<32>(k, v, keep_min); break;
+    }
+}
+
+// One step of a bitonic network on an R-register lane-stride array: pairs
+// (e, e ^ S) inside blocks of B elements; a block runs ascending when
+// ((e & B) == 0) != DESC.  B == 0 means "the whole array ascending" (merge).
+template <int R, int B, int S, bool DESC>
+__device__ __forceinline__ void bitonic_step(float (&k)[R], uint32_t (&v)[R])
+{
+    const int lane = lane_id();
+    if constexpr (S >= 64) {
+        constexpr int RS = S / 64;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if ((r & RS) == 0) {
+                const int e = r * 64; // block bit B >= 2S >= 128 sits in the register index
+                const bool up = (B == 0) ? !DESC : (((e & B) == 0) != DESC);
+                cx_reg(k[r], v[r], k[r | RS], v[r | RS], up);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int e = r * 64 + lane;
+            const bool up = (B == 0) ? !DESC : (((e & B) == 0) != DESC);
+            const bool lower = (lane & S) == 0;
+            cx_lane<S>(k[r], v[r], lower == up);
+        }
+    }
+}
+
+// Bitonic merge (half-cleaner chain S = N/2 .. 1) of a bitonic sequence of
+// N = 64 R elements into ascending order.
+template <int R, int S>
+__device__ __forceinline__ void bitonic_merge_steps(float (&k)[R], uint32_t (&v)[R])
+{
+    if constexpr (S >= 1) {
+        bitonic_step<R, 0, S, false>(k, v);
+        bitonic_merge_steps<R, S / 2>(k, v);
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void bitonic_merge_up(float (&k)[R], uint32_t (&v)[R])
+{
+    bitonic_merge_steps<R, 32 * R>(k, v);
+}
+
+// Full bitonic sort of a 64-element single-register array.
+template <int B, int S, bool DESC>
+__device__ __forceinline__ void sort64_steps(float (&k)[1], uint32_t (&v)[1])
+{
+    if constexpr (B <= 64) {
+        if constexpr (S >= 1) {
+            bitonic_step<1, (B == 64 ? 0 : B), S, DESC>(k, v);
+            sort64_steps<B, S / 2, DESC>(k, v);
+        } else {
+            sort64_steps<B * 2, B, DESC>(k, v);
+        }
+    }
+}
+
+template <bool DESC>
+__device__ __forceinline__ void sort64(float &key, uint32_t &val)
+{
+    float k[1] = {key};
+    uint32_t v[1] = {val};
+    sort64_steps<2, 1, DESC>(k, v);
+    key = k[0];
+    val = v[0];
+}
+
+// Order-preserving map of a float to uint32 (for atomic min of thresholds).
+__device__ __forceinline__ uint32_t float_order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float float_from_order_key(uint32_t u)
+{
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int mbcnt64(uint64_t mask)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+} // namespace ivfpq

@@ -1,0 +1,159 @@
+// Register-resident k-selection for one wave64.
+//
+// Follows the structure of WarpSelect ("Billion-scale similarity search with
+// GPUs", k-selection section: a warp queue W of the k smallest values seen,
+// kept sorted ascending in a lane-stride register array, sentinel +inf,
+// values carried with their indices, and a per-step filter that rejects a
+// value that cannot be among the k smallest), re-shaped for wave64:
+//
+//  * The filter threshold is W[k-1] (the k-th smallest so far), optionally
+//    tightened by an external bound (another wave's W[k-1]: its k values
+//    already beat anything above it).  A value >= threshold is dropped.
+//  * Survivors are compacted, in lane order, into a 64-slot candidate buffer
+//    held one element per lane: ballot + mbcnt give each survivor its slot,
+//    one ds_permute over a bijection (survivors to the free slots, the other
+//    lanes to the remaining slots) moves them, all in registers.  This
+//    replaces the per-lane thread queues of the paper: on wave64 it merges
+//    once per 64 survivors instead of whenever one lane's queue fills.
+//  * When the buffer would overflow (and at the end) it is sorted descending
+//    by a 64-element bitonic network, folded into W's last register with an
+//    element-wise min (the first step of a bitonic merge of W with the
+//    reversed buffer keeps exactly the kw smallest), and W is re-sorted by
+//    a bitonic merge (log2(kw) steps).  All of it is data-independent.
+//
+// Invariant: every value seen so far that belongs to the k smallest (ties
+// aside) is in W or in the buffer; W is sorted ascending.
+#pragma once
+
+#include "wave_ops.hpp"
+
+namespace ivfpq {
+
+template <int NW> // W holds kw = 64 * NW elements, kw >= k
+struct WaveTopK {
+    float wk[NW];
+    uint32_t wv[NW];
+    float bk; // candidate buffer, slot = lane
+    uint32_t bv;
+    int bcount; // filled buffer slots (wave-uniform)
+    int k;
+    float kth; // W[k-1] (wave-uniform)
+    float thr; // filter threshold = min(kth, external bound)
+
+    __device__ __forceinline__ void init(int k_)
+    {
+#pragma unroll
+        for (int r = 0; r < NW; ++r) {
+            wk[r] = INFINITY;
+            wv[r] = kSentinel;
+        }
+        bk = INFINITY;
+        bv = kSentinel;
+        bcount = 0;
+        k = k_;
+        kth = INFINITY;
+        thr = INFINITY;
+    }
+
+    __device__ __forceinline__ float read_kth() const
+    {
+        const int e = k - 1;
+        const int lane = e & 63;
+        float out = INFINITY;
+#pragma unroll
+        for (int r = 0; r < NW; ++r)
+            if (r == (e >> 6))
+                out = __uint_as_float(
+                    (uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(wk[r]), lane));
+        return out;
+    }
+
+    // Merge the buffer into W.
+    __device__ __forceinline__ void flush()
+    {
+        if (bcount == 0)
+            return;
+        const int lane = lane_id();
+        if (lane >= bcount) {
+            bk = INFINITY;
+            bv = kSentinel;
+        }
+        sort64<true>(bk, bv);
+        // first step of the bitonic merge of W (ascending) with the buffer
+        // (descending, padded with +inf to kw): keep the element-wise min
+        {
+            const bool take = bk < wk[NW - 1];
+            wk[NW - 1] = take ? bk : wk[NW - 1];
+            wv[NW - 1] = take ? bv : wv[NW - 1];
+        }
+        bitonic_merge_up<NW>(wk, wv);
+        bk = INFINITY;
+        bv = kSentinel;
+        bcount = 0;
+        kth = read_kth();
+        thr = fminf(thr, kth);
+    }
+
+    // Tighten the filter with an external bound (another wave's k-th value).
+    __device__ __forceinline__ void bound(float ext) { thr = fminf(thr, ext); }
+
+    // One candidate per lane; lanes without a candidate pass key = +inf.
+    __device__ __forceinline__ void push(float key, uint32_t val)
+    {
+        bool pass = key < thr;
+        uint64_t mask = wave_ballot(pass);
+        if (mask == 0)
+            return;
+        int n = __popcll(mask);
+        if (bcount + n > 64) {
+            flush();
+            pass = key < thr;
+            mask = wave_ballot(pass);
+            if (mask == 0)
+                return;
+            n = __popcll(mask);
+        }
+        const int lane = lane_id();
+        const int below = mbcnt64(mask);
+        const int slot = pass ? (bcount + below) : ((bcount + n + (lane - below)) & 63);
+        const float nk = __int_as_float(__builtin_amdgcn_ds_permute(slot << 2, __float_as_int(key)));
+        const uint32_t nv = (uint32_t)__builtin_amdgcn_ds_permute(slot << 2, (int)val);
+        const bool fill = lane >= bcount && lane < bcount + n;
+        bk = fill ? nk : bk;
+        bv = fill ? nv : bv;
+        bcount += n;
+    }
+
+    // Write W (kw elements, lane-stride order) to memory.
+    __device__ __forceinline__ void store(float *keys, uint32_t *vals) const
+    {
+        const int lane = lane_id();
+#pragma unroll
+        for (int r = 0; r < NW; ++r) {
+            keys[r * 64 + lane] = wk[r];
+            vals[r * 64 + lane] = wv[r];
+        }
+    }
+
+    // Merge another sorted kw-array (ascending, in memory) into W: the
+    // element-wise min of W and the reversed other array holds the kw
+    // smallest of both and is bitonic; one bitonic merge sorts it.
+    __device__ __forceinline__ void merge_sorted(const float *keys, const uint32_t *vals)
+    {
+        const int lane = lane_id();
+#pragma unroll
+        for (int r = 0; r < NW; ++r) {
+            const int src = (NW - 1 - r) * 64 + (63 - lane);
+            const float ok = keys[src];
+            const uint32_t ov = vals[src];
+            const bool take = ok < wk[r];
+            wk[r] = take ? ok : wk[r];
+            wv[r] = take ? ov : wv[r];
+        }
+        bitonic_merge_up<NW>(wk, wv);
+        kth = read_kth();
+        thr = fminf(thr, kth);
+    }
+};
+
+} // namespace ivfpq

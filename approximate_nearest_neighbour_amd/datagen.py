@@ -90,15 +90,17 @@ def gmm_centers(rng: np.random.Generator, ncomp: int, d: int) -> np.ndarray:
 
 
 def gmm_draw(rng: np.random.Generator, centers: np.ndarray, n: int, sigma: float,
-             chunk: int = 1 << 20) -> np.ndarray:
+             chunk: int = 1 << 16) -> np.ndarray:
     """n points: a uniformly drawn component center plus sigma * N(0, I)."""
     ncomp, d = centers.shape
     out = np.empty((n, d), dtype=np.float32)
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
         comp = rng.integers(0, ncomp, size=e - s)
-        noise = rng.standard_normal((e - s, d), dtype=np.float32)
-        out[s:e] = centers[comp] + np.float32(sigma) * noise
+        blk = out[s:e]
+        rng.standard_normal(out=blk, dtype=np.float32)
+        blk *= np.float32(sigma)
+        blk += centers[comp]
     return out
 
 
@@ -106,17 +108,23 @@ def gmm_draw(rng: np.random.Generator, centers: np.ndarray, n: int, sigma: float
 # index construction (host only)
 # --------------------------------------------------------------------------
 
-def nearest(x: np.ndarray, c: np.ndarray, chunk: int = 1 << 16) -> np.ndarray:
+def nearest(x: np.ndarray, c: np.ndarray, chunk: int = 1 << 13) -> np.ndarray:
     """Index of the nearest row of c for each row of x (ties -> lowest index).
 
     Build-time helper; float32 BLAS with the norm expansion is plenty for
     training and encoding."""
-    cn = (c.astype(np.float32) ** 2).sum(1)
+    c = np.ascontiguousarray(c, dtype=np.float32)
+    cn = (c ** 2).sum(1)
+    ct = np.ascontiguousarray(c.T)
     out = np.empty(len(x), dtype=np.int64)
+    buf = np.empty((min(chunk, max(len(x), 1)), len(c)), dtype=np.float32)
     for s in range(0, len(x), chunk):
         xs = x[s:s + chunk]
-        dist = cn[None, :] - 2.0 * (xs @ c.T)
-        out[s:s + chunk] = np.argmin(dist, axis=1)
+        b = buf[:len(xs)]
+        np.matmul(xs, ct, out=b)
+        b *= np.float32(-2.0)
+        b += cn[None, :]
+        out[s:s + chunk] = np.argmin(b, axis=1)
     return out
 
 

@@ -1,0 +1,179 @@
+"""IVF-PQ search benchmark on one MI355X.
+
+One step = one IVF-PQ search of the whole query batch (coarse top-nprobe,
+per-(query, list) tables, code scan, top-k merged across the lists) with the
+index, queries and outputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--lut f32|f16]
+
+Synthetic data only (seeded Gaussian mixtures, CPU-built index).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "queries/sec at fixed nprobe,k; PQ-code scan GB/s as % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload(name: str):
+    from approximate_nearest_neighbour_amd import datagen as G
+    makers = {"ivfpq_n1m_d128_m16_nlist1024": G.gmm1m, "ivfpq_tiny_n10k_d32_m4": G.tiny,
+              "ivfpq_n10m_d96_m32_nlist4096": G.gmm10m}
+    if name not in makers:
+        raise SystemExit(f"unknown workload {name}; choose from {sorted(makers)}")
+    return makers[name]()
+
+
+def scanned_entries(index, probes: np.ndarray) -> int:
+    return int(index.list_sizes[probes.astype(np.int64)].sum())
+
+
+def cpu_baseline(w, lut_mode, budget_s: float):
+    """The oracle, as it stands, on a bounded leading sample of the queries."""
+    from oracle import oracle as O
+    threads = O.default_threads()
+    probe_n = min(len(w.queries), max(threads, 16))
+    t = time.perf_counter()
+    O.search(w.index, w.queries[:probe_n], w.nprobe, w.k, lut_mode=lut_mode, nthreads=threads)
+    per_q = (time.perf_counter() - t) / probe_n
+    n = int(min(len(w.queries), max(probe_n, budget_s / max(per_q, 1e-9))))
+    t = time.perf_counter()
+    od, oi, op = O.search(w.index, w.queries[:n], w.nprobe, w.k, lut_mode=lut_mode,
+                          nthreads=threads)
+    wall = time.perf_counter() - t
+    return dict(value=n / wall, unit="queries/s", cores=threads, kind="oracle",
+                sample=f"first {n} of {len(w.queries)} queries, full search (fp64), "
+                       f"{wall:.1f} s wall"), (n, od, oi, op)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ivfpq_n1m_d128_m16_nlist1024")
+    ap.add_argument("--lut", choices=["f32", "f16"], default="f32")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--parity-queries", type=int, default=200)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the multi-GPU path (replicas/shards joined by "
+              "one gather) is not built; run with --gpus 1", file=sys.stderr)
+        raise SystemExit(2)
+
+    import torch
+    import approximate_nearest_neighbour_amd as A
+    from oracle import check
+    from oracle import oracle as O
+
+    if not os.path.exists(A.binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    t0 = time.time()
+    w = workload(args.workload)
+    log(f"workload {w.name}: built in {time.time() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    ix = A.ivfpq_load_index_host(w.index, device=0)
+    q = torch.from_numpy(w.queries).to(dev)
+    nq = q.shape[0]
+    out = (torch.empty((nq, w.k), dtype=torch.float32, device=dev),
+           torch.empty((nq, w.k), dtype=torch.int64, device=dev),
+           torch.empty((nq, w.nprobe), dtype=torch.int32, device=dev))
+
+    def step():
+        A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=args.lut, return_probes=True, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    probes = out[2].cpu().numpy()
+    entries = scanned_entries(w.index, probes)
+    code_bytes = entries * w.index.m
+
+    A.ivfpq_profile_begin(ix, args.steps)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t
+    prof = A.ivfpq_profile_end(ix)
+
+    ms_step = 1e3 * elapsed / args.steps
+    scan_ms = prof["scan_ms"] / max(prof["calls"], 1)
+    coarse_ms = prof["coarse_ms"] / max(prof["calls"], 1)
+    achieved = code_bytes / (scan_ms * 1e-3) / 1e9
+    log(f"step {ms_step:.3f} ms  coarse {coarse_ms:.3f} ms  scan {scan_ms:.3f} ms  "
+        f"entries/query {entries / nq:.0f}  code bytes/launch {code_bytes / 1e9:.3f} GB")
+
+    # k-select cost: same scan with the top-k replaced by a running minimum
+    so = (torch.empty((nq, w.k), dtype=torch.float32, device=dev), out[1], out[2])
+    A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=args.lut, mode=1, out=so, return_probes=True)
+    A.ivfpq_profile_begin(ix, args.steps)
+    for _ in range(args.steps):
+        A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=args.lut, mode=1, out=so, return_probes=True)
+    torch.cuda.synchronize()
+    scan_only_ms = A.ivfpq_profile_end(ix)["scan_ms"] / args.steps
+
+    # parity on a sample of the timed configuration
+    step()
+    torch.cuda.synchronize()
+    pn = min(args.parity_queries, nq)
+    lut_mode = O.LUT_F16 if args.lut == "f16" else O.LUT_F64
+    rep = check.compare_search(w.index, w.queries[:pn], w.nprobe, w.k, out[0][:pn].cpu().numpy(),
+                               out[1][:pn].cpu().numpy(), out[2][:pn].cpu().numpy(),
+                               lut_mode=lut_mode)
+    log("parity", rep.summary())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu, _ = cpu_baseline(w, lut_mode, args.cpu_seconds)
+        log("cpu baseline", cpu)
+
+    res = {
+        "metric": METRIC,
+        "value": nq / (ms_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32" if args.lut == "f32" else "fp32 (binary16 tables)",
+        "data": "synthetic (seeded Gaussian mixture, CPU-built IVF-PQ index)",
+        "config": {"workload": w.name, "n": int(w.index.ntotal), "d": w.index.d,
+                   "nlist": w.index.nlist, "m": w.index.m, "nq": nq, "nprobe": w.nprobe,
+                   "k": w.k, "lut": args.lut},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "scan_kernel", "kernel_ms": scan_ms,
+                     "algorithmic_bytes_per_launch": code_bytes},
+        "cpu_baseline": cpu,
+        "stages_ms": {"coarse": coarse_ms, "scan": scan_ms, "scan_only": scan_only_ms,
+                      "kselect_overhead": scan_ms / scan_only_ms - 1 if scan_only_ms else None},
+        "parity": rep.summary(),
+    }
+    print(json.dumps(res), flush=True)
+    ix.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * ivfpq.h - IVF-PQ approximate nearest-neighbour search on one MI355X (gfx950).
+ *
+ * The problem (k-nearest-neighbour search; "Custom 8-bit floating point value
+ * format for reducing shared memory bank conflict in ANN search", problem
+ * statement and IVFPQ section): given a database of N d-dimensional vectors
+ * compressed into an IVF-PQ index and a batch of queries, return for each
+ * query the k database ids with the smallest approximate squared L2 distance
+ *
+ *     R = sum_{j<m} F_j(code_j),  F_j(v) = | r_j - C_j[v] |^2,  r = x - c_l
+ *
+ * (Eq. (1) there), searching only the nprobe inverted lists whose centroids c_l
+ * are closest to the query ("Billion-scale similarity search with GPUs",
+ * IVFADC section).
+ *
+ * Conventions, all calls:
+ *  - every call returns an ivfpq_status; no exception crosses the ABI;
+ *    ivfpq_last_error() gives a message for the last failing call on the
+ *    calling thread;
+ *  - distances are squared L2, smaller is better, each result row sorted
+ *    ascending; a row with fewer than k candidates is padded with
+ *    (+INFINITY, -1);
+ *  - arguments are validated on the host before any device work; on error
+ *    the output buffers are left unspecified;
+ *  - inputs must be finite (documented precondition, not checked);
+ *  - one search at a time per index handle (the handle owns a workspace).
+ *
+ * Index file, version 1 (little-endian):
+ *   char magic[8] = "IVFPQ01\0"; u32 d, nlist, m, nbits (= 8); u64 ntotal;
+ *   f32 centroids[nlist][d]; f32 codebooks[m][256][d/m];
+ *   u64 list_sizes[nlist]; u8 codes[ntotal][m] (list after list, one row of m
+ *   bytes per entry); i64 ids[ntotal] (same order).
+ * Sub-vector j of a residual is dims j*(d/m) .. (j+1)*(d/m)-1.
+ * Limits: 1 <= m <= 64, m divides d, d <= 1024, ntotal < 2^32.
+ */
+#ifndef IVFPQ_H
+#define IVFPQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ivfpq_index ivfpq_index; /* opaque, owned by the library */
+
+typedef enum {
+    IVFPQ_OK = 0,
+    IVFPQ_E_INVALID_ARG = 1, /* a bad argument: range, null pointer, unsupported shape */
+    IVFPQ_E_IO = 2,          /* the index file cannot be opened or read */
+    IVFPQ_E_FORMAT = 3,      /* the index file or host arrays are malformed */
+    IVFPQ_E_NO_DEVICE = 4,   /* no usable GPU, or the device number is out of range */
+    IVFPQ_E_OUT_OF_MEMORY = 5,
+    IVFPQ_E_DEVICE = 6       /* a HIP runtime or kernel launch error */
+} ivfpq_status;
+
+typedef enum { IVFPQ_LUT_F32 = 0, IVFPQ_LUT_F16 = 1 } ivfpq_lut_type;
+
+typedef enum {
+    IVFPQ_MODE_NORMAL = 0,
+    /* benchmark only: the scan computes every distance but keeps just the
+     * per-wave minimum instead of the top-k (measures what the k-select
+     * costs); results are not a valid search */
+    IVFPQ_MODE_SCAN_ONLY = 1
+} ivfpq_mode;
+
+/* Search parameters.  nprobe in [1, nlist]; k in [1, 1024]; lut selects the
+ * table precision (float32, or float32 computed then stored as IEEE binary16
+ * round-to-nearest-even; sums are float32 in both).  chunk_len: maximum
+ * entries one work item scans (0 = automatic). */
+typedef struct {
+    int32_t nprobe;
+    int32_t k;
+    int32_t lut;  /* ivfpq_lut_type */
+    int32_t mode; /* ivfpq_mode */
+    int32_t chunk_len;
+    int32_t reserved;
+} ivfpq_search_params;
+
+typedef struct {
+    int32_t d, nlist, m, nbits;
+    int64_t ntotal;
+    int64_t max_list; /* longest inverted list */
+    int32_t device;
+    int32_t reserved;
+    int64_t device_bytes; /* device memory held by the index */
+} ivfpq_info;
+
+/* Host arrays describing an index (same layout as the file body).  The
+ * library copies them; the caller keeps ownership. */
+typedef struct {
+    int32_t d, nlist, m, nbits;
+    int64_t ntotal;
+    const float *centroids;    /* [nlist][d] */
+    const float *codebooks;    /* [m][256][d/m] */
+    const int64_t *list_sizes; /* [nlist], sum = ntotal */
+    const uint8_t *codes;      /* [ntotal][m], list after list */
+    const int64_t *ids;        /* [ntotal] */
+} ivfpq_host_index;
+
+/* Per-kernel device time, milliseconds, summed over the searches run between
+ * ivfpq_profile_begin and ivfpq_profile_end (HIP events recorded on the
+ * search stream around each kernel). */
+typedef struct {
+    int32_t calls;
+    int32_t reserved;
+    double coarse_ms;   /* coarse distances + top-nprobe */
+    double worklist_ms; /* work-item builder */
+    double scan_ms;     /* LUT + code scan + first-pass select */
+    double merge_ms;    /* cross-item merge + id gather */
+    double total_ms;    /* first kernel start to last kernel end */
+    int64_t scanned_entries; /* entries scanned (sum over calls) */
+    int64_t work_items;      /* scan work items (sum over calls) */
+} ivfpq_timings;
+
+/* Host-only check of an index file's header and size (no GPU needed).
+ * IVFPQ_E_IO if unreadable, IVFPQ_E_FORMAT if malformed or truncated. */
+ivfpq_status ivfpq_validate_index_file(const char *path);
+
+/* Host-only check of host index arrays (no GPU needed). */
+ivfpq_status ivfpq_validate_host_index(const ivfpq_host_index *src);
+
+/* Read an index file and upload it to GPU `device`.  Codes and centroids stay
+ * resident in HBM for the handle's life ("Billion-scale similarity search
+ * with GPUs", multi-GPU/system section: the index lives on the device, only
+ * queries travel).  *out receives the handle. */
+ivfpq_status ivfpq_load_index(const char *path, int device, ivfpq_index **out);
+
+/* As ivfpq_load_index, from host arrays (copied). */
+ivfpq_status ivfpq_load_index_host(const ivfpq_host_index *src, int device, ivfpq_index **out);
+
+/* Release the handle and its device memory.  NULL is allowed. */
+void ivfpq_free_index(ivfpq_index *idx);
+
+ivfpq_status ivfpq_index_info(const ivfpq_index *idx, ivfpq_info *out);
+
+/* Blocking search with host buffers: queries [nq][d] float32 row-major in,
+ * distances [nq][k] float32 and ids [nq][k] int64 out.  Copies queries to the
+ * device and results back (PCIe included).  nq = 0 is a no-op. */
+ivfpq_status ivfpq_search(const ivfpq_index *idx, const float *queries, int64_t nq, int nprobe,
+                          int k, float *distances, int64_t *ids);
+
+/* Asynchronous search with device buffers on `stream` (a hipStream_t; NULL =
+ * the null stream).  queries_dev [nq][d] float32, distances_dev [nq][k] float32,
+ * ids_dev [nq][k] int64; probes_dev, when not NULL, receives the probed list
+ * numbers [nq][nprobe] int32 in ascending coarse distance.  No host
+ * synchronisation happens between the kernels; the call returns once they are
+ * enqueued.  The buffers must stay valid until the stream reaches them. */
+ivfpq_status ivfpq_search_ex(const ivfpq_index *idx, const ivfpq_search_params *params,
+                             const float *queries_dev, int64_t nq, float *distances_dev,
+                             int64_t *ids_dev, int32_t *probes_dev, void *stream);
+
+/* The coarse step alone (device buffers, asynchronous): for each query the
+ * nprobe lists of smallest |x - c_l|^2, ascending: probes_dev [nq][nprobe]
+ * int32 and, when not NULL, coarse_dist_dev [nq][nprobe] float32. */
+ivfpq_status ivfpq_coarse_ex(const ivfpq_index *idx, const float *queries_dev, int64_t nq,
+                             int nprobe, int32_t *probes_dev, float *coarse_dist_dev,
+                             void *stream);
+
+/* The table step alone (device buffers, asynchronous, for verification): for
+ * each query q and each of its nprobe lists probes_dev[q][p], writes the
+ * m x 256 table F_j(v) to luts_dev[q][p][j][v] as float32 (values of the fp16
+ * variant are the binary16 numbers widened to float32). */
+ivfpq_status ivfpq_compute_luts_ex(const ivfpq_index *idx, const float *queries_dev, int64_t nq,
+                                   const int32_t *probes_dev, int nprobe, int lut,
+                                   float *luts_dev, void *stream);
+
+/* The k-selection on its own (device buffers, asynchronous): for each of
+ * `rows` rows of n float32 keys (keys_dev [rows][n]) the k smallest, ascending,
+ * with their column numbers: out_dist_dev [rows][k] float32, out_pos_dev
+ * [rows][k] int32, padded with (+INFINITY, -1) when n < k.  Ties between equal
+ * keys may resolve to any of the tied columns.  ("Billion-scale similarity
+ * search with GPUs", k-selection section: the k least values of a sequence,
+ * their indices carried along.) */
+ivfpq_status ivfpq_select_topk_ex(const float *keys_dev, int64_t rows, int64_t n, int k,
+                                  float *out_dist_dev, int32_t *out_pos_dev, void *stream);
+
+/* Start summing per-kernel times (HIP events on the search stream, no host
+ * synchronisation during searches).  Up to max_calls searches are recorded. */
+ivfpq_status ivfpq_profile_begin(ivfpq_index *idx, int max_calls);
+
+/* Wait for the recorded searches, write the sums to *out, stop recording. */
+ivfpq_status ivfpq_profile_end(ivfpq_index *idx, ivfpq_timings *out);
+
+/* Message for the last failing call on this thread ("" if none); valid until
+ * the next call on this thread. */
+const char *ivfpq_last_error(void);
+
+const char *ivfpq_status_string(ivfpq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IVFPQ_H */

@@ -84,9 +84,11 @@ def check_probes(index, queries, gpu_probes, oracle_probes, report: Report):
     return differ
 
 
-def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None):
+def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None, lookup=None):
     """Rules 2 and 3 for each row; ora_* hold at least k columns (more give
-    the distances of ids just past the k-th)."""
+    the distances of ids just past the k-th).  lookup(row, ids) -> oracle
+    distances (or None where the id is not a candidate) resolves ids past the
+    oracle's columns (deep ties)."""
     rows = range(len(gpu_d)) if rows is None else rows
     for r in rows:
         gd = np.asarray(gpu_d[r], dtype=np.float64)
@@ -113,6 +115,11 @@ def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None)
         if valid_g == 0:
             continue
         dist_of = {int(i): float(v) for i, v in zip(oi, od) if i >= 0}
+        unknown = [int(i) for i in gi[:valid_g] if int(i) not in dist_of]
+        if unknown and lookup is not None:
+            for i, v in zip(unknown, lookup(r, unknown)):
+                if v is not None:
+                    dist_of[i] = float(v)
         kth = float(od[valid_o - 1])
         band = tau * kth
         gset, oset = set(gi[:valid_g].tolist()), set(oi[:valid_o].tolist())
@@ -127,7 +134,10 @@ def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None)
             continue
         report.tie_swaps += len(gset - oset)
         for i, v in zip(gi[:valid_g], gd[:valid_g]):
-            ref = dist_of[int(i)]
+            ref = dist_of.get(int(i))
+            if ref is None:
+                report.failures.append((r, f"id {i} is not a candidate of the probed lists"))
+                break
             err = abs(float(v) - ref)
             if err > tau * abs(ref):
                 report.failures.append((r, f"id {i}: distance {v} vs oracle {ref}"))
@@ -152,5 +162,27 @@ def compare_search(index, queries, nprobe, k, gpu_d, gpu_i, gpu_probes=None, lut
             d2, i2, _ = O.search(index, queries[sub], nprobe, kx, lut_mode=lut_mode,
                                  probes=np.asarray(gpu_probes)[sub], nthreads=nthreads)
             od[sub], oi[sub] = d2, i2
-    check_results(gpu_d, gpu_i, od, oi, k, tau, rep)
+    ids = np.asarray(_get(index, "ids"), dtype=np.int64)
+    pos_of = np.full(int(ids.max()) + 1 if len(ids) else 1, -1, dtype=np.int64)
+    pos_of[ids] = np.arange(len(ids))
+    sizes = np.asarray(_get(index, "list_sizes"), dtype=np.int64)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    probes_used = op if gpu_probes is None else np.asarray(gpu_probes)
+
+    def lookup(row, id_list):
+        """Exact oracle distance of ids outside the oracle's returned columns,
+        provided they lie in one of the lists the row probed."""
+        pos = np.array([pos_of[i] if 0 <= i < len(pos_of) else -1 for i in id_list])
+        ok = pos >= 0
+        lists = np.searchsorted(off, np.where(ok, pos, 0), side="right") - 1
+        probed = set(int(l) for l in probes_used[row])
+        ok &= np.array([int(l) in probed for l in lists], dtype=bool)
+        out = [None] * len(id_list)
+        if ok.any():
+            vals, _ = O.entry_distances(index, queries[row], pos[ok], lut_mode=lut_mode)
+            for j, v in zip(np.flatnonzero(ok), vals):
+                out[j] = v
+        return out
+
+    check_results(gpu_d, gpu_i, od, oi, k, tau, rep, lookup=lookup)
     return rep

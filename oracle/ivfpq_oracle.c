@@ -146,6 +146,29 @@ static double adc_one(const double *lut, const uint8_t *code, int m)
     return s;
 }
 
+/* Steps 2-4 for single entries: the ADC distance of each listed entry
+ * (entry e lies in list lists[i] and has code row codes[e]) for query x. */
+int oracle_entry_distances(const float *x, const float *centroids, const float *codebooks, int d,
+                           int m, int lut_mode, const int32_t *lists, const uint8_t *code_rows,
+                           int64_t n, double *out)
+{
+    if (m < 1 || d % m || n < 0)
+        return -1;
+    double *lut = (double *)malloc(sizeof(double) * (size_t)m * 256);
+    if (!lut)
+        return -2;
+    for (int64_t i = 0; i < n; i++) {
+        int rc = oracle_lut(x, centroids + (size_t)lists[i] * d, codebooks, d, m, lut_mode, lut);
+        if (rc) {
+            free(lut);
+            return rc;
+        }
+        out[i] = adc_one(lut, code_rows + (size_t)i * m, m);
+    }
+    free(lut);
+    return 0;
+}
+
 typedef struct {
     /* index */
     const float *centroids;

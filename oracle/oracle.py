@@ -50,9 +50,11 @@ def lib():
         L.oracle_lut.argtypes = [P, P, P, i32, i32, i32, P]
         L.oracle_search.argtypes = [P, P, P, P, P, i32, i32, i32, P, i64, i32, i32, i32, P, P, P,
                                     P, i32]
+        L.oracle_entry_distances.argtypes = [P, P, P, i32, i32, i32, P, P, i64, P]
         L.oracle_bruteforce.argtypes = [P, P, i64, i32, P, i64, i32, P, P, i32]
         L.oracle_bruteforce_bf16.argtypes = [P, i64, i32, P, i64, i32, P, P, i32]
-        for f in ("oracle_coarse", "oracle_lut", "oracle_search", "oracle_bruteforce",
+        for f in ("oracle_coarse", "oracle_lut", "oracle_search", "oracle_entry_distances",
+                  "oracle_bruteforce",
                   "oracle_bruteforce_bf16"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -124,6 +126,25 @@ def lut(x, centroid, codebooks, lut_mode=LUT_F64):
     if rc:
         raise ValueError(f"oracle_lut failed ({rc})")
     return out
+
+
+def entry_distances(index, x, positions, lut_mode=LUT_F64):
+    """ADC distance of the entries at the given list-major positions."""
+    get = (lambda n: index[n]) if isinstance(index, dict) else (lambda n: getattr(index, n))
+    cent = np.ascontiguousarray(get("centroids"), dtype=np.float32)
+    books = np.ascontiguousarray(get("codebooks"), dtype=np.float32)
+    sizes = np.asarray(get("list_sizes"), dtype=np.int64)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    pos = np.asarray(positions, dtype=np.int64)
+    lists = (np.searchsorted(off, pos, side="right") - 1).astype(np.int32)
+    rows = np.ascontiguousarray(np.asarray(get("codes"))[pos], dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(len(pos), dtype=np.float64)
+    rc = lib().oracle_entry_distances(_p(x), _p(cent), _p(books), x.shape[0], books.shape[0],
+                                      lut_mode, _p(lists), _p(rows), len(pos), _p(out))
+    if rc:
+        raise ValueError(f"oracle_entry_distances failed ({rc})")
+    return out, lists
 
 
 def search(index, queries, nprobe, k, lut_mode=LUT_F64, probes=None, nthreads=None):

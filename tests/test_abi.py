@@ -1,0 +1,123 @@
+"""C-ABI library checks that need no GPU: it loads, exports every declared
+symbol, and its host-only validation rejects bad files and arrays."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import approximate_nearest_neighbour_amd as A
+from approximate_nearest_neighbour_amd import binding as B
+from approximate_nearest_neighbour_amd import datagen as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "ivfpq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ivfpq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_status_strings():
+    assert A.ivfpq_status_string(0) == "ok"
+    assert A.ivfpq_status_string(3) == "malformed index"
+
+
+def small_index():
+    rng = np.random.default_rng(0)
+    return G.random_index(rng, 4, 8, 2, [3, 0, 5, 2])
+
+
+def test_validate_good_file(tmp_path):
+    p = str(tmp_path / "ok.ivfpq")
+    G.write_index(p, small_index())
+    assert A.ivfpq_validate_index_file(p) == B.OK
+
+
+def test_validate_missing_file(tmp_path):
+    assert A.ivfpq_validate_index_file(str(tmp_path / "none")) == B.E_IO
+
+
+@pytest.mark.parametrize("damage", ["truncate", "magic", "nbits", "m_not_dividing_d", "sizes",
+                                    "trailing", "empty"])
+def test_validate_rejects_corruption(tmp_path, damage):
+    p = str(tmp_path / "bad.ivfpq")
+    G.write_index(p, small_index())
+    raw = bytearray(open(p, "rb").read())
+    if damage == "truncate":
+        raw = raw[:-3]
+    elif damage == "magic":
+        raw[0] = ord("X")
+    elif damage == "nbits":
+        raw[20:24] = (4).to_bytes(4, "little")
+    elif damage == "m_not_dividing_d":
+        raw[16:20] = (3).to_bytes(4, "little")
+    elif damage == "sizes":
+        off = 32 + 4 * 8 * 4 + 4 * 256 * 8
+        raw[off:off + 8] = (4).to_bytes(8, "little")
+    elif damage == "trailing":
+        raw += b"\0"
+    elif damage == "empty":
+        raw = raw[:10]
+    open(p, "wb").write(bytes(raw))
+    assert A.ivfpq_validate_index_file(p) == B.E_FORMAT
+    assert A.ivfpq_last_error() != ""
+
+
+def test_validate_host_arrays():
+    idx = small_index()
+    assert A.ivfpq_validate_host_index(idx) == B.OK
+    bad = G.HostIndex(idx.centroids, idx.codebooks, idx.list_sizes + 1, idx.codes, idx.ids)
+    assert A.ivfpq_validate_host_index(bad) == B.E_FORMAT
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """The ctypes mirrors have the C compiler's sizes and field offsets."""
+    import ctypes
+    import subprocess
+    structs = {"ivfpq_search_params": B.SearchParams, "ivfpq_info": B.Info,
+               "ivfpq_host_index": B.HostIndexStruct, "ivfpq_timings": B.Timings}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ivfpq.h"', "int main(void){"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = dict(l.split() for l in subprocess.check_output([str(exe)], text=True).splitlines())
+    for cname, py in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, (cname, f)
+
+
+def test_load_without_device_or_bad_path_errors(tmp_path):
+    # no GPU here: a valid file gives E_NO_DEVICE, a missing one E_IO,
+    # both before any device work
+    p = str(tmp_path / "ok.ivfpq")
+    G.write_index(p, small_index())
+    with pytest.raises(A.IVFPQError) as e:
+        A.ivfpq_load_index(str(tmp_path / "missing"))
+    assert e.value.status == B.E_IO
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:
+        has_gpu = False
+    if not has_gpu:
+        with pytest.raises(A.IVFPQError) as e:
+            A.ivfpq_load_index(p)
+        assert e.value.status == B.E_NO_DEVICE

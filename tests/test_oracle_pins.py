@@ -136,6 +136,17 @@ def test_adc_equals_reconstruction_distance(nlist, d, m, n):
         assert np.max(np.abs(dist[r] - expl) / expl) < 1e-10
 
 
+def test_entry_distances_equal_reconstruction_distance():
+    idx, rng = random_idx(17, 5, 12, 3, 400)
+    x = rng.standard_normal(12).astype(np.float32)
+    pos = rng.choice(400, 50, replace=False)
+    got, lists = O.entry_distances(idx, x, pos)
+    off = np.concatenate([[0], np.cumsum(idx["list_sizes"])])
+    assert np.all((off[lists] <= pos) & (pos < off[lists + 1]))
+    expl = ((x.astype(np.float64) - reconstruct(idx)[pos]) ** 2).sum(1)
+    np.testing.assert_allclose(got, expl, rtol=1e-12)
+
+
 def test_adc_single_list_matches_reconstruction():
     idx, rng = random_idx(7, 3, 16, 4, 120)
     q = rng.standard_normal((1, 16)).astype(np.float32)
