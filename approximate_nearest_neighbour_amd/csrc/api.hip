@@ -69,6 +69,27 @@ struct EventPair {
 
 constexpr int kStages = 4; // coarse, worklist, scan, merge
 
+// Minimum entries per scan work item when the caller passes chunk_len = 0.
+constexpr uint32_t kDefaultChunk = 32768;
+
+int kw_of(int k)
+{
+    int kw = 64;
+    while (kw < k)
+        kw *= 2;
+    return kw;
+}
+
+// Work items per query at most: the partial top-k buffer stays near 256 MiB
+// (between 2 and 64 items per query).
+uint32_t items_per_query(int64_t nq, int k)
+{
+    const double per = (256.0 * 1024 * 1024) / ((double)(nq > 0 ? nq : 1) * kw_of(k) * 8);
+    if (per < 2)
+        return 2;
+    return per > 64 ? 64u : (uint32_t)per;
+}
+
 } // namespace
 
 struct ivfpq_index {
@@ -496,14 +517,43 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
     if (!g.ok)
         return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    int32_t *probes = probes_dev;
-    if (!probes) {
-        if ((s = ensure_ws(idx, (size_t)nq * p->nprobe * 4)))
-            return s;
-        probes = reinterpret_cast<int32_t *>(idx->ws);
-    }
+    const DeviceIndex &dx = idx->dx;
+    if (scan_lds_bytes(dx.d, dx.m, p->nprobe, p->lut == IVFPQ_LUT_F16, kw_of(p->k) / 64,
+                       dx.m % 2 == 0 ? 2 : 1) > 160 * 1024)
+        return fail(IVFPQ_E_INVALID_ARG, "tables of this m and precision exceed the LDS");
+    // workspace: probes | plan arrays | partial top-k of the work items
+    SearchPlan pl;
+    pl.target = p->chunk_len > 0 ? (uint32_t)p->chunk_len : kDefaultChunk;
+    pl.imax = items_per_query(nq, p->k);
+    pl.max_items = nq * (int64_t)pl.imax;
+    const size_t kw = (size_t)kw_of(p->k);
+    size_t off = 0;
+    auto carve = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return at;
+    };
+    const size_t o_probes = probes_dev ? 0 : carve((size_t)nq * p->nprobe * 4);
+    const size_t o_total = carve((size_t)nq * 4), o_chunk = carve((size_t)nq * 4);
+    const size_t o_count = carve((size_t)nq * 4), o_base = carve(((size_t)nq + 1) * 4);
+    const size_t o_bound = carve((size_t)nq * 4), o_counter = carve(4);
+    const size_t o_pd = carve((size_t)pl.max_items * kw * 4);
+    const size_t o_pp = carve((size_t)pl.max_items * kw * 4);
+    if ((s = ensure_ws(idx, off)))
+        return s;
+    unsigned char *ws = static_cast<unsigned char *>(idx->ws);
+    int32_t *probes = probes_dev ? probes_dev : reinterpret_cast<int32_t *>(ws + o_probes);
+    pl.qtotal = reinterpret_cast<uint32_t *>(ws + o_total);
+    pl.qchunk = reinterpret_cast<uint32_t *>(ws + o_chunk);
+    pl.qcount = reinterpret_cast<uint32_t *>(ws + o_count);
+    pl.item_base = reinterpret_cast<uint32_t *>(ws + o_base);
+    pl.qbound = reinterpret_cast<uint32_t *>(ws + o_bound);
+    pl.counter = reinterpret_cast<uint32_t *>(ws + o_counter);
+    pl.part_d = reinterpret_cast<float *>(ws + o_pd);
+    pl.part_p = reinterpret_cast<uint32_t *>(ws + o_pp);
+
     prof_record(idx, 0, true, st);
-    hipError_t e = launch_coarse(idx->dx, queries_dev, nq, p->nprobe, probes, nullptr, st);
+    hipError_t e = launch_coarse(dx, queries_dev, nq, p->nprobe, probes, nullptr, st);
     prof_record(idx, 0, false, st);
     if (e != hipSuccess)
         return fail(IVFPQ_E_DEVICE, std::string("coarse kernel: ") + hipGetErrorString(e));
@@ -519,11 +569,23 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
     a.out_i = ids_dev;
     a.probes = probes;
     a.probe_d = nullptr;
+    prof_record(idx, 1, true, st);
+    e = launch_plan(dx, a, pl, st);
+    prof_record(idx, 1, false, st);
+    if (e != hipSuccess)
+        return fail(IVFPQ_E_DEVICE, std::string("plan kernels: ") + hipGetErrorString(e));
     prof_record(idx, 2, true, st);
-    e = launch_scan(idx->dx, a, st);
+    e = launch_scan(dx, a, pl, st);
     prof_record(idx, 2, false, st);
     if (e != hipSuccess)
         return fail(IVFPQ_E_DEVICE, std::string("scan kernel: ") + hipGetErrorString(e));
+    if (p->mode == IVFPQ_MODE_NORMAL) {
+        prof_record(idx, 3, true, st);
+        e = launch_merge(dx, a, pl, st);
+        prof_record(idx, 3, false, st);
+        if (e != hipSuccess)
+            return fail(IVFPQ_E_DEVICE, std::string("merge kernel: ") + hipGetErrorString(e));
+    }
     if (idx->profiling && idx->prof_calls < idx->prof_max) {
         idx->prof_calls++;
         idx->prof_items += nq;

@@ -35,10 +35,30 @@ struct SearchArgs {
     float *probe_d;  // [nq][nprobe] or nullptr
 };
 
+// Work plan of one search (device workspace): per query the total probed
+// entries, the entries per work item, the item count and its exclusive
+// prefix (item_base[nq] = number of items), a shared top-k bound, the item
+// counter of the persistent scan, and the partial top-k of every item.
+struct SearchPlan {
+    uint32_t target = 0;   // minimum entries per work item
+    uint32_t imax = 0;     // maximum work items per query
+    int64_t max_items = 0; // nq * imax
+    uint32_t *qtotal = nullptr, *qchunk = nullptr, *qcount = nullptr, *item_base = nullptr;
+    uint32_t *qbound = nullptr, *counter = nullptr;
+    float *part_d = nullptr;   // [max_items][kw]
+    uint32_t *part_p = nullptr; // [max_items][kw]
+};
+
 // Each launcher enqueues on `stream` and returns the launch status.
 hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
                          int32_t *probes, float *probe_d, hipStream_t stream);
-hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &a, hipStream_t stream);
+hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
+                       hipStream_t stream);
+hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
+                       hipStream_t stream);
+hipError_t launch_merge(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
+                        hipStream_t stream);
+size_t scan_lds_bytes(int d, int m, int nprobe, bool f16, int nw, int g);
 hipError_t launch_luts(const DeviceIndex &ix, const float *queries, int64_t nq,
                        const int32_t *probes, int nprobe, int lut, float *out, hipStream_t stream);
 hipError_t launch_cnorms(const DeviceIndex &ix, hipStream_t stream);

@@ -1,27 +1,15 @@
-// IVF-PQ kernels for gfx950: coarse top-nprobe, residual lookup tables in LDS,
-// wave64 code scan with register top-k, cross-wave merge.
+// Auxiliary IVF-PQ kernels for gfx950: the coarse top-nprobe (float32
+// direct differences), the row-wise k-selection on its own, the table
+// writer used for verification, and centroid norms.
 //
-// Definitions ("Custom 8-bit floating point value format for reducing shared
-// memory bank conflict in ANN search", IVFPQ section, search steps 1-5 and
-// Eq. (1); "Billion-scale similarity search with GPUs", IVFADC section):
-//   coarse   D[q,l] = |x_q - c_l|^2, the nprobe smallest are probed;
-//   table    F_j(v) = sum_{t<dsub} (r[j dsub + t] - C_j[v][t])^2, r = x_q - c_l;
-//   scan     R_i = sum_{j<m} F_j(code_i[j]) for every entry i of the list;
-//   top-k    the k smallest R over all probed lists.
-//
-// Work decomposition: one workgroup of four waves per query.  For each
-// probed list the workgroup writes the residual to LDS, builds the m x 256
-// table in LDS (thread v computes codeword v of every sub-quantizer, in the
-// difference form: a sum of squares, no cancellation), then the four waves
-// scan the list with one entry per lane (the m code bytes of 64 consecutive
-// entries are one contiguous 64*m-byte stretch: fully coalesced), each wave
-// keeping its own register top-k.  The waves share a threshold through LDS
-// (the smallest k-th value any wave holds).  At the end the four sorted
-// top-k arrays are merged by bitonic merges and the ids gathered.
+// Coarse step ("Billion-scale similarity search with GPUs", IVFADC section;
+// "Custom 8-bit floating point value format for reducing shared memory bank
+// conflict in ANN search", IVFPQ search step 1): D[q,l] = |x_q - c_l|^2 for
+// every list, the nprobe smallest are probed.  One workgroup of four waves
+// per query; each wave streams a quarter of the centroids through a register
+// top-k; the waves share a bound through LDS and end with a bitonic merge.
+#include "common.hpp"
 #include "internal.hpp"
-#include "wave_select.hpp"
-
-#include <hip/hip_fp16.h>
 
 namespace ivfpq {
 
@@ -61,55 +49,6 @@ __device__ __forceinline__ float table_at(const void *lut, int idx)
         return __half2float(reinterpret_cast<const __half *>(lut)[idx]);
     else
         return reinterpret_cast<const float *>(lut)[idx];
-}
-
-// R = sum_j F_j(code[j]), j ascending.  m % 4 == 0 reads the code row as
-// 32-bit words; other m byte by byte.
-template <bool F16>
-__device__ __forceinline__ float adc_sum(const uint8_t *__restrict__ code, int m, const void *lut)
-{
-    float r = 0.f;
-    if ((m & 3) == 0) {
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(code);
-        for (int j4 = 0; j4 < (m >> 2); ++j4) {
-            const uint32_t word = w[j4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                r += table_at<F16>(lut, (j4 * 4 + b) * 256 + ((word >> (8 * b)) & 255u));
-        }
-    } else {
-        for (int j = 0; j < m; ++j)
-            r += table_at<F16>(lut, j * 256 + code[j]);
-    }
-    return r;
-}
-
-__device__ __forceinline__ void publish_bound(uint32_t *word, float kth)
-{
-    if (kth < INFINITY && lane_id() == 0)
-        atomicMin(word, float_order_key(kth));
-}
-
-__device__ __forceinline__ float read_bound(const uint32_t *word)
-{
-    return float_from_order_key(__atomic_load_n(word, __ATOMIC_RELAXED));
-}
-
-// Merge the top-k of the four waves (each sorted ascending in registers)
-// through LDS scratch; wave 0 ends with the workgroup's top-k.
-template <int NW>
-__device__ __forceinline__ void merge_waves(WaveTopK<NW> &sel, float *mk, uint32_t *mv)
-{
-    const int wave = threadIdx.x >> 6;
-    __syncthreads();
-    if (wave > 0)
-        sel.store(mk + (wave - 1) * 64 * NW, mv + (wave - 1) * 64 * NW);
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll 1
-        for (int w = 0; w < kWaves - 1; ++w)
-            sel.merge_sorted(mk + w * 64 * NW, mv + w * 64 * NW);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -175,7 +114,7 @@ __global__ __launch_bounds__(kBlock) void coarse_kernel(const float *__restrict_
         }
     }
     sel.flush();
-    merge_waves<NW>(sel, mk, mv);
+    merge_waves<NW, kWaves>(sel, mk, mv);
     if (wave == 0) {
 #pragma unroll
         for (int r = 0; r < NW; ++r) {
@@ -184,88 +123,6 @@ __global__ __launch_bounds__(kBlock) void coarse_kernel(const float *__restrict_
                 probes[q * nprobe + e] = (int32_t)sel.wv[r];
                 if (probe_d)
                     probe_d[q * nprobe + e] = sel.wk[r];
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// scan: per probed list, table in LDS + code scan + register top-k
-// ---------------------------------------------------------------------------
-
-template <int NW, bool F16, bool SCAN_ONLY>
-__global__ __launch_bounds__(kBlock) void scan_kernel(
-    const float *__restrict__ queries, int d, int m, int nlist, int nprobe, int k,
-    const float *__restrict__ centroids, const float *__restrict__ codebooks,
-    const uint32_t *__restrict__ list_off, const uint8_t *__restrict__ codes,
-    const int64_t *__restrict__ ids, const int32_t *__restrict__ probes, float *__restrict__ out_d,
-    int64_t *__restrict__ out_i)
-{
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int dpad = (d + 3) & ~3;
-    float *resid = reinterpret_cast<float *>(smem);
-    uint32_t *bound = reinterpret_cast<uint32_t *>(resid + dpad);
-    void *lut = reinterpret_cast<void *>(bound + 4);
-    float *mk = reinterpret_cast<float *>(lut); // reused after the last scan
-    uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (kWaves - 1) * 64 * NW);
-
-    const int64_t q = blockIdx.x;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int dsub = d / m;
-    const float *x = queries + q * d;
-    if (tid == 0)
-        *bound = float_order_key(INFINITY);
-
-    WaveTopK<NW> sel;
-    sel.init(k);
-    float sink = INFINITY;
-
-    for (int p = 0; p < nprobe; ++p) {
-        const int l = probes[q * nprobe + p];
-        if ((unsigned)l >= (unsigned)nlist)
-            continue; // block-uniform: an empty probe slot
-        const uint32_t off = list_off[l];
-        const uint32_t n = list_off[l + 1] - off;
-        __syncthreads(); // everyone is done with the previous table
-        for (int t = tid; t < d; t += kBlock)
-            resid[t] = x[t] - centroids[(size_t)l * d + t];
-        __syncthreads();
-        build_table<F16>(resid, codebooks, m, dsub, lut);
-        __syncthreads();
-        if constexpr (!SCAN_ONLY)
-            sel.bound(read_bound(bound));
-        for (uint32_t base = wave * 64; base < n; base += kBlock) {
-            const uint32_t i = base + lane;
-            float r = INFINITY;
-            if (i < n)
-                r = adc_sum<F16>(codes + (size_t)(off + i) * m, m, lut);
-            if constexpr (SCAN_ONLY)
-                sink = fminf(sink, r);
-            else
-                sel.push(r, off + i);
-        }
-        if constexpr (!SCAN_ONLY)
-            publish_bound(bound, sel.kth);
-    }
-
-    if constexpr (SCAN_ONLY) {
-        // keep every distance live: the wave minimum goes to the output
-        for (int s = 32; s >= 1; s >>= 1)
-            sink = fminf(sink, __shfl_xor(sink, s));
-        if (lane == 0 && wave < k)
-            out_d[q * k + wave] = sink;
-        return;
-    } else {
-        sel.flush();
-        merge_waves<NW>(sel, mk, mv);
-        if (wave == 0) {
-#pragma unroll
-            for (int r = 0; r < NW; ++r) {
-                const int e = r * 64 + lane;
-                if (e < k) {
-                    out_d[q * k + e] = sel.wk[r];
-                    out_i[q * k + e] = sel.wv[r] == kSentinel ? -1 : ids[sel.wv[r]];
-                }
             }
         }
     }
@@ -303,7 +160,7 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const float *__restrict_
         }
     }
     sel.flush();
-    merge_waves<NW>(sel, mk, mv);
+    merge_waves<NW, kWaves>(sel, mk, mv);
     if (wave == 0) {
 #pragma unroll
         for (int r = 0; r < NW; ++r) {
@@ -401,45 +258,6 @@ hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq
     case 4: return coarse_nw<4>(ix, queries, nq, nprobe, probes, probe_d, stream);
     case 8: return coarse_nw<8>(ix, queries, nq, nprobe, probes, probe_d, stream);
     default: return coarse_nw<16>(ix, queries, nq, nprobe, probes, probe_d, stream);
-    }
-}
-
-template <int NW, bool F16, bool SO>
-static hipError_t scan_variant(const DeviceIndex &ix, const SearchArgs &a, hipStream_t stream)
-{
-    const size_t table = (size_t)ix.m * 256 * (F16 ? 2 : 4);
-    const size_t merge = (size_t)(kWaves - 1) * 64 * NW * 8;
-    const size_t lds = (size_t)((ix.d + 3) & ~3) * 4 + 16 + (table > merge ? table : merge);
-    auto kern = scan_kernel<NW, F16, SO>;
-    hipError_t e = set_lds(kern, lds);
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.nq), dim3(kBlock), lds, stream, a.queries, ix.d,
-                       ix.m, ix.nlist, a.nprobe, a.k, ix.centroids, ix.codebooks, ix.list_off, ix.codes,
-                       ix.ids, a.probes, a.out_d, a.out_i);
-    return hipGetLastError();
-}
-
-template <int NW>
-static hipError_t scan_nw(const DeviceIndex &ix, const SearchArgs &a, hipStream_t stream)
-{
-    if (a.mode == 1)
-        return a.lut ? scan_variant<NW, true, true>(ix, a, stream)
-                     : scan_variant<NW, false, true>(ix, a, stream);
-    return a.lut ? scan_variant<NW, true, false>(ix, a, stream)
-                 : scan_variant<NW, false, false>(ix, a, stream);
-}
-
-hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &a, hipStream_t stream)
-{
-    if (a.nq == 0)
-        return hipSuccess;
-    switch (nw_for(a.k)) {
-    case 1: return scan_nw<1>(ix, a, stream);
-    case 2: return scan_nw<2>(ix, a, stream);
-    case 4: return scan_nw<4>(ix, a, stream);
-    case 8: return scan_nw<8>(ix, a, stream);
-    default: return scan_nw<16>(ix, a, stream);
     }
 }
 

@@ -1,0 +1,654 @@
+// IVF-PQ search kernels for gfx950: work planning, table build + code scan +
+// first-pass top-k, cross-item merge.
+//
+// Definitions ("Custom 8-bit floating point value format for reducing shared
+// memory bank conflict in ANN search", IVFPQ section, search steps 2-5 and
+// Eq. (1)):  for each probed list l of query x, r = x - c_l,
+//   F_j(v) = sum_{t<dsub} (r[j dsub + t] - C_j[v][t])^2      (table, in LDS)
+//   R_i    = sum_{j<m} F_j(code_i[j])                          (per entry)
+// and the k smallest R over all probed lists are returned.
+//
+// Work decomposition ("Billion-scale similarity search with GPUs", IVFADC
+// section: (query, list) pairs are independent; a first k-selection pass per
+// piece of work reduces to f*k partial results, a second pass reduces those
+// to k):
+//  * plan:  per query, E = total entries of its probed lists; the query's
+//           entries (lists in probe order, one after the other) are cut into
+//           ceil(E / chunk) work items of chunk entries, chunk = max(target,
+//           ceil(E / imax)), so a query has at most imax items whatever the
+//           list-size skew;
+//  * scan:  persistent workgroups take items from an atomic counter.  For an
+//           item the workgroup lays out its pieces (list, entry range), then
+//           per piece builds the m x 256 table in LDS (double-buffered: the
+//           next piece's table is built while the current one is scanned)
+//           and its waves scan the piece, one entry per lane, code rows read
+//           as wide coalesced loads one step ahead, each wave keeping a
+//           register top-k (WaveTopK).  A per-query bound (the smallest k-th
+//           value any wave of any item of the query holds) is shared through
+//           LDS and global memory.  An item that is its query's only item
+//           writes the final result; otherwise its sorted top-k goes to a
+//           partial slot;
+//  * merge: per query with several items, bitonic merges of the sorted
+//           partials, then the id gather.
+//
+// The codebook lives in registers: thread v of group g holds codeword v of
+// the m/G sub-quantizers of group g, so a table build reads no memory but the
+// residual (an LDS broadcast).  The difference form (sum of squares) is used:
+// no cancellation, every entry and every sum is a sum of non-negative terms.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace ivfpq {
+
+// ---------------------------------------------------------------------------
+// planning
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ probes, int nprobe,
+                                                   int64_t nq, int nlist,
+                                                   const uint32_t *__restrict__ list_off,
+                                                   uint32_t target, uint32_t imax,
+                                                   uint32_t *__restrict__ qtotal,
+                                                   uint32_t *__restrict__ qchunk,
+                                                   uint32_t *__restrict__ qcount,
+                                                   uint32_t *__restrict__ qbound,
+                                                   uint32_t *__restrict__ counter)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q == 0)
+        *counter = 0;
+    if (q >= nq)
+        return;
+    uint64_t e = 0;
+    for (int p = 0; p < nprobe; ++p) {
+        const int l = probes[q * nprobe + p];
+        if ((unsigned)l < (unsigned)nlist)
+            e += list_off[l + 1] - list_off[l];
+    }
+    const uint32_t total = (uint32_t)e;
+    uint32_t chunk = (total + imax - 1) / imax;
+    chunk = chunk > target ? chunk : target;
+    uint32_t count = (total + chunk - 1) / chunk;
+    qtotal[q] = total;
+    qchunk[q] = chunk;
+    qcount[q] = count > 0 ? count : 1;
+    qbound[q] = float_order_key(INFINITY);
+}
+
+// Exclusive prefix sum of qcount into base[0..nq]; one workgroup of 1024.
+__global__ __launch_bounds__(1024) void item_scan_kernel(const uint32_t *__restrict__ qcount,
+                                                         int64_t nq, uint32_t *__restrict__ base)
+{
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t carry_s;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (tid == 0)
+        carry_s = 0;
+    __syncthreads();
+    for (int64_t s = 0; s < nq; s += 1024) {
+        const int64_t i = s + tid;
+        const uint32_t v = i < nq ? qcount[i] : 0u;
+        const uint32_t incl = wave_inclusive_sum(v);
+        if (lane == 63)
+            wsum[wave] = incl;
+        __syncthreads();
+        uint32_t before = carry_s;
+        for (int w = 0; w < wave; ++w)
+            before += wsum[w];
+        if (i < nq)
+            base[i] = before + incl - v;
+        __syncthreads();
+        if (tid == 1023)
+            carry_s = before + incl;
+        __syncthreads();
+    }
+    if (tid == 0)
+        base[nq] = carry_s;
+}
+
+// ---------------------------------------------------------------------------
+// scan
+// ---------------------------------------------------------------------------
+
+struct ScanArgs {
+    const float *queries;
+    int d, m, dsub, nlist, nprobe, k, kw;
+    const float *centroids;
+    const float *codebooks;
+    const uint32_t *list_off;
+    const uint8_t *codes;
+    const int64_t *ids;
+    const int32_t *probes;
+    const uint32_t *qtotal, *qchunk, *item_base;
+    uint32_t *qbound;
+    uint32_t *counter;
+    int64_t nq;
+    float *part_d;
+    uint32_t *part_p;
+    float *out_d;
+    int64_t *out_i;
+};
+
+// A code row of M bytes read with the widest loads its size allows.
+template <int M>
+struct CodeRow {
+    static constexpr int W = M / 4;
+    uint32_t w[W];
+    __device__ __forceinline__ void load(const uint8_t *p)
+    {
+        if constexpr (M % 16 == 0) {
+#pragma unroll
+            for (int i = 0; i < M / 16; ++i) {
+                const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+                w[4 * i] = v.x;
+                w[4 * i + 1] = v.y;
+                w[4 * i + 2] = v.z;
+                w[4 * i + 3] = v.w;
+            }
+        } else if constexpr (M % 8 == 0) {
+#pragma unroll
+            for (int i = 0; i < M / 8; ++i) {
+                const uint2 v = reinterpret_cast<const uint2 *>(p)[i];
+                w[2 * i] = v.x;
+                w[2 * i + 1] = v.y;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < W; ++i)
+                w[i] = reinterpret_cast<const uint32_t *>(p)[i];
+        }
+    }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+            w[i] = 0;
+    }
+};
+
+// R = sum_{j<M} F_j(code[j]), j ascending.
+template <int M, bool F16>
+__device__ __forceinline__ float adc(const CodeRow<M> &row, const void *lut)
+{
+    float r = 0.f;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        const uint32_t c = (row.w[j >> 2] >> (8 * (j & 3))) & 255u;
+        r += Table<F16>::get(lut, j * 256 + (int)c);
+    }
+    return r;
+}
+
+// Run-time m (any m, byte loads when m % 4 != 0).
+template <bool F16>
+__device__ __forceinline__ float adc_rt(const uint8_t *__restrict__ code, int m, const void *lut)
+{
+    float r = 0.f;
+    if ((m & 3) == 0) {
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(code);
+        for (int j4 = 0; j4 < (m >> 2); ++j4) {
+            const uint32_t word = w[j4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                r += Table<F16>::get(lut, (j4 * 4 + b) * 256 + ((word >> (8 * b)) & 255u));
+        }
+    } else {
+        for (int j = 0; j < m; ++j)
+            r += Table<F16>::get(lut, j * 256 + code[j]);
+    }
+    return r;
+}
+
+struct Piece {
+    int32_t list;
+    uint32_t b, e;
+};
+
+// Shapes: M > 0 compile-time m and dsub with the codebook in registers
+// (G groups of 256 threads, each holding m/G sub-quantizers); M == 0 run-time
+// m and dsub, codebook read from memory, G == 1.
+template <int M, int DSUB, int G, int NW, bool F16, bool SO>
+__global__ __launch_bounds__(256 * G) void scan_items_kernel(ScanArgs a)
+{
+    constexpr int WAVES = 4 * G;
+    constexpr int THREADS = 256 * G;
+    constexpr int JG = M > 0 ? M / G : 1;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int d = a.d;
+    const int m = M > 0 ? M : a.m;
+    const int dsub = M > 0 ? DSUB : a.dsub;
+    const int dpad = (d + 3) & ~3;
+    const size_t tbytes = (size_t)m * 256 * (F16 ? 2 : 4);
+
+    // LDS layout by byte offsets from smem (pointer arithmetic on the LDS
+    // array keeps every access a DS instruction)
+    const uint32_t o_misc = 3u * dpad * 4u;
+    const uint32_t o_pieces = o_misc + 16u;
+    const uint32_t o_tab = (o_pieces + (uint32_t)a.nprobe * (uint32_t)sizeof(Piece) + 15u) & ~15u;
+    float *xs = reinterpret_cast<float *>(smem);
+    float *rs0 = xs + dpad;
+    float *rs1 = rs0 + dpad;
+    uint32_t *misc = reinterpret_cast<uint32_t *>(smem + o_misc); // [0] item [1] pieces [2] bound
+    Piece *pieces = reinterpret_cast<Piece *>(smem + o_pieces);
+    unsigned char *tab = smem + o_tab;
+    void *lut0 = tab;
+    void *lut1 = tab + tbytes;
+    float *mk = reinterpret_cast<float *>(tab);
+    uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (WAVES - 1) * 64 * NW);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int v = tid & 255, g = tid >> 8;
+
+    // codebook slice in registers
+    float cb[M > 0 ? JG * DSUB : 1];
+    if constexpr (M > 0) {
+#pragma unroll
+        for (int jj = 0; jj < JG; ++jj)
+#pragma unroll
+            for (int s = 0; s < DSUB; ++s)
+                cb[jj * DSUB + s] = a.codebooks[((size_t)(g * JG + jj) * 256 + v) * DSUB + s];
+    }
+
+    auto build = [&](const float *rs, void *lut) {
+        if constexpr (M > 0) {
+#pragma unroll
+            for (int jj = 0; jj < JG; ++jj) {
+                const int j = g * JG + jj;
+                float acc = 0.f;
+#pragma unroll
+                for (int s = 0; s < DSUB; ++s) {
+                    const float df = rs[j * DSUB + s] - cb[jj * DSUB + s];
+                    acc = fmaf(df, df, acc);
+                }
+                Table<F16>::put(lut, j * 256 + v, acc);
+            }
+        } else {
+            for (int j = 0; j < m; ++j) {
+                const float *cw = a.codebooks + ((size_t)j * 256 + v) * dsub;
+                float acc = 0.f;
+                for (int s = 0; s < dsub; ++s) {
+                    const float df = rs[j * dsub + s] - cw[s];
+                    acc = fmaf(df, df, acc);
+                }
+                Table<F16>::put(lut, j * 256 + v, acc);
+            }
+        }
+    };
+    auto residual = [&](const Piece &pc, float *rs) {
+        const float *c = a.centroids + (size_t)pc.list * d;
+        for (int t = tid; t < d; t += THREADS)
+            rs[t] = xs[t] - c[t];
+    };
+
+    const uint32_t total_items = a.item_base[a.nq];
+    for (;;) {
+        if (tid == 0)
+            misc[0] = atomicAdd(a.counter, 1u);
+        __syncthreads();
+        const uint32_t item = misc[0];
+        if (item >= total_items)
+            break;
+        // the query owning this item: last q with item_base[q] <= item
+        int64_t lo = 0, hi = a.nq - 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (a.item_base[mid] <= item)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int64_t q = lo;
+        const uint32_t first = a.item_base[q];
+        const uint32_t count = a.item_base[q + 1] - first;
+        const uint32_t chunk = a.qchunk[q];
+        const uint32_t start = (item - first) * chunk;
+        const uint32_t total = a.qtotal[q];
+        const uint32_t stop = start + chunk < total ? start + chunk : total;
+
+        for (int t = tid; t < d; t += THREADS)
+            xs[t] = a.queries[q * d + t];
+        // pieces of [start, stop) of the query's concatenated probed lists
+        if (wave == 0) {
+            uint32_t acc = 0, np = 0;
+            for (int p0 = 0; p0 < a.nprobe; p0 += 64) {
+                const int p = p0 + lane;
+                int l = -1;
+                uint32_t sz = 0, off = 0;
+                if (p < a.nprobe) {
+                    l = a.probes[q * a.nprobe + p];
+                    if ((unsigned)l < (unsigned)a.nlist) {
+                        off = a.list_off[l];
+                        sz = a.list_off[l + 1] - off;
+                    }
+                }
+                const uint32_t incl = wave_inclusive_sum(sz);
+                const uint32_t lo_e = acc + incl - sz, hi_e = acc + incl;
+                const bool take = sz > 0 && lo_e < stop && hi_e > start;
+                const uint64_t mask = wave_ballot(take);
+                if (take) {
+                    const int slot = (int)np + mbcnt64(mask);
+                    Piece pc;
+                    pc.list = l;
+                    pc.b = (start > lo_e ? start : lo_e) - lo_e;
+                    pc.e = (stop < hi_e ? stop : hi_e) - lo_e;
+                    pieces[slot] = pc;
+                }
+                np += (uint32_t)__popcll(mask);
+                acc += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+            }
+            if (lane == 0) {
+                misc[1] = np;
+                misc[2] = a.qbound[q];
+            }
+        }
+        __syncthreads();
+        const int np = (int)misc[1];
+
+        WaveTopK<NW> sel;
+        sel.init(a.k);
+        float sink = INFINITY;
+
+        if (np > 0) {
+            residual(pieces[0], rs0);
+            __syncthreads();
+            build(rs0, lut0);
+            if (np > 1)
+                residual(pieces[1], rs1);
+            __syncthreads();
+        }
+        for (int pi = 0; pi < np; ++pi) {
+            void *lut = (pi & 1) ? lut1 : lut0;
+            if (pi + 1 < np)
+                build((pi & 1) ? rs0 : rs1, (pi & 1) ? lut0 : lut1);
+            if (pi + 2 < np)
+                residual(pieces[pi + 2], (pi & 1) ? rs1 : rs0);
+            if constexpr (!SO)
+                sel.bound(read_bound(&misc[2]));
+
+            const Piece pc = pieces[pi];
+            const uint32_t off = a.list_off[pc.list];
+            const uint8_t *base = a.codes + (size_t)off * m;
+            constexpr uint32_t STRIDE = 64 * WAVES;
+            uint32_t i0 = pc.b + wave * 64;
+            if constexpr (M > 0) {
+                CodeRow<M> cur, nxt;
+                if (i0 < pc.e) {
+                    if (i0 + lane < pc.e)
+                        cur.load(base + (size_t)(i0 + lane) * M);
+                    else
+                        cur.zero();
+                }
+                for (; i0 < pc.e; i0 += STRIDE) {
+                    const uint32_t n0 = i0 + STRIDE;
+                    if (n0 < pc.e) {
+                        if (n0 + lane < pc.e)
+                            nxt.load(base + (size_t)(n0 + lane) * M);
+                        else
+                            nxt.zero();
+                    }
+                    const uint32_t i = i0 + lane;
+                    const float r = i < pc.e ? adc<M, F16>(cur, lut) : INFINITY;
+                    if constexpr (SO)
+                        sink = fminf(sink, r);
+                    else
+                        sel.push(r, off + i);
+                    cur = nxt;
+                }
+            } else {
+                for (; i0 < pc.e; i0 += STRIDE) {
+                    const uint32_t i = i0 + lane;
+                    const float r =
+                        i < pc.e ? adc_rt<F16>(base + (size_t)i * m, m, lut) : INFINITY;
+                    if constexpr (SO)
+                        sink = fminf(sink, r);
+                    else
+                        sel.push(r, off + i);
+                }
+            }
+            if constexpr (!SO) {
+                publish_bound(&misc[2], sel.kth);
+                if (tid == 0) {
+                    const uint32_t mine = misc[2];
+                    const uint32_t old = atomicMin(&a.qbound[q], mine);
+                    if (old < mine)
+                        atomicMin(&misc[2], old);
+                }
+            }
+            __syncthreads();
+        }
+
+        if constexpr (SO) {
+#pragma unroll
+            for (int s = 32; s >= 1; s >>= 1)
+                sink = fminf(sink, __shfl_xor(sink, s));
+            if (tid == 0)
+                a.out_d[q * a.k] = sink;
+            __syncthreads();
+        } else {
+            sel.flush();
+            merge_waves<NW, WAVES>(sel, mk, mv);
+            if (wave == 0) {
+                if (count == 1) {
+#pragma unroll
+                    for (int r = 0; r < NW; ++r) {
+                        const int e = r * 64 + lane;
+                        if (e < a.k) {
+                            a.out_d[q * a.k + e] = sel.wk[r];
+                            a.out_i[q * a.k + e] =
+                                sel.wv[r] == kSentinel ? -1 : a.ids[sel.wv[r]];
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < NW; ++r) {
+                        const size_t e = (size_t)item * (64 * NW) + r * 64 + lane;
+                        a.part_d[e] = sel.wk[r];
+                        a.part_p[e] = sel.wv[r];
+                    }
+                }
+            }
+            __syncthreads(); // merge scratch aliases the tables
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// merge of the partial top-k of a query's items
+// ---------------------------------------------------------------------------
+
+template <int NW>
+__global__ __launch_bounds__(256) void merge_items_kernel(const uint32_t *__restrict__ item_base,
+                                                          const float *__restrict__ part_d,
+                                                          const uint32_t *__restrict__ part_p,
+                                                          const int64_t *__restrict__ ids, int k,
+                                                          float *__restrict__ out_d,
+                                                          int64_t *__restrict__ out_i)
+{
+    __shared__ __align__(16) float mk[3 * 64 * NW];
+    __shared__ __align__(16) uint32_t mv[3 * 64 * NW];
+    const int64_t q = blockIdx.x;
+    const uint32_t first = item_base[q], count = item_base[q + 1] - first;
+    if (count <= 1)
+        return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    WaveTopK<NW> sel;
+    sel.init(k);
+    for (uint32_t it = wave; it < count; it += 4)
+        sel.merge_sorted(part_d + (size_t)(first + it) * 64 * NW,
+                         part_p + (size_t)(first + it) * 64 * NW);
+    merge_waves<NW, 4>(sel, mk, mv);
+    if (wave == 0) {
+#pragma unroll
+        for (int r = 0; r < NW; ++r) {
+            const int e = r * 64 + lane;
+            if (e < k) {
+                out_d[q * k + e] = sel.wk[r];
+                out_i[q * k + e] = sel.wv[r] == kSentinel ? -1 : ids[sel.wv[r]];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+static int nw_of(int k)
+{
+    int nw = 1;
+    while (nw * 64 < k)
+        nw *= 2;
+    return nw;
+}
+
+static int cu_count()
+{
+    static int n = 0;
+    if (!n) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+    }
+    return n;
+}
+
+size_t scan_lds_bytes(int d, int m, int nprobe, bool f16, int nw, int g)
+{
+    const size_t dpad = (size_t)((d + 3) & ~3);
+    const size_t table = 2 * (size_t)m * 256 * (f16 ? 2 : 4);
+    const size_t merge = (size_t)(4 * g - 1) * 64 * nw * 8;
+    const size_t o_tab = (dpad * 4 * 3 + 16 + (size_t)nprobe * sizeof(Piece) + 15) & ~(size_t)15;
+    return o_tab + (table > merge ? table : merge);
+}
+
+template <int M, int DSUB, int G, int NW, bool F16, bool SO>
+static hipError_t scan_variant(const ScanArgs &a, const SearchPlan &pl, hipStream_t stream)
+{
+    auto kern = scan_items_kernel<M, DSUB, G, NW, F16, SO>;
+    const size_t lds = scan_lds_bytes(a.d, a.m, a.nprobe, F16, NW, G);
+    if (lds > 160 * 1024)
+        return hipErrorInvalidValue;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256 * G, lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    int64_t grid = (int64_t)per_cu * cu_count();
+    if (grid > pl.max_items)
+        grid = pl.max_items > 0 ? pl.max_items : 1;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256 * G), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int M, int DSUB, int G, int NW>
+static hipError_t scan_shape(const ScanArgs &a, const SearchPlan &pl, int f16, int so,
+                             hipStream_t stream)
+{
+    if (so)
+        return f16 ? scan_variant<M, DSUB, G, NW, true, true>(a, pl, stream)
+                   : scan_variant<M, DSUB, G, NW, false, true>(a, pl, stream);
+    return f16 ? scan_variant<M, DSUB, G, NW, true, false>(a, pl, stream)
+               : scan_variant<M, DSUB, G, NW, false, false>(a, pl, stream);
+}
+
+template <int NW>
+static hipError_t scan_nw(const ScanArgs &a, const SearchPlan &pl, int f16, int so,
+                          hipStream_t stream)
+{
+    if (a.m == 4 && a.dsub == 8)
+        return scan_shape<4, 8, 1, NW>(a, pl, f16, so, stream);
+    if (a.m == 16 && a.dsub == 8)
+        return scan_shape<16, 8, 2, NW>(a, pl, f16, so, stream);
+    if (a.m == 32 && a.dsub == 3)
+        return scan_shape<32, 3, 2, NW>(a, pl, f16, so, stream);
+    if (a.m == 8 && a.dsub == 12)
+        return scan_shape<8, 12, 2, NW>(a, pl, f16, so, stream);
+    return scan_shape<0, 0, 1, NW>(a, pl, f16, so, stream);
+}
+
+template <int NW>
+static hipError_t merge_nw(const SearchArgs &s, const SearchPlan &pl, const DeviceIndex &ix,
+                           hipStream_t stream)
+{
+    hipLaunchKernelGGL(merge_items_kernel<NW>, dim3((unsigned)s.nq), dim3(256), 0, stream,
+                       pl.item_base, pl.part_d, pl.part_p, ix.ids, s.k, s.out_d, s.out_i);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
+                       hipStream_t stream)
+{
+    const unsigned blocks = (unsigned)((s.nq + 255) / 256);
+    hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(256), 0, stream, s.probes, s.nprobe, s.nq,
+                       ix.nlist, ix.list_off, pl.target, pl.imax, pl.qtotal, pl.qchunk, pl.qcount,
+                       pl.qbound, pl.counter);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(item_scan_kernel, dim3(1), dim3(1024), 0, stream, pl.qcount, s.nq,
+                       pl.item_base);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
+                       hipStream_t stream)
+{
+    if (s.nq == 0)
+        return hipSuccess;
+    ScanArgs a;
+    a.queries = s.queries;
+    a.d = ix.d;
+    a.m = ix.m;
+    a.dsub = ix.d / ix.m;
+    a.nlist = ix.nlist;
+    a.nprobe = s.nprobe;
+    a.k = s.k;
+    a.kw = 64 * nw_of(s.k);
+    a.centroids = ix.centroids;
+    a.codebooks = ix.codebooks;
+    a.list_off = ix.list_off;
+    a.codes = ix.codes;
+    a.ids = ix.ids;
+    a.probes = s.probes;
+    a.qtotal = pl.qtotal;
+    a.qchunk = pl.qchunk;
+    a.item_base = pl.item_base;
+    a.qbound = pl.qbound;
+    a.counter = pl.counter;
+    a.nq = s.nq;
+    a.part_d = pl.part_d;
+    a.part_p = pl.part_p;
+    a.out_d = s.out_d;
+    a.out_i = s.out_i;
+    switch (nw_of(s.k)) {
+    case 1: return scan_nw<1>(a, pl, s.lut, s.mode, stream);
+    case 2: return scan_nw<2>(a, pl, s.lut, s.mode, stream);
+    case 4: return scan_nw<4>(a, pl, s.lut, s.mode, stream);
+    case 8: return scan_nw<8>(a, pl, s.lut, s.mode, stream);
+    default: return scan_nw<16>(a, pl, s.lut, s.mode, stream);
+    }
+}
+
+hipError_t launch_merge(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
+                        hipStream_t stream)
+{
+    if (s.nq == 0)
+        return hipSuccess;
+    switch (nw_of(s.k)) {
+    case 1: return merge_nw<1>(s, pl, ix, stream);
+    case 2: return merge_nw<2>(s, pl, ix, stream);
+    case 4: return merge_nw<4>(s, pl, ix, stream);
+    case 8: return merge_nw<8>(s, pl, ix, stream);
+    default: return merge_nw<16>(s, pl, ix, stream);
+    }
+}
+
+} // namespace ivfpq

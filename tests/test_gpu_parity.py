@@ -191,6 +191,34 @@ def test_search_random_shapes(dev, shape):
     assert_parity(idx, q, nprobe, k)
 
 
+@pytest.mark.parametrize("chunk,shape", [
+    (64, (24, 128, 16, 30000, 12, 10, 100)),     # many items per query, capped count
+    (500, (32, 96, 32, 20000, 10, 8, 100)),
+    (1000, (40, 96, 8, 50000, 8, 16, 1000)),     # large k across items
+    (300, (16, 32, 4, 8000, 20, 5, 10)),
+    (200, (10, 12, 6, 3000, 6, 4, 50)),          # run-time m path
+])
+def test_search_split_into_items(dev, chunk, shape):
+    """Small work items: each query's entries are cut into many items whose
+    partial top-k are merged by the second pass."""
+    nlist, d, m, n, nq, nprobe, k = shape
+    say("items", chunk, shape)
+    rng = np.random.default_rng(n + chunk)
+    sizes = rng.multinomial(n, rng.dirichlet(np.ones(nlist) * 0.5))
+    idx = G.random_index(rng, nlist, d, m, sizes, codebook_scale=0.3)
+    q = (idx.centroids[rng.integers(0, nlist, nq)]
+         + 0.3 * rng.standard_normal((nq, d))).astype(np.float32)
+    ix = A.ivfpq_load_index_host(idx)
+    qt = torch.from_numpy(q).to(dev)
+    d1, i1, p1 = A.ivfpq_search_ex(ix, qt, nprobe, k, chunk_len=chunk, return_probes=True)
+    torch.cuda.synchronize()
+    rep = check.compare_search(idx, q, nprobe, k, d1.cpu().numpy(), i1.cpu().numpy(),
+                               p1.cpu().numpy())
+    say("parity", rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    ix.close()
+
+
 def pq_exact(seed, nlist=7, d=16, m=4, n=3000, nq=12):
     rng = np.random.default_rng(seed)
     cent = rng.integers(-3, 4, (nlist, d)).astype(np.float32)
