@@ -68,6 +68,7 @@ __global__ __launch_bounds__(kBlock) void coarse_kernel(const float *__restrict_
     uint32_t *bound = reinterpret_cast<uint32_t *>(x + dpad);
     float *mk = reinterpret_cast<float *>(bound + 4);
     uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (kWaves - 1) * 64 * NW);
+    uint32_t *stage = mv + (kWaves - 1) * 64 * NW; // [kWaves][128]
 
     const int64_t q = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(kBlock) void coarse_kernel(const float *__restrict_
     __syncthreads();
 
     WaveTopK<NW> sel;
-    sel.init(nprobe);
+    sel.init(nprobe, stage + wave * 128);
     int since = 0;
     for (int base = wave * 64; base < nlist; base += kBlock) {
         const int l = base + lane;
@@ -141,13 +142,14 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const float *__restrict_
     uint32_t *bound = reinterpret_cast<uint32_t *>(smem);
     float *mk = reinterpret_cast<float *>(bound + 4);
     uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (kWaves - 1) * 64 * NW);
+    uint32_t *stage = mv + (kWaves - 1) * 64 * NW; // [kWaves][128]
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if (tid == 0)
         *bound = float_order_key(INFINITY);
     __syncthreads();
     WaveTopK<NW> sel;
-    sel.init(k);
+    sel.init(k, stage + wave * 128);
     const float *rk = keys + row * n;
     int since = 0;
     for (int64_t base = wave * 64; base < n; base += kBlock) {
@@ -237,7 +239,8 @@ template <int NW>
 static hipError_t coarse_nw(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
                             int32_t *probes, float *probe_d, hipStream_t stream)
 {
-    const size_t lds = (size_t)((ix.d + 3) & ~3) * 4 + 16 + (size_t)(kWaves - 1) * 64 * NW * 8;
+    const size_t lds = (size_t)((ix.d + 3) & ~3) * 4 + 16 + (size_t)(kWaves - 1) * 64 * NW * 8 +
+                       (size_t)kWaves * 512;
     auto kern = coarse_kernel<NW>;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess)
@@ -289,7 +292,7 @@ template <int NW>
 static hipError_t select_nw(const float *keys, int64_t rows, int64_t n, int k, float *out_d,
                             int32_t *out_pos, hipStream_t stream)
 {
-    const size_t lds = 16 + (size_t)(kWaves - 1) * 64 * NW * 8;
+    const size_t lds = 16 + (size_t)(kWaves - 1) * 64 * NW * 8 + (size_t)kWaves * 512;
     hipLaunchKernelGGL(select_kernel<NW>, dim3((unsigned)rows), dim3(kBlock), lds, stream, keys, n,
                        k, out_d, out_pos);
     return hipGetLastError();

@@ -166,16 +166,22 @@ struct CodeRow {
     }
 };
 
-// R = sum_{j<M} F_j(code[j]), j ascending.
+// R = sum_{j<M} F_j(code[j]), j ascending.  The M table reads are all
+// issued before the first add (they are independent), so one entry costs one
+// LDS round trip rather than M of them.
 template <int M, bool F16>
 __device__ __forceinline__ float adc(const CodeRow<M> &row, const void *lut)
 {
-    float r = 0.f;
+    float t[M];
 #pragma unroll
     for (int j = 0; j < M; ++j) {
         const uint32_t c = (row.w[j >> 2] >> (8 * (j & 3))) & 255u;
-        r += Table<F16>::get(lut, j * 256 + (int)c);
+        t[j] = Table<F16>::get(lut, j * 256 + (int)c);
     }
+    float r = t[0];
+#pragma unroll
+    for (int j = 1; j < M; ++j)
+        r += t[j];
     return r;
 }
 
@@ -208,7 +214,11 @@ struct Piece {
 // (G groups of 256 threads, each holding m/G sub-quantizers); M == 0 run-time
 // m and dsub, codebook read from memory, G == 1.
 template <int M, int DSUB, int G, int NW, bool F16, bool SO>
-__global__ __launch_bounds__(256 * G) void scan_items_kernel(ScanArgs a)
+// Register budget: 128 VGPRs, i.e. four waves per SIMD, so that two
+// workgroups of eight waves share a CU and their table-build and scan
+// phases overlap.
+__global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(4)))
+void scan_items_kernel(ScanArgs a)
 {
     constexpr int WAVES = 4 * G;
     constexpr int THREADS = 256 * G;
@@ -224,12 +234,15 @@ __global__ __launch_bounds__(256 * G) void scan_items_kernel(ScanArgs a)
     // LDS layout by byte offsets from smem (pointer arithmetic on the LDS
     // array keeps every access a DS instruction)
     const uint32_t o_misc = 3u * dpad * 4u;
-    const uint32_t o_pieces = o_misc + 16u;
-    const uint32_t o_tab = (o_pieces + (uint32_t)a.nprobe * (uint32_t)sizeof(Piece) + 15u) & ~15u;
+    const uint32_t o_pieces = o_misc + 64u;
+    const uint32_t o_stage = (o_pieces + (uint32_t)a.nprobe * (uint32_t)sizeof(Piece) + 15u) & ~15u;
+    const uint32_t o_tab = o_stage + WAVES * 512u;
     float *xs = reinterpret_cast<float *>(smem);
     float *rs0 = xs + dpad;
     float *rs1 = rs0 + dpad;
-    uint32_t *misc = reinterpret_cast<uint32_t *>(smem + o_misc); // [0] item [1] pieces [2] bound
+    // misc: [0] item [1] pieces [2] min bound [4 .. 4+WAVES) per-wave rank values
+    uint32_t *misc = reinterpret_cast<uint32_t *>(smem + o_misc);
+    uint32_t *pub = misc + 4;
     Piece *pieces = reinterpret_cast<Piece *>(smem + o_pieces);
     unsigned char *tab = smem + o_tab;
     void *lut0 = tab;
@@ -341,13 +354,35 @@ __global__ __launch_bounds__(256 * G) void scan_items_kernel(ScanArgs a)
                 misc[1] = np;
                 misc[2] = a.qbound[q];
             }
+            if (lane < WAVES)
+                pub[lane] = float_order_key(INFINITY);
         }
         __syncthreads();
         const int np = (int)misc[1];
 
+        // Union bound: wave w publishes its rk-th smallest value, rk =
+        // ceil(k / WAVES); each wave then holds >= rk values <= the largest
+        // published value, so together >= k: that maximum bounds the item's
+        // k-th distance from above and filters every wave.
         WaveTopK<NW> sel;
-        sel.init(a.k);
-        float sink = INFINITY;
+        sel.init(a.k, reinterpret_cast<uint32_t *>(smem + o_stage) + wave * 128,
+                 (a.k + WAVES - 1) / WAVES);
+        float sink = INFINITY, published = INFINITY;
+        int tick = 0;
+        auto exchange = [&]() {
+            if (sel.part < published) {
+                published = sel.part;
+                if (lane == 0)
+                    pub[wave] = float_order_key(published);
+            }
+            if ((++tick & 3) != 0)
+                return;
+            uint32_t mx = 0;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w)
+                mx = mx > pub[w] ? mx : pub[w];
+            sel.bound(float_from_order_key(mx));
+        };
 
         if (np > 0) {
             residual(pieces[0], rs0);
@@ -372,44 +407,68 @@ __global__ __launch_bounds__(256 * G) void scan_items_kernel(ScanArgs a)
             constexpr uint32_t STRIDE = 64 * WAVES;
             uint32_t i0 = pc.b + wave * 64;
             if constexpr (M > 0) {
-                CodeRow<M> cur, nxt;
+                // full 64-entry steps (no per-lane bounds), code rows read one
+                // step ahead; then at most one partial step
+                constexpr size_t PSTEP = (size_t)STRIDE * M;
+                const uint8_t *p = base + (size_t)(i0 + lane) * M;
+                if (i0 + 64 <= pc.e) {
+                    CodeRow<M> cur;
+                    cur.load(p);
+                    for (;;) {
+                        const uint32_t n0 = i0 + STRIDE;
+                        const bool more = n0 + 64 <= pc.e;
+                        CodeRow<M> nxt;
+                        if (more)
+                            nxt.load(p + PSTEP);
+                        const float r = adc<M, F16>(cur, lut);
+                        if constexpr (SO) {
+                            sink = fminf(sink, r);
+                        } else {
+                            sel.push(r, off + i0 + lane);
+                            exchange();
+                        }
+                        i0 = n0;
+                        p += PSTEP;
+                        if (!more)
+                            break;
+                        cur = nxt;
+                    }
+                }
                 if (i0 < pc.e) {
-                    if (i0 + lane < pc.e)
-                        cur.load(base + (size_t)(i0 + lane) * M);
+                    const bool in = i0 + lane < pc.e;
+                    CodeRow<M> cur;
+                    if (in)
+                        cur.load(p);
                     else
                         cur.zero();
-                }
-                for (; i0 < pc.e; i0 += STRIDE) {
-                    const uint32_t n0 = i0 + STRIDE;
-                    if (n0 < pc.e) {
-                        if (n0 + lane < pc.e)
-                            nxt.load(base + (size_t)(n0 + lane) * M);
-                        else
-                            nxt.zero();
-                    }
-                    const uint32_t i = i0 + lane;
-                    const float r = i < pc.e ? adc<M, F16>(cur, lut) : INFINITY;
-                    if constexpr (SO)
+                    const float r = in ? adc<M, F16>(cur, lut) : INFINITY;
+                    if constexpr (SO) {
                         sink = fminf(sink, r);
-                    else
-                        sel.push(r, off + i);
-                    cur = nxt;
+                    } else {
+                        sel.push(r, off + i0 + lane);
+                        exchange();
+                    }
                 }
             } else {
                 for (; i0 < pc.e; i0 += STRIDE) {
                     const uint32_t i = i0 + lane;
                     const float r =
                         i < pc.e ? adc_rt<F16>(base + (size_t)i * m, m, lut) : INFINITY;
-                    if constexpr (SO)
+                    if constexpr (SO) {
                         sink = fminf(sink, r);
-                    else
+                    } else {
                         sel.push(r, off + i);
+                        exchange();
+                    }
                 }
             }
             if constexpr (!SO) {
                 publish_bound(&misc[2], sel.kth);
                 if (tid == 0) {
-                    const uint32_t mine = misc[2];
+                    uint32_t mx = 0;
+                    for (int w = 0; w < WAVES; ++w)
+                        mx = mx > pub[w] ? mx : pub[w];
+                    const uint32_t mine = misc[2] < mx ? misc[2] : mx;
                     const uint32_t old = atomicMin(&a.qbound[q], mine);
                     if (old < mine)
                         atomicMin(&misc[2], old);
@@ -472,8 +531,8 @@ __global__ __launch_bounds__(256) void merge_items_kernel(const uint32_t *__rest
     if (count <= 1)
         return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    WaveTopK<NW> sel;
-    sel.init(k);
+    WaveTopK<NW> sel; // merges sorted arrays only: no staging buffer
+    sel.init(k, nullptr);
     for (uint32_t it = wave; it < count; it += 4)
         sel.merge_sorted(part_d + (size_t)(first + it) * 64 * NW,
                          part_p + (size_t)(first + it) * 64 * NW);
@@ -520,7 +579,8 @@ size_t scan_lds_bytes(int d, int m, int nprobe, bool f16, int nw, int g)
     const size_t dpad = (size_t)((d + 3) & ~3);
     const size_t table = 2 * (size_t)m * 256 * (f16 ? 2 : 4);
     const size_t merge = (size_t)(4 * g - 1) * 64 * nw * 8;
-    const size_t o_tab = (dpad * 4 * 3 + 16 + (size_t)nprobe * sizeof(Piece) + 15) & ~(size_t)15;
+    const size_t o_tab = ((dpad * 4 * 3 + 64 + (size_t)nprobe * sizeof(Piece) + 15) & ~(size_t)15) +
+                         (size_t)4 * g * 512;
     return o_tab + (table > merge ? table : merge);
 }
 

@@ -9,14 +9,15 @@
 //  * The filter threshold is W[k-1] (the k-th smallest so far), optionally
 //    tightened by an external bound (another wave's W[k-1]: its k values
 //    already beat anything above it).  A value >= threshold is dropped.
-//  * Survivors are compacted, in lane order, into a 64-slot candidate buffer
-//    held one element per lane: ballot + mbcnt give each survivor its slot,
-//    one ds_permute over a bijection (survivors to the free slots, the other
-//    lanes to the remaining slots) moves them, all in registers.  This
-//    replaces the per-lane thread queues of the paper: on wave64 it merges
-//    once per 64 survivors instead of whenever one lane's queue fills.
-//  * When the buffer would overflow (and at the end) it is sorted descending
-//    by a 64-element bitonic network, folded into W's last register with an
+//  * Survivors are compacted, in lane order, into a 64-slot staging buffer
+//    of the wave in LDS: ballot + mbcnt give each survivor its slot and it
+//    writes itself there (a store nobody waits for; a pass with survivors
+//    costs a few instructions and no round trip).  This replaces the per-lane
+//    thread queues of the paper: on wave64 it merges once per 64 survivors
+//    instead of whenever one lane's queue fills.
+//  * When the buffer would overflow (and at the end) it is read back one
+//    element per lane, sorted descending by a 64-element bitonic network in
+//    registers, folded into W's last register with an
 //    element-wise min (the first step of a bitonic merge of W with the
 //    reversed buffer keeps exactly the kw smallest), and W is re-sorted by
 //    a bitonic merge (log2(kw) steps).  All of it is data-independent.
@@ -33,31 +34,36 @@ template <int NW> // W holds kw = 64 * NW elements, kw >= k
 struct WaveTopK {
     float wk[NW];
     uint32_t wv[NW];
-    float bk; // candidate buffer, slot = lane
-    uint32_t bv;
+    float *sk;    // 64-slot candidate staging buffer of this wave (LDS)
+    uint32_t *sv;
     int bcount; // filled buffer slots (wave-uniform)
     int k;
-    float kth; // W[k-1] (wave-uniform)
-    float thr; // filter threshold = min(kth, external bound)
+    int rk;     // rank whose value the wave publishes for the union bound
+    float kth;  // W[k-1] (wave-uniform)
+    float part; // W[rk-1] (wave-uniform)
+    float thr;  // filter threshold = min(kth, external bounds)
 
-    __device__ __forceinline__ void init(int k_)
+    // stage: 64 keys then 64 values of LDS owned by this wave
+    __device__ __forceinline__ void init(int k_, uint32_t *stage, int rk_ = 0)
     {
 #pragma unroll
         for (int r = 0; r < NW; ++r) {
             wk[r] = INFINITY;
             wv[r] = kSentinel;
         }
-        bk = INFINITY;
-        bv = kSentinel;
+        sk = reinterpret_cast<float *>(stage);
+        sv = stage + 64;
         bcount = 0;
         k = k_;
+        rk = rk_ > 0 ? rk_ : k_;
         kth = INFINITY;
+        part = INFINITY;
         thr = INFINITY;
     }
 
-    __device__ __forceinline__ float read_kth() const
+    // W[e] (wave-uniform), e < 64 * NW
+    __device__ __forceinline__ float read_rank(int e) const
     {
-        const int e = k - 1;
         const int lane = e & 63;
         float out = INFINITY;
 #pragma unroll
@@ -74,9 +80,11 @@ struct WaveTopK {
         if (bcount == 0)
             return;
         const int lane = lane_id();
-        if (lane >= bcount) {
-            bk = INFINITY;
-            bv = kSentinel;
+        float bk = INFINITY;
+        uint32_t bv = kSentinel;
+        if (lane < bcount) {
+            bk = sk[lane];
+            bv = sv[lane];
         }
         sort64<true>(bk, bv);
         // first step of the bitonic merge of W (ascending) with the buffer
@@ -87,10 +95,9 @@ struct WaveTopK {
             wv[NW - 1] = take ? bv : wv[NW - 1];
         }
         bitonic_merge_up<NW>(wk, wv);
-        bk = INFINITY;
-        bv = kSentinel;
         bcount = 0;
-        kth = read_kth();
+        kth = read_rank(k - 1);
+        part = read_rank(rk - 1);
         thr = fminf(thr, kth);
     }
 
@@ -113,14 +120,11 @@ struct WaveTopK {
                 return;
             n = __popcll(mask);
         }
-        const int lane = lane_id();
-        const int below = mbcnt64(mask);
-        const int slot = pass ? (bcount + below) : ((bcount + n + (lane - below)) & 63);
-        const float nk = __int_as_float(__builtin_amdgcn_ds_permute(slot << 2, __float_as_int(key)));
-        const uint32_t nv = (uint32_t)__builtin_amdgcn_ds_permute(slot << 2, (int)val);
-        const bool fill = lane >= bcount && lane < bcount + n;
-        bk = fill ? nk : bk;
-        bv = fill ? nv : bv;
+        if (pass) {
+            const int slot = bcount + mbcnt64(mask);
+            sk[slot] = key;
+            sv[slot] = val;
+        }
         bcount += n;
     }
 
@@ -151,7 +155,8 @@ struct WaveTopK {
             wv[r] = take ? ov : wv[r];
         }
         bitonic_merge_up<NW>(wk, wv);
-        kth = read_kth();
+        kth = read_rank(k - 1);
+        part = read_rank(rk - 1);
         thr = fminf(thr, kth);
     }
 };
