@@ -38,6 +38,65 @@ def workload(name: str):
     return makers[name]()
 
 
+def source_digest() -> str:
+    """SHA-256 over the HIP sources: ties stored counter readings to a kernel
+    version."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "approximate_nearest_neighbour_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, lut: str):
+    """HBM bytes per scan launch from profiles/traffic.json (FETCH_SIZE and
+    WRITE_SIZE of rocprofv3 --pmc runs scaled by a copy-kernel calibration),
+    only while the kernels are the ones the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        import json as _json
+        rec = _json.load(open(path)).get(f"{workload}:{lut}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_digest():
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
+def summarize_counters(paths):
+    """Print per-kernel averages of rocprofv3 counter CSVs (one per pass)."""
+    import collections
+    import csv
+    for path in paths:
+        agg = collections.defaultdict(lambda: collections.defaultdict(float))
+        disp = collections.defaultdict(set)
+        for r in csv.DictReader(open(path)):
+            k = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[k].add(r["Dispatch_Id"])
+        print(f"## {os.path.basename(path)}")
+        for k in sorted(agg):
+            n = len(disp[k])
+            vals = ", ".join(f"{c}={v / n:.6g}" for c, v in sorted(agg[k].items()))
+            print(f"- `{k}` ({n} dispatches, per dispatch): {vals}")
+
+
+def summarize_stats(paths):
+    """Print rocprofv3 --stats kernel tables (CSV) as markdown."""
+    import csv
+    for path in paths:
+        rows = list(csv.DictReader(open(path)))
+        print(f"## {os.path.basename(path)}")
+        print("| kernel | calls | total ms | average us |")
+        print("|---|---:|---:|---:|")
+        for r in rows:
+            print(f"| `{r['Name'].split('(')[0].replace('void ', '')}` | {r['Calls']} | "
+                  f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['AverageNs']) / 1e3:.1f} |")
+
+
 def scanned_entries(index, probes: np.ndarray) -> int:
     return int(index.list_sizes[probes.astype(np.int64)].sum())
 
@@ -70,7 +129,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parity-queries", type=int, default=200)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs="+", help="print rocprofv3 counter CSVs")
+    ap.add_argument("--summarize-stats", nargs="+", help="print rocprofv3 kernel_stats CSVs")
     args = ap.parse_args()
+    if args.summarize_counters or args.summarize_stats:
+        summarize_counters(args.summarize_counters or [])
+        summarize_stats(args.summarize_stats or [])
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the multi-GPU path (replicas/shards joined by "
               "one gather) is not built; run with --gpus 1", file=sys.stderr)
@@ -99,6 +166,12 @@ def main():
     def step():
         A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=args.lut, return_probes=True, out=out)
 
+    if args.copy_calibration_mib:
+        # known traffic for the counters: a fill writes N bytes, a sum reads N
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
+        float(src.sum())
+        torch.cuda.synchronize()
+        del src
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -163,7 +236,8 @@ def main():
                    "nlist": w.index.nlist, "m": w.index.m, "nq": nq, "nprobe": w.nprobe,
                    "k": w.k, "lut": args.lut},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": stored_traffic(w.name, args.lut),
                      "kernel": "scan_kernel", "kernel_ms": scan_ms,
                      "algorithmic_bytes_per_launch": code_bytes},
         "cpu_baseline": cpu,
