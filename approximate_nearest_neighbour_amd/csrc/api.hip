@@ -191,7 +191,8 @@ void release(ivfpq_index *ix)
     DeviceGuard g(ix->device);
     DeviceIndex &d = ix->dx;
     (void)hipFree(d.centroids);
-    (void)hipFree(d.cnorms);
+    (void)hipFree(d.cblk);
+    (void)hipFree(d.cnorm_pad);
     (void)hipFree(d.codebooks);
     (void)hipFree(d.list_off);
     (void)hipFree(d.codes);
@@ -256,7 +257,10 @@ ivfpq_status alloc_index(int device, int d, int nlist, int m, int64_t ntotal,
     }
     dx.max_list = mx;
     ALLOC_OR_FAIL(dx.centroids, (size_t)nlist * d * 4);
-    ALLOC_OR_FAIL(dx.cnorms, (size_t)nlist * 4);
+    dx.d4 = (d + 3) / 4;
+    dx.nblk = (nlist + 15) / 16;
+    ALLOC_OR_FAIL(dx.cblk, (size_t)dx.nblk * dx.d4 * 64 * 4);
+    ALLOC_OR_FAIL(dx.cnorm_pad, (size_t)dx.nblk * 16 * 4);
     ALLOC_OR_FAIL(dx.codebooks, (size_t)d * 256 * 4);
     ALLOC_OR_FAIL(dx.list_off, ((size_t)nlist + 1) * 4);
     ALLOC_OR_FAIL(dx.codes, (size_t)ntotal * m);
@@ -268,9 +272,10 @@ ivfpq_status alloc_index(int device, int d, int nlist, int m, int64_t ntotal,
 
 ivfpq_status finish_load(ivfpq_index *ix)
 {
-    if (launch_cnorms(ix->dx, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    if (launch_centroid_blocks(ix->dx, nullptr) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
         release(ix);
-        return fail(IVFPQ_E_DEVICE, "centroid norm kernel failed");
+        return fail(IVFPQ_E_DEVICE, "centroid layout kernel failed");
     }
     return IVFPQ_OK;
 }
@@ -539,6 +544,7 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
     const size_t o_total = carve((size_t)nq * 4), o_chunk = carve((size_t)nq * 4);
     const size_t o_count = carve((size_t)nq * 4), o_base = carve(((size_t)nq + 1) * 4);
     const size_t o_bound = carve((size_t)nq * 4), o_counter = carve(4);
+    const size_t o_coarse = carve(coarse_ws_bytes(dx, nq, p->nprobe));
     const size_t o_pd = carve((size_t)pl.max_items * kw * 4);
     const size_t o_pp = carve((size_t)pl.max_items * kw * 4);
     if ((s = ensure_ws(idx, off)))
@@ -555,7 +561,8 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
     pl.part_p = reinterpret_cast<uint32_t *>(ws + o_pp);
 
     prof_record(idx, 0, true, st);
-    hipError_t e = launch_coarse(dx, queries_dev, nq, p->nprobe, probes, nullptr, st);
+    hipError_t e =
+        launch_coarse(dx, queries_dev, nq, p->nprobe, ws + o_coarse, probes, nullptr, st);
     prof_record(idx, 0, false, st);
     if (e != hipSuccess)
         return fail(IVFPQ_E_DEVICE, std::string("coarse kernel: ") + hipGetErrorString(e));
@@ -651,8 +658,12 @@ ivfpq_status ivfpq_coarse_ex(const ivfpq_index *idx, const float *queries_dev, i
     if (!queries_dev || !probes_dev)
         return fail(IVFPQ_E_INVALID_ARG, "a required device pointer is NULL");
     DeviceGuard g(idx->device);
-    hipError_t e = launch_coarse(idx->dx, queries_dev, nq, nprobe, probes_dev, coarse_dist_dev,
-                                 reinterpret_cast<hipStream_t>(stream));
+    ivfpq_index *ix = const_cast<ivfpq_index *>(idx);
+    ivfpq_status s = ensure_ws(ix, coarse_ws_bytes(ix->dx, nq, nprobe));
+    if (s)
+        return s;
+    hipError_t e = launch_coarse(idx->dx, queries_dev, nq, nprobe, ix->ws, probes_dev,
+                                 coarse_dist_dev, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(IVFPQ_E_DEVICE, std::string("coarse kernel: ") + hipGetErrorString(e));
     return ok();

@@ -14,7 +14,10 @@ struct DeviceIndex {
     int64_t ntotal = 0;
     int64_t max_list = 0;
     float *centroids = nullptr;  // [nlist][d]
-    float *cnorms = nullptr;     // [nlist] |c_l|^2
+    int d4 = 0;                  // ceil(d / 4): K-steps of the coarse MFMA
+    int nblk = 0;                // ceil(nlist / 16): 16-centroid blocks
+    float *cblk = nullptr;       // centroids in MFMA B-operand order [nblk][d4][64]
+    float *cnorm_pad = nullptr;  // [nblk * 16] |c_l|^2, +inf past nlist
     float *codebooks = nullptr;  // [m][256][dsub]
     uint32_t *list_off = nullptr; // [nlist + 1]
     uint8_t *codes = nullptr;    // [ntotal][m]
@@ -51,7 +54,11 @@ struct SearchPlan {
 
 // Each launcher enqueues on `stream` and returns the launch status.
 hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
-                         int32_t *probes, float *probe_d, hipStream_t stream);
+                         void *ws, int32_t *probes, float *probe_d, hipStream_t stream);
+hipError_t launch_coarse_valu(const DeviceIndex &ix, const float *queries, int64_t nq,
+                              int nprobe, int32_t *probes, float *probe_d, hipStream_t stream);
+size_t coarse_ws_bytes(const DeviceIndex &ix, int64_t nq, int nprobe);
+hipError_t launch_centroid_blocks(const DeviceIndex &ix, hipStream_t stream);
 hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
                        hipStream_t stream);
 hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
@@ -61,7 +68,6 @@ hipError_t launch_merge(const DeviceIndex &ix, const SearchArgs &s, const Search
 size_t scan_lds_bytes(int d, int m, int nprobe, bool f16, int nw, int g);
 hipError_t launch_luts(const DeviceIndex &ix, const float *queries, int64_t nq,
                        const int32_t *probes, int nprobe, int lut, float *out, hipStream_t stream);
-hipError_t launch_cnorms(const DeviceIndex &ix, hipStream_t stream);
 hipError_t launch_select(const float *keys, int64_t rows, int64_t n, int k, float *out_d,
                          int32_t *out_pos, hipStream_t stream);
 

@@ -1,12 +1,14 @@
 // Auxiliary IVF-PQ kernels for gfx950: the coarse top-nprobe (float32
 // direct differences), the row-wise k-selection on its own, the table
-// writer used for verification, and centroid norms.
+// writer used for verification.
 //
-// Coarse step ("Billion-scale similarity search with GPUs", IVFADC section;
-// "Custom 8-bit floating point value format for reducing shared memory bank
-// conflict in ANN search", IVFPQ search step 1): D[q,l] = |x_q - c_l|^2 for
-// every list, the nprobe smallest are probed.  One workgroup of four waves
-// per query; each wave streams a quarter of the centroids through a register
+// Coarse step on the vector ALUs ("Billion-scale similarity search with
+// GPUs", IVFADC section; "Custom 8-bit floating point value format for
+// reducing shared memory bank conflict in ANN search", IVFPQ search step 1):
+// D[q,l] = |x_q - c_l|^2 for every list by direct differences, the nprobe
+// smallest are probed.  Used where the matrix-core form does not apply
+// (nprobe above 256 or very large d).  One workgroup of four waves per
+// query; each wave streams a quarter of the centroids through a register
 // top-k; the waves share a bound through LDS and end with a bitonic merge.
 #include "common.hpp"
 #include "internal.hpp"
@@ -203,17 +205,6 @@ __global__ __launch_bounds__(kBlock) void lut_kernel(const float *__restrict__ q
         out[pair * m * 256 + e] = table_at<F16>(lut, e);
 }
 
-__global__ void cnorm_kernel(const float *__restrict__ c, int d, int nlist, float *__restrict__ out)
-{
-    const int l = blockIdx.x * blockDim.x + threadIdx.x;
-    if (l < nlist) {
-        float s = 0.f;
-        for (int t = 0; t < d; ++t)
-            s = fmaf(c[(size_t)l * d + t], c[(size_t)l * d + t], s);
-        out[l] = s;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -250,8 +241,8 @@ static hipError_t coarse_nw(const DeviceIndex &ix, const float *queries, int64_t
     return hipGetLastError();
 }
 
-hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
-                         int32_t *probes, float *probe_d, hipStream_t stream)
+hipError_t launch_coarse_valu(const DeviceIndex &ix, const float *queries, int64_t nq,
+                              int nprobe, int32_t *probes, float *probe_d, hipStream_t stream)
 {
     if (nq == 0)
         return hipSuccess;
@@ -312,12 +303,5 @@ hipError_t launch_select(const float *keys, int64_t rows, int64_t n, int k, floa
     }
 }
 
-hipError_t launch_cnorms(const DeviceIndex &ix, hipStream_t stream)
-{
-    const int blocks = (ix.nlist + 255) / 256;
-    hipLaunchKernelGGL(cnorm_kernel, dim3(blocks), dim3(256), 0, stream, ix.centroids, ix.d,
-                       ix.nlist, ix.cnorms);
-    return hipGetLastError();
-}
 
 } // namespace ivfpq
