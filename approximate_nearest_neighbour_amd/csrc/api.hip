@@ -257,8 +257,10 @@ ivfpq_status alloc_index(int device, int d, int nlist, int m, int64_t ntotal,
     }
     dx.max_list = mx;
     ALLOC_OR_FAIL(dx.centroids, (size_t)nlist * d * 4);
-    dx.d4 = (d + 3) / 4;
-    dx.nblk = (nlist + 15) / 16;
+    // K-steps padded to the coarse kernel's register blocking (8, 16, 24 or
+    // 32) and blocks to whole 64-centroid tiles; the padding is zero (norm +inf)
+    dx.d4 = (d + 3) / 4 <= 32 ? ((d + 31) / 32) * 8 : (d + 3) / 4;
+    dx.nblk = ((nlist + 63) / 64) * 4;
     ALLOC_OR_FAIL(dx.cblk, (size_t)dx.nblk * dx.d4 * 64 * 4);
     ALLOC_OR_FAIL(dx.cnorm_pad, (size_t)dx.nblk * 16 * 4);
     ALLOC_OR_FAIL(dx.codebooks, (size_t)d * 256 * 4);

@@ -14,8 +14,8 @@ struct DeviceIndex {
     int64_t ntotal = 0;
     int64_t max_list = 0;
     float *centroids = nullptr;  // [nlist][d]
-    int d4 = 0;                  // ceil(d / 4): K-steps of the coarse MFMA
-    int nblk = 0;                // ceil(nlist / 16): 16-centroid blocks
+    int d4 = 0;                  // K-steps of the coarse MFMA: ceil(d/4) padded to 8/16/24/32
+    int nblk = 0;                // 16-centroid blocks, a multiple of 4 (whole 64-wide tiles)
     float *cblk = nullptr;       // centroids in MFMA B-operand order [nblk][d4][64]
     float *cnorm_pad = nullptr;  // [nblk * 16] |c_l|^2, +inf past nlist
     float *codebooks = nullptr;  // [m][256][dsub]

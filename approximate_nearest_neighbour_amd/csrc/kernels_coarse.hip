@@ -6,14 +6,18 @@
 // search step 1).
 //
 // The dot products are v_mfma_f32_16x16x4_f32 (float32 products and sums).
-// A workgroup of four waves takes TQ = 16*RB queries and sweeps a range of
-// 64-centroid tiles: wave w computes the 16 centroids 16w..16w+15 of a tile
-// for all TQ queries (RB accumulators of 16x16).  Query rows sit in LDS with
-// an odd row stride (conflict-free A-operand reads); centroids were re-laid
-// out at index load so that the B operand of one K-step of one 16-centroid
-// block is 64 consecutive floats (one coalesced load per wave).  The distance
-// tile goes through LDS to the selection: wave w owns QW = TQ/4 queries, each
-// with a register top-k (WaveTopK) fed 64 candidates per tile.
+// A workgroup of 4*RG waves takes TQ = 16*RG queries and sweeps a range of
+// 64-centroid tiles: wave w computes the 16x16 block of query rows
+// 16*(w/4).. and centroids 16*(w%4).. of a tile.  Its A operand (the query
+// rows, all K-steps) stays in registers for the whole sweep; centroids were
+// re-laid out at index load so that the B operand of one K-step of one
+// 16-centroid block is 64 consecutive floats (one coalesced load per wave),
+// and the next tile's B operand is loaded while the current tile is
+// multiplied.  K-steps (KD) and blocks are padded with zeros at load, so the
+// inner loop has no bounds tests.  The
+// distance tile goes through LDS to the selection: each wave owns four
+// queries, each with a register top-k (WaveTopK) fed 64 candidates per tile.
+// More row groups per workgroup = fewer passes over the centroids.
 //
 // With `splits` > 1 the centroid tiles are divided among several workgroups
 // per query tile; their sorted partial top-k are merged by a second kernel.
@@ -53,37 +57,41 @@ __global__ void centroid_blocks_kernel(const float *__restrict__ c, int d, int d
     }
 }
 
-template <int NW, int RB>
-__global__ __launch_bounds__(256) void coarse_mfma_kernel(
-    const float *__restrict__ queries, int64_t nq, int d, int d4, int nblk, int nprobe,
+constexpr int kQueriesPerWave = 4;
+
+template <int NW, int RG, int KD>
+__global__ __launch_bounds__(256 * RG) void coarse_mfma_kernel(
+    const float *__restrict__ queries, int64_t nq, int d, int nblk, int nprobe,
     const float *__restrict__ cblk, const float *__restrict__ cnorm_pad, int splits,
     float *__restrict__ part_d, uint32_t *__restrict__ part_p, int32_t *__restrict__ probes,
     float *__restrict__ probe_d)
 {
-    constexpr int TQ = 16 * RB, QW = TQ / 4, KW = 64 * NW;
+    constexpr int TQ = 16 * RG, THREADS = 256 * RG, QW = kQueriesPerWave, KW = 64 * NW;
+    static_assert(TQ == QW * 4 * RG, "four queries per wave");
     extern __shared__ __align__(16) unsigned char smem[];
-    const int xs = 4 * d4 + 1; // odd stride: the 16 rows of an A read hit 16 banks
-    float *xt = reinterpret_cast<float *>(smem);                 // [TQ][xs]
-    float *xn = xt + TQ * xs;                                     // [TQ]
-    float *dt = xn + TQ;                                          // [2][TQ][64]
+    const int xs = 4 * KD + 1; // odd stride: the 16 rows of an A read hit 16 banks
+    float *xt = reinterpret_cast<float *>(smem);                      // [TQ][xs]
+    float *xn = xt + TQ * xs;                                          // [TQ]
+    float *dt = xn + TQ;                                               // [2][TQ][64]
     uint32_t *stage = reinterpret_cast<uint32_t *>(dt + 2 * TQ * 64); // [TQ][128]
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int rg = wave >> 2, cbk = wave & 3;
     const int64_t q0 = (int64_t)blockIdx.x * TQ;
     const int split = blockIdx.y;
     const int ntile = (nblk + 3) / 4;
     const int t0 = (int)((int64_t)ntile * split / splits);
     const int t1 = (int)((int64_t)ntile * (split + 1) / splits);
 
-    for (int i = tid; i < TQ * 4 * d4; i += 256) {
-        const int row = i / (4 * d4), col = i % (4 * d4);
+    for (int i = tid; i < TQ * 4 * KD; i += THREADS) {
+        const int row = i / (4 * KD), col = i % (4 * KD);
         const int64_t q = q0 + row;
         xt[row * xs + col] = (q < nq && col < d) ? queries[q * d + col] : 0.f;
     }
     __syncthreads();
     if (tid < TQ) {
         float s = 0.f;
-        for (int c = 0; c < 4 * d4; ++c)
+        for (int c = 0; c < 4 * KD; ++c)
             s = fmaf(xt[tid * xs + c], xt[tid * xs + c], s);
         xn[tid] = s;
     }
@@ -94,44 +102,53 @@ __global__ __launch_bounds__(256) void coarse_mfma_kernel(
     for (int i = 0; i < QW; ++i)
         sel[i].init(nprobe, stage + (wave * QW + i) * 128);
 
-    const int arow = lane & 15, acol = lane >> 4;
-    int buf = 0;
-    for (int tile = t0; tile < t1; ++tile) {
-        const int blk = tile * 4 + wave;
-        v4f acc[RB];
+    // A layout of 16x16x4: lane l supplies row l%16, K-index l/16 of each step
+    float a[KD];
+    {
+        const float *ap = xt + (rg * 16 + (lane & 15)) * xs + (lane >> 4);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-            acc[rb] = v4f{0.f, 0.f, 0.f, 0.f};
-        if (blk < nblk) {
-            const float *bp = cblk + (size_t)blk * d4 * 64 + lane;
-#pragma unroll 4
-            for (int s = 0; s < d4; ++s) {
-                const float b = bp[(size_t)s * 64];
+        for (int s = 0; s < KD; ++s)
+            a[s] = ap[4 * s];
+    }
+    float b0[KD], b1[KD];
+    auto load_b = [&](int tile, float (&b)[KD]) {
+        if (tile < t1) {
+            const float *bp = cblk + (size_t)(tile * 4 + cbk) * KD * 64 + lane;
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    const float av = xt[(rb * 16 + arow) * xs + 4 * s + acol];
-                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b, acc[rb], 0, 0, 0);
-                }
-            }
+            for (int s = 0; s < KD; ++s)
+                b[s] = bp[(size_t)s * 64];
         }
+    };
+    // one tile: prefetch the next tile's B into `bn`, multiply with `bc`,
+    // distances through LDS buffer tile&1, then the four selections
+    auto step = [&](int tile, const float (&bc)[KD], float (&bn)[KD]) {
+        const int blk = tile * 4 + cbk, col = lane & 15;
+        load_b(tile + 1, bn);
+        const float cn = cnorm_pad[blk * 16 + col];
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KD; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bc[s], acc, 0, 0, 0);
         // D layout of 16x16x4: lane l holds rows 4*(l/16) + r (r = 0..3) of column l%16
-        const int col = lane & 15;
-        const float cn = blk < nblk ? cnorm_pad[blk * 16 + col] : INFINITY;
-        float *dtile = dt + buf * TQ * 64;
+        float *dtile = dt + (tile & 1) * TQ * 64;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = rb * 16 + 4 * (lane >> 4) + r;
-                dtile[row * 64 + wave * 16 + col] = xn[row] + cn - 2.f * acc[rb][r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int row = rg * 16 + 4 * (lane >> 4) + r;
+            dtile[row * 64 + cbk * 16 + col] = xn[row] + cn - 2.f * acc[r];
         }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < QW; ++i)
             sel[i].push(dtile[(wave * QW + i) * 64 + lane], (uint32_t)(tile * 64 + lane));
-        buf ^= 1;
+    };
+    load_b(t0, b0);
+    int tile = t0;
+    for (; tile + 1 < t1; tile += 2) {
+        step(tile, b0, b1);
+        step(tile + 1, b1, b0);
     }
+    if (tile < t1)
+        step(tile, b0, b1);
 
 #pragma unroll
     for (int i = 0; i < QW; ++i) {
@@ -214,13 +231,17 @@ hipError_t launch_centroid_blocks(const DeviceIndex &ix, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Query rows per workgroup and the centroid split the MFMA path uses.
-static void coarse_shape(int64_t nq, int nblk, int nw, int *rb, int *splits)
+// Row groups per workgroup (16 queries each) and the centroid split: many
+// centroids -> 4 row groups (fewer passes over the centroid array) when the
+// registers allow it (1024 threads leave 128 per lane); the split keeps
+// about 4 workgroup-waves per SIMD busy.
+static void coarse_shape(int64_t nq, int nblk, int d4, int *rg, int *splits)
 {
-    *rb = nw <= 2 ? 2 : 1;
-    const int64_t wgs = (nq + 16 * *rb - 1) / (16 * *rb);
+    *rg = nblk >= 1024 && d4 <= 24 ? 4 : 2;
+    const int64_t wgs = (nq + 16 * *rg - 1) / (16 * *rg);
     const int ntile = (nblk + 3) / 4;
-    int s = (int)((2 * (int64_t)coarse_cu_count() + wgs - 1) / wgs);
+    const int64_t want = (int64_t)coarse_cu_count() * 16 / *rg; // ~4 waves per SIMD
+    int s = (int)((want + wgs - 1) / wgs);
     s = s < 1 ? 1 : s;
     s = s > ntile ? ntile : s;
     s = s > 64 ? 64 : s;
@@ -232,21 +253,21 @@ size_t coarse_ws_bytes(const DeviceIndex &ix, int64_t nq, int nprobe)
     int nw = 1;
     while (nw * 64 < nprobe)
         nw *= 2;
-    if (nw > 4)
+    if (nw > 2 || ix.d4 > 32)
         return 0;
-    int rb, splits;
-    coarse_shape(nq, ix.nblk, nw, &rb, &splits);
+    int rg, splits;
+    coarse_shape(nq, ix.nblk, ix.d4, &rg, &splits);
     return splits > 1 ? (size_t)nq * splits * 64 * nw * 8 : 0;
 }
 
-template <int NW, int RB>
+template <int NW, int RG, int KD>
 static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *queries, int64_t nq,
                                       int nprobe, int splits, void *ws, int32_t *probes,
                                       float *probe_d, hipStream_t stream)
 {
-    constexpr int TQ = 16 * RB;
-    const size_t lds = (size_t)TQ * (4 * ix.d4 + 1) * 4 + TQ * 4 + 2 * TQ * 64 * 4 + TQ * 512;
-    auto kern = coarse_mfma_kernel<NW, RB>;
+    constexpr int TQ = 16 * RG;
+    const size_t lds = (size_t)TQ * (4 * KD + 1) * 4 + TQ * 4 + 2 * TQ * 64 * 4 + TQ * 512;
+    auto kern = coarse_mfma_kernel<NW, RG, KD>;
     if (lds > 160 * 1024)
         return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
@@ -258,7 +279,7 @@ static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *querie
     float *part_d = static_cast<float *>(ws);
     uint32_t *part_p = reinterpret_cast<uint32_t *>(part_d + (size_t)nq * splits * 64 * NW);
     const dim3 grid((unsigned)((nq + TQ - 1) / TQ), (unsigned)splits);
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, queries, nq, ix.d, ix.d4, ix.nblk,
+    hipLaunchKernelGGL(kern, grid, dim3(256 * RG), lds, stream, queries, nq, ix.d, ix.nblk,
                        nprobe, ix.cblk, ix.cnorm_pad, splits, part_d, part_p, probes, probe_d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
@@ -266,6 +287,31 @@ static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *querie
     hipLaunchKernelGGL(coarse_merge_kernel<NW>, dim3((unsigned)nq), dim3(64), 0, stream, part_d,
                        part_p, nq, splits, nprobe, probes, probe_d);
     return hipGetLastError();
+}
+
+template <int NW, int RG>
+static hipError_t coarse_mfma_k(const DeviceIndex &ix, const float *queries, int64_t nq,
+                                int nprobe, int splits, void *ws, int32_t *probes, float *probe_d,
+                                hipStream_t stream)
+{
+    switch (ix.d4) {
+    case 8:
+        return coarse_mfma_variant<NW, RG, 8>(ix, queries, nq, nprobe, splits, ws, probes,
+                                              probe_d, stream);
+    case 16:
+        return coarse_mfma_variant<NW, RG, 16>(ix, queries, nq, nprobe, splits, ws, probes,
+                                               probe_d, stream);
+    case 24:
+        return coarse_mfma_variant<NW, RG, 24>(ix, queries, nq, nprobe, splits, ws, probes,
+                                               probe_d, stream);
+    case 32:
+        if (RG == 2)
+            return coarse_mfma_variant<NW, 2, 32>(ix, queries, nq, nprobe, splits, ws, probes,
+                                                  probe_d, stream);
+        return hipErrorInvalidValue;
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
@@ -276,20 +322,21 @@ hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq
     int nw = 1;
     while (nw * 64 < nprobe)
         nw *= 2;
-    // the MFMA form needs the query tile in LDS (d up to ~2000 fits)
-    const size_t lds_rb2 = (size_t)32 * (4 * ix.d4 + 1) * 4 + 32 * 4 + 2 * 32 * 64 * 4 + 32 * 512;
-    if (nw > 4 || lds_rb2 > 160 * 1024)
+    // the matrix-core form keeps a tile's B operand in registers (d up to 128)
+    // and four register top-k per wave (nprobe up to 128)
+    if (nw > 2 || ix.d4 > 32)
         return launch_coarse_valu(ix, queries, nq, nprobe, probes, probe_d, stream);
-    int rb, splits;
-    coarse_shape(nq, ix.nblk, nw, &rb, &splits);
-    switch (nw) {
-    case 1: return coarse_mfma_variant<1, 2>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
+    int rg, splits;
+    coarse_shape(nq, ix.nblk, ix.d4, &rg, &splits);
+    if (nw == 1)
+        return rg == 4 ? coarse_mfma_k<1, 4>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
+                                             stream)
+                       : coarse_mfma_k<1, 2>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
                                              stream);
-    case 2: return coarse_mfma_variant<2, 2>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
-                                             stream);
-    default: return coarse_mfma_variant<4, 1>(ix, queries, nq, nprobe, splits, ws, probes,
-                                              probe_d, stream);
-    }
+    return rg == 4 ? coarse_mfma_k<2, 4>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
+                                         stream)
+                   : coarse_mfma_k<2, 2>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
+                                         stream);
 }
 
 } // namespace ivfpq

@@ -113,6 +113,7 @@ __global__ __launch_bounds__(1024) void item_scan_kernel(const uint32_t *__restr
 struct ScanArgs {
     const float *queries;
     int d, m, dsub, nlist, nprobe, k, kw;
+    int pg; // tables per group
     const float *centroids;
     const float *codebooks;
     const uint32_t *list_off;
@@ -166,16 +167,16 @@ struct CodeRow {
     }
 };
 
-// R = sum_{j<M} F_j(code[j]), j ascending.  The M table reads are all
-// issued before the first add (they are independent), so one entry costs one
-// LDS round trip rather than M of them.
+// R = sum_{j<M} F_j(code[j]), j ascending, for the M code bytes in the M/4
+// words w.  The M table reads are all issued before the first add (they are
+// independent), so one entry costs one LDS round trip rather than M of them.
 template <int M, bool F16>
-__device__ __forceinline__ float adc(const CodeRow<M> &row, const void *lut)
+__device__ __forceinline__ float adc_words(const uint32_t *w, const void *lut)
 {
     float t[M];
 #pragma unroll
     for (int j = 0; j < M; ++j) {
-        const uint32_t c = (row.w[j >> 2] >> (8 * (j & 3))) & 255u;
+        const uint32_t c = (w[j >> 2] >> (8 * (j & 3))) & 255u;
         t[j] = Table<F16>::get(lut, j * 256 + (int)c);
     }
     float r = t[0];
@@ -231,22 +232,26 @@ void scan_items_kernel(ScanArgs a)
     const int dpad = (d + 3) & ~3;
     const size_t tbytes = (size_t)m * 256 * (F16 ? 2 : 4);
 
+    // Pieces (list, entry range) are handled in groups of PG: one barrier per
+    // group, tables of the next group built while the current one is
+    // scanned (two buffers of PG tables, two of PG residuals).
+    const int PG = a.pg;
     // LDS layout by byte offsets from smem (pointer arithmetic on the LDS
     // array keeps every access a DS instruction)
-    const uint32_t o_misc = 3u * dpad * 4u;
+    const uint32_t o_misc = (1u + 2u * (uint32_t)PG) * dpad * 4u;
     const uint32_t o_pieces = o_misc + 64u;
     const uint32_t o_stage = (o_pieces + (uint32_t)a.nprobe * (uint32_t)sizeof(Piece) + 15u) & ~15u;
     const uint32_t o_tab = o_stage + WAVES * 512u;
     float *xs = reinterpret_cast<float *>(smem);
-    float *rs0 = xs + dpad;
-    float *rs1 = rs0 + dpad;
     // misc: [0] item [1] pieces [2] min bound [4 .. 4+WAVES) per-wave rank values
     uint32_t *misc = reinterpret_cast<uint32_t *>(smem + o_misc);
     uint32_t *pub = misc + 4;
     Piece *pieces = reinterpret_cast<Piece *>(smem + o_pieces);
     unsigned char *tab = smem + o_tab;
-    void *lut0 = tab;
-    void *lut1 = tab + tbytes;
+    auto rsbuf = [&](int b, int p) { return xs + dpad + (b * PG + p) * dpad; };
+    auto tabp = [&](int b, int p) {
+        return reinterpret_cast<void *>(tab + (size_t)(b * PG + p) * tbytes);
+    };
     float *mk = reinterpret_cast<float *>(tab);
     uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (WAVES - 1) * 64 * NW);
 
@@ -288,10 +293,21 @@ void scan_items_kernel(ScanArgs a)
             }
         }
     };
-    auto residual = [&](const Piece &pc, float *rs) {
-        const float *c = a.centroids + (size_t)pc.list * d;
-        for (int t = tid; t < d; t += THREADS)
-            rs[t] = xs[t] - c[t];
+    int np = 0;
+    auto group_size = [&](int grp) { return np - grp * PG < PG ? np - grp * PG : PG; };
+    // residuals x - c_l of the pieces of group grp into residual buffer b
+    auto residual_group = [&](int grp, int b) {
+        const int pn = group_size(grp);
+        for (int i = tid; i < pn * d; i += THREADS) {
+            const int p = i / d, t = i - p * d;
+            const float *c = a.centroids + (size_t)pieces[grp * PG + p].list * d;
+            rsbuf(b, p)[t] = xs[t] - c[t];
+        }
+    };
+    auto build_group = [&](int grp, int b) {
+        const int pn = group_size(grp);
+        for (int p = 0; p < pn; ++p)
+            build(rsbuf(b, p), tabp(b, p));
     };
 
     const uint32_t total_items = a.item_base[a.nq];
@@ -358,7 +374,7 @@ void scan_items_kernel(ScanArgs a)
                 pub[lane] = float_order_key(INFINITY);
         }
         __syncthreads();
-        const int np = (int)misc[1];
+        np = (int)misc[1];
 
         // Union bound: wave w publishes its rk-th smallest value, rk =
         // ceil(k / WAVES); each wave then holds >= rk values <= the largest
@@ -384,70 +400,94 @@ void scan_items_kernel(ScanArgs a)
             sel.bound(float_from_order_key(mx));
         };
 
-        if (np > 0) {
-            residual(pieces[0], rs0);
+        const int ng = (np + PG - 1) / PG;
+        if (ng > 0) {
+            residual_group(0, 0);
             __syncthreads();
-            build(rs0, lut0);
-            if (np > 1)
-                residual(pieces[1], rs1);
+            build_group(0, 0);
+            if (ng > 1)
+                residual_group(1, 1);
             __syncthreads();
         }
-        for (int pi = 0; pi < np; ++pi) {
-            void *lut = (pi & 1) ? lut1 : lut0;
-            if (pi + 1 < np)
-                build((pi & 1) ? rs0 : rs1, (pi & 1) ? lut0 : lut1);
-            if (pi + 2 < np)
-                residual(pieces[pi + 2], (pi & 1) ? rs1 : rs0);
+        for (int grp = 0; grp < ng; ++grp) {
+            if (grp + 1 < ng)
+                build_group(grp + 1, (grp + 1) & 1);
+            if (grp + 2 < ng)
+                residual_group(grp + 2, grp & 1);
             if constexpr (!SO)
                 sel.bound(read_bound(&misc[2]));
-
+            const int pn = group_size(grp);
+            for (int pp = 0; pp < pn; ++pp) {
+            const int pi = grp * PG + pp;
+            void *lut = tabp(grp & 1, pp);
+            // the wave that starts a piece rotates, so that a group of short
+            // lists spreads over the waves
+            const int rank = (wave - pi) & (WAVES - 1);
             const Piece pc = pieces[pi];
             const uint32_t off = a.list_off[pc.list];
             const uint8_t *base = a.codes + (size_t)off * m;
             constexpr uint32_t STRIDE = 64 * WAVES;
-            uint32_t i0 = pc.b + wave * 64;
+            uint32_t i0 = pc.b + rank * 64;
             if constexpr (M > 0) {
-                // full 64-entry steps (no per-lane bounds), code rows read one
-                // step ahead; then at most one partial step
-                constexpr size_t PSTEP = (size_t)STRIDE * M;
-                const uint8_t *p = base + (size_t)(i0 + lane) * M;
-                if (i0 + 64 <= pc.e) {
-                    CodeRow<M> cur;
-                    cur.load(p);
-                    for (;;) {
-                        const uint32_t n0 = i0 + STRIDE;
-                        const bool more = n0 + 64 <= pc.e;
-                        CodeRow<M> nxt;
-                        if (more)
-                            nxt.load(p + PSTEP);
-                        const float r = adc<M, F16>(cur, lut);
+                // Each lane takes EPL consecutive entries per step (16 bytes
+                // of code rows at m <= 8: more bytes in flight per wave).
+                // Full steps need no per-lane bounds and read one step
+                // ahead; then at most one partial step.
+                constexpr int EPL = M >= 16 ? 1 : 16 / M;
+                constexpr uint32_t SPAN = 64 * EPL;          // entries per wave-step
+                constexpr uint32_t WSTRIDE = SPAN * WAVES;   // entries per workgroup-step
+                constexpr size_t PSTEP = (size_t)WSTRIDE * M;
+                using Row = CodeRow<M * EPL>;
+                auto consume = [&](const Row &row, uint32_t first, uint32_t limit) {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        const uint32_t i = first + e;
+                        const float r = i < limit
+                                            ? adc_words<M, F16>(row.w + e * (M / 4), lut)
+                                            : INFINITY;
                         if constexpr (SO) {
                             sink = fminf(sink, r);
                         } else {
-                            sel.push(r, off + i0 + lane);
+                            sel.push(r, off + i);
                             exchange();
                         }
-                        i0 = n0;
+                    }
+                };
+                uint32_t s0 = pc.b + rank * SPAN;
+                const uint8_t *p = base + ((size_t)s0 + (size_t)lane * EPL) * M;
+                if (s0 + SPAN <= pc.e) {
+                    Row cur;
+                    cur.load(p);
+                    for (;;) {
+                        const uint32_t n0 = s0 + WSTRIDE;
+                        const bool more = n0 + SPAN <= pc.e;
+                        Row nxt;
+                        if (more)
+                            nxt.load(p + PSTEP);
+                        consume(cur, s0 + lane * EPL, 0xFFFFFFFFu);
+                        s0 = n0;
                         p += PSTEP;
                         if (!more)
                             break;
                         cur = nxt;
                     }
                 }
-                if (i0 < pc.e) {
-                    const bool in = i0 + lane < pc.e;
-                    CodeRow<M> cur;
-                    if (in)
+                if (s0 < pc.e) {
+                    const uint32_t first = s0 + lane * EPL;
+                    Row cur;
+                    if (first + EPL <= pc.e) {
                         cur.load(p);
-                    else
-                        cur.zero();
-                    const float r = in ? adc<M, F16>(cur, lut) : INFINITY;
-                    if constexpr (SO) {
-                        sink = fminf(sink, r);
                     } else {
-                        sel.push(r, off + i0 + lane);
-                        exchange();
+                        cur.zero();
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e)
+                            if (first + e < pc.e)
+#pragma unroll
+                                for (int wi = 0; wi < M / 4; ++wi)
+                                    cur.w[e * (M / 4) + wi] =
+                                        reinterpret_cast<const uint32_t *>(p + e * M)[wi];
                     }
+                    consume(cur, first, pc.e);
                 }
             } else {
                 for (; i0 < pc.e; i0 += STRIDE) {
@@ -462,6 +502,7 @@ void scan_items_kernel(ScanArgs a)
                     }
                 }
             }
+            } // pieces of the group
             if constexpr (!SO) {
                 publish_bound(&misc[2], sel.kth);
                 if (tid == 0) {
@@ -574,13 +615,23 @@ static int cu_count()
     return n;
 }
 
+// Tables per group: as many as 32 KiB holds (1..8), two groups resident.
+static int tables_per_group(int m, bool f16)
+{
+    const int t = 32768 / (m * 256 * (f16 ? 2 : 4));
+    return t < 1 ? 1 : (t > 8 ? 8 : t);
+}
+
 size_t scan_lds_bytes(int d, int m, int nprobe, bool f16, int nw, int g)
 {
+    const int pg = tables_per_group(m, f16);
     const size_t dpad = (size_t)((d + 3) & ~3);
-    const size_t table = 2 * (size_t)m * 256 * (f16 ? 2 : 4);
+    const size_t table = 2 * (size_t)pg * m * 256 * (f16 ? 2 : 4);
     const size_t merge = (size_t)(4 * g - 1) * 64 * nw * 8;
-    const size_t o_tab = ((dpad * 4 * 3 + 64 + (size_t)nprobe * sizeof(Piece) + 15) & ~(size_t)15) +
-                         (size_t)4 * g * 512;
+    const size_t o_tab =
+        ((dpad * 4 * (1 + 2 * (size_t)pg) + 64 + (size_t)nprobe * sizeof(Piece) + 15) &
+         ~(size_t)15) +
+        (size_t)4 * g * 512;
     return o_tab + (table > merge ? table : merge);
 }
 
@@ -672,6 +723,7 @@ hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     a.nprobe = s.nprobe;
     a.k = s.k;
     a.kw = 64 * nw_of(s.k);
+    a.pg = tables_per_group(ix.m, s.lut != 0);
     a.centroids = ix.centroids;
     a.codebooks = ix.codebooks;
     a.list_off = ix.list_off;

@@ -286,7 +286,7 @@ def zipf_workload(n: int = 1_000_000_000, nlist: int = 262_144, d: int = 96, m: 
     for s in range(0, n, step):
         e = min(n, s + step)
         codes[s:e] = rd.integers(0, 256, size=(e - s, m), dtype=np.uint8)
-    ids = rd.permutation(n).astype(np.int64) if permute_ids else np.arange(n, dtype=np.int64)
+    ids = rd.permutation(n) if permute_ids else np.arange(n, dtype=np.int64)
     q = np.random.default_rng(sq).standard_normal((nq, d), dtype=np.float32)
     return Workload(f"ivfpq_zipf_n{n}_d{d}_m{m}_nlist{nlist}", HostIndex(cent, books, sizes, codes, ids),
                     q, nprobe, k)

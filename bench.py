@@ -32,7 +32,8 @@ def log(*a):
 def workload(name: str):
     from approximate_nearest_neighbour_amd import datagen as G
     makers = {"ivfpq_n1m_d128_m16_nlist1024": G.gmm1m, "ivfpq_tiny_n10k_d32_m4": G.tiny,
-              "ivfpq_n10m_d96_m32_nlist4096": G.gmm10m}
+              "ivfpq_n10m_d96_m32_nlist4096": G.gmm10m,
+              "ivfpq_zipf_n1000000000_d96_m8_nlist262144": G.zipf_workload}
     if name not in makers:
         raise SystemExit(f"unknown workload {name}; choose from {sorted(makers)}")
     return makers[name]()
