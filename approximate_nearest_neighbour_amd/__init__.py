@@ -5,8 +5,10 @@ The search runs in hand-written HIP kernels behind the C ABI of
 (``binding``), the in-tree build (``build_lib``) and host-side input tooling
 (``datagen``: seeded generators, CPU index builder, index file).
 """
-from .binding import (IVFPQError, Index, ivfpq_compute_luts_ex, ivfpq_coarse_ex,  # noqa: F401
-                      ivfpq_free_index, ivfpq_index_info, ivfpq_last_error, ivfpq_load_index,
+from .binding import (IVFPQError, FlatIndex, Index, ivfpq_compute_luts_ex,  # noqa: F401
+                      ivfpq_coarse_ex, ivfpq_flat_free, ivfpq_flat_load_bf16,
+                      ivfpq_flat_profile_begin, ivfpq_flat_profile_end, ivfpq_flat_search_bf16,
+                      ivfpq_flat_search_bf16_ex, ivfpq_free_index, ivfpq_index_info, ivfpq_last_error, ivfpq_load_index,
                       ivfpq_load_index_host, ivfpq_profile_begin, ivfpq_profile_end,
                       ivfpq_search, ivfpq_search_ex, ivfpq_select_topk_ex, ivfpq_status_string,
                       ivfpq_validate_host_index, ivfpq_validate_index_file)

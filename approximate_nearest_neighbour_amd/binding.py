@@ -56,11 +56,20 @@ class Timings(ctypes.Structure):
                 ("work_items", ctypes.c_int64)]
 
 
+class FlatTimings(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("minima_ms", ctypes.c_double), ("kth_ms", ctypes.c_double),
+                ("collect_ms", ctypes.c_double), ("select_ms", ctypes.c_double),
+                ("fallback_ms", ctypes.c_double), ("total_ms", ctypes.c_double)]
+
+
 EXPORTS = ("ivfpq_validate_index_file", "ivfpq_validate_host_index", "ivfpq_load_index",
            "ivfpq_load_index_host", "ivfpq_free_index", "ivfpq_index_info", "ivfpq_search",
            "ivfpq_search_ex", "ivfpq_coarse_ex", "ivfpq_compute_luts_ex", "ivfpq_select_topk_ex",
            "ivfpq_profile_begin",
-           "ivfpq_profile_end", "ivfpq_last_error", "ivfpq_status_string")
+           "ivfpq_profile_end", "ivfpq_flat_load_bf16", "ivfpq_flat_free",
+           "ivfpq_flat_search_bf16_ex", "ivfpq_flat_search_bf16", "ivfpq_flat_profile_begin",
+           "ivfpq_flat_profile_end", "ivfpq_last_error", "ivfpq_status_string")
 
 _lib = None
 
@@ -89,6 +98,12 @@ def lib():
             "ivfpq_select_topk_ex": ([P, i64, i64, i32, P, P, P], st),
             "ivfpq_profile_begin": ([P, i32], st),
             "ivfpq_profile_end": ([P, P], st),
+            "ivfpq_flat_load_bf16": ([P, i64, i32, i32, P], st),
+            "ivfpq_flat_free": ([P], None),
+            "ivfpq_flat_search_bf16_ex": ([P, P, i64, i32, P, P, P], st),
+            "ivfpq_flat_search_bf16": ([P, P, i64, i32, P, P], st),
+            "ivfpq_flat_profile_begin": ([P, i32], st),
+            "ivfpq_flat_profile_end": ([P, P], st),
             "ivfpq_last_error": ([], ctypes.c_char_p),
             "ivfpq_status_string": ([i32], ctypes.c_char_p),
         }
@@ -289,3 +304,89 @@ def ivfpq_profile_end(index: Index) -> dict:
     t = Timings()
     _check(lib().ivfpq_profile_end(index.handle, ctypes.byref(t)))
     return {f: getattr(t, f) for f, _ in Timings._fields_ if f != "reserved"}
+
+
+# ---------------------------------------------------------------------------
+# exact search over a flat bfloat16 database
+# ---------------------------------------------------------------------------
+
+class FlatIndex:
+    """Owner of a device flat-database handle."""
+
+    def __init__(self, handle: ctypes.c_void_p, n: int, d: int):
+        self._h = handle
+        self.n, self.d = n, d
+
+    @property
+    def handle(self):
+        if not self._h:
+            raise ValueError("flat index is closed")
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().ivfpq_flat_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def ivfpq_flat_load_bf16(vectors: np.ndarray, device: int = 0) -> FlatIndex:
+    """Upload [n, d] bfloat16 bit patterns (uint16, host)."""
+    v = np.ascontiguousarray(vectors, dtype=np.uint16)
+    h = ctypes.c_void_p()
+    _check(lib().ivfpq_flat_load_bf16(_np_ptr(v), v.shape[0], v.shape[1], device,
+                                      ctypes.byref(h)))
+    return FlatIndex(h, v.shape[0], v.shape[1])
+
+
+def ivfpq_flat_free(flat: FlatIndex) -> None:
+    flat.close()
+
+
+def _bf16_bits(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    return _dev(t, torch.int16)
+
+
+def ivfpq_flat_search_bf16_ex(flat: FlatIndex, queries: torch.Tensor, k: int, out=None,
+                              stream=None):
+    """Asynchronous exact search; queries: [nq, d] device tensor of bfloat16 (or
+    its bit patterns as int16).  Returns (distances [nq,k] float32, ids [nq,k]
+    int64 row numbers)."""
+    q = _bf16_bits(queries)
+    nq = q.shape[0]
+    if out is None:
+        dist = torch.empty((nq, k), dtype=torch.float32, device=q.device)
+        ids = torch.empty((nq, k), dtype=torch.int64, device=q.device)
+    else:
+        dist, ids = out
+    _check(lib().ivfpq_flat_search_bf16_ex(flat.handle, ctypes.c_void_p(q.data_ptr()), nq, k,
+                                           ctypes.c_void_p(dist.data_ptr()),
+                                           ctypes.c_void_p(ids.data_ptr()), _stream_ptr(stream)))
+    return dist, ids
+
+
+def ivfpq_flat_search_bf16(flat: FlatIndex, queries: np.ndarray, k: int):
+    """Blocking exact search on host bfloat16 bit patterns (uint16 [nq, d])."""
+    q = np.ascontiguousarray(queries, dtype=np.uint16)
+    nq = q.shape[0]
+    d = np.empty((nq, k), dtype=np.float32)
+    i = np.empty((nq, k), dtype=np.int64)
+    _check(lib().ivfpq_flat_search_bf16(flat.handle, _np_ptr(q), nq, k, _np_ptr(d), _np_ptr(i)))
+    return d, i
+
+
+def ivfpq_flat_profile_begin(flat: FlatIndex, max_calls: int) -> None:
+    _check(lib().ivfpq_flat_profile_begin(flat.handle, max_calls))
+
+
+def ivfpq_flat_profile_end(flat: FlatIndex) -> dict:
+    t = FlatTimings()
+    _check(lib().ivfpq_flat_profile_end(flat.handle, ctypes.byref(t)))
+    return {f: getattr(t, f) for f, _ in FlatTimings._fields_ if f != "reserved"}

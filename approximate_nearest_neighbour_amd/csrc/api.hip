@@ -334,6 +334,59 @@ void prof_record(ivfpq_index *ix, int stage, bool start, hipStream_t s)
         ix->prof_used[(size_t)ix->prof_calls * kStages + stage] = 1;
 }
 
+// Flat bfloat16 database handle.
+struct FlatEvent {
+    int stage;
+    EventPair ev;
+};
+
+} // namespace
+
+struct ivfpq_flat {
+    int device = 0;
+    FlatDevice fx;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    bool profiling = false;
+    int prof_max = 0, prof_calls = 0;
+    size_t prof_next = 0;
+    std::vector<FlatEvent> prof_pool;
+    std::vector<size_t> prof_call_first; // first pool slot of each recorded call
+};
+
+namespace {
+
+constexpr size_t kFlatWsBudget = (size_t)4 << 30; // workspace cap; larger batches run in chunks
+constexpr int kFlatEventsPerCall = 64;
+constexpr int kFlatStages = 5; // minima, kth, collect, select, fallback
+
+void flat_release(ivfpq_flat *f)
+{
+    if (!f)
+        return;
+    DeviceGuard g(f->device);
+    (void)hipFree(f->fx.vec);
+    (void)hipFree(f->fx.norms);
+    (void)hipFree(f->ws);
+    for (auto &e : f->prof_pool) {
+        if (e.ev.start)
+            (void)hipEventDestroy(e.ev.start);
+        if (e.ev.stop)
+            (void)hipEventDestroy(e.ev.stop);
+    }
+    delete f;
+}
+
+// Event pair for one flat kernel launch while profiling, else nullptr.
+EventPair *flat_prof_slot(ivfpq_flat *f, int stage)
+{
+    if (!f->profiling || f->prof_calls >= f->prof_max || f->prof_next >= f->prof_pool.size())
+        return nullptr;
+    FlatEvent &e = f->prof_pool[f->prof_next++];
+    e.stage = stage;
+    return &e.ev;
+}
+
 } // namespace
 
 extern "C" {
@@ -766,6 +819,231 @@ ivfpq_status ivfpq_profile_end(ivfpq_index *idx, ivfpq_timings *out)
     out->scanned_entries = idx->prof_entries;
     out->work_items = idx->prof_items;
     idx->profiling = false;
+    return ok();
+}
+
+
+// ---------------------------------------------------------------------------
+// flat bfloat16 exact search
+// ---------------------------------------------------------------------------
+
+ivfpq_status ivfpq_flat_load_bf16(const uint16_t *vectors, int64_t n, int d, int device,
+                                  ivfpq_flat **out)
+{
+    if (!out)
+        return fail(IVFPQ_E_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (d < 1 || d > 256)
+        return fail(IVFPQ_E_INVALID_ARG, "d must be in [1, 256]");
+    if (n < 0 || n >= (int64_t)0xFFFFFFFFll - 64)
+        return fail(IVFPQ_E_INVALID_ARG, "n must be in [0, 2^32 - 65]");
+    if (!vectors && n > 0)
+        return fail(IVFPQ_E_INVALID_ARG, "vectors is NULL");
+    ivfpq_status s = device_check(device);
+    if (s)
+        return s;
+    DeviceGuard g(device);
+    if (!g.ok)
+        return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
+    ivfpq_flat *f = new (std::nothrow) ivfpq_flat;
+    if (!f)
+        return fail(IVFPQ_E_OUT_OF_MEMORY, "host allocation failed");
+    f->device = device;
+    FlatDevice &fx = f->fx;
+    fx.d = d;
+    fx.dp = (d + 31) / 32 * 32;
+    fx.n = n;
+    fx.npad = (n + 63) / 64 * 64;
+    void *src = nullptr;
+    if (dev_alloc(reinterpret_cast<void **>(&fx.vec), (size_t)fx.npad * fx.dp * 2) != hipSuccess ||
+        dev_alloc(reinterpret_cast<void **>(&fx.norms), (size_t)fx.npad * 4) != hipSuccess ||
+        dev_alloc(&src, (size_t)n * d * 2) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(src);
+        flat_release(f);
+        return fail(IVFPQ_E_OUT_OF_MEMORY, "device allocation failed");
+    }
+    if ((n > 0 && hipMemcpy(src, vectors, (size_t)n * d * 2, hipMemcpyHostToDevice) != hipSuccess) ||
+        launch_flat_pack(static_cast<const uint16_t *>(src), n, d, fx.dp, fx.npad, fx.vec,
+                         fx.norms, nullptr) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(src);
+        flat_release(f);
+        return fail(IVFPQ_E_DEVICE, "database upload failed");
+    }
+    (void)hipFree(src);
+    // max |y|^2 (the rounding allowance of the collect bound)
+    if (n > 0) {
+        std::vector<float> nrm((size_t)n);
+        if (hipMemcpy(nrm.data(), fx.norms, (size_t)n * 4, hipMemcpyDeviceToHost) != hipSuccess) {
+            flat_release(f);
+            return fail(IVFPQ_E_DEVICE, "database upload failed");
+        }
+        for (float v : nrm)
+            fx.ymax = v > fx.ymax ? v : fx.ymax;
+    }
+    *out = f;
+    return ok();
+}
+
+void ivfpq_flat_free(ivfpq_flat *f) { flat_release(f); }
+
+ivfpq_status ivfpq_flat_search_bf16_ex(const ivfpq_flat *cf, const uint16_t *queries_dev,
+                                       int64_t nq, int k, float *distances_dev,
+                                       int64_t *ids_dev, void *stream)
+{
+    ivfpq_flat *f = const_cast<ivfpq_flat *>(cf);
+    if (!f)
+        return fail(IVFPQ_E_INVALID_ARG, "flat handle is NULL");
+    if (nq < 0 || nq > (int64_t)0x7FFFFFFF)
+        return fail(IVFPQ_E_INVALID_ARG, "nq must be in [0, 2^31)");
+    if (k < 1 || k > kMaxK)
+        return fail(IVFPQ_E_INVALID_ARG, "k must be in [1, 1024]");
+    if (nq == 0)
+        return ok();
+    if (!queries_dev || !distances_dev || !ids_dev)
+        return fail(IVFPQ_E_INVALID_ARG, "a required device pointer is NULL");
+    DeviceGuard g(f->device);
+    if (!g.ok)
+        return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const FlatDevice &fx = f->fx;
+    const FlatPlan plan = flat_plan(fx.n, k, nq);
+    const size_t per_q = flat_ws_bytes(plan, 1);
+    // test hook: IVFPQ_TEST_FLAT_WS_BYTES=n caps the workspace (forces chunks)
+    size_t budget = kFlatWsBudget;
+    if (const char *env = std::getenv("IVFPQ_TEST_FLAT_WS_BYTES"))
+        budget = (size_t)std::atoll(env);
+    int64_t chunk = (int64_t)(budget / per_q);
+    chunk = chunk < 1 ? 1 : chunk > nq ? nq : chunk;
+    // the same plan for every chunk (the bound pass's shape depends on nq only
+    // through the parts count, fixed above)
+    if (f->ws_bytes < flat_ws_bytes(plan, chunk)) {
+        if (f->ws) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(f->ws);
+            f->ws = nullptr;
+            f->ws_bytes = 0;
+        }
+        if (dev_alloc(&f->ws, flat_ws_bytes(plan, chunk)) != hipSuccess) {
+            (void)hipGetLastError();
+            f->ws = nullptr;
+            return fail(IVFPQ_E_OUT_OF_MEMORY, "workspace allocation failed");
+        }
+        f->ws_bytes = flat_ws_bytes(plan, chunk);
+    }
+    if (f->profiling && f->prof_calls < f->prof_max)
+        f->prof_call_first.push_back(f->prof_next);
+    static const char *names[kFlatStages] = {"minima", "kth", "collect", "select", "fallback"};
+    for (int64_t c0 = 0; c0 < nq; c0 += chunk) {
+        const int64_t cn = nq - c0 < chunk ? nq - c0 : chunk;
+        for (int stage = 0; stage < kFlatStages; ++stage) {
+            EventPair *ev = flat_prof_slot(f, stage);
+            if (ev)
+                (void)hipEventRecord(ev->start, st);
+            hipError_t e = launch_flat_stage(fx, queries_dev + c0 * fx.d, cn, k, plan, f->ws,
+                                             distances_dev + c0 * k, ids_dev + c0 * k, stage, st);
+            if (ev)
+                (void)hipEventRecord(ev->stop, st);
+            if (e != hipSuccess)
+                return fail(IVFPQ_E_DEVICE,
+                            std::string("flat ") + names[stage] + " kernel: " + hipGetErrorString(e));
+        }
+    }
+    if (f->profiling && f->prof_calls < f->prof_max)
+        f->prof_calls++;
+    return ok();
+}
+
+ivfpq_status ivfpq_flat_search_bf16(const ivfpq_flat *f, const uint16_t *queries, int64_t nq,
+                                    int k, float *distances, int64_t *ids)
+{
+    if (!f)
+        return fail(IVFPQ_E_INVALID_ARG, "flat handle is NULL");
+    if (nq < 0 || nq > (int64_t)0x7FFFFFFF)
+        return fail(IVFPQ_E_INVALID_ARG, "nq must be in [0, 2^31)");
+    if (k < 1 || k > kMaxK)
+        return fail(IVFPQ_E_INVALID_ARG, "k must be in [1, 1024]");
+    if (nq == 0)
+        return ok();
+    if (!queries || !distances || !ids)
+        return fail(IVFPQ_E_INVALID_ARG, "a required pointer is NULL");
+    DeviceGuard g(f->device);
+    if (!g.ok)
+        return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
+    const size_t qb = ((size_t)nq * f->fx.d * 2 + 255) & ~(size_t)255;
+    const size_t db = (size_t)nq * k * 4, ib = (size_t)nq * k * 8;
+    void *buf = nullptr;
+    if (dev_alloc(&buf, qb + db + ib) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(IVFPQ_E_OUT_OF_MEMORY, "device allocation failed");
+    }
+    unsigned char *b = static_cast<unsigned char *>(buf);
+    uint16_t *dq = reinterpret_cast<uint16_t *>(b);
+    int64_t *di = reinterpret_cast<int64_t *>(b + qb);
+    float *dd = reinterpret_cast<float *>(b + qb + ib);
+    if (hipMemcpy(dq, queries, (size_t)nq * f->fx.d * 2, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(buf);
+        return fail(IVFPQ_E_DEVICE, "query upload failed");
+    }
+    ivfpq_status s = ivfpq_flat_search_bf16_ex(f, dq, nq, k, dd, di, nullptr);
+    if (s == IVFPQ_OK) {
+        if (hipStreamSynchronize(nullptr) != hipSuccess ||
+            hipMemcpy(distances, dd, db, hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(ids, di, ib, hipMemcpyDeviceToHost) != hipSuccess)
+            s = fail(IVFPQ_E_DEVICE, "search failed on the device");
+    }
+    (void)hipFree(buf);
+    return s;
+}
+
+ivfpq_status ivfpq_flat_profile_begin(ivfpq_flat *f, int max_calls)
+{
+    if (!f || max_calls < 1 || max_calls > 100000)
+        return fail(IVFPQ_E_INVALID_ARG, "bad profile arguments");
+    DeviceGuard g(f->device);
+    const size_t need = (size_t)max_calls * kFlatEventsPerCall;
+    while (f->prof_pool.size() < need) {
+        FlatEvent e{0, {}};
+        if (hipEventCreate(&e.ev.start) != hipSuccess || hipEventCreate(&e.ev.stop) != hipSuccess)
+            return fail(IVFPQ_E_DEVICE, "event creation failed");
+        f->prof_pool.push_back(e);
+    }
+    f->profiling = true;
+    f->prof_max = max_calls;
+    f->prof_calls = 0;
+    f->prof_next = 0;
+    f->prof_call_first.clear();
+    return ok();
+}
+
+ivfpq_status ivfpq_flat_profile_end(ivfpq_flat *f, ivfpq_flat_timings *out)
+{
+    if (!f || !out)
+        return fail(IVFPQ_E_INVALID_ARG, "NULL argument");
+    DeviceGuard g(f->device);
+    std::memset(out, 0, sizeof *out);
+    double *slot[kFlatStages] = {&out->minima_ms, &out->kth_ms, &out->collect_ms, &out->select_ms,
+                                 &out->fallback_ms};
+    for (size_t i = 0; i < f->prof_next; ++i) {
+        const FlatEvent &e = f->prof_pool[i];
+        if (hipEventSynchronize(e.ev.stop) != hipSuccess)
+            return fail(IVFPQ_E_DEVICE, "event synchronisation failed");
+        float ms = 0.f;
+        (void)hipEventElapsedTime(&ms, e.ev.start, e.ev.stop);
+        *slot[e.stage] += ms;
+    }
+    for (size_t c = 0; c < f->prof_call_first.size(); ++c) {
+        const size_t a = f->prof_call_first[c];
+        const size_t z = c + 1 < f->prof_call_first.size() ? f->prof_call_first[c + 1] : f->prof_next;
+        if (z > a) {
+            float ms = 0.f;
+            (void)hipEventElapsedTime(&ms, f->prof_pool[a].ev.start, f->prof_pool[z - 1].ev.stop);
+            out->total_ms += ms;
+        }
+    }
+    out->calls = f->prof_calls;
+    f->profiling = false;
     return ok();
 }
 

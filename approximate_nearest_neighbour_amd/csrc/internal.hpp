@@ -71,6 +71,34 @@ hipError_t launch_luts(const DeviceIndex &ix, const float *queries, int64_t nq,
 hipError_t launch_select(const float *keys, int64_t rows, int64_t n, int k, float *out_d,
                          int32_t *out_pos, hipStream_t stream);
 
+// Flat bfloat16 database on the device: rows padded to dp = 32*ceil(d/32)
+// values (zeros) and to npad = 64*ceil(n/64) rows (zero rows, norm +inf).
+struct FlatDevice {
+    int d = 0, dp = 0;
+    int64_t n = 0, npad = 0;
+    uint16_t *vec = nullptr; // [npad][dp]
+    float *norms = nullptr;  // [npad] |y|^2 in float32
+    float ymax = 0.f;        // max |y|^2 over the rows
+};
+
+// Shape of one flat search: 64-row tiles, segments of `seg` tiles (16 slot
+// minima per query each), and the candidate capacity per query.
+struct FlatPlan {
+    int64_t ntile = 0;
+    int seg = 1;
+    int64_t nseg = 0, nslot = 0;
+    uint32_t cap = 0;
+};
+
+FlatPlan flat_plan(int64_t n, int k, int64_t nq);
+size_t flat_ws_bytes(const FlatPlan &p, int64_t nq);
+hipError_t launch_flat_pack(const uint16_t *src, int64_t n, int d, int dp, int64_t npad,
+                            uint16_t *dst, float *norms, hipStream_t stream);
+// stage 0: clear + slot minima, 1: k-th minimum, 2: collect, 3: select, 4: fallback
+hipError_t launch_flat_stage(const FlatDevice &fx, const uint16_t *queries, int64_t nq, int k,
+                             const FlatPlan &p, void *ws, float *out_d, int64_t *out_i, int stage,
+                             hipStream_t stream);
+
 // Largest k / nprobe the selection supports.
 constexpr int kMaxK = 1024;
 

@@ -1,0 +1,672 @@
+// Exact k-nearest-neighbour search over a flat bfloat16 database
+// ("Billion-scale similarity search with GPUs", exact search section: the
+// squared L2 distance expands into |x|^2 + |y|^2 - 2 x.y, the x.y term is a
+// matrix multiply, and a k-selection over each row of the distance matrix
+// gives the result; here bf16 x bf16 products with float32 sums on the
+// matrix cores, v_mfma_f32_16x16x32_bf16).
+//
+// The distance matrix is never stored.  Four passes per batch of queries:
+//
+//  1. minima:  the GEMM over every 64-row tile; per query, each lane keeps the
+//              running minimum of u = |y|^2 - 2 x.y over the rows it sees in
+//              a segment of G tiles (16 rows per tile: its column in each of
+//              the 4 column blocks) and writes it out per segment: P = 16 *
+//              segments "slot minima" per query, each the value of a
+//              distinct row.
+//  2. kth:     a value v with at least k slot minima <= v, close above the
+//              k-th smallest (histogram of the minima).  Those k slot rows
+//              are distinct rows with u <= v, so the k-th smallest distance is
+//              at most |x|^2 + v (plus rounding).  tu = v + slack, slack =
+//              2^-20 (|x|^2 + max |y|^2), covers the float32 rounding of u and
+//              of the distance.
+//  3. collect: the GEMM again; rows with u <= tu (a superset of the true top
+//              k, about k rows) are appended with their distance to the
+//              query's candidate buffer (capacity C).
+//  4. select:  exact top-k of each buffer (four-wave register selection).
+//              A query whose candidates overflowed C (only when very many rows
+//              tie) is redone by `fallback`, an exact streaming selection over
+//              the whole database.
+//
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace ivfpq {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// |v|^2 of a bf16 row in float32, terms added in index order.
+__device__ __forceinline__ float bf16_row_norm(const uint16_t *v, int d)
+{
+    float s = 0.f;
+    for (int t = 0; t < d; ++t) {
+        const float x = bf16_to_float(v[t]);
+        s = fmaf(x, x, s);
+    }
+    return s;
+}
+
+// The distance from the accumulated dot product: |x|^2 + |y|^2 - 2 x.y.
+__device__ __forceinline__ float flat_distance(float xn, float yn, float dot)
+{
+    return fmaf(-2.f, dot, xn + yn);
+}
+
+// Device copy of the database: rows padded to dp = 32 * ks bf16 (zeros) and
+// to a whole number of 64-row tiles (zero rows with norm +inf).
+__global__ void flat_pack_kernel(const uint16_t *__restrict__ src, int64_t n, int d, int dp,
+                                 int64_t npad, uint16_t *__restrict__ dst, float *__restrict__ norms)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < npad * dp) {
+        const int64_t row = i / dp;
+        const int col = (int)(i % dp);
+        dst[i] = (row < n && col < d) ? src[row * d + col] : (uint16_t)0;
+    }
+    if (i < npad)
+        norms[i] = i < n ? bf16_row_norm(src + i * d, d) : INFINITY;
+}
+
+// A operand of 16x16x32: lane l supplies row l%16, K-indices 8*(l/16)..+7 of
+// each 32-wide K-step (the B operand uses the same K-split, so the dot
+// product does not depend on how the hardware pairs them).
+template <int KS>
+__device__ __forceinline__ void load_a(const uint16_t *__restrict__ q, int64_t nq, int d,
+                                       int64_t row, int lane, bf16x8 (&a)[KS])
+{
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int k = 32 * s + 8 * (lane >> 4) + e;
+            v[e] = (row < nq && k < d) ? q[row * d + k] : (uint16_t)0;
+        }
+        a[s] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+template <int KS>
+__device__ __forceinline__ v4f mfma_block(const bf16x8 (&a)[KS], const bf16x8 (&b)[KS])
+{
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
+    return acc;
+}
+
+// u = |y|^2 - 2 x.y: the distance less |x|^2, one instruction per pair.
+__device__ __forceinline__ float flat_u(float yn, float dot) { return fmaf(-2.f, dot, yn); }
+
+// Rounding allowance between u + |x|^2 and the float32 distance (both from
+// the same dot product): 16 units of 2^-24 of |x|^2 + max |y|^2.
+__device__ __forceinline__ float flat_slack(float xn, float ymax)
+{
+    return 0x1p-20f * (xn + ymax);
+}
+
+enum FlatPass { kPassMinima = 0, kPassCollect = 1 };
+
+// Passes 1 and 3 (GEMM over every tile).  Workgroup: 4 waves, TQ = 64*RB
+// queries (wave w: row blocks w*RB..), tiles [t0, t1) made of whole
+// segments of `seg` tiles.  Tiles are staged in LDS (double buffer, one
+// barrier per tile); each wave multiplies its RB row blocks by the tile's 4
+// column blocks, one column block at a time (RB accumulators live).
+template <int KS, int RB, int PASS>
+__global__ __launch_bounds__(256) void flat_gemm_kernel(
+    const uint16_t *__restrict__ queries, int64_t nq, int d, const uint16_t *__restrict__ db,
+    const float *__restrict__ dbn, int64_t n, int64_t ntile, int seg, int64_t nseg, int splits,
+    float *__restrict__ slots, int64_t nslot, const float *__restrict__ tuq, uint32_t cap,
+    uint32_t *__restrict__ cnt, float *__restrict__ cand_d, uint32_t *__restrict__ cand_p)
+{
+    constexpr int DP = 32 * KS, TQ = 64 * RB, RS = DP + 8; // LDS row stride (bf16), +16 B
+    constexpr int CHUNKS = 64 * DP / 8 / 256;              // 16-byte pieces per thread per tile
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *xn = reinterpret_cast<float *>(smem);          // [TQ]
+    float *tq = xn + TQ;                                   // [TQ]
+    float *yn = tq + TQ;                                   // [2][64]
+    uint16_t *bt = reinterpret_cast<uint16_t *>(yn + 128); // [2][64][RS]
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t q0 = (int64_t)blockIdx.x * TQ;
+    const int64_t s0 = nseg * blockIdx.y / splits, s1 = nseg * (blockIdx.y + 1) / splits;
+    const int64_t t0 = s0 * seg, t1 = s1 * seg < ntile ? s1 * seg : ntile;
+
+    if (PASS == kPassCollect) {
+        for (int r = tid; r < TQ; r += 256) {
+            const int64_t q = q0 + r;
+            xn[r] = q < nq ? bf16_row_norm(queries + q * d, d) : 0.f;
+            tq[r] = q < nq ? tuq[q] : -INFINITY;
+        }
+    }
+    bf16x8 a[RB][KS];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+        load_a<KS>(queries, nq, d, q0 + (wave * RB + rb) * 16 + (lane & 15), lane, a[rb]);
+
+    u16x8 stg[CHUNKS];
+    float ystg = INFINITY;
+    auto fetch = [&](int64_t t) {
+        if (t < t1) {
+#pragma unroll
+            for (int c = 0; c < CHUNKS; ++c) {
+                const int piece = c * 256 + tid; // 16-byte piece of the 64 x DP tile
+                const int row = piece / (DP / 8), col = (piece % (DP / 8)) * 8;
+                stg[c] = *reinterpret_cast<const u16x8 *>(db + (t * 64 + row) * DP + col);
+            }
+            if (tid < 64)
+                ystg = dbn[t * 64 + tid];
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) {
+            const int piece = c * 256 + tid;
+            const int row = piece / (DP / 8), col = (piece % (DP / 8)) * 8;
+            *reinterpret_cast<u16x8 *>(bt + (buf * 64 + row) * RS + col) = stg[c];
+        }
+        if (tid < 64)
+            yn[buf * 64 + tid] = ystg;
+    };
+    fetch(t0);
+    stash(0);
+    __syncthreads();
+    // per lane: the 16 query rows it holds in the D layout (4*(lane/16) + r of
+    // each row block)
+    float xr[RB][4], tr[RB][4], mn[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = (wave * RB + rb) * 16 + 4 * (lane >> 4) + r;
+            if (PASS == kPassCollect) {
+                xr[rb][r] = xn[row];
+                tr[rb][r] = tq[row];
+            }
+            mn[rb][r] = INFINITY;
+        }
+
+    for (int64_t t = t0; t < t1; ++t) {
+        const int buf = (int)(t - t0) & 1;
+        fetch(t + 1);
+        // not unrolled: the compiler would keep all four blocks' operands live
+#pragma unroll 1
+        for (int cb = 0; cb < 4; ++cb) {
+            bf16x8 b[KS];
+            const uint16_t *bp = bt + (buf * 64 + cb * 16 + (lane & 15)) * RS + 8 * (lane >> 4);
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                b[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(bp + 32 * s));
+            const float ycol = yn[buf * 64 + cb * 16 + (lane & 15)];
+            v4f acc[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                acc[rb] = mfma_block<KS>(a[rb], b);
+            if (PASS == kPassMinima) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        mn[rb][r] = fminf(mn[rb][r], flat_u(ycol, acc[rb][r]));
+            } else {
+                // rows under the bound are rare (about k of n per query): one
+                // scalar test per row block (its 4 rows), then per row
+                const int64_t row = t * 64 + cb * 16 + (lane & 15);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    bool pass[4];
+                    bool any = false;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pass[r] = flat_u(ycol, acc[rb][r]) <= tr[rb][r];
+                        any |= pass[r];
+                    }
+                    if (!__builtin_amdgcn_ballot_w64(any))
+                        continue;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t q = q0 + (wave * RB + rb) * 16 + 4 * (lane >> 4) + r;
+                        if (pass[r] && row < n && q < nq) {
+                            const uint32_t slot = atomicAdd(cnt + q, 1u);
+                            if (slot < cap) {
+                                cand_d[(size_t)q * cap + slot] =
+                                    flat_distance(xr[rb][r], ycol, acc[rb][r]);
+                                cand_p[(size_t)q * cap + slot] = (uint32_t)row;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        if (PASS == kPassMinima && ((t + 1) % seg == 0 || t + 1 == t1)) {
+            const int64_t sg = t / seg;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t q = q0 + (wave * RB + rb) * 16 + 4 * (lane >> 4) + r;
+                    if (q < nq)
+                        slots[q * nslot + sg * 16 + (lane & 15)] = mn[rb][r];
+                    mn[rb][r] = INFINITY;
+                }
+        }
+        if (t + 1 < t1)
+            stash(buf ^ 1);
+        __syncthreads();
+    }
+}
+
+// Block-wide (256 threads) reductions through LDS scratch red[8].
+__device__ __forceinline__ float block_min(float v, float *red)
+{
+    for (int s = 32; s >= 1; s >>= 1)
+        v = fminf(v, __shfl_xor(v, s));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return fminf(fminf(red[0], red[1]), fminf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_max(float v, float *red)
+{
+    return -block_min(-v, red);
+}
+
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *red)
+{
+    for (int s = 32; s >= 1; s >>= 1)
+        v += (uint32_t)__shfl_xor((int)v, s);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+}
+
+constexpr int kKthBins = 2048; // 8 per thread
+
+// Pass 2: per query an upper bound v of the k-th smallest of its nslot slot
+// minima with at least k minima <= v: a 2048-bin histogram of the finite
+// minima over [min, max] (count and largest member per bin); v = the largest
+// member of the bins up to the one that holds the k-th.  Then the collect
+// threshold tu = v + slack (+inf when fewer than k minima are finite).
+__global__ __launch_bounds__(256) void flat_kth_kernel(const uint16_t *__restrict__ queries, int d,
+                                                       const float *__restrict__ slots,
+                                                       int64_t nslot, int k, float ymax,
+                                                       float *__restrict__ tuq)
+{
+    __shared__ uint32_t cnt[kKthBins], bmax[kKthBins];
+    __shared__ float redf[8];
+    __shared__ uint32_t redu[8];
+    const int64_t q = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float *sq = slots + q * nslot;
+    float lo = INFINITY, hi = -INFINITY;
+    uint32_t fin = 0;
+    for (int64_t i = tid; i < nslot; i += 256) {
+        const float v = sq[i];
+        if (v < INFINITY) {
+            lo = fminf(lo, v);
+            hi = fmaxf(hi, v);
+            ++fin;
+        }
+    }
+    lo = block_min(lo, redf);
+    hi = block_max(hi, redf);
+    fin = block_sum(fin, redu);
+    float v;
+    if (fin < (uint32_t)k) {
+        v = INFINITY;
+    } else if (!(hi > lo)) {
+        v = lo;
+    } else {
+        const float scale = kKthBins / (hi - lo);
+        for (int b = tid; b < kKthBins; b += 256) {
+            cnt[b] = 0;
+            bmax[b] = 0;
+        }
+        __syncthreads();
+        for (int64_t i = tid; i < nslot; i += 256) {
+            const float x = sq[i];
+            if (x < INFINITY) {
+                int b = (int)((x - lo) * scale);
+                b = b < 0 ? 0 : b >= kKthBins ? kKthBins - 1 : b;
+                atomicAdd(&cnt[b], 1u);
+                atomicMax(&bmax[b], float_order_key(x));
+            }
+        }
+        __syncthreads();
+        // thread t owns bins 8t..8t+7: local sums, block prefix, find the bin
+        uint32_t local = 0;
+        for (int j = 0; j < 8; ++j)
+            local += cnt[8 * tid + j];
+        const int wave = tid >> 6, lane = tid & 63;
+        uint32_t incl = wave_inclusive_sum(local);
+        __syncthreads();
+        if (lane == 63)
+            redu[wave] = incl;
+        __syncthreads();
+        for (int w = 0; w < wave; ++w)
+            incl += redu[w];
+        uint32_t before = incl - local;
+        int found = kKthBins;
+        if (before < (uint32_t)k && incl >= (uint32_t)k) {
+            for (int j = 0; j < 8; ++j) {
+                before += cnt[8 * tid + j];
+                if (before >= (uint32_t)k) {
+                    found = 8 * tid + j;
+                    break;
+                }
+            }
+            redu[4] = (uint32_t)found;
+        }
+        __syncthreads();
+        const int bsel = (int)redu[4];
+        // largest member of bins 0..bsel
+        float m = -INFINITY;
+        for (int j = 0; j < 8; ++j) {
+            const int b = 8 * tid + j;
+            if (b <= bsel && cnt[b])
+                m = fmaxf(m, float_from_order_key(bmax[b]));
+        }
+        v = block_max(m, redf);
+    }
+    if (tid == 0) {
+        const float xn = bf16_row_norm(queries + q * d, d);
+        tuq[q] = v + flat_slack(xn, ymax);
+    }
+}
+
+constexpr int kFlatSelWaves = 4;
+
+// Pass 3: exact top-k of each query's candidate buffer; an overflowed
+// buffer marks the query for the fallback.
+template <int NW>
+__global__ __launch_bounds__(64 * kFlatSelWaves) void flat_select_kernel(
+    const uint32_t *__restrict__ cnt, const float *__restrict__ cand_d,
+    const uint32_t *__restrict__ cand_p, uint32_t cap, int64_t nq, int k, uint32_t *__restrict__ over,
+    float *__restrict__ out_d, int64_t *__restrict__ out_i)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *bound = reinterpret_cast<uint32_t *>(smem);
+    float *mk = reinterpret_cast<float *>(bound + 4);
+    uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (kFlatSelWaves - 1) * 64 * NW);
+    uint32_t *stage = mv + (kFlatSelWaves - 1) * 64 * NW;
+    const int64_t q = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const uint32_t c = cnt[q];
+    if (c > cap) {
+        if (tid == 0)
+            over[q] = 1u;
+        return;
+    }
+    if (tid == 0)
+        *bound = float_order_key(INFINITY);
+    __syncthreads();
+    WaveTopK<NW> sel;
+    sel.init(k, stage + wave * 128);
+    const float *kd = cand_d + (size_t)q * cap;
+    const uint32_t *kp = cand_p + (size_t)q * cap;
+    int since = 0;
+    for (uint32_t base = wave * 64; base < c; base += 64 * kFlatSelWaves) {
+        const uint32_t i = base + lane;
+        sel.push(i < c ? kd[i] : INFINITY, i < c ? kp[i] : kSentinel);
+        if (++since == 4) {
+            since = 0;
+            publish_bound(bound, sel.kth);
+            sel.bound(read_bound(bound));
+        }
+    }
+    sel.flush();
+    merge_waves<NW, kFlatSelWaves>(sel, mk, mv);
+    if (wave == 0) {
+#pragma unroll
+        for (int r = 0; r < NW; ++r) {
+            const int e = r * 64 + lane;
+            if (e < k) {
+                out_d[q * k + e] = sel.wk[r];
+                out_i[q * k + e] = sel.wv[r] == kSentinel ? -1 : (int64_t)sel.wv[r];
+            }
+        }
+    }
+}
+
+// Pass 4: exact streaming top-k over every row for the queries the select
+// pass marked; the others return at once.  One lane per row, dot product in
+// float32 over the padded row (the padding is zero).
+template <int NW>
+__global__ __launch_bounds__(64 * kFlatSelWaves) void flat_fallback_kernel(
+    const uint16_t *__restrict__ queries, int d, const uint16_t *__restrict__ db, int dp,
+    const float *__restrict__ dbn, int64_t n, int k, const uint32_t *__restrict__ over,
+    float *__restrict__ out_d, int64_t *__restrict__ out_i)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int64_t q = blockIdx.x;
+    if (!over[q])
+        return;
+    uint32_t *bound = reinterpret_cast<uint32_t *>(smem);
+    float *xq = reinterpret_cast<float *>(bound + 4); // [dp]
+    float *mk = xq + dp;
+    uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (kFlatSelWaves - 1) * 64 * NW);
+    uint32_t *stage = mv + (kFlatSelWaves - 1) * 64 * NW;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int t = tid; t < dp; t += 64 * kFlatSelWaves)
+        xq[t] = t < d ? bf16_to_float(queries[q * d + t]) : 0.f;
+    if (tid == 0)
+        *bound = float_order_key(INFINITY);
+    __syncthreads();
+    const float xn = bf16_row_norm(queries + q * d, d);
+    WaveTopK<NW> sel;
+    sel.init(k, stage + wave * 128);
+    int since = 0;
+    for (int64_t base = wave * 64; base < n; base += 64 * kFlatSelWaves) {
+        const int64_t row = base + lane;
+        float dist = INFINITY;
+        if (row < n) {
+            const uint16_t *y = db + row * dp;
+            float dot = 0.f;
+            for (int t = 0; t < dp; ++t)
+                dot = fmaf(xq[t], bf16_to_float(y[t]), dot);
+            dist = flat_distance(xn, dbn[row], dot);
+        }
+        sel.push(dist, (uint32_t)row);
+        if (++since == 4) {
+            since = 0;
+            publish_bound(bound, sel.kth);
+            sel.bound(read_bound(bound));
+        }
+    }
+    sel.flush();
+    merge_waves<NW, kFlatSelWaves>(sel, mk, mv);
+    if (wave == 0) {
+#pragma unroll
+        for (int r = 0; r < NW; ++r) {
+            const int e = r * 64 + lane;
+            if (e < k) {
+                out_d[q * k + e] = sel.wk[r];
+                out_i[q * k + e] = sel.wv[r] == kSentinel ? -1 : (int64_t)sel.wv[r];
+            }
+        }
+    }
+}
+
+__global__ void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n, uint32_t v)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_flat_pack(const uint16_t *src, int64_t n, int d, int dp, int64_t npad,
+                            uint16_t *dst, float *norms, hipStream_t stream)
+{
+    const int64_t total = npad * dp;
+    if (total == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(flat_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, src, n, d, dp, npad, dst, norms);
+    return hipGetLastError();
+}
+
+static int flat_cu_count()
+{
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
+
+FlatPlan flat_plan(int64_t n, int k, int64_t nq)
+{
+    (void)nq;
+    FlatPlan p;
+    p.ntile = (n + 63) / 64;
+    // at most 1000 segments (16000 slot minima per query): about 16 per
+    // top-k row at k = 1024, so few top-k rows share a slot
+    p.seg = (int)((p.ntile + 999) / 1000);
+    p.seg = p.seg < 1 ? 1 : p.seg;
+    p.nseg = (p.ntile + p.seg - 1) / p.seg;
+    p.nslot = 16 * p.nseg;
+    const int64_t c = 4 * (int64_t)k;
+    p.cap = (uint32_t)(c < 4096 ? 4096 : c);
+    return p;
+}
+
+size_t flat_ws_bytes(const FlatPlan &p, int64_t nq)
+{
+    return (size_t)nq * ((size_t)p.nslot * 4 + 12 + (size_t)p.cap * 8) + 256;
+}
+
+template <int KS, int RB, int PASS>
+static hipError_t gemm_variant(const FlatDevice &fx, const uint16_t *q, int64_t nq,
+                               const FlatPlan &p, float *slots, const float *tuq, uint32_t *cnt,
+                               float *cand_d, uint32_t *cand_p, hipStream_t stream)
+{
+    constexpr int TQ = 64 * RB, DP = 32 * KS;
+    const size_t lds = (size_t)TQ * 8 + 128 * 4 + 2 * 64 * (DP + 8) * 2;
+    auto kern = flat_gemm_kernel<KS, RB, PASS>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+    }
+    const int64_t qg = (nq + TQ - 1) / TQ;
+    // about 10 workgroups per CU in all (2-3 resident per CU)
+    int64_t splits = ((int64_t)flat_cu_count() * 10 + qg - 1) / qg;
+    splits = splits < 1 ? 1 : splits > p.nseg ? p.nseg : splits;
+    hipLaunchKernelGGL(kern, dim3((unsigned)qg, (unsigned)splits), dim3(256), lds, stream, q, nq,
+                       fx.d, fx.vec, fx.norms, fx.n, p.ntile, p.seg, p.nseg, (int)splits, slots,
+                       p.nslot, tuq, p.cap, cnt, cand_d, cand_p);
+    return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t select_variant(const FlatDevice &fx, const uint16_t *q, int64_t nq, int k,
+                                 const FlatPlan &p, const uint32_t *cnt, const float *cand_d,
+                                 const uint32_t *cand_p, uint32_t *over, float *out_d,
+                                 int64_t *out_i, hipStream_t stream, bool fallback)
+{
+    const size_t lds = 16 + (size_t)(kFlatSelWaves - 1) * 64 * NW * 8 + kFlatSelWaves * 512;
+    if (!fallback) {
+        hipLaunchKernelGGL(flat_select_kernel<NW>, dim3((unsigned)nq), dim3(64 * kFlatSelWaves),
+                           lds, stream, cnt, cand_d, cand_p, p.cap, nq, k, over, out_d, out_i);
+        return hipGetLastError();
+    }
+    const size_t lds_fb = lds + (size_t)fx.dp * 4;
+    hipLaunchKernelGGL(flat_fallback_kernel<NW>, dim3((unsigned)nq), dim3(64 * kFlatSelWaves),
+                       lds_fb, stream, q, fx.d, fx.vec, fx.dp, fx.norms, fx.n, k, over, out_d,
+                       out_i);
+    return hipGetLastError();
+}
+
+template <int KS>
+static hipError_t gemm_pass(const FlatDevice &fx, const uint16_t *q, int64_t nq,
+                            const FlatPlan &p, float *slots, const float *tuq, uint32_t *cnt,
+                            float *cand_d, uint32_t *cand_p, hipStream_t stream, int pass)
+{
+    // four row blocks per wave while the A operand fits the registers
+    constexpr int RB = KS <= 4 ? 4 : 2;
+    if (pass == kPassMinima)
+        return gemm_variant<KS, RB, kPassMinima>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p,
+                                                 stream);
+    return gemm_variant<KS, RB, kPassCollect>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p,
+                                              stream);
+}
+
+hipError_t launch_flat_stage(const FlatDevice &fx, const uint16_t *q, int64_t nq, int k,
+                             const FlatPlan &p, void *ws, float *out_d, int64_t *out_i,
+                             int stage, hipStream_t stream)
+{
+    if (nq == 0)
+        return hipSuccess;
+    float *slots = static_cast<float *>(ws);
+    float *tuq = slots + (size_t)nq * p.nslot;
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(tuq + nq);
+    uint32_t *over = cnt + nq;
+    float *cand_d = reinterpret_cast<float *>(over + nq);
+    uint32_t *cand_p = reinterpret_cast<uint32_t *>(cand_d + (size_t)nq * p.cap);
+    switch (stage) {
+    case 0:   // clear the counters, slot minima
+    case 2: { // collect
+        if (stage == 0) {
+            hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((2 * nq + 255) / 256)), dim3(256),
+                               0, stream, cnt, 2 * nq, 0u);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        if (p.ntile == 0) // empty database: every row of the result is padding
+            return hipSuccess;
+        const int pass = stage == 0 ? kPassMinima : kPassCollect;
+        switch (fx.dp / 32) {
+        case 1: return gemm_pass<1>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 2: return gemm_pass<2>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 3: return gemm_pass<3>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 4: return gemm_pass<4>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 5: return gemm_pass<5>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 6: return gemm_pass<6>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 7: return gemm_pass<7>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 8: return gemm_pass<8>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    case 1: { // k-th slot minimum -> collect threshold
+        if (p.ntile == 0)
+            return hipSuccess;
+        hipLaunchKernelGGL(flat_kth_kernel, dim3((unsigned)nq), dim3(256), 0, stream, q, fx.d,
+                           slots, p.nslot, k, fx.ymax, tuq);
+        return hipGetLastError();
+    }
+    default: { // 3: select, 4: fallback
+        const bool fb = stage == 4;
+        int nw = 1;
+        while (nw * 64 < k)
+            nw *= 2;
+        switch (nw) {
+        case 1: return select_variant<1>(fx, q, nq, k, p, cnt, cand_d, cand_p, over, out_d, out_i, stream, fb);
+        case 2: return select_variant<2>(fx, q, nq, k, p, cnt, cand_d, cand_p, over, out_d, out_i, stream, fb);
+        case 4: return select_variant<4>(fx, q, nq, k, p, cnt, cand_d, cand_p, over, out_d, out_i, stream, fb);
+        case 8: return select_variant<8>(fx, q, nq, k, p, cnt, cand_d, cand_p, over, out_d, out_i, stream, fb);
+        default: return select_variant<16>(fx, q, nq, k, p, cnt, cand_d, cand_p, over, out_d, out_i, stream, fb);
+        }
+    }
+    }
+}
+
+} // namespace ivfpq

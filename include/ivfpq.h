@@ -183,6 +183,54 @@ ivfpq_status ivfpq_profile_begin(ivfpq_index *idx, int max_calls);
 /* Wait for the recorded searches, write the sums to *out, stop recording. */
 ivfpq_status ivfpq_profile_end(ivfpq_index *idx, ivfpq_timings *out);
 
+/* ---- exact k-NN over a flat bfloat16 database --------------------------
+ *
+ * Brute-force search ("Billion-scale similarity search with GPUs", exact
+ * search section): the exact k nearest database rows of each query by squared
+ * L2 distance, evaluated as |x|^2 + |y|^2 - 2 x.y with bfloat16 x bfloat16
+ * products summed in float32 (matrix cores) and |x|^2, |y|^2 in float32 from
+ * the bfloat16 values.  Ids are database row numbers (0-based).  Ties at the
+ * k-th distance may resolve to any of the tied rows.  Limits: 1 <= d <= 256,
+ * 0 <= n < 2^32 - 64, k in [1, 1024]. */
+typedef struct ivfpq_flat ivfpq_flat; /* opaque, owned by the library */
+
+/* Per-kernel device time, milliseconds, summed over the recorded searches. */
+typedef struct {
+    int32_t calls;
+    int32_t reserved;
+    double minima_ms;   /* all distances; per-lane minima over segments of rows */
+    double kth_ms;      /* k-th smallest minimum per query: the collect bound */
+    double collect_ms;  /* all distances again; rows under the bound kept */
+    double select_ms;   /* exact top-k of the kept rows */
+    double fallback_ms; /* exact streaming top-k for queries whose kept rows overflowed */
+    double total_ms;    /* first kernel start to last kernel end */
+} ivfpq_flat_timings;
+
+/* Upload n rows of d bfloat16 values (bit patterns, row-major [n][d], host
+ * memory; copied) to GPU `device`.  *out receives the handle. */
+ivfpq_status ivfpq_flat_load_bf16(const uint16_t *vectors, int64_t n, int d, int device,
+                                  ivfpq_flat **out);
+
+/* Release the handle and its device memory.  NULL is allowed. */
+void ivfpq_flat_free(ivfpq_flat *f);
+
+/* Asynchronous exact search with device buffers on `stream` (hipStream_t,
+ * NULL = null stream): queries_dev [nq][d] bfloat16 bit patterns,
+ * distances_dev [nq][k] float32 ascending, ids_dev [nq][k] int64 row numbers,
+ * padded with (+INFINITY, -1) when n < k.  One search at a time per handle
+ * (the handle owns the workspace). */
+ivfpq_status ivfpq_flat_search_bf16_ex(const ivfpq_flat *f, const uint16_t *queries_dev,
+                                       int64_t nq, int k, float *distances_dev,
+                                       int64_t *ids_dev, void *stream);
+
+/* Blocking variant with host buffers (PCIe copies included). */
+ivfpq_status ivfpq_flat_search_bf16(const ivfpq_flat *f, const uint16_t *queries, int64_t nq,
+                                    int k, float *distances, int64_t *ids);
+
+/* Per-kernel timing of flat searches, as ivfpq_profile_begin / _end. */
+ivfpq_status ivfpq_flat_profile_begin(ivfpq_flat *f, int max_calls);
+ivfpq_status ivfpq_flat_profile_end(ivfpq_flat *f, ivfpq_flat_timings *out);
+
 /* Message for the last failing call on this thread ("" if none); valid until
  * the next call on this thread. */
 const char *ivfpq_last_error(void);

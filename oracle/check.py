@@ -84,13 +84,16 @@ def check_probes(index, queries, gpu_probes, oracle_probes, report: Report):
     return differ
 
 
-def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None, lookup=None):
+def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None, lookup=None,
+                  abs_tol=None):
     """Rules 2 and 3 for each row; ora_* hold at least k columns (more give
     the distances of ids just past the k-th).  lookup(row, ids) -> oracle
     distances (or None where the id is not a candidate) resolves ids past the
-    oracle's columns (deep ties)."""
+    oracle's columns (deep ties).  abs_tol[row], when given, widens both
+    tolerances by an absolute term (the norm-expansion error near zero)."""
     rows = range(len(gpu_d)) if rows is None else rows
     for r in rows:
+        at = 0.0 if abs_tol is None else float(abs_tol[r])
         gd = np.asarray(gpu_d[r], dtype=np.float64)
         gi = np.asarray(gpu_i[r], dtype=np.int64)
         od = np.asarray(ora_d[r], dtype=np.float64)
@@ -121,7 +124,7 @@ def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None,
                 if v is not None:
                     dist_of[i] = float(v)
         kth = float(od[valid_o - 1])
-        band = tau * kth
+        band = tau * kth + at
         gset, oset = set(gi[:valid_g].tolist()), set(oi[:valid_o].tolist())
         bad = False
         for i in gset ^ oset:
@@ -139,7 +142,7 @@ def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None,
                 report.failures.append((r, f"id {i} is not a candidate of the probed lists"))
                 break
             err = abs(float(v) - ref)
-            if err > tau * abs(ref):
+            if err > tau * abs(ref) + at:
                 report.failures.append((r, f"id {i}: distance {v} vs oracle {ref}"))
                 break
             if ref != 0:
@@ -186,3 +189,35 @@ def compare_search(index, queries, nprobe, k, gpu_d, gpu_i, gpu_probes=None, lut
 
     check_results(gpu_d, gpu_i, od, oi, k, tau, rep, lookup=lookup)
     return rep
+
+
+def compare_flat(db_bits, query_bits, k, gpu_d, gpu_i, tau=TAU_F32, k_extra=32,
+                 nthreads=None) -> Report:
+    """Acceptance check of a device exact search over bfloat16 rows against
+    the oracle's brute force (exact, double precision).  The device evaluates
+    |x|^2 + |y|^2 - 2 x.y in float32, so next to the relative tolerance each
+    row allows the absolute forward-error term 4 gamma_{d+2} (|x|^2 + max |y|^2)
+    (bf16 products are exact in float32; the sums carry the error)."""
+    db = np.ascontiguousarray(db_bits, dtype=np.uint16)
+    q = np.ascontiguousarray(query_bits, dtype=np.uint16)
+    rep = Report(nq=len(q))
+    od, oi = O.bruteforce_bf16(db, q, k + k_extra, nthreads=nthreads)
+    widen = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    dbf = widen(db)
+    qf = widen(q)
+    d = db.shape[1]
+    ymax = float(np.max(np.sum(dbf * dbf, axis=1))) if len(db) else 0.0
+    abs_tol = 4.0 * gamma(d + 2) * (np.sum(qf * qf, axis=1) + ymax)
+
+    def lookup(row, id_list):
+        ids = np.asarray(id_list, dtype=np.int64)
+        ok = (ids >= 0) & (ids < len(db))
+        out = [None] * len(ids)
+        for j in np.flatnonzero(ok):
+            diff = qf[row] - dbf[ids[j]]
+            out[j] = float(np.dot(diff, diff))
+        return out
+
+    check_results(gpu_d, gpu_i, od, oi, k, tau, rep, lookup=lookup, abs_tol=abs_tol)
+    return rep
+

@@ -86,7 +86,8 @@ def test_struct_layouts_match_header(tmp_path):
     import ctypes
     import subprocess
     structs = {"ivfpq_search_params": B.SearchParams, "ivfpq_info": B.Info,
-               "ivfpq_host_index": B.HostIndexStruct, "ivfpq_timings": B.Timings}
+               "ivfpq_host_index": B.HostIndexStruct, "ivfpq_timings": B.Timings,
+               "ivfpq_flat_timings": B.FlatTimings}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ivfpq.h"', "int main(void){"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -120,4 +121,22 @@ def test_load_without_device_or_bad_path_errors(tmp_path):
     if not has_gpu:
         with pytest.raises(A.IVFPQError) as e:
             A.ivfpq_load_index(p)
+        assert e.value.status == B.E_NO_DEVICE
+
+
+def test_flat_load_argument_errors():
+    # shape errors are reported before any device work; without a GPU a valid
+    # shape gives E_NO_DEVICE
+    for bad in (np.zeros((4, 0), np.uint16), np.zeros((4, 257), np.uint16)):
+        with pytest.raises(A.IVFPQError) as e:
+            A.ivfpq_flat_load_bf16(bad)
+        assert e.value.status == B.E_INVALID_ARG
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:
+        has_gpu = False
+    if not has_gpu:
+        with pytest.raises(A.IVFPQError) as e:
+            A.ivfpq_flat_load_bf16(np.zeros((4, 8), np.uint16))
         assert e.value.status == B.E_NO_DEVICE
