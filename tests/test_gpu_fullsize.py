@@ -1,0 +1,90 @@
+"""Full-size IVF-PQ parity: the benchmark shapes (1M x 128 / m 16, 10M x 96 /
+m 32, 1B entries / m 8 with Zipf lists), all 10,000 queries searched in the
+launch configuration the benchmark times, a sample of the queries checked
+against the oracle (exact, double precision) one by one."""
+import time
+
+import numpy as np
+import pytest
+
+from approximate_nearest_neighbour_amd import datagen as G
+from oracle import check
+from oracle import oracle as O
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def A():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import approximate_nearest_neighbour_amd as A
+    return A
+
+
+def sample_rows(nq, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = set([0, nq - 1]) | set(rng.choice(nq, size=count - 2, replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def search_and_check(A, w, lut="f32", sample=16):
+    t = time.time()
+    ix = A.ivfpq_load_index_host(w.index, device=0)
+    q = torch.from_numpy(w.queries).cuda()
+    d, i, p = A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=lut, return_probes=True)
+    torch.cuda.synchronize()
+    print(f"  {w.name} lut={lut}: searched {len(w.queries)} queries "
+          f"({time.time() - t:.1f} s incl. upload)", flush=True)
+    rows = sample_rows(len(w.queries), sample, 11)
+    rep = check.compare_search(w.index, w.queries[rows], w.nprobe, w.k, d.cpu().numpy()[rows],
+                               i.cpu().numpy()[rows], p.cpu().numpy()[rows],
+                               lut_mode=O.LUT_F16 if lut == "f16" else O.LUT_F64)
+    print(f"  parity {rep.summary()}", flush=True)
+    ix.close()
+    assert rep.ok(), rep.failures[:5]
+
+
+def test_fullsize_gmm_1m(A):
+    print("full size: 1M x 128, nlist 1024, m 16, nprobe 32, k 100", flush=True)
+    w = G.gmm1m()
+    search_and_check(A, w)
+
+
+def test_fullsize_10m_shape(A):
+    # the 10M x 96 / nlist 4096 / m 32 shape with random centroids, codebooks
+    # and codes (a trained index of this size takes minutes of host time;
+    # the kernels and launch shapes are the same)
+    print("full size: 10M entries, d 96, nlist 4096, m 32, nprobe 64, k 100", flush=True)
+    rng = np.random.default_rng(404)
+    nlist, n = 4096, 10_000_000
+    sizes = np.bincount(rng.integers(0, nlist, size=n), minlength=nlist)
+    index = G.random_index(rng, nlist, 96, 32, sizes, codebook_scale=0.3)
+    queries = rng.standard_normal((10_000, 96), dtype=np.float32)
+    w = G.Workload("ivfpq_shape_n10m_d96_m32_nlist4096", index, queries, 64, 100)
+    search_and_check(A, w, "f32")
+    search_and_check(A, w, "f16")
+
+
+def test_fullsize_zipf_1b(A):
+    print("full size: 1B entries, d 96, nlist 262144 (Zipf), m 8, nprobe 128, k 100",
+          flush=True)
+    w = G.zipf_workload()
+    search_and_check(A, w)
+
+
+def test_fullsize_flat_bf16(A):
+    print("full size: flat bf16 1M x 128, 10,000 queries, k 1024", flush=True)
+    w = G.flat_bf16_workload()
+    f = A.ivfpq_flat_load_bf16(w.vectors)
+    q = torch.from_numpy(w.queries.view(np.int16)).cuda()
+    d, i = A.ivfpq_flat_search_bf16_ex(f, q, w.k)
+    torch.cuda.synchronize()
+    rows = sample_rows(len(w.queries), 12, 13)
+    rep = check.compare_flat(w.vectors, w.queries[rows], w.k, d.cpu().numpy()[rows],
+                             i.cpu().numpy()[rows])
+    print(f"  parity {rep.summary()}", flush=True)
+    f.close()
+    assert rep.ok(), rep.failures[:5]
