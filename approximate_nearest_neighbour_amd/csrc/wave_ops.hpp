@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace ivfpq {
 
 constexpr uint32_t kSentinel = 0xFFFFFFFFu;
@@ -61,6 +63,45 @@ __device__ __forceinline__ void cx_lane(float &k, uint32_t &v, bool keep_min)
     bool take = keep_min ? (pk < k) : (pk > k);
     k = take ? pk : k;
     v = take ? pv : v;
+}
+
+// The same with keep_min given for all 64 lanes as a compile-time mask: the
+// two comparisons become lane masks, the choice between them three scalar
+// mask operations, and the exchange two selects.
+template <int S, uint64_t KEEP_MIN>
+__device__ __forceinline__ void cx_lane_mask(float &k, uint32_t &v)
+{
+    const float pk = xor_lane<S>(k);
+    const uint32_t pv = xor_lane<S>(v);
+    const uint64_t lt = __builtin_amdgcn_ballot_w64(pk < k);
+    const uint64_t gt = __builtin_amdgcn_ballot_w64(pk > k);
+    const bool take = __builtin_amdgcn_inverse_ballot_w64((lt & KEEP_MIN) | (gt & ~KEEP_MIN));
+    k = take ? pk : k;
+    v = take ? pv : v;
+}
+
+// Lanes of register r that keep the smaller key in a bitonic step (pairs
+// (e, e ^ S), blocks of B elements ascending when ((e & B) == 0) != DESC;
+// B == 0: the whole array ascending).
+constexpr uint64_t keep_min_mask(int S, int B, bool DESC, int r)
+{
+    uint64_t m = 0;
+    for (int l = 0; l < 64; ++l) {
+        const int e = r * 64 + l;
+        const bool lower = (l & S) == 0;
+        const bool up = B == 0 ? !DESC : (((e & B) == 0) != DESC);
+        if (lower == up)
+            m |= 1ull << l;
+    }
+    return m;
+}
+
+// The lane compare-exchanges of one bitonic step, register by register.
+template <int S, int B, bool DESC, int R, int... RR>
+__device__ __forceinline__ void cx_lanes(float (&k)[R], uint32_t (&v)[R],
+                                         std::integer_sequence<int, RR...>)
+{
+    (cx_lane_mask<S, keep_min_mask(S, B, DESC, RR)>(k[RR], v[RR]), ...);
 }
 
 // In-lane compare-exchange between registers (a holds the lower element).
@@ -111,13 +152,8 @@ __device__ __forceinline__ void bitonic_step(float (&k)[R], uint32_t (&v)[R])
             }
         }
     } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int e = r * 64 + lane;
-            const bool up = (B == 0) ? !DESC : (((e & B) == 0) != DESC);
-            const bool lower = (lane & S) == 0;
-            cx_lane<S>(k[r], v[r], lower == up);
-        }
+        (void)lane;
+        cx_lanes<S, B, DESC>(k, v, std::make_integer_sequence<int, R>{});
     }
 }
 
