@@ -255,7 +255,10 @@ void scan_items_kernel(ScanArgs a)
     float *mk = reinterpret_cast<float *>(tab);
     uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (WAVES - 1) * 64 * NW);
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave number is the same in all lanes: say so, so that what derives
+    // from it (piece rotation, loop bounds) is scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int v = tid & 255, g = tid >> 8;
 
     // codebook slice in registers
@@ -315,7 +318,9 @@ void scan_items_kernel(ScanArgs a)
         if (tid == 0)
             misc[0] = atomicAdd(a.counter, 1u);
         __syncthreads();
-        const uint32_t item = misc[0];
+        // values read from LDS that every lane shares: scalar registers, so
+        // the control flow that depends on them stays uniform
+        const uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane((int)misc[0]);
         if (item >= total_items)
             break;
         // the query owning this item: last q with item_base[q] <= item
@@ -374,7 +379,7 @@ void scan_items_kernel(ScanArgs a)
                 pub[lane] = float_order_key(INFINITY);
         }
         __syncthreads();
-        np = (int)misc[1];
+        np = __builtin_amdgcn_readfirstlane((int)misc[1]);
 
         // Union bound: wave w publishes its rk-th smallest value, rk =
         // ceil(k / WAVES); each wave then holds >= rk values <= the largest
@@ -423,7 +428,10 @@ void scan_items_kernel(ScanArgs a)
             // the wave that starts a piece rotates, so that a group of short
             // lists spreads over the waves
             const int rank = (wave - pi) & (WAVES - 1);
-            const Piece pc = pieces[pi];
+            Piece pc = pieces[pi];
+            pc.list = __builtin_amdgcn_readfirstlane(pc.list);
+            pc.b = (uint32_t)__builtin_amdgcn_readfirstlane((int)pc.b);
+            pc.e = (uint32_t)__builtin_amdgcn_readfirstlane((int)pc.e);
             const uint32_t off = a.list_off[pc.list];
             const uint8_t *base = a.codes + (size_t)off * m;
             constexpr uint32_t STRIDE = 64 * WAVES;

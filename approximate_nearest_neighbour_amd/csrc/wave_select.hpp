@@ -74,6 +74,13 @@ struct WaveTopK {
         return out;
     }
 
+    // Wave-uniform values kept in scalar registers.
+    __device__ __forceinline__ static float uni(float x)
+    {
+        return __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(x)));
+    }
+    __device__ __forceinline__ static int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
     // Merge the buffer into W.
     __device__ __forceinline__ void flush()
     {
@@ -96,13 +103,13 @@ struct WaveTopK {
         }
         bitonic_merge_up<NW>(wk, wv);
         bcount = 0;
-        kth = read_rank(k - 1);
-        part = read_rank(rk - 1);
-        thr = fminf(thr, kth);
+        kth = uni(read_rank(k - 1));
+        part = uni(read_rank(rk - 1));
+        thr = uni(fminf(thr, kth));
     }
 
     // Tighten the filter with an external bound (another wave's k-th value).
-    __device__ __forceinline__ void bound(float ext) { thr = fminf(thr, ext); }
+    __device__ __forceinline__ void bound(float ext) { thr = uni(fminf(thr, ext)); }
 
     // One candidate per lane; lanes without a candidate pass key = +inf.
     __device__ __forceinline__ void push(float key, uint32_t val)
@@ -111,21 +118,21 @@ struct WaveTopK {
         uint64_t mask = wave_ballot(pass);
         if (mask == 0)
             return;
-        int n = __popcll(mask);
+        int n = uni((int)__popcll(mask));
         if (bcount + n > 64) {
             flush();
             pass = key < thr;
             mask = wave_ballot(pass);
             if (mask == 0)
                 return;
-            n = __popcll(mask);
+            n = uni((int)__popcll(mask));
         }
         if (pass) {
             const int slot = bcount + mbcnt64(mask);
             sk[slot] = key;
             sv[slot] = val;
         }
-        bcount += n;
+        bcount = uni(bcount + n);
     }
 
     // Write W (kw elements, lane-stride order) to memory.
