@@ -25,7 +25,7 @@ __device__ __forceinline__ float read_bound(const uint32_t *word)
 template <int NW, int WAVES>
 __device__ __forceinline__ void merge_waves(WaveTopK<NW> &sel, float *mk, uint32_t *mv)
 {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     __syncthreads();
     if (wave > 0)
         sel.store(mk + (wave - 1) * 64 * NW, mv + (wave - 1) * 64 * NW);

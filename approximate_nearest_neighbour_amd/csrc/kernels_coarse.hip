@@ -75,7 +75,8 @@ __global__ __launch_bounds__(256 * RG) void coarse_mfma_kernel(
     float *dt = xn + TQ;                                               // [2][TQ][64]
     uint32_t *stage = reinterpret_cast<uint32_t *>(dt + 2 * TQ * 64); // [TQ][128]
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
     const int rg = wave >> 2, cbk = wave & 3;
     const int64_t q0 = (int64_t)blockIdx.x * TQ;
     const int split = blockIdx.y;

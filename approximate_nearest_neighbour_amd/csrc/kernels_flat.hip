@@ -131,7 +131,8 @@ __global__ __launch_bounds__(256) void flat_gemm_kernel(
     float *yn = tq + TQ;                                   // [2][64]
     uint16_t *bt = reinterpret_cast<uint16_t *>(yn + 128); // [2][64][RS]
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
     const int64_t q0 = (int64_t)blockIdx.x * TQ;
     const int64_t s0 = nseg * blockIdx.y / splits, s1 = nseg * (blockIdx.y + 1) / splits;
     const int64_t t0 = s0 * seg, t1 = s1 * seg < ntile ? s1 * seg : ntile;
@@ -398,7 +399,8 @@ __global__ __launch_bounds__(64 * kFlatSelWaves) void flat_select_kernel(
     uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (kFlatSelWaves - 1) * 64 * NW);
     uint32_t *stage = mv + (kFlatSelWaves - 1) * 64 * NW;
     const int64_t q = blockIdx.x;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
     const uint32_t c = cnt[q];
     if (c > cap) {
         if (tid == 0)
@@ -454,7 +456,8 @@ __global__ __launch_bounds__(64 * kFlatSelWaves) void flat_fallback_kernel(
     float *mk = xq + dp;
     uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (kFlatSelWaves - 1) * 64 * NW);
     uint32_t *stage = mv + (kFlatSelWaves - 1) * 64 * NW;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
     for (int t = tid; t < dp; t += 64 * kFlatSelWaves)
         xq[t] = t < d ? bf16_to_float(queries[q * d + t]) : 0.f;
     if (tid == 0)

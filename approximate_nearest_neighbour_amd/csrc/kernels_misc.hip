@@ -73,7 +73,8 @@ __global__ __launch_bounds__(kBlock) void coarse_kernel(const float *__restrict_
     uint32_t *stage = mv + (kWaves - 1) * 64 * NW; // [kWaves][128]
 
     const int64_t q = blockIdx.x;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
     for (int t = tid; t < d; t += kBlock)
         x[t] = queries[q * d + t];
     if (tid == 0)
@@ -146,7 +147,8 @@ __global__ __launch_bounds__(kBlock) void select_kernel(const float *__restrict_
     uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (kWaves - 1) * 64 * NW);
     uint32_t *stage = mv + (kWaves - 1) * 64 * NW; // [kWaves][128]
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
     if (tid == 0)
         *bound = float_order_key(INFINITY);
     __syncthreads();

@@ -81,7 +81,8 @@ __global__ __launch_bounds__(1024) void item_scan_kernel(const uint32_t *__restr
 {
     __shared__ uint32_t wsum[16];
     __shared__ uint32_t carry_s;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
     if (tid == 0)
         carry_s = 0;
     __syncthreads();
@@ -579,7 +580,7 @@ __global__ __launch_bounds__(256) void merge_items_kernel(const uint32_t *__rest
     const uint32_t first = item_base[q], count = item_base[q + 1] - first;
     if (count <= 1)
         return;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
     WaveTopK<NW> sel; // merges sorted arrays only: no staging buffer
     sel.init(k, nullptr);
     for (uint32_t it = wave; it < count; it += 4)
