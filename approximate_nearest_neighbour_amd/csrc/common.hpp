@@ -7,6 +7,15 @@
 
 namespace ivfpq {
 
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wave's LDS operations, not for its global loads, stores or atomics (a
+// prefetch stays in flight across it, unlike __syncthreads' release fence).
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier()
+{
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Order-preserving float bound shared through memory with atomicMin.
 __device__ __forceinline__ void publish_bound(uint32_t *word, float kth)
 {

@@ -16,7 +16,7 @@ struct DeviceIndex {
     float *centroids = nullptr;  // [nlist][d]
     int d4 = 0;                  // K-steps of the coarse MFMA: ceil(d/4) padded to 8/16/24/32
     int nblk = 0;                // 16-centroid blocks, a multiple of 4 (whole 64-wide tiles)
-    float *cblk = nullptr;       // centroids in MFMA B-operand order [nblk][d4][64]
+    float *cblk = nullptr;       // centroids in MFMA B-operand order [nblk][d4/4][64][4]
     float *cnorm_pad = nullptr;  // [nblk * 16] |c_l|^2, +inf past nlist
     float *codebooks = nullptr;  // [m][256][dsub]
     uint32_t *list_off = nullptr; // [nlist + 1]

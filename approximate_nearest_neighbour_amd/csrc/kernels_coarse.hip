@@ -29,8 +29,10 @@ namespace ivfpq {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Centroids in MFMA B-operand order: block b (16 centroids), K-step s (4
-// dims), lane l -> c[16b + l%16][4s + l/16]; zero beyond nlist or d.  Norms
-// padded with +inf so a padding centroid is never selected.
+// dims), lane l -> c[16b + l%16][4s + l/16], stored as [b][s/4][l][s%4] so
+// that one 16-byte load gives a lane four consecutive K-steps (a wave reads
+// 1 KiB contiguous); zero beyond nlist or d.  Norms padded with +inf so a
+// padding centroid is never selected.  d4 is a multiple of 8.
 __global__ void centroid_blocks_kernel(const float *__restrict__ c, int d, int d4, int nlist,
                                        int nblk, float *__restrict__ cblk,
                                        float *__restrict__ cnorm_pad)
@@ -38,10 +40,11 @@ __global__ void centroid_blocks_kernel(const float *__restrict__ c, int d, int d
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = (int64_t)nblk * d4 * 64;
     if (i < total) {
-        const int lane = (int)(i & 63);
-        const int64_t bs = i >> 6;
-        const int s = (int)(bs % d4);
-        const int64_t b = bs / d4;
+        const int j = (int)(i & 3);
+        const int lane = (int)((i >> 2) & 63);
+        const int64_t rest = i >> 8;
+        const int s = 4 * (int)(rest % (d4 / 4)) + j;
+        const int64_t b = rest / (d4 / 4);
         const int64_t row = 16 * b + (lane & 15);
         const int col = 4 * s + (lane >> 4);
         cblk[i] = (row < nlist && col < d) ? c[row * d + col] : 0.f;
@@ -57,17 +60,23 @@ __global__ void centroid_blocks_kernel(const float *__restrict__ c, int d, int d
     }
 }
 
-constexpr int kQueriesPerWave = 4;
-
-template <int NW, int RG, int KD>
-__global__ __launch_bounds__(256 * RG) void coarse_mfma_kernel(
+// Workgroup of 16 waves in two roles, pipelined over the tiles of its range
+// (one barrier per tile, distance tiles double-buffered in LDS):
+//  * 8 matrix waves: wave w computes column block w%4 of row groups
+//    RPW*(w/4) .. +RPW of tile t+1 (A operand of its rows in registers, the
+//    next tile's B operand prefetched) and writes |x|^2 + |c|^2 - 2 x.c;
+//  * 8 selection waves: each owns QS = TQ/8 queries and pushes their 64
+//    distances of tile t into its register top-k (WaveTopK).
+// So the matrix cores and the selection run at the same time on every SIMD.
+template <int NW, int RG, int RPW, int KD>
+__global__ __launch_bounds__(1024) void coarse_mfma_kernel(
     const float *__restrict__ queries, int64_t nq, int d, int nblk, int nprobe,
     const float *__restrict__ cblk, const float *__restrict__ cnorm_pad, int splits,
-    float *__restrict__ part_d, uint32_t *__restrict__ part_p, int32_t *__restrict__ probes,
-    float *__restrict__ probe_d)
+    float *__restrict__ part_d, uint32_t *__restrict__ part_p, uint32_t *__restrict__ qbound,
+    int32_t *__restrict__ probes, float *__restrict__ probe_d)
 {
-    constexpr int TQ = 16 * RG, THREADS = 256 * RG, QW = kQueriesPerWave, KW = 64 * NW;
-    static_assert(TQ == QW * 4 * RG, "four queries per wave");
+    constexpr int TQ = 16 * RG, THREADS = 1024, MW = 8, QS = TQ / 8, KW = 64 * NW;
+    static_assert(4 * RG / RPW == MW, "eight matrix waves");
     extern __shared__ __align__(16) unsigned char smem[];
     const int xs = 4 * KD + 1; // odd stride: the 16 rows of an A read hit 16 banks
     float *xt = reinterpret_cast<float *>(smem);                      // [TQ][xs]
@@ -77,7 +86,9 @@ __global__ __launch_bounds__(256 * RG) void coarse_mfma_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
-    const int rg = wave >> 2, cbk = wave & 3;
+    const bool matrix = wave < MW;
+    const int cbk = wave & 3, rg0 = RPW * ((wave & 7) >> 2);
+    const int sw = wave - MW; // selection wave number
     const int64_t q0 = (int64_t)blockIdx.x * TQ;
     const int split = blockIdx.y;
     const int ntile = (nblk + 3) / 4;
@@ -91,70 +102,140 @@ __global__ __launch_bounds__(256 * RG) void coarse_mfma_kernel(
     }
     __syncthreads();
     if (tid < TQ) {
-        float s = 0.f;
+        float acc = 0.f;
         for (int c = 0; c < 4 * KD; ++c)
-            s = fmaf(xt[tid * xs + c], xt[tid * xs + c], s);
-        xn[tid] = s;
+            acc = fmaf(xt[tid * xs + c], xt[tid * xs + c], acc);
+        xn[tid] = acc;
     }
     __syncthreads();
 
-    WaveTopK<NW> sel[QW];
+    // The two roles run separate loops with the same barriers (1 + tiles), so
+    // each keeps only its own registers live.
+    if (matrix) {
+        // A layout of 16x16x4: lane l supplies row l%16, K-index l/16 of each step
+        float a[RPW][KD];
 #pragma unroll
-    for (int i = 0; i < QW; ++i)
-        sel[i].init(nprobe, stage + (wave * QW + i) * 128);
-
-    // A layout of 16x16x4: lane l supplies row l%16, K-index l/16 of each step
-    float a[KD];
-    {
-        const float *ap = xt + (rg * 16 + (lane & 15)) * xs + (lane >> 4);
-#pragma unroll
-        for (int s = 0; s < KD; ++s)
-            a[s] = ap[4 * s];
-    }
-    float b0[KD], b1[KD];
-    auto load_b = [&](int tile, float (&b)[KD]) {
-        if (tile < t1) {
-            const float *bp = cblk + (size_t)(tile * 4 + cbk) * KD * 64 + lane;
+        for (int g = 0; g < RPW; ++g) {
+            const float *ap = xt + ((rg0 + g) * 16 + (lane & 15)) * xs + (lane >> 4);
 #pragma unroll
             for (int s = 0; s < KD; ++s)
-                b[s] = bp[(size_t)s * 64];
+                a[g][s] = ap[4 * s];
         }
-    };
-    // one tile: prefetch the next tile's B into `bn`, multiply with `bc`,
-    // distances through LDS buffer tile&1, then the four selections
-    auto step = [&](int tile, const float (&bc)[KD], float (&bn)[KD]) {
-        const int blk = tile * 4 + cbk, col = lane & 15;
-        load_b(tile + 1, bn);
-        const float cn = cnorm_pad[blk * 16 + col];
-        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+        // |x|^2 of the 4*RPW query rows this lane holds in the D layout
+        float xr[RPW][4];
 #pragma unroll
-        for (int s = 0; s < KD; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bc[s], acc, 0, 0, 0);
-        // D layout of 16x16x4: lane l holds rows 4*(l/16) + r (r = 0..3) of column l%16
-        float *dtile = dt + (tile & 1) * TQ * 64;
+        for (int g = 0; g < RPW; ++g)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = rg * 16 + 4 * (lane >> 4) + r;
-            dtile[row * 64 + cbk * 16 + col] = xn[row] + cn - 2.f * acc[r];
+            for (int r = 0; r < 4; ++r)
+                xr[g][r] = xn[(rg0 + g) * 16 + 4 * (lane >> 4) + r];
+        // B operand and |c|^2 of a tile, loaded one tile ahead
+        float b0[KD], b1[KD], c0 = INFINITY, c1 = INFINITY;
+        // Unconditional (past the range it re-reads the last tile): a load
+        // under a branch makes the compiler wait for it too early.
+        auto load_b = [&](int tile, float (&b)[KD], float &cn) {
+            tile = tile < t1 ? tile : t1 - 1;
+            const float4 *bp =
+                reinterpret_cast<const float4 *>(cblk) + (size_t)(tile * 4 + cbk) * (KD / 4) * 64 + lane;
+#pragma unroll
+            for (int s4 = 0; s4 < KD / 4; ++s4) {
+                const float4 v = bp[(size_t)s4 * 64];
+                b[4 * s4] = v.x;
+                b[4 * s4 + 1] = v.y;
+                b[4 * s4 + 2] = v.z;
+                b[4 * s4 + 3] = v.w;
+            }
+            cn = cnorm_pad[(tile * 4 + cbk) * 16 + (lane & 15)];
+        };
+        // tile `tile` into LDS buffer tile&1, prefetching the next tile
+        auto multiply = [&](int tile, const float (&bc)[KD], float cc, float (&bn)[KD],
+                            float &cnext) {
+            const int col = lane & 15;
+            load_b(tile + 1, bn, cnext);
+            // keep the next tile's loads ahead of this tile's MFMAs (the
+            // scheduler would otherwise sink them to the barrier)
+            __builtin_amdgcn_sched_barrier(0);
+            float *dtile = dt + (tile & 1) * TQ * 64;
+#pragma unroll
+            for (int g = 0; g < RPW; ++g) {
+                v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KD; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][s], bc[s], acc, 0, 0, 0);
+                // D layout of 16x16x4: lane l holds rows 4*(l/16) + r of column l%16
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = (rg0 + g) * 16 + 4 * (lane >> 4) + r;
+                    dtile[row * 64 + cbk * 16 + col] = xr[g][r] + cc - 2.f * acc[r];
+                }
+            }
+        };
+        if (t0 < t1) {
+            load_b(t0, b0, c0);
+            multiply(t0, b0, c0, b1, c1);
         }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < QW; ++i)
-            sel[i].push(dtile[(wave * QW + i) * 64 + lane], (uint32_t)(tile * 64 + lane));
-    };
-    load_b(t0, b0);
-    int tile = t0;
-    for (; tile + 1 < t1; tile += 2) {
-        step(tile, b0, b1);
-        step(tile + 1, b1, b0);
+        lds_barrier();
+        // iteration t: produce tile t+1 while the selection waves consume t
+        int t = t0;
+        for (; t + 2 < t1; t += 2) {
+            multiply(t + 1, b1, c1, b0, c0);
+            lds_barrier();
+            multiply(t + 2, b0, c0, b1, c1);
+            lds_barrier();
+        }
+        for (; t < t1; ++t) {
+            if (t + 1 < t1)
+                multiply(t + 1, b1, c1, b0, c0);
+            lds_barrier();
+        }
+        return;
     }
-    if (tile < t1)
-        step(tile, b0, b1);
 
+    WaveTopK<NW> sel[QS];
 #pragma unroll
-    for (int i = 0; i < QW; ++i) {
+    for (int i = 0; i < QS; ++i)
+        sel[i].init(nprobe, stage + (sw * QS + i) * 128);
+    lds_barrier();
+    // Splits of a query share a bound: each split's k-th value is >= the
+    // query's k-th, so the smallest of them filters every split.  Every 8
+    // tiles a wave publishes its k-th values (atomic min, no wait) and reads
+    // the shared ones, which it applies a tile later (the loads complete
+    // meanwhile).
+    // Lane i of a selection wave handles query i of the wave here: one
+    // atomic and one load per exchange, the loaded value kept in a vector
+    // register until it is applied (so nothing waits for it).
+    int64_t ql = q0 + sw * QS + (lane < QS ? lane : 0);
+    const bool qvalid = lane < QS && ql < nq;
+    ql = ql < nq ? ql : nq - 1; // the loads stay unconditional
+    uint32_t nb = float_order_key(INFINITY);
+    bool pending = false;
+    for (int t = t0; t < t1; ++t) {
+        if (pending) {
+#pragma unroll
+            for (int i = 0; i < QS; ++i)
+                sel[i].bound(
+                    float_from_order_key((uint32_t)__builtin_amdgcn_readlane((int)nb, i)));
+            pending = false;
+        }
+        const float *dtile = dt + (t & 1) * TQ * 64;
+#pragma unroll
+        for (int i = 0; i < QS; ++i)
+            sel[i].push(dtile[(sw * QS + i) * 64 + lane], (uint32_t)(t * 64 + lane));
+        if (splits > 1 && ((t - t0) & 7) == 7) {
+            float mine = INFINITY;
+#pragma unroll
+            for (int i = 0; i < QS; ++i)
+                mine = lane == i ? sel[i].kth : mine;
+            if (qvalid && mine < INFINITY)
+                atomicMin(qbound + ql, float_order_key(mine));
+            nb = __hip_atomic_load(qbound + ql, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pending = true;
+        }
+        lds_barrier();
+    }
+#pragma unroll
+    for (int i = 0; i < QS; ++i) {
         sel[i].flush();
-        const int64_t q = q0 + wave * QW + i;
+        const int64_t q = q0 + sw * QS + i;
         if (q >= nq)
             continue;
         if (splits == 1) {
@@ -241,12 +322,19 @@ static void coarse_shape(int64_t nq, int nblk, int d4, int *rg, int *splits)
     *rg = nblk >= 1024 && d4 <= 24 ? 4 : 2;
     const int64_t wgs = (nq + 16 * *rg - 1) / (16 * *rg);
     const int ntile = (nblk + 3) / 4;
-    const int64_t want = (int64_t)coarse_cu_count() * 16 / *rg; // ~4 waves per SIMD
+    const int64_t want = (int64_t)coarse_cu_count() * 4; // one resident per CU, ~4 rounds
     int s = (int)((want + wgs - 1) / wgs);
     s = s < 1 ? 1 : s;
     s = s > ntile ? ntile : s;
     s = s > 64 ? 64 : s;
     *splits = s;
+}
+
+__global__ void coarse_bound_init_kernel(uint32_t *__restrict__ qbound, int64_t nq)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nq)
+        qbound[i] = float_order_key(INFINITY);
 }
 
 size_t coarse_ws_bytes(const DeviceIndex &ix, int64_t nq, int nprobe)
@@ -258,17 +346,17 @@ size_t coarse_ws_bytes(const DeviceIndex &ix, int64_t nq, int nprobe)
         return 0;
     int rg, splits;
     coarse_shape(nq, ix.nblk, ix.d4, &rg, &splits);
-    return splits > 1 ? (size_t)nq * splits * 64 * nw * 8 : 0;
+    return splits > 1 ? (size_t)nq * splits * 64 * nw * 8 + (size_t)nq * 4 : 0;
 }
 
-template <int NW, int RG, int KD>
+template <int NW, int RG, int RPW, int KD>
 static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *queries, int64_t nq,
                                       int nprobe, int splits, void *ws, int32_t *probes,
                                       float *probe_d, hipStream_t stream)
 {
     constexpr int TQ = 16 * RG;
     const size_t lds = (size_t)TQ * (4 * KD + 1) * 4 + TQ * 4 + 2 * TQ * 64 * 4 + TQ * 512;
-    auto kern = coarse_mfma_kernel<NW, RG, KD>;
+    auto kern = coarse_mfma_kernel<NW, RG, RPW, KD>;
     if (lds > 160 * 1024)
         return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
@@ -279,9 +367,17 @@ static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *querie
     }
     float *part_d = static_cast<float *>(ws);
     uint32_t *part_p = reinterpret_cast<uint32_t *>(part_d + (size_t)nq * splits * 64 * NW);
+    uint32_t *qbound = part_p + (size_t)nq * splits * 64 * NW;
+    if (splits > 1) {
+        hipLaunchKernelGGL(coarse_bound_init_kernel, dim3((unsigned)((nq + 255) / 256)),
+                           dim3(256), 0, stream, qbound, nq);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     const dim3 grid((unsigned)((nq + TQ - 1) / TQ), (unsigned)splits);
-    hipLaunchKernelGGL(kern, grid, dim3(256 * RG), lds, stream, queries, nq, ix.d, ix.nblk,
-                       nprobe, ix.cblk, ix.cnorm_pad, splits, part_d, part_p, probes, probe_d);
+    hipLaunchKernelGGL(kern, grid, dim3(1024), lds, stream, queries, nq, ix.d, ix.nblk, nprobe,
+                       ix.cblk, ix.cnorm_pad, splits, part_d, part_p, qbound, probes, probe_d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;
@@ -290,26 +386,32 @@ static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *querie
     return hipGetLastError();
 }
 
-template <int NW, int RG>
+// 64 queries per workgroup (two row groups per matrix wave) while the two A
+// operands fit the registers (K-steps <= 24), else 32.
+template <int NW>
 static hipError_t coarse_mfma_k(const DeviceIndex &ix, const float *queries, int64_t nq,
-                                int nprobe, int splits, void *ws, int32_t *probes, float *probe_d,
-                                hipStream_t stream)
+                                int nprobe, int rg, int splits, void *ws, int32_t *probes,
+                                float *probe_d, hipStream_t stream)
 {
     switch (ix.d4) {
     case 8:
-        return coarse_mfma_variant<NW, RG, 8>(ix, queries, nq, nprobe, splits, ws, probes,
-                                              probe_d, stream);
+        return rg == 4 ? coarse_mfma_variant<NW, 4, 2, 8>(ix, queries, nq, nprobe, splits, ws,
+                                                          probes, probe_d, stream)
+                       : coarse_mfma_variant<NW, 2, 1, 8>(ix, queries, nq, nprobe, splits, ws,
+                                                          probes, probe_d, stream);
     case 16:
-        return coarse_mfma_variant<NW, RG, 16>(ix, queries, nq, nprobe, splits, ws, probes,
-                                               probe_d, stream);
+        return rg == 4 ? coarse_mfma_variant<NW, 4, 2, 16>(ix, queries, nq, nprobe, splits, ws,
+                                                           probes, probe_d, stream)
+                       : coarse_mfma_variant<NW, 2, 1, 16>(ix, queries, nq, nprobe, splits, ws,
+                                                           probes, probe_d, stream);
     case 24:
-        return coarse_mfma_variant<NW, RG, 24>(ix, queries, nq, nprobe, splits, ws, probes,
-                                               probe_d, stream);
+        return rg == 4 ? coarse_mfma_variant<NW, 4, 2, 24>(ix, queries, nq, nprobe, splits, ws,
+                                                           probes, probe_d, stream)
+                       : coarse_mfma_variant<NW, 2, 1, 24>(ix, queries, nq, nprobe, splits, ws,
+                                                           probes, probe_d, stream);
     case 32:
-        if (RG == 2)
-            return coarse_mfma_variant<NW, 2, 32>(ix, queries, nq, nprobe, splits, ws, probes,
-                                                  probe_d, stream);
-        return hipErrorInvalidValue;
+        return coarse_mfma_variant<NW, 2, 1, 32>(ix, queries, nq, nprobe, splits, ws, probes,
+                                                 probe_d, stream);
     default:
         return hipErrorInvalidValue;
     }
@@ -330,14 +432,8 @@ hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq
     int rg, splits;
     coarse_shape(nq, ix.nblk, ix.d4, &rg, &splits);
     if (nw == 1)
-        return rg == 4 ? coarse_mfma_k<1, 4>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
-                                             stream)
-                       : coarse_mfma_k<1, 2>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
-                                             stream);
-    return rg == 4 ? coarse_mfma_k<2, 4>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
-                                         stream)
-                   : coarse_mfma_k<2, 2>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
-                                         stream);
+        return coarse_mfma_k<1>(ix, queries, nq, nprobe, rg, splits, ws, probes, probe_d, stream);
+    return coarse_mfma_k<2>(ix, queries, nq, nprobe, rg, splits, ws, probes, probe_d, stream);
 }
 
 } // namespace ivfpq
