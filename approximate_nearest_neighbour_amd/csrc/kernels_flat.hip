@@ -603,13 +603,15 @@ static hipError_t gemm_pass(const FlatDevice &fx, const uint16_t *q, int64_t nq,
                             const FlatPlan &p, float *slots, const float *tuq, uint32_t *cnt,
                             float *cand_d, uint32_t *cand_p, hipStream_t stream, int pass)
 {
-    // four row blocks per wave while the A operand fits the registers
-    constexpr int RB = KS <= 4 ? 4 : 2;
+    // minima pass: four row blocks per wave while the A operand fits the
+    // registers (fewer B reads per product); collect pass: two (its append
+    // path needs the registers, and more waves hide its latency)
+    constexpr int RBM = KS <= 4 ? 4 : 2;
     if (pass == kPassMinima)
-        return gemm_variant<KS, RB, kPassMinima>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p,
-                                                 stream);
-    return gemm_variant<KS, RB, kPassCollect>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p,
-                                              stream);
+        return gemm_variant<KS, RBM, kPassMinima>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p,
+                                                  stream);
+    return gemm_variant<KS, 2, kPassCollect>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p,
+                                             stream);
 }
 
 hipError_t launch_flat_stage(const FlatDevice &fx, const uint16_t *q, int64_t nq, int k,
