@@ -94,7 +94,11 @@ def test_select_with_heavy_ties(dev, n, k):
 
 @pytest.mark.parametrize("nlist,d,nprobe", [(16, 32, 4), (1024, 128, 32), (300, 24, 100),
                                             (5000, 96, 128), (2000, 17, 1024), (777, 40, 200),
-                                            (5, 8, 5), (20000, 96, 64)])
+                                            (5, 8, 5), (20000, 96, 64),
+                                            # 64-query workgroups with 8 / 16 K-steps,
+                                            # 32 K-steps at many centroids, d > 128
+                                            (20000, 32, 16), (17000, 64, 100),
+                                            (20000, 128, 50), (300, 200, 10)])
 def test_coarse_parity(dev, nlist, d, nprobe):
     say("coarse", nlist, d, nprobe)
     rng = np.random.default_rng(nlist + d)
@@ -180,6 +184,7 @@ SHAPES = [
     (20, 16, 4, 3000, 12, 20, 1024),     # k = 1024
     (50, 32, 8, 4000, 10, 1, 1),         # k = 1, nprobe = 1
     (12, 64, 16, 100000, 4, 2, 64),      # long lists (many scan steps)
+    (24, 256, 32, 6000, 8, 5, 50),       # d > 128: direct coarse step, run-time m scan
 ]
 
 
