@@ -216,10 +216,15 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
                     float_from_order_key((uint32_t)__builtin_amdgcn_readlane((int)nb, i)));
             pending = false;
         }
+        // all reads first (one LDS round trip), then the selections
         const float *dtile = dt + (t & 1) * TQ * 64;
+        float cand[QS];
 #pragma unroll
         for (int i = 0; i < QS; ++i)
-            sel[i].push(dtile[(sw * QS + i) * 64 + lane], (uint32_t)(t * 64 + lane));
+            cand[i] = dtile[(sw * QS + i) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < QS; ++i)
+            sel[i].push(cand[i], (uint32_t)(t * 64 + lane));
         if (splits > 1 && ((t - t0) & 7) == 7) {
             float mine = INFINITY;
 #pragma unroll
