@@ -438,22 +438,24 @@ void scan_items_kernel(ScanArgs a)
             constexpr uint32_t STRIDE = 64 * WAVES;
             uint32_t i0 = pc.b + rank * 64;
             if constexpr (M > 0) {
-                // Each lane takes EPL consecutive entries per step (16 bytes
-                // of code rows at m <= 8: more bytes in flight per wave).
+                // Each lane takes EPL consecutive entries per step (32 bytes
+                // of code rows at m <= 32: more bytes in flight per wave).
                 // Full steps need no per-lane bounds and read one step
                 // ahead; then at most one partial step.
-                constexpr int EPL = M >= 16 ? 1 : 16 / M;
+                constexpr int EPL = M >= 32 ? 1 : 32 / M;
                 constexpr uint32_t SPAN = 64 * EPL;          // entries per wave-step
                 constexpr uint32_t WSTRIDE = SPAN * WAVES;   // entries per workgroup-step
                 constexpr size_t PSTEP = (size_t)WSTRIDE * M;
                 using Row = CodeRow<M * EPL>;
-                auto consume = [&](const Row &row, uint32_t first, uint32_t limit) {
+                // FULL: every entry of the step exists (no per-lane bound)
+                auto consume = [&](auto full, const Row &row, uint32_t first, uint32_t limit) {
+                    constexpr bool FULL = decltype(full)::value;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) {
                         const uint32_t i = first + e;
-                        const float r = i < limit
-                                            ? adc_words<M, F16>(row.w + e * (M / 4), lut)
-                                            : INFINITY;
+                        float r = adc_words<M, F16>(row.w + e * (M / 4), lut);
+                        if constexpr (!FULL)
+                            r = i < limit ? r : INFINITY;
                         if constexpr (SO) {
                             sink = fminf(sink, r);
                         } else {
@@ -470,10 +472,12 @@ void scan_items_kernel(ScanArgs a)
                     for (;;) {
                         const uint32_t n0 = s0 + WSTRIDE;
                         const bool more = n0 + SPAN <= pc.e;
+                        // unconditional (the current step again when there is
+                        // no next one), so that the wait before the scan of
+                        // this step leaves the next step's load in flight
                         Row nxt;
-                        if (more)
-                            nxt.load(p + PSTEP);
-                        consume(cur, s0 + lane * EPL, 0xFFFFFFFFu);
+                        nxt.load(more ? p + PSTEP : p);
+                        consume(std::true_type{}, cur, s0 + lane * EPL, 0u);
                         s0 = n0;
                         p += PSTEP;
                         if (!more)
@@ -496,7 +500,7 @@ void scan_items_kernel(ScanArgs a)
                                     cur.w[e * (M / 4) + wi] =
                                         reinterpret_cast<const uint32_t *>(p + e * M)[wi];
                     }
-                    consume(cur, first, pc.e);
+                    consume(std::false_type{}, cur, first, pc.e);
                 }
             } else {
                 for (; i0 < pc.e; i0 += STRIDE) {
