@@ -82,11 +82,14 @@ int kw_of(int k)
     return kw;
 }
 
-// Work items per query at most: the partial top-k buffer stays near 256 MiB
-// (between 2 and 64 items per query).
+// Work items per query: as many as a 1 GiB partial top-k buffer holds, 2 to
+// 64.  With heavy-tailed list sizes a query that probes the largest lists
+// holds many times the average work; cutting it into more items keeps the
+// largest item small against the work per workgroup (the persistent
+// workgroups otherwise wait on one long item at the end).
 uint32_t items_per_query(int64_t nq, int k)
 {
-    const double per = (256.0 * 1024 * 1024) / ((double)(nq > 0 ? nq : 1) * kw_of(k) * 8);
+    const double per = (1024.0 * 1024 * 1024) / ((double)(nq > 0 ? nq : 1) * kw_of(k) * 8);
     if (per < 2)
         return 2;
     return per > 64 ? 64u : (uint32_t)per;

@@ -324,7 +324,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp32" if args.lut == "f32" else "fp32 (binary16 tables)",
-        "data": "synthetic (seeded Gaussian mixture, CPU-built IVF-PQ index)",
+        "data": ("synthetic (seeded N(0,1) centroids, codebooks and queries; uniform random "
+                 "codes; Zipf(1.1) list sizes)" if "zipf" in w.name else
+                 "synthetic (seeded Gaussian mixture, CPU-built IVF-PQ index)"),
         "config": {"workload": w.name, "n": int(w.index.ntotal), "d": w.index.d,
                    "nlist": w.index.nlist, "m": w.index.m, "nq": nq, "nprobe": w.nprobe,
                    "k": w.k, "lut": args.lut},
