@@ -390,21 +390,6 @@ void scan_items_kernel(ScanArgs a)
         sel.init(a.k, reinterpret_cast<uint32_t *>(smem + o_stage) + wave * 128,
                  (a.k + WAVES - 1) / WAVES);
         float sink = INFINITY, published = INFINITY;
-        int tick = 0;
-        auto exchange = [&]() {
-            if (sel.part < published) {
-                published = sel.part;
-                if (lane == 0)
-                    pub[wave] = float_order_key(published);
-            }
-            if ((++tick & 3) != 0)
-                return;
-            uint32_t mx = 0;
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w)
-                mx = mx > pub[w] ? mx : pub[w];
-            sel.bound(float_from_order_key(mx));
-        };
 
         const int ng = (np + PG - 1) / PG;
         if (ng > 0) {
@@ -456,12 +441,10 @@ void scan_items_kernel(ScanArgs a)
                         float r = adc_words<M, F16>(row.w + e * (M / 4), lut);
                         if constexpr (!FULL)
                             r = i < limit ? r : INFINITY;
-                        if constexpr (SO) {
+                        if constexpr (SO)
                             sink = fminf(sink, r);
-                        } else {
+                        else
                             sel.push(r, off + i);
-                            exchange();
-                        }
                     }
                 };
                 uint32_t s0 = pc.b + rank * SPAN;
@@ -507,16 +490,25 @@ void scan_items_kernel(ScanArgs a)
                     const uint32_t i = i0 + lane;
                     const float r =
                         i < pc.e ? adc_rt<F16>(base + (size_t)i * m, m, lut) : INFINITY;
-                    if constexpr (SO) {
+                    if constexpr (SO)
                         sink = fminf(sink, r);
-                    } else {
+                    else
                         sel.push(r, off + i);
-                        exchange();
-                    }
                 }
             }
             } // pieces of the group
             if constexpr (!SO) {
+                // union bound, once per group (per step it cost more than it
+                // saved): the wave publishes its rank value; the maximum over
+                // the waves enters the item's bound (misc[2], read by every
+                // wave after the barrier) and the query's.  A wave whose
+                // current value tid 0 does not see yet counts with an older,
+                // larger one: still a bound.
+                if (sel.part < published) {
+                    published = sel.part;
+                    if (lane == 0)
+                        pub[wave] = float_order_key(published);
+                }
                 publish_bound(&misc[2], sel.kth);
                 if (tid == 0) {
                     uint32_t mx = 0;
@@ -524,8 +516,7 @@ void scan_items_kernel(ScanArgs a)
                         mx = mx > pub[w] ? mx : pub[w];
                     const uint32_t mine = misc[2] < mx ? misc[2] : mx;
                     const uint32_t old = atomicMin(&a.qbound[q], mine);
-                    if (old < mine)
-                        atomicMin(&misc[2], old);
+                    atomicMin(&misc[2], old < mine ? old : mine);
                 }
             }
             __syncthreads();
