@@ -116,8 +116,14 @@ enum FlatPass { kPassMinima = 0, kPassCollect = 1 };
 // segments of `seg` tiles.  Tiles are staged in LDS (double buffer, one
 // barrier per tile); each wave multiplies its RB row blocks by the tile's 4
 // column blocks, one column block at a time (RB accumulators live).
+// Collect-pass staging of candidates in LDS: entries per workgroup.
+constexpr int kFlatStage = 1024;
+
+// The collect pass keeps three waves per SIMD (its staging adds registers);
+// the minima pass runs at two (four row blocks of A operands).
 template <int KS, int RB, int PASS>
-__global__ __launch_bounds__(256) void flat_gemm_kernel(
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(PASS == kPassCollect ? 3 : 1))) void flat_gemm_kernel(
     const uint16_t *__restrict__ queries, int64_t nq, int d, const uint16_t *__restrict__ db,
     const float *__restrict__ dbn, int64_t n, int64_t ntile, int seg, int64_t nseg, int splits,
     float *__restrict__ slots, int64_t nslot, const float *__restrict__ tuq, uint32_t cap,
@@ -130,6 +136,13 @@ __global__ __launch_bounds__(256) void flat_gemm_kernel(
     float *tq = xn + TQ;                                   // [TQ]
     float *yn = tq + TQ;                                   // [2][64]
     uint16_t *bt = reinterpret_cast<uint16_t *>(yn + 128); // [2][64][RS]
+    // collect pass: candidates staged in LDS (count, rows, distances, query
+    // offsets) and appended to the query buffers in bulk, so that a wave does
+    // not wait for a global atomic's return per candidate
+    uint32_t *scount = reinterpret_cast<uint32_t *>(bt + 2 * 64 * RS);
+    uint32_t *srow = scount + 4;
+    float *sdist = reinterpret_cast<float *>(srow + kFlatStage);
+    uint16_t *sq = reinterpret_cast<uint16_t *>(sdist + kFlatStage);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
@@ -143,7 +156,29 @@ __global__ __launch_bounds__(256) void flat_gemm_kernel(
             xn[r] = q < nq ? bf16_row_norm(queries + q * d, d) : 0.f;
             tq[r] = q < nq ? tuq[q] : -INFINITY;
         }
+        if (tid == 0)
+            scount[0] = 0;
     }
+    // one candidate into its query's buffer (the global append)
+    auto append = [&](int64_t q, uint32_t row, float dist) {
+        const uint32_t slot = atomicAdd(cnt + q, 1u);
+        if (slot < cap) {
+            cand_d[(size_t)q * cap + slot] = dist;
+            cand_p[(size_t)q * cap + slot] = row;
+        }
+    };
+    // all staged candidates to the global buffers (256 appends in flight at a
+    // time), then the stage is empty; every thread calls it (barriers)
+    auto drain = [&]() {
+        const uint32_t sc = scount[0];
+        const uint32_t m = sc < (uint32_t)kFlatStage ? sc : (uint32_t)kFlatStage;
+        for (uint32_t i = tid; i < m; i += 256)
+            append(q0 + sq[i], srow[i], sdist[i]);
+        __syncthreads();
+        if (tid == 0)
+            scount[0] = 0;
+        __syncthreads();
+    };
     bf16x8 a[RB][KS];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -230,13 +265,26 @@ __global__ __launch_bounds__(256) void flat_gemm_kernel(
                         continue;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int64_t q = q0 + (wave * RB + rb) * 16 + 4 * (lane >> 4) + r;
-                        if (pass[r] && row < n && q < nq) {
-                            const uint32_t slot = atomicAdd(cnt + q, 1u);
-                            if (slot < cap) {
-                                cand_d[(size_t)q * cap + slot] =
-                                    flat_distance(xr[rb][r], ycol, acc[rb][r]);
-                                cand_p[(size_t)q * cap + slot] = (uint32_t)row;
+                        const int ql = (wave * RB + rb) * 16 + 4 * (lane >> 4) + r;
+                        const int64_t q = q0 + ql;
+                        const bool take = pass[r] && row < n && q < nq;
+                        const uint64_t mask = __builtin_amdgcn_ballot_w64(take);
+                        if (mask == 0)
+                            continue;
+                        // one LDS atomic per wave and row for all its lanes
+                        uint32_t base = 0;
+                        if (lane == 0)
+                            base = atomicAdd(scount, (uint32_t)__popcll(mask));
+                        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+                        if (take) {
+                            const uint32_t at = base + mbcnt64(mask);
+                            const float dist = flat_distance(xr[rb][r], ycol, acc[rb][r]);
+                            if (at < (uint32_t)kFlatStage) {
+                                srow[at] = (uint32_t)row;
+                                sdist[at] = dist;
+                                sq[at] = (uint16_t)ql;
+                            } else {
+                                append(q, (uint32_t)row, dist); // stage full
                             }
                         }
                     }
@@ -258,7 +306,15 @@ __global__ __launch_bounds__(256) void flat_gemm_kernel(
         if (t + 1 < t1)
             stash(buf ^ 1);
         __syncthreads();
+        if (PASS == kPassCollect) {
+            // drain at half full (a tile rarely adds more than the rest)
+            const uint32_t sc = (uint32_t)__builtin_amdgcn_readfirstlane((int)scount[0]);
+            if (sc >= (uint32_t)kFlatStage / 2)
+                drain();
+        }
     }
+    if (PASS == kPassCollect)
+        drain();
 }
 
 // Block-wide (256 threads) reductions through LDS scratch red[8].
@@ -561,7 +617,8 @@ static hipError_t gemm_variant(const FlatDevice &fx, const uint16_t *q, int64_t 
                                float *cand_d, uint32_t *cand_p, hipStream_t stream)
 {
     constexpr int TQ = 64 * RB, DP = 32 * KS;
-    const size_t lds = (size_t)TQ * 8 + 128 * 4 + 2 * 64 * (DP + 8) * 2;
+    const size_t lds = (size_t)TQ * 8 + 128 * 4 + 2 * 64 * (DP + 8) * 2 +
+                       (PASS == kPassCollect ? 16 + (size_t)kFlatStage * 10 : 0);
     auto kern = flat_gemm_kernel<KS, RB, PASS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
