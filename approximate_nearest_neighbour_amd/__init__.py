@@ -11,4 +11,5 @@ from .binding import (IVFPQError, FlatIndex, Index, ivfpq_compute_luts_ex,  # no
                       ivfpq_flat_search_bf16_ex, ivfpq_free_index, ivfpq_index_info, ivfpq_last_error, ivfpq_load_index,
                       ivfpq_load_index_host, ivfpq_profile_begin, ivfpq_profile_end,
                       ivfpq_search, ivfpq_search_ex, ivfpq_select_topk_ex, ivfpq_status_string,
+                      ivfpq_stream_read,
                       ivfpq_validate_host_index, ivfpq_validate_index_file)

@@ -69,7 +69,8 @@ EXPORTS = ("ivfpq_validate_index_file", "ivfpq_validate_host_index", "ivfpq_load
            "ivfpq_profile_begin",
            "ivfpq_profile_end", "ivfpq_flat_load_bf16", "ivfpq_flat_free",
            "ivfpq_flat_search_bf16_ex", "ivfpq_flat_search_bf16", "ivfpq_flat_profile_begin",
-           "ivfpq_flat_profile_end", "ivfpq_last_error", "ivfpq_status_string")
+           "ivfpq_flat_profile_end", "ivfpq_stream_read", "ivfpq_last_error",
+           "ivfpq_status_string")
 
 _lib = None
 
@@ -104,6 +105,7 @@ def lib():
             "ivfpq_flat_search_bf16": ([P, P, i64, i32, P, P], st),
             "ivfpq_flat_profile_begin": ([P, i32], st),
             "ivfpq_flat_profile_end": ([P, P], st),
+            "ivfpq_stream_read": ([P, ctypes.c_size_t, P, i32, P], st),
             "ivfpq_last_error": ([], ctypes.c_char_p),
             "ivfpq_status_string": ([i32], ctypes.c_char_p),
         }
@@ -294,6 +296,17 @@ def ivfpq_select_topk_ex(keys: torch.Tensor, k: int, stream=None):
                                       ctypes.c_void_p(d.data_ptr()), ctypes.c_void_p(p.data_ptr()),
                                       _stream_ptr(stream)))
     return d, p
+
+
+def ivfpq_stream_read(data: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Enqueue the reference streaming read of a contiguous device tensor
+    (measurement support); sink: an int32 device tensor of scratch words."""
+    if not data.is_cuda or not data.is_contiguous():
+        raise ValueError("expected a contiguous device tensor")
+    s = _dev(sink, torch.int32)
+    _check(lib().ivfpq_stream_read(ctypes.c_void_p(data.data_ptr()),
+                                   data.numel() * data.element_size(),
+                                   ctypes.c_void_p(s.data_ptr()), s.numel(), _stream_ptr(stream)))
 
 
 def ivfpq_profile_begin(index: Index, max_calls: int) -> None:

@@ -767,6 +767,20 @@ ivfpq_status ivfpq_select_topk_ex(const float *keys_dev, int64_t rows, int64_t n
     return ok();
 }
 
+ivfpq_status ivfpq_stream_read(const void *data_dev, size_t bytes, uint32_t *sink_dev,
+                               int sink_words, void *stream)
+{
+    if (!data_dev || !sink_dev || sink_words < 1 ||
+        (reinterpret_cast<uintptr_t>(data_dev) & 15) != 0)
+        return fail(IVFPQ_E_INVALID_ARG,
+                    "data_dev must be a 16-byte aligned device pointer and sink_words >= 1");
+    hipError_t e = launch_stream_read(data_dev, bytes, sink_dev, sink_words,
+                                      reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(IVFPQ_E_DEVICE, std::string("stream read kernel: ") + hipGetErrorString(e));
+    return ok();
+}
+
 ivfpq_status ivfpq_profile_begin(ivfpq_index *idx, int max_calls)
 {
     if (!idx || max_calls < 1 || max_calls > 100000)

@@ -68,6 +68,8 @@ hipError_t launch_merge(const DeviceIndex &ix, const SearchArgs &s, const Search
 size_t scan_lds_bytes(int d, int m, int nprobe, bool f16, int nw, int g);
 hipError_t launch_luts(const DeviceIndex &ix, const float *queries, int64_t nq,
                        const int32_t *probes, int nprobe, int lut, float *out, hipStream_t stream);
+hipError_t launch_stream_read(const void *data, size_t bytes, uint32_t *sink, int sink_words,
+                              hipStream_t stream);
 hipError_t launch_select(const float *keys, int64_t rows, int64_t n, int k, float *out_d,
                          int32_t *out_pos, hipStream_t stream);
 

@@ -304,6 +304,63 @@ hipError_t launch_select(const float *keys, int64_t rows, int64_t n, int k, floa
     default: return select_nw<16>(keys, rows, n, k, out_d, out_pos, stream);
     }
 }
+// ---------------------------------------------------------------------------
+// reference streaming read (measurement support for the bandwidth roofline)
+// ---------------------------------------------------------------------------
 
+// Every 16-byte word of p is read once: a lane reads 64 contiguous bytes
+// (four 16-byte loads) of each of two chunks per step, a grid-stride loop
+// over 64-byte chunks, then the tail words.  The words are folded by XOR and
+// a block writes its fold only when it equals a constant no data is expected
+// to produce, so the loads stay live and next to nothing is written.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restrict__ p, size_t n16,
+                                                          uint32_t *__restrict__ sink)
+{
+    const size_t nchunk = n16 / 4;
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; c + stride < nchunk; c += 2 * stride) {
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = p[c * 4 + j];
+            v[4 + j] = p[(c + stride) * 4 + j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+    for (; c < nchunk; c += stride)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 a = p[c * 4 + j];
+            acc ^= a.x ^ a.y ^ a.z ^ a.w;
+        }
+    const size_t t = nchunk * 4 + (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (t < n16) {
+        const uint4 a = p[t];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == 0x9E3779B9u)
+        sink[blockIdx.x] = acc;
+}
+
+hipError_t launch_stream_read(const void *data, size_t bytes, uint32_t *sink, int sink_words,
+                              hipStream_t stream)
+{
+    const size_t n16 = bytes / 16;
+    if (n16 == 0)
+        return hipSuccess;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    int grid = cus * 8;
+    grid = grid < sink_words ? grid : sink_words;
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4 *>(data), n16, sink);
+    return hipGetLastError();
+}
 
 } // namespace ivfpq

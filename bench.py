@@ -39,16 +39,21 @@ def workload(name: str):
     return makers[name]()
 
 
+# The sources that define the scan kernel and how a search launches it (work
+# items, workspace): a change to any of them retires stored counter readings.
+SCAN_SOURCES = ("api.hip", "common.hpp", "internal.hpp", "kernels_search.hip", "wave_ops.hpp",
+                "wave_select.hpp")
+
+
 def source_digest() -> str:
-    """SHA-256 over the HIP sources: ties stored counter readings to a kernel
-    version."""
+    """SHA-256 over the scan path's HIP sources: ties stored counter readings
+    to a kernel version."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "approximate_nearest_neighbour_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in SCAN_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()
 
 
@@ -96,6 +101,37 @@ def summarize_stats(paths):
         for r in rows:
             print(f"| `{r['Name'].split('(')[0].replace('void ', '')}` | {r['Calls']} | "
                   f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['AverageNs']) / 1e3:.1f} |")
+
+
+def measured_read_gbs(torch, A, gib: int = 4, reps: int = 5) -> float:
+    """Streaming-read rate of this GPU: the library's reference read kernel
+    over `gib` GiB (every byte read once, 16-byte loads), timed with events on
+    the current stream; the best of `reps`."""
+    x = torch.ones((gib << 28,), dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros((8192,), dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    A.ivfpq_stream_read(x, sink, stream=st)
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        A.ivfpq_stream_read(x, sink, stream=st)
+        b.record(st)
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del x, sink
+    torch.cuda.empty_cache()
+    return (gib << 30) / (best * 1e-3) / 1e9
+
+
+def host_pointer_qps(search, nq: int, reps: int = 3) -> float:
+    """Queries/s of the blocking host-pointer entry point: queries copied in,
+    results copied out (PCIe included), after one untimed call."""
+    search()
+    t = time.perf_counter()
+    for _ in range(reps):
+        search()
+    return nq * reps / (time.perf_counter() - t)
 
 
 def scanned_entries(index, probes: np.ndarray) -> int:
@@ -166,6 +202,9 @@ def bench_flat(args):
     flops = 2.0 * nq * n * d  # one pass over the distance matrix
     achieved = flops / (stages["minima"] * 1e-3) / 1e12
 
+    host_qps = host_pointer_qps(lambda: A.ivfpq_flat_search_bf16(f, qbits, k), nq)
+    log(f"host-pointer entry point: {host_qps:.0f} queries/s (PCIe copies included)")
+
     pn = min(args.parity_queries, nq, 64)
     rep = check.compare_flat(db, qbits[:pn], k, out[0][:pn].cpu().numpy(),
                              out[1][:pn].cpu().numpy())
@@ -204,6 +243,7 @@ def bench_flat(args):
                      "kernel_ms": stages["minima"], "algorithmic_flops_per_launch": flops},
         "cpu_baseline": cpu,
         "stages_ms": stages,
+        "host_pointer_qps": host_qps,
         "parity": rep.summary(),
     }
     print(json.dumps(res), flush=True)
@@ -297,6 +337,11 @@ def main():
     torch.cuda.synchronize()
     scan_only_ms = A.ivfpq_profile_end(ix)["scan_ms"] / args.steps
 
+    host_qps = host_pointer_qps(lambda: A.ivfpq_search(ix, w.queries, w.nprobe, w.k), nq)
+    log(f"host-pointer entry point: {host_qps:.0f} queries/s (PCIe copies included)")
+    read_gbs = measured_read_gbs(torch, A)
+    log(f"measured streaming read: {read_gbs:.0f} GB/s")
+
     # parity on a sample of the timed configuration
     step()
     torch.cuda.synchronize()
@@ -334,10 +379,12 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": stored_traffic(w.name, args.lut),
                      "kernel": "scan_kernel", "kernel_ms": scan_ms,
-                     "algorithmic_bytes_per_launch": code_bytes},
+                     "algorithmic_bytes_per_launch": code_bytes,
+                     "measured_read_gbs": read_gbs, "frac_of_measured_read": achieved / read_gbs},
         "cpu_baseline": cpu,
         "stages_ms": {"coarse": coarse_ms, "scan": scan_ms, "scan_only": scan_only_ms,
                       "kselect_overhead": scan_ms / scan_only_ms - 1 if scan_only_ms else None},
+        "host_pointer_qps": host_qps,
         "parity": rep.summary(),
     }
     print(json.dumps(res), flush=True)

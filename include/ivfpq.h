@@ -231,6 +231,19 @@ ivfpq_status ivfpq_flat_search_bf16(const ivfpq_flat *f, const uint16_t *queries
 ivfpq_status ivfpq_flat_profile_begin(ivfpq_flat *f, int max_calls);
 ivfpq_status ivfpq_flat_profile_end(ivfpq_flat *f, ivfpq_flat_timings *out);
 
+/* ---- measurement support ------------------------------------------------
+
+/* Reference streaming read for the bandwidth roofline (not part of the search
+ * path): reads the `bytes` bytes at data_dev (device memory, 16-byte aligned;
+ * a tail shorter than 16 bytes is not read) once, enqueued on `stream`
+ * (NULL = default), asynchronous.  sink_dev: device scratch of sink_words >= 1
+ * uint32 that the kernel may write (its contents are meaningless); the grid is
+ * at most sink_words workgroups.  The caller times it with events on the same
+ * stream.  Errors: IVFPQ_E_INVALID_ARG for a NULL pointer, a misaligned
+ * data_dev or sink_words < 1; IVFPQ_E_DEVICE if the launch fails. */
+ivfpq_status ivfpq_stream_read(const void *data_dev, size_t bytes, uint32_t *sink_dev,
+                               int sink_words, void *stream);
+
 /* Message for the last failing call on this thread ("" if none); valid until
  * the next call on this thread. */
 const char *ivfpq_last_error(void);

@@ -140,3 +140,15 @@ def test_flat_load_argument_errors():
         with pytest.raises(A.IVFPQError) as e:
             A.ivfpq_flat_load_bf16(np.zeros((4, 8), np.uint16))
         assert e.value.status == B.E_NO_DEVICE
+
+
+def test_stream_read_argument_errors():
+    # checked before any device work: NULL pointers, misalignment, no sink
+    import ctypes
+    L = B.lib()
+    buf = (ctypes.c_uint32 * 8)()
+    addr = ctypes.addressof(buf)
+    for args in ((None, 64, addr, 4), (addr, 64, None, 4), (addr, 64, addr, 0),
+                 (addr + 4, 64, addr, 4)):
+        st = L.ivfpq_stream_read(args[0], args[1], args[2], args[3], None)
+        assert st == B.E_INVALID_ARG, args

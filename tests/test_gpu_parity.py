@@ -319,3 +319,15 @@ def test_scan_only_mode_and_profile(dev):
     assert t["calls"] == 2 and t["scan_ms"] > 0 and t["coarse_ms"] > 0
     assert math.isfinite(t["total_ms"])
     ix.close()
+
+
+def test_stream_read_runs(dev):
+    # the reference streaming read used for the bandwidth roofline: runs on a
+    # device buffer (tail shorter than 16 bytes included) and leaves it intact
+    x = torch.arange(1 << 20, dtype=torch.int32, device=dev).view(torch.float32)
+    x = x[: (1 << 20) - 3]
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    A.ivfpq_stream_read(x.contiguous(), sink)
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int32).cpu(),
+                       torch.arange((1 << 20) - 3, dtype=torch.int32))
