@@ -200,6 +200,7 @@ void release(ivfpq_index *ix)
     (void)hipFree(d.list_off);
     (void)hipFree(d.codes);
     (void)hipFree(d.ids);
+    (void)hipFree(d.t1);
     (void)hipFree(ix->ws);
     for (auto &e : ix->prof_events) {
         if (e.start)
@@ -270,6 +271,11 @@ ivfpq_status alloc_index(int device, int d, int nlist, int m, int64_t ntotal,
     ALLOC_OR_FAIL(dx.list_off, ((size_t)nlist + 1) * 4);
     ALLOC_OR_FAIL(dx.codes, (size_t)ntotal * m);
     ALLOC_OR_FAIL(dx.ids, (size_t)ntotal * 8);
+    // list term of the decomposed tables (test hook: IVFPQ_TEST_NO_LIST_TERM=1
+    // keeps the difference form everywhere)
+    const char *no_lt = std::getenv("IVFPQ_TEST_NO_LIST_TERM");
+    if (scan_uses_list_term(m, d, nlist) && !(no_lt && no_lt[0] == '1'))
+        ALLOC_OR_FAIL(dx.t1, (size_t)nlist * m * 256 * 4);
     COPY_OR_FAIL(dx.list_off, ix->host_off.data(), ((size_t)nlist + 1) * 4);
     *out = ix;
     return IVFPQ_OK;
@@ -278,9 +284,9 @@ ivfpq_status alloc_index(int device, int d, int nlist, int m, int64_t ntotal,
 ivfpq_status finish_load(ivfpq_index *ix)
 {
     if (launch_centroid_blocks(ix->dx, nullptr) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
+        launch_list_term(ix->dx, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         release(ix);
-        return fail(IVFPQ_E_DEVICE, "centroid layout kernel failed");
+        return fail(IVFPQ_E_DEVICE, "centroid layout or list term kernel failed");
     }
     return IVFPQ_OK;
 }

@@ -22,6 +22,9 @@ struct DeviceIndex {
     uint32_t *list_off = nullptr; // [nlist + 1]
     uint8_t *codes = nullptr;    // [ntotal][m]
     int64_t *ids = nullptr;      // [ntotal]
+    // list term of the decomposed tables (only for the shapes and sizes that
+    // use them, else nullptr): t1[l][j][c] = |C_j[c]|^2 + 2 <c_l,j, C_j[c]>
+    float *t1 = nullptr;         // [nlist][m][256]
 };
 
 struct SearchArgs {
@@ -61,6 +64,10 @@ size_t coarse_ws_bytes(const DeviceIndex &ix, int64_t nq, int nprobe);
 hipError_t launch_centroid_blocks(const DeviceIndex &ix, hipStream_t stream);
 hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
                        hipStream_t stream);
+// Decomposed tables for this index? (compiled shape, list term small enough
+// to stay cache resident)
+bool scan_uses_list_term(int m, int d, int nlist);
+hipError_t launch_list_term(const DeviceIndex &ix, hipStream_t stream);
 hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
                        hipStream_t stream);
 hipError_t launch_merge(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,

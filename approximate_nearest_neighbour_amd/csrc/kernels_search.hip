@@ -117,6 +117,7 @@ struct ScanArgs {
     int pg; // tables per group
     const float *centroids;
     const float *codebooks;
+    const float *t1; // list term of the decomposed tables (PRE)
     const uint32_t *list_off;
     const uint8_t *codes;
     const int64_t *ids;
@@ -215,7 +216,18 @@ struct Piece {
 // Shapes: M > 0 compile-time m and dsub with the codebook in registers
 // (G groups of 256 threads, each holding m/G sub-quantizers); M == 0 run-time
 // m and dsub, codebook read from memory, G == 1.
-template <int M, int DSUB, int G, int NW, bool F16, bool SO>
+//
+// PRE (M > 0): decomposed tables.  With r = x - c_l,
+//   F_j(v) = |r_j - C_j[v]|^2 = |r_j|^2 + t1[l][j][v] - 2 <x_j, C_j[v]>,
+// t1[l][j][v] = |C_j[v]|^2 + 2 <c_l,j, C_j[v]> held per list in memory, and
+// sum_j |r_j|^2 = |x - c_l|^2.  A thread keeps t2[jj] = -2 <x_j, C_j[v]> of
+// its sub-quantizers (computed once per item, no codebook in registers); a
+// table entry is t1 + t2, with |x - c_l|^2 (computed per piece) added to the
+// entries of sub-quantizer 0, so that sum_j F_j is unchanged and the scan
+// is the same.  The sums now cancel where |x - c_l - C(code)| is small
+// against |x - c_l| and |C(code)|: float32 rounding of order 1e-7 of those
+// norms, against the same order of the result in the difference form.
+template <int M, int DSUB, int G, int NW, bool F16, bool SO, bool PRE>
 // Register budget: 128 VGPRs, i.e. four waves per SIMD, so that two
 // workgroups of eight waves share a CU and their table-build and scan
 // phases overlap.
@@ -262,9 +274,11 @@ void scan_items_kernel(ScanArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int v = tid & 255, g = tid >> 8;
 
-    // codebook slice in registers
-    float cb[M > 0 ? JG * DSUB : 1];
-    if constexpr (M > 0) {
+    static_assert(!PRE || M > 0, "decomposed tables need a compile-time shape");
+    // codebook slice in registers (difference form) or the query term (PRE)
+    float cb[(M > 0 && !PRE) ? JG * DSUB : 1];
+    float t2[PRE ? JG : 1];
+    if constexpr (M > 0 && !PRE) {
 #pragma unroll
         for (int jj = 0; jj < JG; ++jj)
 #pragma unroll
@@ -272,8 +286,21 @@ void scan_items_kernel(ScanArgs a)
                 cb[jj * DSUB + s] = a.codebooks[((size_t)(g * JG + jj) * 256 + v) * DSUB + s];
     }
 
-    auto build = [&](const float *rs, void *lut) {
-        if constexpr (M > 0) {
+    // rs: the piece's residual (difference form) or, in rs[0], |x - c_l|^2
+    // (PRE); list: the piece's list
+    auto build = [&](const float *rs, int list, void *lut) {
+        if constexpr (PRE) {
+            const float cst = rs[0];
+            const float *t1l = a.t1 + (size_t)list * M * 256;
+#pragma unroll
+            for (int jj = 0; jj < JG; ++jj) {
+                const int j = g * JG + jj;
+                float e = t1l[j * 256 + v] + t2[jj];
+                if (j == 0)
+                    e += cst;
+                Table<F16>::put(lut, j * 256 + v, e);
+            }
+        } else if constexpr (M > 0) {
 #pragma unroll
             for (int jj = 0; jj < JG; ++jj) {
                 const int j = g * JG + jj;
@@ -300,18 +327,36 @@ void scan_items_kernel(ScanArgs a)
     int np = 0;
     auto group_size = [&](int grp) { return np - grp * PG < PG ? np - grp * PG : PG; };
     // residuals x - c_l of the pieces of group grp into residual buffer b
+    // (PRE: their squared norms, one wave per piece, into the buffer's first
+    // word)
     auto residual_group = [&](int grp, int b) {
         const int pn = group_size(grp);
-        for (int i = tid; i < pn * d; i += THREADS) {
-            const int p = i / d, t = i - p * d;
-            const float *c = a.centroids + (size_t)pieces[grp * PG + p].list * d;
-            rsbuf(b, p)[t] = xs[t] - c[t];
+        if constexpr (PRE) {
+            for (int p = wave; p < pn; p += WAVES) {
+                const float *c = a.centroids + (size_t)pieces[grp * PG + p].list * d;
+                float acc = 0.f;
+                for (int t = lane; t < d; t += 64) {
+                    const float df = xs[t] - c[t];
+                    acc = fmaf(df, df, acc);
+                }
+#pragma unroll
+                for (int sh = 32; sh >= 1; sh >>= 1)
+                    acc += __shfl_xor(acc, sh);
+                if (lane == 0)
+                    rsbuf(b, p)[0] = acc;
+            }
+        } else {
+            for (int i = tid; i < pn * d; i += THREADS) {
+                const int p = i / d, t = i - p * d;
+                const float *c = a.centroids + (size_t)pieces[grp * PG + p].list * d;
+                rsbuf(b, p)[t] = xs[t] - c[t];
+            }
         }
     };
     auto build_group = [&](int grp, int b) {
         const int pn = group_size(grp);
         for (int p = 0; p < pn; ++p)
-            build(rsbuf(b, p), tabp(b, p));
+            build(rsbuf(b, p), pieces[grp * PG + p].list, tabp(b, p));
     };
 
     const uint32_t total_items = a.item_base[a.nq];
@@ -381,6 +426,29 @@ void scan_items_kernel(ScanArgs a)
         }
         __syncthreads();
         np = __builtin_amdgcn_readfirstlane((int)misc[1]);
+        if constexpr (PRE) {
+            // the query term of this thread's sub-quantizers and code value
+            // (the codebook pointer made opaque here: loads the compiler
+            // could hoist out of the item loop would keep the codebook
+            // slice in registers again)
+            uint64_t cbase = reinterpret_cast<uint64_t>(a.codebooks);
+            __asm__ volatile("" : "+s"(cbase));
+            using gfloat = __attribute__((address_space(1))) const float;
+            gfloat *cbk = reinterpret_cast<gfloat *>(cbase);
+#pragma unroll
+            for (int jj = 0; jj < JG; ++jj) {
+                const int j = g * JG + jj;
+                gfloat *cw = cbk + ((size_t)j * 256 + v) * DSUB;
+                float acc = 0.f;
+#pragma unroll
+                for (int s = 0; s < DSUB; ++s)
+                    acc = fmaf(xs[j * DSUB + s], cw[s], acc);
+                t2[jj] = -2.f * acc;
+                // materialised here (the compiler would otherwise recompute
+                // it in every table build and keep the codebook values live)
+                __asm__ volatile("" : "+v"(t2[jj]));
+            }
+        }
 
         // Union bound: wave w publishes its rk-th smallest value, rk =
         // ceil(k / WAVES); each wave then holds >= rk values <= the largest
@@ -639,10 +707,10 @@ size_t scan_lds_bytes(int d, int m, int nprobe, bool f16, int nw, int g)
     return o_tab + (table > merge ? table : merge);
 }
 
-template <int M, int DSUB, int G, int NW, bool F16, bool SO>
+template <int M, int DSUB, int G, int NW, bool F16, bool SO, bool PRE = false>
 static hipError_t scan_variant(const ScanArgs &a, const SearchPlan &pl, hipStream_t stream)
 {
-    auto kern = scan_items_kernel<M, DSUB, G, NW, F16, SO>;
+    auto kern = scan_items_kernel<M, DSUB, G, NW, F16, SO, PRE>;
     const size_t lds = scan_lds_bytes(a.d, a.m, a.nprobe, F16, NW, G);
     if (lds > 160 * 1024)
         return hipErrorInvalidValue;
@@ -667,6 +735,15 @@ template <int M, int DSUB, int G, int NW>
 static hipError_t scan_shape(const ScanArgs &a, const SearchPlan &pl, int f16, int so,
                              hipStream_t stream)
 {
+    if constexpr (M == 16 && DSUB == 8) {
+        if (a.t1) {
+            if (so)
+                return f16 ? scan_variant<M, DSUB, G, NW, true, true, true>(a, pl, stream)
+                           : scan_variant<M, DSUB, G, NW, false, true, true>(a, pl, stream);
+            return f16 ? scan_variant<M, DSUB, G, NW, true, false, true>(a, pl, stream)
+                       : scan_variant<M, DSUB, G, NW, false, false, true>(a, pl, stream);
+        }
+    }
     if (so)
         return f16 ? scan_variant<M, DSUB, G, NW, true, true>(a, pl, stream)
                    : scan_variant<M, DSUB, G, NW, false, true>(a, pl, stream);
@@ -695,6 +772,49 @@ static hipError_t merge_nw(const SearchArgs &s, const SearchPlan &pl, const Devi
 {
     hipLaunchKernelGGL(merge_items_kernel<NW>, dim3((unsigned)s.nq), dim3(256), 0, stream,
                        pl.item_base, pl.part_d, pl.part_p, ix.ids, s.k, s.out_d, s.out_i);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// list term of the decomposed tables (index load)
+// ---------------------------------------------------------------------------
+
+// t1[l][j][c] = |C_j[c]|^2 + 2 <c_l,j, C_j[c]> in double precision, rounded
+// once; one thread per entry.
+__global__ __launch_bounds__(256) void list_term_kernel(const float *__restrict__ centroids,
+                                                        const float *__restrict__ codebooks,
+                                                        int nlist, int m, int dsub,
+                                                        float *__restrict__ t1)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)nlist * m * 256;
+    if (i >= total)
+        return;
+    const int c = (int)(i & 255);
+    const int j = (int)((i >> 8) % m);
+    const int64_t l = (i >> 8) / m;
+    const float *cw = codebooks + ((size_t)j * 256 + c) * dsub;
+    const float *cl = centroids + (size_t)l * m * dsub + (size_t)j * dsub;
+    double acc = 0.0;
+    for (int s = 0; s < dsub; ++s)
+        acc += (double)cw[s] * ((double)cw[s] + 2.0 * (double)cl[s]);
+    t1[i] = (float)acc;
+}
+
+// The shape with the compiled decomposed-table scan (m 16, dsub 8), while the
+// list term stays small enough to be cache resident (<= 64 MiB).
+bool scan_uses_list_term(int m, int d, int nlist)
+{
+    return m == 16 && d == 128 && (size_t)nlist * m * 256 * 4 <= ((size_t)64 << 20);
+}
+
+hipError_t launch_list_term(const DeviceIndex &ix, hipStream_t stream)
+{
+    if (!ix.t1 || ix.nlist == 0)
+        return hipSuccess;
+    const int64_t total = (int64_t)ix.nlist * ix.m * 256;
+    hipLaunchKernelGGL(list_term_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, ix.centroids, ix.codebooks, ix.nlist, ix.m, ix.d / ix.m, ix.t1);
     return hipGetLastError();
 }
 
@@ -730,6 +850,7 @@ hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     a.pg = tables_per_group(ix.m, s.lut != 0);
     a.centroids = ix.centroids;
     a.codebooks = ix.codebooks;
+    a.t1 = ix.t1;
     a.list_off = ix.list_off;
     a.codes = ix.codes;
     a.ids = ix.ids;

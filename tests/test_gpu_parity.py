@@ -331,3 +331,24 @@ def test_stream_read_runs(dev):
     torch.cuda.synchronize()
     assert torch.equal(x.view(torch.int32).cpu(),
                        torch.arange((1 << 20) - 3, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("lut", ["f32", "f16"])
+@pytest.mark.parametrize("decomposed", [True, False])
+def test_m16_tables_both_forms(dev, monkeypatch, lut, decomposed):
+    """The (m 16, dsub 8) scan with the decomposed tables (per-list term from
+    index load + per-query term; chosen while the list term is small) and,
+    with the test hook set at index load, with the difference form: both
+    against the oracle's difference-form tables."""
+    if decomposed:
+        monkeypatch.delenv("IVFPQ_TEST_NO_LIST_TERM", raising=False)
+    else:
+        monkeypatch.setenv("IVFPQ_TEST_NO_LIST_TERM", "1")
+    nlist, d, m, n, nq, nprobe, k = 48, 128, 16, 40000, 16, 9, 100
+    say("m16 tables", "decomposed" if decomposed else "difference", lut)
+    rng = np.random.default_rng(1616)
+    sizes = rng.multinomial(n, rng.dirichlet(np.ones(nlist)))
+    idx = G.random_index(rng, nlist, d, m, sizes, codebook_scale=0.3)
+    q = (idx.centroids[rng.integers(0, nlist, nq)]
+         + 0.3 * rng.standard_normal((nq, d))).astype(np.float32)
+    assert_parity(idx, q, nprobe, k, lut=lut)
