@@ -52,22 +52,11 @@ __device__ __forceinline__ float xor_lane(float v)
     return __uint_as_float(xor_lane<S>(__float_as_uint(v)));
 }
 
-// Compare-exchange of (k, v) with the partner lane at distance S.  keep_min
-// says whether this lane keeps the smaller key.  Equal keys never move, so
-// the two lanes always take consistent decisions.
-template <int S>
-__device__ __forceinline__ void cx_lane(float &k, uint32_t &v, bool keep_min)
-{
-    float pk = xor_lane<S>(k);
-    uint32_t pv = xor_lane<S>(v);
-    bool take = keep_min ? (pk < k) : (pk > k);
-    k = take ? pk : k;
-    v = take ? pv : v;
-}
-
-// The same with keep_min given for all 64 lanes as a compile-time mask: the
-// two comparisons become lane masks, the choice between them three scalar
-// mask operations, and the exchange two selects.
+// Compare-exchange of (k, v) with the partner lane at distance S, keep_min
+// (this lane keeps the smaller key) given for all 64 lanes as a compile-time
+// mask: the two comparisons become lane masks, the choice between them three
+// scalar mask operations, and the exchange two selects.  Equal keys never
+// move, so the two lanes of a pair always take consistent decisions.
 template <int S, uint64_t KEEP_MIN>
 __device__ __forceinline__ void cx_lane_mask(float &k, uint32_t &v)
 {
@@ -116,31 +105,12 @@ __device__ __forceinline__ void cx_reg(float &ka, uint32_t &va, float &kb, uint3
     vb = swap ? tv : vb;
 }
 
-template <int S>
-__device__ __forceinline__ void cx_lane_dispatch(float &k, uint32_t &v, bool keep_min)
-{
-    cx_lane<S>(k, v, keep_min);
-}
-
-__device__ __forceinline__ void cx_lane_rt(int s, float &k, uint32_t &v, bool keep_min)
-{
-    switch (s) {
-    case 1: cx_lane<1>(k, v, keep_min); break;
-    case 2: cx_lane<2>(k, v, keep_min); break;
-    case 4: cx_lane<4>(k, v, keep_min); break;
-    case 8: cx_lane<8>(k, v, keep_min); break;
-    case 16: cx_lane<16>(k, v, keep_min); break;
-    default: cx_lane<32>(k, v, keep_min); break;
-    }
-}
-
 // One step of a bitonic network on an R-register lane-stride array: pairs
 // (e, e ^ S) inside blocks of B elements; a block runs ascending when
 // ((e & B) == 0) != DESC.  B == 0 means "the whole array ascending" (merge).
 template <int R, int B, int S, bool DESC>
 __device__ __forceinline__ void bitonic_step(float (&k)[R], uint32_t (&v)[R])
 {
-    const int lane = lane_id();
     if constexpr (S >= 64) {
         constexpr int RS = S / 64;
 #pragma unroll
@@ -152,7 +122,6 @@ __device__ __forceinline__ void bitonic_step(float (&k)[R], uint32_t (&v)[R])
             }
         }
     } else {
-        (void)lane;
         cx_lanes<S, B, DESC>(k, v, std::make_integer_sequence<int, R>{});
     }
 }
