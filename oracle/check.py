@@ -15,6 +15,19 @@ rules below say when a device result counts as the oracle's result:
    matches.
 3. Distances.  Every returned id's distance is within tau relative of the
    oracle's distance for that id (tau = 1e-4 float32 tables, 1e-2 fp16).
+
+Index building (assignment and encoding of database vectors):
+
+4. Lists.  A device list may differ from the oracle's (the nearest centroid)
+   only by a list whose oracle coarse distance is within delta_c of the
+   nearest one (delta_c as in rule 1).
+5. Codes.  With l the device's list and F the oracle's table of l (the same
+   F_j(v) as the search's, r = x - c_l), each device code v of sub-quantizer j
+   satisfies F_j(v) <= min_w F_j(w) + delta_e(j), delta_e(j) = 4
+   gamma_{dsub+3} sum_s (2 |r_s| + max_w |C_j[w][s]|)^2 over the dsub dims s
+   of sub-vector j: a forward-error bound of a float32 evaluation of
+   sum_s (fl(x_s - c_s) - C_j[w][s])^2, times two.  Where no other code is
+   that close, the codes must be equal.
 """
 from __future__ import annotations
 
@@ -221,3 +234,66 @@ def compare_flat(db_bits, query_bits, k, gpu_d, gpu_i, tau=TAU_F32, k_extra=32,
     check_results(gpu_d, gpu_i, od, oi, k, tau, rep, lookup=lookup, abs_tol=abs_tol)
     return rep
 
+
+
+@dataclasses.dataclass
+class EncodeReport:
+    n: int = 0
+    list_flips: int = 0
+    code_flips: int = 0
+    failures: list = dataclasses.field(default_factory=list)
+
+    def ok(self) -> bool:
+        return not self.failures
+
+    def summary(self) -> dict:
+        return dict(n=self.n, list_flips=self.list_flips, code_flips=self.code_flips,
+                    failures=len(self.failures))
+
+
+def compare_encode(vectors, centroids, codebooks, gpu_lists, gpu_codes, oracle_out=None,
+                   nthreads=None) -> EncodeReport:
+    """Rules 4 and 5: device list assignment and PQ codes against the oracle.
+    oracle_out: a precomputed ``O.assign_encode`` result for the same inputs."""
+    x = np.ascontiguousarray(vectors, dtype=np.float32)
+    cent = np.ascontiguousarray(centroids, dtype=np.float32)
+    books = np.ascontiguousarray(codebooks, dtype=np.float32)
+    gl = np.asarray(gpu_lists).reshape(-1).astype(np.int64)
+    gc = np.asarray(gpu_codes).reshape(len(x), -1)
+    n, d = x.shape
+    nlist, m, dsub = cent.shape[0], books.shape[0], books.shape[2]
+    rep = EncodeReport(n=n)
+    if gl.shape[0] != n or gc.shape[1] != m:
+        rep.failures.append((-1, "output shape"))
+        return rep
+    lists, codes, _, _ = (O.assign_encode(x, cent, books, nthreads=nthreads)
+                          if oracle_out is None else oracle_out)
+    cmax = float(np.max(np.sum(cent.astype(np.float64) ** 2, axis=1))) if nlist else 0.0
+    bmax = np.max(np.abs(books.astype(np.float64)), axis=1)           # [m, dsub]
+    for i in range(n):
+        li = int(gl[i])
+        if not 0 <= li < nlist:
+            rep.failures.append((i, f"list {li} out of range"))
+            continue
+        if li != lists[i]:
+            allp, alld = O.coarse(x[i], cent, nlist)
+            dist_of = dict(zip(allp.tolist(), alld.tolist()))
+            x2 = float(np.sum(x[i].astype(np.float64) ** 2))
+            delta = 4.0 * gamma(d + 2) * (x2 + cmax)
+            if dist_of[li] - float(alld[0]) > delta:
+                rep.failures.append((i, f"list {li} outside the coarse tie band"))
+                continue
+            rep.list_flips += 1
+        elif np.array_equal(gc[i], codes[i]):
+            continue
+        table = O.lut(x[i], cent[li], books)
+        r = np.abs(x[i].astype(np.float64) - cent[li].astype(np.float64)).reshape(m, dsub)
+        delta_e = 4.0 * gamma(dsub + 3) * np.sum((2.0 * r + bmax) ** 2, axis=1)
+        best = table.min(axis=1)
+        for j in range(m):
+            v = int(gc[i, j])
+            if table[j, v] - best[j] > delta_e[j]:
+                rep.failures.append((i, f"code {v} of sub-quantizer {j} is not the nearest"))
+            elif li == lists[i] and v != codes[i, j]:
+                rep.code_flips += 1
+    return rep

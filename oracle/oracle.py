@@ -176,6 +176,65 @@ def search(index, queries, nprobe, k, lut_mode=LUT_F64, probes=None, nthreads=No
     return od, oi, op
 
 
+def assign_encode(vectors, centroids, codebooks, nthreads=None):
+    """Index building: list assignment and PQ encoding of database vectors.
+
+    The index-building steps of "Custom 8-bit floating point value format for
+    reducing shared memory bank conflict in ANN search" (IVFPQ section, steps
+    1-3: a vector belongs to the cluster of its nearest centroid, its residual
+    to that centroid is cut into sub-vectors, each sub-vector is quantized),
+    with the quantizers of "Billion-scale similarity search with GPUs"
+    (IVFADC section: the coarse quantizer q1, and on the residual a product
+    of m quantizers with 256 reproduction values each).  A quantizer maps its
+    input to the nearest reproduction value in squared L2, ties to the
+    smaller index.
+
+    Both decisions reuse the oracle's search steps: the list is the first of
+    the coarse order (``coarse``: distance, then list number), and the code
+    of sub-quantizer j is the smallest entry of row j of the table of that
+    list (``lut``: F_j(v) = |r_j - C_j[v]|^2 with r = x - c_list, double
+    precision), the first one on ties.
+
+    Returns (lists int32 [n], codes uint8 [n, m], list_gap float64 [n],
+    code_gap float64 [n, m]): the gaps are the second-smallest minus the
+    smallest distance of each decision (+inf when there is one list), i.e.
+    how far the decision is from a tie.
+    """
+    x = np.ascontiguousarray(vectors, dtype=np.float32)
+    cent = np.ascontiguousarray(centroids, dtype=np.float32)
+    books = np.ascontiguousarray(codebooks, dtype=np.float32)
+    n = x.shape[0]
+    nlist, m = cent.shape[0], books.shape[0]
+    lists = np.empty(n, dtype=np.int32)
+    codes = np.empty((n, m), dtype=np.uint8)
+    list_gap = np.empty(n, dtype=np.float64)
+    code_gap = np.empty((n, m), dtype=np.float64)
+    take = 2 if nlist > 1 else 1
+
+    def one(i):
+        pr, dist = coarse(x[i], cent, take)
+        lists[i] = pr[0]
+        list_gap[i] = dist[1] - dist[0] if take == 2 else np.inf
+        table = lut(x[i], cent[pr[0]], books)
+        codes[i] = np.argmin(table, axis=1)
+        two = np.partition(table, 1, axis=1)
+        code_gap[i] = two[:, 1] - two[:, 0]
+
+    def run(lo, hi):
+        for i in range(lo, hi):
+            one(i)
+
+    nt = max(1, min(nthreads or default_threads(), n))
+    if nt == 1:
+        run(0, n)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        step = (n + nt - 1) // nt
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(lambda s: run(s, min(n, s + step)), range(0, n, step)))
+    return lists, codes, list_gap, code_gap
+
+
 def bruteforce(db, queries, k, db_ids=None, nthreads=None):
     db = np.ascontiguousarray(db, dtype=np.float32)
     q = np.ascontiguousarray(queries, dtype=np.float32)

@@ -317,3 +317,96 @@ def test_checker_accepts_oracle_and_rejects_perturbations():
     pp[2, 0] = [l for l in range(8) if l not in p[2]][0]
     rep = check.compare_search(idx, q, 3, 20, d.astype(np.float32), i, pp)
     assert not rep.ok()
+
+
+# ---------------------------------------------------------------------------
+# index building: list assignment and PQ encoding
+# ---------------------------------------------------------------------------
+
+def test_encode_recovers_the_codewords_a_vector_was_made_of():
+    # x = c_l + (C_0[v_0], ..., C_{m-1}[v_{m-1}]) with far-apart centroids and
+    # small codewords: the encoder must return l and the v_j
+    rng = np.random.default_rng(31)
+    nlist, d, m = 8, 16, 4
+    cent = (10.0 * rng.standard_normal((nlist, d))).astype(np.float32)
+    books = (0.1 * rng.standard_normal((m, 256, d // m))).astype(np.float32)
+    n = 300
+    lst = rng.integers(0, nlist, n)
+    code = rng.integers(0, 256, (n, m))
+    x = (cent[lst] + np.concatenate([books[j][code[:, j]] for j in range(m)], axis=1))
+    lists, codes, lgap, cgap = O.assign_encode(x.astype(np.float32), cent, books)
+    assert np.array_equal(lists, lst)
+    assert np.array_equal(codes, code)
+    assert np.all(lgap > 0) and np.all(cgap > 0)
+
+
+def test_encode_is_the_joint_optimum_by_enumeration():
+    # the per-sub-quantizer choice must minimise the whole reconstruction
+    # error |x - c_l - (C_0[v_0], C_1[v_1])|^2 over all 256^2 code pairs, and
+    # the list must be the nearest centroid (numpy, double precision)
+    rng = np.random.default_rng(32)
+    nlist, d = 3, 4
+    cent = rng.standard_normal((nlist, d)).astype(np.float32)
+    books = rng.standard_normal((2, 256, 2)).astype(np.float32)
+    x = rng.standard_normal((40, d)).astype(np.float32)
+    lists, codes, _, _ = O.assign_encode(x, cent, books)
+    v0, v1 = np.meshgrid(np.arange(256), np.arange(256), indexing="ij")
+    recon = np.concatenate([books[0][v0.ravel()], books[1][v1.ravel()]], axis=1).astype(np.float64)
+    for i in range(len(x)):
+        dc = ((x[i].astype(np.float64) - cent.astype(np.float64)) ** 2).sum(1)
+        assert lists[i] == int(np.argmin(dc))
+        r = x[i].astype(np.float64) - cent[lists[i]].astype(np.float64)
+        err = ((r[None, :] - recon) ** 2).sum(1)
+        best = int(np.argmin(err))
+        assert (int(codes[i, 0]), int(codes[i, 1])) == (best // 256, best % 256)
+
+
+def test_encode_ties_go_to_the_smaller_index():
+    cent = np.array([[0, 0, 0, 0], [5, 5, 5, 5], [0, 0, 0, 0]], dtype=np.float32)
+    books = np.full((2, 256, 2), 100.0, dtype=np.float32)
+    books[0, 7] = books[0, 3] = (0.5, 0.5)
+    books[1, 200] = books[1, 9] = (1.0, 1.0)
+    x = np.array([[0.4, 0.6, 1.1, 0.9]], dtype=np.float32)
+    lists, codes, lgap, cgap = O.assign_encode(x, cent, books)
+    assert lists[0] == 0 and lgap[0] == 0.0
+    assert codes[0].tolist() == [3, 9] and cgap[0].tolist() == [0.0, 0.0]
+
+
+def test_encode_agrees_with_the_index_builder_where_decisions_are_clear():
+    # the CPU index builder (float32 norm expansion, numpy) is an independent
+    # encoder: it must agree wherever the decision is not a near-tie
+    from approximate_nearest_neighbour_amd import datagen as G
+    rng = np.random.default_rng(33)
+    nlist, d, m = 16, 32, 4
+    cent = rng.standard_normal((nlist, d)).astype(np.float32)
+    books = (0.3 * rng.standard_normal((m, 256, d // m))).astype(np.float32)
+    x = (cent[rng.integers(0, nlist, 500)] + 0.3 * rng.standard_normal((500, d))).astype(np.float32)
+    lists, codes, lgap, cgap = O.assign_encode(x, cent, books)
+    gl = G.nearest(x, cent)
+    gc = G.encode_pq(x - cent[lists], books)
+    clear_l = lgap > 1e-3
+    assert np.array_equal(lists[clear_l], gl[clear_l])
+    clear_c = cgap > 1e-3
+    assert np.array_equal(codes[clear_c], gc[clear_c])
+    assert clear_l.mean() > 0.95 and clear_c.mean() > 0.95
+
+
+def test_encode_checker_accepts_oracle_and_rejects_perturbations():
+    rng = np.random.default_rng(34)
+    nlist, d, m = 12, 24, 4
+    cent = rng.standard_normal((nlist, d)).astype(np.float32)
+    books = (0.4 * rng.standard_normal((m, 256, d // m))).astype(np.float32)
+    x = (cent[rng.integers(0, nlist, 200)] + 0.4 * rng.standard_normal((200, d))).astype(np.float32)
+    out = O.assign_encode(x, cent, books)
+    lists, codes, lgap, cgap = out
+    assert check.compare_encode(x, cent, books, lists, codes, oracle_out=out).ok()
+    i = int(np.argmax(cgap[:, 1]))                     # the clearest decision of sub-quantizer 1
+    bad = codes.copy()
+    table = O.lut(x[i], cent[lists[i]], books)
+    bad[i, 1] = int(np.argmax(table[1]))
+    assert not check.compare_encode(x, cent, books, lists, bad, oracle_out=out).ok()
+    i = int(np.argmax(lgap))
+    far = lists.copy()
+    far[i] = int(O.coarse(x[i], cent, nlist)[0][-1])   # the farthest list
+    assert not check.compare_encode(x, cent, books, far, codes, oracle_out=out).ok()
+    assert not check.compare_encode(x, cent, books, np.full(200, nlist), codes, oracle_out=out).ok()
