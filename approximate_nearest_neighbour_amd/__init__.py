@@ -5,7 +5,8 @@ The search runs in hand-written HIP kernels behind the C ABI of
 (``binding``), the in-tree build (``build_lib``) and host-side input tooling
 (``datagen``: seeded generators, CPU index builder, index file).
 """
-from .binding import (IVFPQError, FlatIndex, Index, ivfpq_compute_luts_ex,  # noqa: F401
+from .binding import (IVFPQError, FlatIndex, Index, ivfpq_assign_encode_ex,  # noqa: F401
+                      ivfpq_compute_luts_ex,
                       ivfpq_coarse_ex, ivfpq_flat_free, ivfpq_flat_load_bf16,
                       ivfpq_flat_profile_begin, ivfpq_flat_profile_end, ivfpq_flat_search_bf16,
                       ivfpq_flat_search_bf16_ex, ivfpq_free_index, ivfpq_index_info, ivfpq_last_error, ivfpq_load_index,

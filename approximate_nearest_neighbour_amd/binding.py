@@ -65,7 +65,8 @@ class FlatTimings(ctypes.Structure):
 
 EXPORTS = ("ivfpq_validate_index_file", "ivfpq_validate_host_index", "ivfpq_load_index",
            "ivfpq_load_index_host", "ivfpq_free_index", "ivfpq_index_info", "ivfpq_search",
-           "ivfpq_search_ex", "ivfpq_coarse_ex", "ivfpq_compute_luts_ex", "ivfpq_select_topk_ex",
+           "ivfpq_search_ex", "ivfpq_coarse_ex", "ivfpq_assign_encode_ex", "ivfpq_compute_luts_ex",
+           "ivfpq_select_topk_ex",
            "ivfpq_profile_begin",
            "ivfpq_profile_end", "ivfpq_flat_load_bf16", "ivfpq_flat_free",
            "ivfpq_flat_search_bf16_ex", "ivfpq_flat_search_bf16", "ivfpq_flat_profile_begin",
@@ -95,6 +96,7 @@ def lib():
             "ivfpq_search": ([P, P, i64, i32, i32, P, P], st),
             "ivfpq_search_ex": ([P, P, P, i64, P, P, P, P], st),
             "ivfpq_coarse_ex": ([P, P, i64, i32, P, P, P], st),
+            "ivfpq_assign_encode_ex": ([P, P, i64, P, P, P], st),
             "ivfpq_compute_luts_ex": ([P, P, i64, P, i32, i32, P, P], st),
             "ivfpq_select_topk_ex": ([P, i64, i64, i32, P, P, P], st),
             "ivfpq_profile_begin": ([P, i32], st),
@@ -269,6 +271,21 @@ def ivfpq_coarse_ex(index: Index, queries: torch.Tensor, nprobe: int, stream=Non
                                  ctypes.c_void_p(probes.data_ptr()),
                                  ctypes.c_void_p(dist.data_ptr()), _stream_ptr(stream)))
     return probes, dist
+
+
+def ivfpq_assign_encode_ex(index: Index, vectors: torch.Tensor, stream=None):
+    """List assignment and PQ codes of database vectors with the index's
+    centroids and codebooks: (lists [n] int32, codes [n, m] uint8)."""
+    x = _dev(vectors, torch.float32)
+    if x.dim() != 2 or x.shape[1] != index.info["d"]:
+        raise ValueError(f"expected vectors of shape [n, {index.info['d']}]")
+    n = x.shape[0]
+    lists = torch.empty(n, dtype=torch.int32, device=x.device)
+    codes = torch.empty((n, index.info["m"]), dtype=torch.uint8, device=x.device)
+    _check(lib().ivfpq_assign_encode_ex(index.handle, ctypes.c_void_p(x.data_ptr()), n,
+                                        ctypes.c_void_p(lists.data_ptr()),
+                                        ctypes.c_void_p(codes.data_ptr()), _stream_ptr(stream)))
+    return lists, codes
 
 
 def ivfpq_compute_luts_ex(index: Index, queries: torch.Tensor, probes: torch.Tensor,

@@ -733,6 +733,32 @@ ivfpq_status ivfpq_coarse_ex(const ivfpq_index *idx, const float *queries_dev, i
     return ok();
 }
 
+ivfpq_status ivfpq_assign_encode_ex(const ivfpq_index *idx, const float *vectors_dev, int64_t n,
+                                    int32_t *lists_dev, uint8_t *codes_dev, void *stream)
+{
+    if (!idx)
+        return fail(IVFPQ_E_INVALID_ARG, "index handle is NULL");
+    if (n < 0 || n > (int64_t)0x7FFFFFFF)
+        return fail(IVFPQ_E_INVALID_ARG, "n must be in [0, 2^31)");
+    if (n == 0)
+        return ok();
+    if (!vectors_dev || !lists_dev || !codes_dev)
+        return fail(IVFPQ_E_INVALID_ARG, "a required device pointer is NULL");
+    DeviceGuard g(idx->device);
+    ivfpq_index *ix = const_cast<ivfpq_index *>(idx);
+    ivfpq_status s = ensure_ws(ix, coarse_ws_bytes(ix->dx, n, 1));
+    if (s)
+        return s;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = launch_coarse(idx->dx, vectors_dev, n, 1, ix->ws, lists_dev, nullptr, st);
+    if (e != hipSuccess)
+        return fail(IVFPQ_E_DEVICE, std::string("coarse kernel: ") + hipGetErrorString(e));
+    e = launch_encode(idx->dx, vectors_dev, n, lists_dev, codes_dev, st);
+    if (e != hipSuccess)
+        return fail(IVFPQ_E_DEVICE, std::string("encode kernel: ") + hipGetErrorString(e));
+    return ok();
+}
+
 ivfpq_status ivfpq_compute_luts_ex(const ivfpq_index *idx, const float *queries_dev, int64_t nq,
                                    const int32_t *probes_dev, int nprobe, int lut,
                                    float *luts_dev, void *stream)

@@ -68,6 +68,9 @@ hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
 // to stay cache resident)
 bool scan_uses_list_term(int m, int d, int nlist);
 hipError_t launch_list_term(const DeviceIndex &ix, hipStream_t stream);
+// PQ codes of n vectors (x [n][d]) given their lists (index building)
+hipError_t launch_encode(const DeviceIndex &ix, const float *x, int64_t n, const int32_t *lists,
+                         uint8_t *codes, hipStream_t stream);
 hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
                        hipStream_t stream);
 hipError_t launch_merge(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,

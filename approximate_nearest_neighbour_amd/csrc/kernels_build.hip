@@ -1,0 +1,128 @@
+// Index building on the device: PQ encoding of database vectors.
+//
+// "Custom 8-bit floating point value format for reducing shared memory bank
+// conflict in ANN search", IVFPQ section, index-building steps 2-3: the
+// residual of a vector to the centroid of its cluster is cut into m
+// sub-vectors of dsub consecutive dims and each one is quantized; with the
+// product quantizer of "Billion-scale similarity search with GPUs" (IVFADC
+// section: m quantizers of 256 reproduction values each on the residual of
+// the coarse quantizer q1).  A quantizer returns its nearest reproduction
+// value in squared L2; ties go to the smaller codeword.  The cluster (q1) is
+// the coarse step's nearest list, computed before this kernel.
+//
+// A sub-quantizer's distance is evaluated exactly as the search evaluates a
+// table entry F_j(v): r = x - c_l in float32, then sum_s (r_s - C_j[v][s])^2
+// with fused multiply-adds over the dims in order.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace ivfpq {
+
+// Workgroup: 64 vectors (vector v0 + l in lane l of every wave); its four
+// waves take the sub-quantizers j = wave, wave + 4, ...  For sub-quantizer j a
+// lane scans the 256 codewords in order and keeps the first smallest
+// distance.  The codeword being tested is the same for every lane of the wave,
+// so its values arrive through scalar loads; the residual sub-vector stays in
+// registers (DSUB > 0) or is re-formed per codeword from memory (DSUB == 0,
+// any dsub).  Codes are staged in LDS and written as whole rows.
+template <int DSUB>
+__global__ __launch_bounds__(256) void encode_kernel(const float *__restrict__ x, int64_t n, int d,
+                                                     int m, int dsub_rt,
+                                                     const int32_t *__restrict__ lists, int nlist,
+                                                     const float *__restrict__ centroids,
+                                                     const float *__restrict__ codebooks,
+                                                     uint8_t *__restrict__ codes)
+{
+    extern __shared__ uint8_t stage[]; // [64][m]
+    const int dsub = DSUB > 0 ? DSUB : dsub_rt;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t v0 = (int64_t)blockIdx.x * 64;
+    const int64_t i = v0 + lane;
+    const bool valid = i < n;
+    int l = valid ? lists[i] : 0;
+    // the coarse step returns lists in [0, nlist); anything else reads list 0
+    // rather than memory outside the centroids
+    l = (unsigned)l < (unsigned)nlist ? l : 0;
+    const float *xi = x + (valid ? i : 0) * d;
+    const float *cl = centroids + (size_t)l * d;
+
+    for (int j = wave; j < m; j += 4) {
+        const float *cb = codebooks + (size_t)j * 256 * dsub;
+        float best = INFINITY;
+        int arg = 0;
+        if constexpr (DSUB > 0) {
+            float r[DSUB];
+#pragma unroll
+            for (int s = 0; s < DSUB; ++s)
+                r[s] = xi[j * DSUB + s] - cl[j * DSUB + s];
+            for (int w = 0; w < 256; ++w) {
+                float acc = 0.f;
+#pragma unroll
+                for (int s = 0; s < DSUB; ++s) {
+                    const float df = r[s] - cb[w * DSUB + s];
+                    acc = fmaf(df, df, acc);
+                }
+                if (acc < best) {
+                    best = acc;
+                    arg = w;
+                }
+            }
+        } else {
+            for (int w = 0; w < 256; ++w) {
+                float acc = 0.f;
+                for (int s = 0; s < dsub; ++s) {
+                    const float df = (xi[j * dsub + s] - cl[j * dsub + s]) - cb[w * dsub + s];
+                    acc = fmaf(df, df, acc);
+                }
+                if (acc < best) {
+                    best = acc;
+                    arg = w;
+                }
+            }
+        }
+        stage[lane * m + j] = (uint8_t)arg;
+    }
+    __syncthreads();
+    const int64_t rows = n - v0 < 64 ? n - v0 : 64;
+    for (int64_t b = threadIdx.x; b < rows * m; b += 256)
+        codes[v0 * m + b] = stage[b];
+}
+
+template <int DSUB>
+static hipError_t encode_variant(const DeviceIndex &ix, const float *x, int64_t n,
+                                 const int32_t *lists, uint8_t *codes, hipStream_t stream)
+{
+    const int64_t blocks = (n + 63) / 64;
+    const size_t lds = (size_t)64 * ix.m;
+    hipLaunchKernelGGL(encode_kernel<DSUB>, dim3((unsigned)blocks), dim3(256), lds, stream, x, n,
+                       ix.d, ix.m, ix.d / ix.m, lists, ix.nlist, ix.centroids, ix.codebooks, codes);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode(const DeviceIndex &ix, const float *x, int64_t n, const int32_t *lists,
+                         uint8_t *codes, hipStream_t stream)
+{
+    if (n <= 0)
+        return hipSuccess;
+    if ((n + 63) / 64 > 0x7FFFFFFF || (size_t)64 * ix.m > 64 * 1024)
+        return hipErrorInvalidValue;
+    switch (ix.d / ix.m) {
+    case 2:
+        return encode_variant<2>(ix, x, n, lists, codes, stream);
+    case 3:
+        return encode_variant<3>(ix, x, n, lists, codes, stream);
+    case 4:
+        return encode_variant<4>(ix, x, n, lists, codes, stream);
+    case 8:
+        return encode_variant<8>(ix, x, n, lists, codes, stream);
+    case 12:
+        return encode_variant<12>(ix, x, n, lists, codes, stream);
+    case 16:
+        return encode_variant<16>(ix, x, n, lists, codes, stream);
+    default:
+        return encode_variant<0>(ix, x, n, lists, codes, stream);
+    }
+}
+
+} // namespace ivfpq

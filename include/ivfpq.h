@@ -158,6 +158,28 @@ ivfpq_status ivfpq_coarse_ex(const ivfpq_index *idx, const float *queries_dev, i
                              int nprobe, int32_t *probes_dev, float *coarse_dist_dev,
                              void *stream);
 
+/* Index building, list assignment and PQ encoding of database vectors
+ * (device buffers, asynchronous on `stream`).  "Custom 8-bit floating point
+ * value format for reducing shared memory bank conflict in ANN search", IVFPQ
+ * section, index-building steps 1-3, with the quantizers of "Billion-scale
+ * similarity search with GPUs", IVFADC section (coarse quantizer q1, and m
+ * quantizers of 256 reproduction values on the residual).
+ *
+ * vectors_dev [n][d] float32 row-major.  lists_dev [n] int32 receives the
+ * list of smallest |x - c_l|^2 (the coarse step with nprobe = 1);
+ * codes_dev [n][m] uint8 receives, for each sub-quantizer j, the codeword v
+ * of smallest F_j(v) = sum_s (r[j dsub + s] - C_j[v][s])^2 with r = x - c_list
+ * (float32, evaluated as the search evaluates its tables; ties to the smaller
+ * v).  The index's centroids and codebooks are used; the index's own lists
+ * are not changed.  n = 0 is a no-op; n must be < 2^31.  Errors:
+ * IVFPQ_E_INVALID_ARG (NULL handle or pointer, bad n),
+ * IVFPQ_E_OUT_OF_MEMORY (coarse workspace), IVFPQ_E_DEVICE (launch).  The
+ * buffers belong to the caller and must stay valid until the stream reaches
+ * the kernels; the call uses the handle's workspace, so it must not overlap a
+ * search on the same handle. */
+ivfpq_status ivfpq_assign_encode_ex(const ivfpq_index *idx, const float *vectors_dev, int64_t n,
+                                    int32_t *lists_dev, uint8_t *codes_dev, void *stream);
+
 /* The table step alone (device buffers, asynchronous, for verification): for
  * each query q and each of its nprobe lists probes_dev[q][p], writes the
  * m x 256 table F_j(v) to luts_dev[q][p][j][v] as float32 (values of the fp16
