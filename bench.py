@@ -35,7 +35,8 @@ def workload(name: str):
               "ivfpq_n10m_d96_m32_nlist4096": G.gmm10m,
               "ivfpq_zipf_n1000000000_d96_m8_nlist262144": G.zipf_workload}
     if name not in makers:
-        raise SystemExit(f"unknown workload {name}; choose from {sorted(makers) + [FLAT_WORKLOAD]}")
+        raise SystemExit(f"unknown workload {name}; choose from "
+                         f"{sorted(makers) + [FLAT_WORKLOAD, ENCODE_WORKLOAD]}")
     return makers[name]()
 
 
@@ -250,6 +251,113 @@ def bench_flat(args):
     f.close()
 
 
+ENCODE_WORKLOAD = "encode_n1m_d128_m16_nlist1024"
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32: matrix cores and (packed) vector ALU alike
+
+
+def bench_encode(args):
+    """Index building on the device: list assignment (coarse step, nprobe 1)
+    and PQ codes of the 1M x 128 workload's 1M database vectors with its
+    trained centroids (nlist 1024) and codebooks (m 16): one step = one call
+    over all 1M vectors."""
+    import torch
+    import approximate_nearest_neighbour_amd as A
+    from approximate_nearest_neighbour_amd import datagen as G
+    from oracle import check
+    from oracle import oracle as O
+
+    t0 = time.time()
+    w = G.gmm1m(keep_vectors=True)
+    log(f"workload {ENCODE_WORKLOAD}: built in {time.time() - t0:.1f} s")
+    ix = A.ivfpq_load_index_host(w.index, device=0)
+    x = torch.from_numpy(w.vectors).cuda()
+    n, d = x.shape
+    nlist, m = ix.info["nlist"], ix.info["m"]
+    dsub = d // m
+
+    def step():
+        return A.ivfpq_assign_encode_ex(ix, x)
+
+    def timed(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(args.steps):
+        lists, codes = step()
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t) / args.steps
+    # the two kernels on the call's stream: the whole call, then the coarse
+    # step alone (the same kernel the call launches first)
+    call_ms = timed(step, args.steps)
+    coarse_ms = timed(lambda: A.ivfpq_coarse_ex(ix, x, 1), args.steps)
+    encode_ms = max(call_ms - coarse_ms, 1e-6)
+    coarse_flops = 2.0 * n * nlist * d          # x.c for every (vector, centroid)
+    encode_flops = 3.0 * n * m * 256 * dsub     # (r - C)^2 summed: sub, mul, add
+    log(f"step {ms_step:.3f} ms  call {call_ms:.3f} ms  coarse {coarse_ms:.3f} ms  "
+        f"encode {encode_ms:.3f} ms")
+    if coarse_ms >= encode_ms:
+        roof = {"bound": "mfma", "achieved": coarse_flops / (coarse_ms * 1e-3) / 1e12,
+                "kernel": "coarse_mfma_kernel (nprobe 1)", "kernel_ms": coarse_ms,
+                "algorithmic_flops_per_launch": coarse_flops}
+    else:
+        roof = {"bound": "alu", "achieved": encode_flops / (encode_ms * 1e-3) / 1e12,
+                "kernel": "encode_kernel", "kernel_ms": encode_ms,
+                "algorithmic_flops_per_launch": encode_flops}
+    roof.update(peak=FP32_PEAK_TFLOPS, unit="TFLOP/s", frac=roof["achieved"] / FP32_PEAK_TFLOPS,
+                traffic=None)
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, min(n, 254), replace=False)]))
+    xs = w.vectors[rows]
+    rep = check.compare_encode(xs, w.index.centroids, w.index.codebooks,
+                               lists.cpu().numpy()[rows], codes.cpu().numpy()[rows])
+    log("parity", rep.summary())
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = O.default_threads()
+        t = time.perf_counter()
+        O.assign_encode(w.vectors[:4 * threads], w.index.centroids, w.index.codebooks,
+                        nthreads=threads)
+        per_v = (time.perf_counter() - t) / (4 * threads)
+        cnt = int(min(n, max(4 * threads, args.cpu_seconds / max(per_v, 1e-9))))
+        t = time.perf_counter()
+        O.assign_encode(w.vectors[:cnt], w.index.centroids, w.index.codebooks, nthreads=threads)
+        wall = time.perf_counter() - t
+        cpu = dict(value=cnt / wall, unit="vectors/s", cores=threads, kind="oracle",
+                   sample=f"first {cnt} of {n} vectors, assignment and encoding in double "
+                          f"precision, {wall:.1f} s wall")
+        log("cpu baseline", cpu)
+    res = {
+        "metric": "database vectors assigned and PQ-encoded per second",
+        "value": n / (ms_step * 1e-3),
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded Gaussian mixture, CPU-trained centroids and codebooks)",
+        "config": {"workload": ENCODE_WORKLOAD, "n": n, "d": d, "nlist": nlist, "m": m},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stages_ms": {"call": call_ms, "coarse": coarse_ms, "encode": encode_ms},
+        "parity": rep.summary(),
+    }
+    print(json.dumps(res), flush=True)
+    ix.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +392,8 @@ def main():
         __graft_entry__.build()
     if args.workload == FLAT_WORKLOAD:
         return bench_flat(args)
+    if args.workload == ENCODE_WORKLOAD:
+        return bench_encode(args)
 
     t0 = time.time()
     w = workload(args.workload)
