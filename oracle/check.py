@@ -28,6 +28,14 @@ Index building (assignment and encoding of database vectors):
    of sub-vector j: a forward-error bound of a float32 evaluation of
    sum_s (fl(x_s - c_s) - C_j[w][s])^2, times two.  Where no other code is
    that close, the codes must be equal.
+
+k-means (Lloyd's algorithm on the device):
+
+6. One round.  The device assignment obeys rule 4 against the round's input
+   centers; with that assignment the oracle's update (double-precision means)
+   gives the counts exactly, and each device center equals the float32
+   rounding of the oracle's mean or its float32 neighbour on the other side
+   of the exact mean (the device sums in double precision in another order).
 """
 from __future__ import annotations
 
@@ -296,4 +304,65 @@ def compare_encode(vectors, centroids, codebooks, gpu_lists, gpu_codes, oracle_o
                 rep.failures.append((i, f"code {v} of sub-quantizer {j} is not the nearest"))
             elif li == lists[i] and v != codes[i, j]:
                 rep.code_flips += 1
+    return rep
+
+
+@dataclasses.dataclass
+class KmeansReport:
+    n: int = 0
+    k: int = 0
+    assign_flips: int = 0
+    ulp_diffs: int = 0
+    failures: list = dataclasses.field(default_factory=list)
+
+    def ok(self) -> bool:
+        return not self.failures
+
+    def summary(self) -> dict:
+        return dict(n=self.n, k=self.k, assign_flips=self.assign_flips, ulp_diffs=self.ulp_diffs,
+                    failures=len(self.failures))
+
+
+def compare_kmeans_round(vectors, centers_in, gpu_assign, gpu_centers, gpu_counts=None,
+                         nthreads=None) -> KmeansReport:
+    """Rule 6: one device round (assignment + update) from centers_in."""
+    x = np.ascontiguousarray(vectors, dtype=np.float32)
+    c0 = np.ascontiguousarray(centers_in, dtype=np.float32)
+    ga = np.asarray(gpu_assign).reshape(-1).astype(np.int64)
+    gc = np.asarray(gpu_centers, dtype=np.float32)
+    n, d = x.shape
+    k = c0.shape[0]
+    rep = KmeansReport(n=n, k=k)
+    if ga.shape[0] != n or gc.shape != c0.shape:
+        rep.failures.append((-1, "output shape"))
+        return rep
+    if n and (ga.min() < 0 or ga.max() >= k):
+        rep.failures.append((-1, "assignment out of range"))
+        return rep
+    ol, _ = O.nearest_lists(x, c0, nthreads=nthreads)
+    cmax = float(np.max(np.sum(c0.astype(np.float64) ** 2, axis=1)))
+    for i in np.flatnonzero(ga != ol):
+        allp, alld = O.coarse(x[i], c0, k)
+        dist_of = dict(zip(allp.tolist(), alld.tolist()))
+        delta = 4.0 * gamma(d + 2) * (float(np.sum(x[i].astype(np.float64) ** 2)) + cmax)
+        if dist_of[int(ga[i])] - float(alld[0]) > delta:
+            rep.failures.append((int(i), f"assigned to {int(ga[i])}, outside the tie band"))
+        else:
+            rep.assign_flips += 1
+    want, means, counts = O.kmeans_update(x, ga, c0)
+    if gpu_counts is not None and not np.array_equal(np.asarray(gpu_counts).reshape(-1), counts):
+        rep.failures.append((-1, "counts differ"))
+    same = gc == want
+    if not same.all():
+        # the other float32 neighbour of the exact mean
+        other = np.where(want.astype(np.float64) < means,
+                         np.nextafter(want, np.float32(np.inf)),
+                         np.nextafter(want, np.float32(-np.inf)))
+        near = (gc == other) & (want.astype(np.float64) != means)
+        rep.ulp_diffs = int(np.sum(~same & near))
+        for c, t in zip(*np.nonzero(~same & ~near)):
+            rep.failures.append((int(c), f"center {int(c)} dim {int(t)}: {gc[c, t]!r} "
+                                          f"against mean {means[c, t]!r}"))
+            if len(rep.failures) > 20:
+                break
     return rep

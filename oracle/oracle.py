@@ -235,6 +235,73 @@ def assign_encode(vectors, centroids, codebooks, nthreads=None):
     return lists, codes, list_gap, code_gap
 
 
+def kmeans_update(vectors, assign, centers):
+    """The update step of Lloyd's algorithm (k-means: the clustering of the
+    index-building step 1 of the IVFPQ section of "Custom 8-bit floating
+    point value format for reducing shared memory bank conflict in ANN
+    search"; exact k-means in "Billion-scale similarity search with GPUs"):
+    each center becomes the mean of the vectors assigned to it, a center
+    with no vector keeps its value.  Sums and means in double precision; the
+    new centers are then rounded to float32, the type the index stores
+    centroids in.
+
+    Returns (centers float32 [k, d], means float64 [k, d], counts int64 [k]).
+    """
+    x = np.asarray(vectors, dtype=np.float64)
+    a = np.asarray(assign, dtype=np.int64)
+    old = np.asarray(centers, dtype=np.float32)
+    k, d = old.shape
+    sums = np.zeros((k, d), dtype=np.float64)
+    np.add.at(sums, a, x)
+    counts = np.bincount(a, minlength=k).astype(np.int64)
+    means = np.where(counts[:, None] > 0, sums / np.maximum(counts, 1)[:, None],
+                     old.astype(np.float64))
+    return means.astype(np.float32), means, counts
+
+
+def nearest_lists(vectors, centers, nthreads=None):
+    """The assignment step: for each vector the first of the coarse order
+    (nearest center, ties to the smaller index).  Returns (lists int32 [n],
+    gap float64 [n]: second-nearest minus nearest distance, +inf with one
+    center)."""
+    x = np.ascontiguousarray(vectors, dtype=np.float32)
+    cent = np.ascontiguousarray(centers, dtype=np.float32)
+    n, k = x.shape[0], cent.shape[0]
+    lists = np.empty(n, dtype=np.int32)
+    gap = np.empty(n, dtype=np.float64)
+    take = 2 if k > 1 else 1
+
+    def run(lo, hi):
+        for i in range(lo, hi):
+            pr, dist = coarse(x[i], cent, take)
+            lists[i] = pr[0]
+            gap[i] = dist[1] - dist[0] if take == 2 else np.inf
+
+    nt = max(1, min(nthreads or default_threads(), n))
+    if nt == 1:
+        run(0, n)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        step = (n + nt - 1) // nt
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(lambda s: run(s, min(n, s + step)), range(0, n, step)))
+    return lists, gap
+
+
+def kmeans(vectors, init, iters, nthreads=None):
+    """Lloyd's algorithm from the given float32 initial centers: `iters`
+    rounds of assignment (``nearest_lists``) then update
+    (``kmeans_update``).  Returns (centers float32 [k, d], the last round's
+    assignment int32 [n], its counts int64 [k])."""
+    c = np.ascontiguousarray(init, dtype=np.float32)
+    a = np.zeros(len(vectors), dtype=np.int32)
+    counts = np.zeros(c.shape[0], dtype=np.int64)
+    for _ in range(iters):
+        a, _ = nearest_lists(vectors, c, nthreads=nthreads)
+        c, _, counts = kmeans_update(vectors, a, c)
+    return c, a, counts
+
+
 def bruteforce(db, queries, k, db_ids=None, nthreads=None):
     db = np.ascontiguousarray(db, dtype=np.float32)
     q = np.ascontiguousarray(queries, dtype=np.float32)

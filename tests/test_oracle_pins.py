@@ -410,3 +410,93 @@ def test_encode_checker_accepts_oracle_and_rejects_perturbations():
     far[i] = int(O.coarse(x[i], cent, nlist)[0][-1])   # the farthest list
     assert not check.compare_encode(x, cent, books, far, codes, oracle_out=out).ok()
     assert not check.compare_encode(x, cent, books, np.full(200, nlist), codes, oracle_out=out).ok()
+
+
+# ---------------------------------------------------------------------------
+# k-means (Lloyd's algorithm)
+# ---------------------------------------------------------------------------
+
+def test_kmeans_update_pure_python():
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((37, 3)).astype(np.float32)
+    a = rng.integers(0, 5, 37)
+    a[a == 4] = 3                                  # center 4 gets nothing
+    c0 = rng.standard_normal((5, 3)).astype(np.float32)
+    got, means, counts = O.kmeans_update(x, a, c0)
+    for c in range(5):
+        members = [x[i] for i in range(37) if a[i] == c]
+        assert counts[c] == len(members)
+        for t in range(3):
+            if members:
+                want = math.fsum(float(v[t]) for v in members) / len(members)
+            else:
+                want = float(c0[c, t])
+            assert abs(means[c, t] - want) <= 1e-15 * max(1.0, abs(want))
+            assert got[c, t] == np.float32(want)
+
+
+def test_kmeans_update_closed_forms():
+    # identical members: their value; symmetric pairs: the midpoint; shifting
+    # every vector shifts every mean
+    p = np.array([1.5, -2.25, 3.0], dtype=np.float32)
+    q = np.array([0.5, 0.5, -0.5], dtype=np.float32)
+    x = np.stack([p, p, p, q + 1, q - 1])
+    a = np.array([0, 0, 0, 1, 1])
+    c0 = np.zeros((3, 3), dtype=np.float32)
+    got, _, counts = O.kmeans_update(x, a, c0)
+    assert np.array_equal(got[0], p) and np.array_equal(got[1], q)
+    assert np.array_equal(got[2], c0[2]) and counts.tolist() == [3, 2, 0]
+    rng = np.random.default_rng(52)
+    y = rng.standard_normal((200, 4))
+    b = rng.integers(0, 6, 200)
+    _, m1, _ = O.kmeans_update(y, b, np.zeros((6, 4), dtype=np.float32))
+    _, m2, _ = O.kmeans_update(y + 7.0, b, np.zeros((6, 4), dtype=np.float32))
+    np.testing.assert_allclose(m2, m1 + 7.0, rtol=0, atol=1e-12)
+
+
+def test_kmeans_lloyd_decreases_the_objective_and_finds_separated_clusters():
+    rng = np.random.default_rng(53)
+    k, d = 6, 8
+    true = 20.0 * rng.standard_normal((k, d))
+    lab = rng.integers(0, k, 600)
+    x = (true[lab] + rng.standard_normal((600, d))).astype(np.float32)
+    init = x[[int(np.flatnonzero(lab == c)[0]) for c in range(k)]]   # one point per cluster
+
+    def objective(c, a):
+        return float(np.sum((x.astype(np.float64) - c.astype(np.float64)[a]) ** 2))
+
+    c, prev = init, None
+    for it in range(4):
+        a, _ = O.nearest_lists(x, c)
+        if prev is not None:
+            assert objective(c, a) <= prev * (1 + 1e-9)
+        c, _, counts = O.kmeans_update(x, a, c)
+        prev = objective(c, a)
+    # one point per true cluster to start: the first assignment is the
+    # clustering itself, and the centers are the cluster means
+    assert np.array_equal(a, lab)
+    for j in range(k):
+        assert np.array_equal(c[j], x[lab == j].astype(np.float64).mean(0).astype(np.float32))
+    c2, a2, n2 = O.kmeans(x, init, 4)
+    assert np.array_equal(c2, c) and np.array_equal(a2, a) and np.array_equal(n2, counts)
+
+
+def test_kmeans_checker_accepts_oracle_and_rejects_perturbations():
+    rng = np.random.default_rng(54)
+    x = rng.standard_normal((300, 6)).astype(np.float32)
+    c0 = x[:10].copy()
+    a, _ = O.nearest_lists(x, c0)
+    c1, means, counts = O.kmeans_update(x, a, c0)
+    assert check.compare_kmeans_round(x, c0, a, c1, counts).ok()
+    other = c1.copy()
+    c, t = 3, 2
+    other[c, t] = np.nextafter(c1[c, t], np.float32(np.inf if means[c, t] > c1[c, t] else -np.inf))
+    assert check.compare_kmeans_round(x, c0, a, other, counts).ok()      # the other neighbour
+    far = c1.copy()
+    far[c, t] = np.nextafter(c1[c, t], np.float32(-np.inf if means[c, t] > c1[c, t] else np.inf))
+    assert not check.compare_kmeans_round(x, c0, a, far, counts).ok()
+    bad = a.copy()
+    i = int(np.argmax([np.sum((x[j] - c0[a[j]]) ** 2) for j in range(300)]))
+    bad[i] = int(O.coarse(x[i], c0, 10)[0][-1])
+    assert not check.compare_kmeans_round(x, c0, bad, c1, counts).ok()
+    assert not check.compare_kmeans_round(x, c0, a, c1, counts + 1).ok()
