@@ -9,7 +9,8 @@ from .binding import (IVFPQError, FlatIndex, Index, ivfpq_assign_encode_ex,  # n
                       ivfpq_compute_luts_ex,
                       ivfpq_coarse_ex, ivfpq_flat_free, ivfpq_flat_load_bf16,
                       ivfpq_flat_profile_begin, ivfpq_flat_profile_end, ivfpq_flat_search_bf16,
-                      ivfpq_flat_search_bf16_ex, ivfpq_free_index, ivfpq_index_info, ivfpq_last_error, ivfpq_load_index,
+                      ivfpq_flat_search_bf16_ex, ivfpq_free_index, ivfpq_index_info, ivfpq_kmeans_ex,
+                      ivfpq_last_error, ivfpq_load_index,
                       ivfpq_load_index_host, ivfpq_profile_begin, ivfpq_profile_end,
                       ivfpq_search, ivfpq_search_ex, ivfpq_select_topk_ex, ivfpq_status_string,
                       ivfpq_stream_read,

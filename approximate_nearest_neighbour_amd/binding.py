@@ -65,7 +65,8 @@ class FlatTimings(ctypes.Structure):
 
 EXPORTS = ("ivfpq_validate_index_file", "ivfpq_validate_host_index", "ivfpq_load_index",
            "ivfpq_load_index_host", "ivfpq_free_index", "ivfpq_index_info", "ivfpq_search",
-           "ivfpq_search_ex", "ivfpq_coarse_ex", "ivfpq_assign_encode_ex", "ivfpq_compute_luts_ex",
+           "ivfpq_search_ex", "ivfpq_coarse_ex", "ivfpq_assign_encode_ex", "ivfpq_kmeans_ex",
+           "ivfpq_compute_luts_ex",
            "ivfpq_select_topk_ex",
            "ivfpq_profile_begin",
            "ivfpq_profile_end", "ivfpq_flat_load_bf16", "ivfpq_flat_free",
@@ -97,6 +98,7 @@ def lib():
             "ivfpq_search_ex": ([P, P, P, i64, P, P, P, P], st),
             "ivfpq_coarse_ex": ([P, P, i64, i32, P, P, P], st),
             "ivfpq_assign_encode_ex": ([P, P, i64, P, P, P], st),
+            "ivfpq_kmeans_ex": ([P, i64, i32, i32, i32, P, P, P, P], st),
             "ivfpq_compute_luts_ex": ([P, P, i64, P, i32, i32, P, P], st),
             "ivfpq_select_topk_ex": ([P, i64, i64, i32, P, P, P], st),
             "ivfpq_profile_begin": ([P, i32], st),
@@ -286,6 +288,23 @@ def ivfpq_assign_encode_ex(index: Index, vectors: torch.Tensor, stream=None):
                                         ctypes.c_void_p(lists.data_ptr()),
                                         ctypes.c_void_p(codes.data_ptr()), _stream_ptr(stream)))
     return lists, codes
+
+
+def ivfpq_kmeans_ex(vectors: torch.Tensor, centers: torch.Tensor, iters: int, stream=None):
+    """Lloyd's algorithm on the device: `centers` ([k, d] float32, updated in
+    place) from `vectors` ([n, d] float32).  Returns the last round's
+    (assignment [n] int32, counts [k] int32)."""
+    x = _dev(vectors, torch.float32)
+    c = _dev(centers, torch.float32)
+    if x.dim() != 2 or c.dim() != 2 or x.shape[1] != c.shape[1]:
+        raise ValueError("expected vectors [n, d] and centers [k, d]")
+    n, (k, d) = x.shape[0], c.shape
+    assign = torch.full((n,), -1, dtype=torch.int32, device=x.device)
+    counts = torch.zeros(k, dtype=torch.int32, device=x.device)
+    _check(lib().ivfpq_kmeans_ex(ctypes.c_void_p(x.data_ptr()), n, d, k, iters,
+                                 ctypes.c_void_p(c.data_ptr()), ctypes.c_void_p(assign.data_ptr()),
+                                 ctypes.c_void_p(counts.data_ptr()), _stream_ptr(stream)))
+    return assign, counts
 
 
 def ivfpq_compute_luts_ex(index: Index, queries: torch.Tensor, probes: torch.Tensor,

@@ -759,6 +759,62 @@ ivfpq_status ivfpq_assign_encode_ex(const ivfpq_index *idx, const float *vectors
     return ok();
 }
 
+ivfpq_status ivfpq_kmeans_ex(const float *vectors_dev, int64_t n, int d, int k, int iters,
+                             float *centers_dev, int32_t *assign_dev, int32_t *counts_dev,
+                             void *stream)
+{
+    if (n < 0 || n > (int64_t)0x7FFFFFFF)
+        return fail(IVFPQ_E_INVALID_ARG, "n must be in [0, 2^31)");
+    if (d < 1 || d > 4096 || k < 1 || k > (1 << 24) || iters < 0 || iters > 100000)
+        return fail(IVFPQ_E_INVALID_ARG, "need 1 <= d <= 4096, 1 <= k <= 2^24, 0 <= iters");
+    if (!centers_dev || (n > 0 && !vectors_dev))
+        return fail(IVFPQ_E_INVALID_ARG, "a required device pointer is NULL");
+    if (iters == 0)
+        return ok();
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess)
+        return fail(IVFPQ_E_NO_DEVICE, "no current device");
+    // the centers as a coarse quantizer (layout of the coarse kernel)
+    DeviceIndex dx;
+    dx.d = d;
+    dx.nlist = k;
+    dx.d4 = (d + 3) / 4 <= 32 ? ((d + 31) / 32) * 8 : (d + 3) / 4;
+    dx.nblk = ((k + 63) / 64) * 4;
+    dx.centroids = centers_dev;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    void *cblk = nullptr, *cnorm = nullptr, *sums = nullptr, *own_a = nullptr, *own_c = nullptr,
+         *ws = nullptr;
+    const size_t ws_bytes = coarse_ws_bytes(dx, n > 0 ? n : 1, 1);
+    ivfpq_status s = IVFPQ_OK;
+    if (dev_alloc(&cblk, (size_t)dx.nblk * dx.d4 * 64 * 4) != hipSuccess ||
+        dev_alloc(&cnorm, (size_t)dx.nblk * 16 * 4) != hipSuccess ||
+        dev_alloc(&sums, (size_t)k * d * 8) != hipSuccess ||
+        (!assign_dev && dev_alloc(&own_a, (size_t)(n > 0 ? n : 1) * 4) != hipSuccess) ||
+        (!counts_dev && dev_alloc(&own_c, (size_t)k * 4) != hipSuccess) ||
+        (ws_bytes && dev_alloc(&ws, ws_bytes) != hipSuccess))
+        s = fail(IVFPQ_E_OUT_OF_MEMORY, "k-means scratch allocation failed");
+    dx.cblk = static_cast<float *>(cblk);
+    dx.cnorm_pad = static_cast<float *>(cnorm);
+    int32_t *assign = assign_dev ? assign_dev : static_cast<int32_t *>(own_a);
+    int32_t *counts = counts_dev ? counts_dev : static_cast<int32_t *>(own_c);
+    for (int it = 0; it < iters && s == IVFPQ_OK; ++it) {
+        hipError_t e = launch_centroid_blocks(dx, st);
+        if (e == hipSuccess)
+            e = launch_coarse(dx, vectors_dev, n, 1, ws, assign, nullptr, st);
+        if (e == hipSuccess)
+            e = launch_kmeans_update(vectors_dev, n, d, assign, k, static_cast<double *>(sums),
+                                     counts, centers_dev, st);
+        if (e != hipSuccess)
+            s = fail(IVFPQ_E_DEVICE, std::string("k-means round: ") + hipGetErrorString(e));
+    }
+    if (hipStreamSynchronize(st) != hipSuccess && s == IVFPQ_OK)
+        s = fail(IVFPQ_E_DEVICE, "k-means failed on the device");
+    for (void *p : {cblk, cnorm, sums, own_a, own_c, ws})
+        if (p)
+            (void)hipFree(p);
+    return s;
+}
+
 ivfpq_status ivfpq_compute_luts_ex(const ivfpq_index *idx, const float *queries_dev, int64_t nq,
                                    const int32_t *probes_dev, int nprobe, int lut,
                                    float *luts_dev, void *stream)

@@ -71,6 +71,10 @@ hipError_t launch_list_term(const DeviceIndex &ix, hipStream_t stream);
 // PQ codes of n vectors (x [n][d]) given their lists (index building)
 hipError_t launch_encode(const DeviceIndex &ix, const float *x, int64_t n, const int32_t *lists,
                          uint8_t *codes, hipStream_t stream);
+// k-means update step: centers = means of their assigned vectors (sums [k][d]
+// double and counts [k] are scratch / output)
+hipError_t launch_kmeans_update(const float *x, int64_t n, int d, const int32_t *assign, int k,
+                                double *sums, int32_t *counts, float *centers, hipStream_t stream);
 hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
                        hipStream_t stream);
 hipError_t launch_merge(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,

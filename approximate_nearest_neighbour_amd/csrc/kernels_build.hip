@@ -125,4 +125,74 @@ hipError_t launch_encode(const DeviceIndex &ix, const float *x, int64_t n, const
     }
 }
 
+// ---------------------------------------------------------------------------
+// k-means (Lloyd's algorithm), the update step: each center becomes the mean
+// of the vectors assigned to it; a center with no vector keeps its value.
+// "Custom 8-bit floating point value format for reducing shared memory bank
+// conflict in ANN search", IVFPQ section, index-building step 1 (clusters by
+// k-means).  The assignment step is the coarse kernel with nprobe 1.
+// ---------------------------------------------------------------------------
+
+__global__ void kmeans_zero_kernel(double *__restrict__ sums, int64_t nsum,
+                                   int32_t *__restrict__ counts, int k)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nsum)
+        sums[i] = 0.0;
+    if (i < k)
+        counts[i] = 0;
+}
+
+// One wave per vector: its coordinates go into its center's sums with
+// double-precision atomic adds (exact enough that the float32 mean is the
+// same whatever the order of the adds, up to a rounding-boundary case).
+__global__ __launch_bounds__(256) void kmeans_accumulate_kernel(
+    const float *__restrict__ x, int64_t n, int d, const int32_t *__restrict__ assign, int k,
+    double *__restrict__ sums, int32_t *__restrict__ counts)
+{
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (i >= n)
+        return;
+    const int a = assign[i];
+    if ((unsigned)a >= (unsigned)k)
+        return;
+    const float *xi = x + i * d;
+    double *s = sums + (size_t)a * d;
+    for (int t = lane; t < d; t += 64)
+        unsafeAtomicAdd(s + t, (double)xi[t]);
+    if (lane == 0)
+        atomicAdd(counts + a, 1);
+}
+
+__global__ void kmeans_finalize_kernel(float *__restrict__ centers, const double *__restrict__ sums,
+                                       const int32_t *__restrict__ counts, int k, int d)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (int64_t)k * d)
+        return;
+    const int cnt = counts[e / d];
+    if (cnt > 0)
+        centers[e] = (float)(sums[e] / (double)cnt);
+}
+
+hipError_t launch_kmeans_update(const float *x, int64_t n, int d, const int32_t *assign, int k,
+                                double *sums, int32_t *counts, float *centers, hipStream_t stream)
+{
+    const int64_t nsum = (int64_t)k * d;
+    const int64_t zn = nsum > k ? nsum : k;
+    hipLaunchKernelGGL(kmeans_zero_kernel, dim3((unsigned)((zn + 255) / 256)), dim3(256), 0,
+                       stream, sums, nsum, counts, k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n == 0)
+        return e;
+    hipLaunchKernelGGL(kmeans_accumulate_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0,
+                       stream, x, n, d, assign, k, sums, counts);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(kmeans_finalize_kernel, dim3((unsigned)((nsum + 255) / 256)), dim3(256), 0,
+                       stream, centers, sums, counts, k, d);
+    return hipGetLastError();
+}
+
 } // namespace ivfpq

@@ -180,6 +180,29 @@ ivfpq_status ivfpq_coarse_ex(const ivfpq_index *idx, const float *queries_dev, i
 ivfpq_status ivfpq_assign_encode_ex(const ivfpq_index *idx, const float *vectors_dev, int64_t n,
                                     int32_t *lists_dev, uint8_t *codes_dev, void *stream);
 
+/* k-means by Lloyd's algorithm on the device (the clustering of "Custom 8-bit
+ * floating point value format for reducing shared memory bank conflict in ANN
+ * search", IVFPQ section, index-building step 1; run it on the residuals of
+ * one sub-vector to train a sub-quantizer's 256 codewords).  Each of `iters`
+ * rounds assigns every vector to its nearest center (the coarse step with
+ * nprobe = 1: squared L2 through the float32 norm expansion on the matrix
+ * cores) and then moves every center to the mean of its vectors (sums in
+ * double precision, the mean rounded to float32); a center with no vector
+ * keeps its value.
+ *
+ * vectors_dev [n][d] float32 row-major; centers_dev [k][d] float32: the
+ * initial centers on entry, the centers after the last round on return.
+ * assign_dev [n] int32 and counts_dev [k] int32, when not NULL, receive the
+ * last round's assignment and cluster sizes.  On the current device and
+ * `stream`; scratch is allocated and freed inside, and the call returns after
+ * the device work is done.  iters = 0 changes nothing; n = 0 leaves the centers
+ * as they are.  Errors: IVFPQ_E_INVALID_ARG (n outside [0, 2^31), d outside
+ * [1, 4096], k outside [1, 2^24], iters < 0, NULL centers, NULL vectors with
+ * n > 0), IVFPQ_E_OUT_OF_MEMORY, IVFPQ_E_NO_DEVICE, IVFPQ_E_DEVICE. */
+ivfpq_status ivfpq_kmeans_ex(const float *vectors_dev, int64_t n, int d, int k, int iters,
+                             float *centers_dev, int32_t *assign_dev, int32_t *counts_dev,
+                             void *stream);
+
 /* The table step alone (device buffers, asynchronous, for verification): for
  * each query q and each of its nprobe lists probes_dev[q][p], writes the
  * m x 256 table F_j(v) to luts_dev[q][p][j][v] as float32 (values of the fp16

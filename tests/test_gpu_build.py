@@ -6,6 +6,11 @@ the nearest centroid only inside the coarse tie band; each device code must
 be the nearest codeword of the oracle's table of the device's list up to the
 float32 forward-error bound, so codes are equal wherever the decision is not
 a near-tie.  Exact ties must go to the smaller codeword.
+
+k-means (ivfpq_kmeans_ex, rule 6): each device round's assignment obeys the
+coarse tie band against its input centers, its counts equal the oracle's
+for that assignment, and every center equals the float32 rounding of the
+oracle's double-precision mean or the float32 neighbour across it.
 """
 import sys
 
@@ -165,3 +170,107 @@ def test_encode_fullsize_1m(dev):
     say(f"agreement with the CPU builder: lists {same_list.mean():.5f}, "
         f"codes {(same_code & same_list).mean():.5f}")
     assert same_list.mean() > 0.99 and (same_code & same_list).mean() > 0.95
+
+
+# ---------------------------------------------------------------------------
+# k-means (Lloyd's algorithm) on the device
+# ---------------------------------------------------------------------------
+
+def gpu_kmeans(x, init, iters):
+    xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    c = torch.from_numpy(np.array(init, dtype=np.float32)).cuda()
+    a, cnt = A.ivfpq_kmeans_ex(xt, c, iters)
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), a.cpu().numpy(), cnt.cpu().numpy()
+
+
+def mixture(seed, n, d, ncomp, spread=0.5):
+    rng = np.random.default_rng(seed)
+    comp = rng.standard_normal((ncomp, d))
+    x = (comp[rng.integers(0, ncomp, n)] + spread * rng.standard_normal((n, d))).astype(np.float32)
+    return x, rng
+
+
+@pytest.mark.parametrize("n,d,k", [
+    (5000, 32, 16),
+    (20000, 128, 1024),   # the 1M workload's coarse training shape, smaller n
+    (3000, 96, 4096),     # more centers than vectors: empty and duplicate centers
+    (2000, 200, 50),      # d > 128: the direct-difference coarse kernel
+    (1000, 8, 300),
+    (777, 60, 7),
+    (1, 4, 1),
+])
+def test_kmeans_one_round(dev, n, d, k):
+    say(f"k-means round n={n} d={d} k={k}")
+    x, rng = mixture(200 + d + k, n, d, max(k // 4, 2))
+    init = x[rng.choice(n, k, replace=k > n)]
+    c1, a, cnt = gpu_kmeans(x, init, 1)
+    rep = check.compare_kmeans_round(x, init, a, c1, cnt)
+    say("k-means parity", rep.summary())
+    assert rep.ok(), rep.failures[:5]
+
+
+def test_kmeans_chained_rounds(dev):
+    # four rounds, each its own call and each checked against the oracle's
+    # round from the same input centers
+    x, rng = mixture(61, 6000, 48, 20)
+    c = x[rng.choice(6000, 64, replace=False)]
+    for r in range(4):
+        say(f"k-means chained round {r}")
+        c_next, a, cnt = gpu_kmeans(x, c, 1)
+        rep = check.compare_kmeans_round(x, c, a, c_next, cnt)
+        assert rep.ok(), (r, rep.failures[:5])
+        c = c_next
+
+
+def test_kmeans_rounds_in_one_call_match_the_oracle(dev):
+    # separated clusters, one initial center in each: every round's
+    # assignment is unambiguous, so five rounds in one call must give the
+    # oracle's assignment and counts, and its centers up to the float32
+    # neighbour of each exact mean
+    rng = np.random.default_rng(62)
+    k, d = 32, 64
+    true = 30.0 * rng.standard_normal((k, d))
+    lab = rng.integers(0, k, 8000)
+    x = (true[lab] + rng.standard_normal((8000, d))).astype(np.float32)
+    init = x[[int(np.flatnonzero(lab == c)[0]) for c in range(k)]]
+    say("k-means five rounds")
+    c, a, cnt = gpu_kmeans(x, init, 5)
+    oc, oa, ocnt = O.kmeans(x, init, 5)
+    assert np.array_equal(a, oa) and np.array_equal(cnt, ocnt)
+    assert np.all(np.abs(c.astype(np.float64) - oc) <= np.spacing(np.abs(oc)))
+
+
+def test_kmeans_edge_cases_and_errors(dev):
+    x, rng = mixture(63, 100, 16, 4)
+    init = x[:5].copy()
+    c, a, cnt = gpu_kmeans(x, init, 0)                 # no rounds: nothing changes
+    assert np.array_equal(c, init) and np.all(a == -1) and np.all(cnt == 0)
+    c, a, cnt = gpu_kmeans(np.zeros((0, 16), np.float32), init, 3)
+    assert np.array_equal(c, init) and np.all(cnt == 0)
+    from approximate_nearest_neighbour_amd import binding as B
+    L = B.lib()
+    ct = torch.from_numpy(init.copy()).cuda()
+    p = ct.data_ptr()
+    for args in [(None, 5, 16, 5, 1, p), (None, 0, 0, 5, 1, p), (None, 0, 16, 0, 1, p),
+                 (None, 0, 16, 5, -1, p), (None, 0, 16, 5, 1, None), (None, -1, 16, 5, 1, p)]:
+        vec, n, d, k, it, cen = args
+        st = L.ivfpq_kmeans_ex(vec, n, d, k, it, cen, None, None, None)
+        assert st == B.E_INVALID_ARG, args
+    with pytest.raises(ValueError):
+        A.ivfpq_kmeans_ex(torch.zeros((4, 8), device="cuda"), torch.zeros((2, 9), device="cuda"), 1)
+
+
+@pytest.mark.slow
+def test_kmeans_fullsize_round(dev):
+    # one round at the 1M workload's coarse training shape (262,144 sampled
+    # vectors, 1,024 centers, d 128), checked in full
+    say("k-means full size: 262,144 x 128, k 1024, one round")
+    w = G.gmm1m(keep_vectors=True)
+    rng = np.random.default_rng(64)
+    x = w.vectors[np.sort(rng.choice(len(w.vectors), 262_144, replace=False))]
+    init = x[rng.choice(len(x), 1024, replace=False)]
+    c1, a, cnt = gpu_kmeans(x, init, 1)
+    rep = check.compare_kmeans_round(x, init, a, c1, cnt)
+    say("k-means parity", rep.summary())
+    assert rep.ok(), rep.failures[:5]
