@@ -36,7 +36,7 @@ def workload(name: str):
               "ivfpq_zipf_n1000000000_d96_m8_nlist262144": G.zipf_workload}
     if name not in makers:
         raise SystemExit(f"unknown workload {name}; choose from "
-                         f"{sorted(makers) + [FLAT_WORKLOAD, ENCODE_WORKLOAD]}")
+                         f"{sorted(makers) + [FLAT_WORKLOAD, ENCODE_WORKLOAD, KMEANS_WORKLOAD]}")
     return makers[name]()
 
 
@@ -358,6 +358,86 @@ def bench_encode(args):
     ix.close()
 
 
+KMEANS_WORKLOAD = "kmeans_n262144_d128_k1024"
+
+
+def bench_kmeans(args):
+    """k-means on the device at the 1M x 128 workload's coarse training shape:
+    262,144 of its vectors (seeded sample), 1,024 centers initialised with
+    1,024 distinct sampled vectors; one step = one call of 10 Lloyd rounds."""
+    import torch
+    import approximate_nearest_neighbour_amd as A
+    from approximate_nearest_neighbour_amd import datagen as G
+    from oracle import check
+    from oracle import oracle as O
+
+    rounds = 10
+    t0 = time.time()
+    w = G.gmm1m(keep_vectors=True)
+    rng = np.random.default_rng(2003)
+    xs = w.vectors[np.sort(rng.choice(len(w.vectors), 262_144, replace=False))]
+    init = xs[rng.choice(len(xs), 1024, replace=False)]
+    log(f"workload {KMEANS_WORKLOAD}: built in {time.time() - t0:.1f} s")
+    x = torch.from_numpy(xs).cuda()
+    c0 = torch.from_numpy(init).cuda()
+    c = c0.clone()
+    n, d = xs.shape
+    k = init.shape[0]
+
+    def step(iters=rounds):
+        c.copy_(c0)
+        return A.ivfpq_kmeans_ex(x, c, iters)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t) / args.steps
+    ms_round = ms_step / rounds
+    flops = 2.0 * n * k * d                       # the assignment's x.c per round
+    achieved = flops / (ms_round * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms = {rounds} rounds, {ms_round:.3f} ms per round")
+    # parity: the first round, checked in full against the oracle
+    a1, n1 = step(1)
+    rep = check.compare_kmeans_round(xs, init, a1.cpu().numpy(), c.cpu().numpy(), n1.cpu().numpy())
+    log("parity (round 1)", rep.summary())
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = O.default_threads()
+        t = time.perf_counter()
+        O.kmeans(xs, init, 1, nthreads=threads)
+        wall = time.perf_counter() - t
+        cpu = dict(value=1.0 / wall, unit="rounds/s", cores=threads, kind="oracle",
+                   sample=f"one round over all {n} vectors (assignment in double precision, "
+                          f"full sort per vector; double-precision means), {wall:.1f} s wall")
+        log("cpu baseline", cpu)
+    res = {
+        "metric": "k-means (Lloyd) rounds per second",
+        "value": 1e3 / ms_round,
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 (double-precision sums)",
+        "data": "synthetic (seeded Gaussian mixture sample)",
+        "config": {"workload": KMEANS_WORKLOAD, "n": n, "d": d, "k": k, "rounds_per_step": rounds},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "one round (coarse assignment + update), assignment flops",
+                     "kernel_ms": ms_round, "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": cpu,
+        "parity": rep.summary(),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -394,6 +474,8 @@ def main():
         return bench_flat(args)
     if args.workload == ENCODE_WORKLOAD:
         return bench_encode(args)
+    if args.workload == KMEANS_WORKLOAD:
+        return bench_kmeans(args)
 
     t0 = time.time()
     w = workload(args.workload)
