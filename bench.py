@@ -36,7 +36,7 @@ def workload(name: str):
               "ivfpq_zipf_n1000000000_d96_m8_nlist262144": G.zipf_workload}
     if name not in makers:
         raise SystemExit(f"unknown workload {name}; choose from "
-                         f"{sorted(makers) + [FLAT_WORKLOAD, ENCODE_WORKLOAD, KMEANS_WORKLOAD]}")
+                         f"{sorted(makers) + [FLAT_WORKLOAD, ENCODE_WORKLOAD, KMEANS_WORKLOAD, KNN_GRAPH_WORKLOAD]}")
     return makers[name]()
 
 
@@ -438,6 +438,97 @@ def bench_kmeans(args):
     print(json.dumps(res), flush=True)
 
 
+KNN_GRAPH_WORKLOAD = "knn_graph_n1m_d128_k10"
+
+
+def bench_knn_graph(args):
+    """The k-NN graph of the 1M x 128 workload ("Billion-scale similarity
+    search with GPUs", k-NN graph experiment: every database vector searched
+    for its k = 10 nearest neighbours): one step = one IVF-PQ search of all
+    1M database vectors (nprobe 32, float32 tables) against the workload's
+    index; a vector's own entry is among its results like any other."""
+    import torch
+    import approximate_nearest_neighbour_amd as A
+    from approximate_nearest_neighbour_amd import datagen as G
+    from oracle import check
+    from oracle import oracle as O
+
+    t0 = time.time()
+    w = G.gmm1m(keep_vectors=True)
+    log(f"workload {KNN_GRAPH_WORKLOAD}: built in {time.time() - t0:.1f} s")
+    k, nprobe = 10, w.nprobe
+    ix = A.ivfpq_load_index_host(w.index, device=0)
+    q = torch.from_numpy(w.vectors).cuda()
+    nq = q.shape[0]
+    out = (torch.empty((nq, k), dtype=torch.float32, device="cuda"),
+           torch.empty((nq, k), dtype=torch.int64, device="cuda"),
+           torch.empty((nq, nprobe), dtype=torch.int32, device="cuda"))
+
+    def step():
+        A.ivfpq_search_ex(ix, q, nprobe, k, return_probes=True, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    entries = scanned_entries(w.index, out[2].cpu().numpy())
+    code_bytes = entries * w.index.m
+    A.ivfpq_profile_begin(ix, args.steps)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t) / args.steps
+    prof = A.ivfpq_profile_end(ix)
+    calls = max(prof["calls"], 1)
+    scan_ms, coarse_ms = prof["scan_ms"] / calls, prof["coarse_ms"] / calls
+    achieved = code_bytes / (scan_ms * 1e-3) / 1e9
+    log(f"step {ms_step:.3f} ms  coarse {coarse_ms:.3f} ms  scan {scan_ms:.3f} ms  "
+        f"code bytes/launch {code_bytes / 1e9:.3f} GB")
+    rng = np.random.default_rng(2004)
+    rows = np.sort(rng.choice(nq, min(nq, args.parity_queries), replace=False))
+    rep = check.compare_search(w.index, w.vectors[rows], nprobe, k, out[0].cpu().numpy()[rows],
+                               out[1].cpu().numpy()[rows], out[2].cpu().numpy()[rows])
+    log("parity", rep.summary())
+    # graph quality: the fraction of the 10 found within the exact 10 nearest
+    # (oracle brute force, double precision) on a sample of vectors
+    qs = np.sort(rng.choice(nq, 500, replace=False))
+    _, true_ids = O.bruteforce(w.vectors, w.vectors[qs], k)
+    recall = O.recall_k_at_k(out[1].cpu().numpy()[qs], true_ids)
+    log(f"10-recall@10 on 500 sampled vectors: {recall:.4f}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        gw = G.Workload(KNN_GRAPH_WORKLOAD, w.index, w.vectors, nprobe, k)
+        cpu, _ = cpu_baseline(gw, O.LUT_F64, args.cpu_seconds)
+        cpu["unit"] = "vectors/s"
+        log("cpu baseline", cpu)
+    res = {
+        "metric": "k-NN graph construction: database vectors searched per second (k 10)",
+        "value": nq / (ms_step * 1e-3),
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded Gaussian mixture, CPU-built IVF-PQ index)",
+        "config": {"workload": KNN_GRAPH_WORKLOAD, "n": nq, "d": w.index.d,
+                   "nlist": w.index.nlist, "m": w.index.m, "nprobe": nprobe, "k": k},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "scan_kernel",
+                     "kernel_ms": scan_ms, "algorithmic_bytes_per_launch": code_bytes},
+        "cpu_baseline": cpu,
+        "stages_ms": {"coarse": coarse_ms, "scan": scan_ms},
+        "recall_10_at_10": recall,
+        "parity": rep.summary(),
+    }
+    print(json.dumps(res), flush=True)
+    ix.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -476,6 +567,8 @@ def main():
         return bench_encode(args)
     if args.workload == KMEANS_WORKLOAD:
         return bench_kmeans(args)
+    if args.workload == KNN_GRAPH_WORKLOAD:
+        return bench_knn_graph(args)
 
     t0 = time.time()
     w = workload(args.workload)

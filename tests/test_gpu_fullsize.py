@@ -88,3 +88,13 @@ def test_fullsize_flat_bf16(A):
     print(f"  parity {rep.summary()}", flush=True)
     f.close()
     assert rep.ok(), rep.failures[:5]
+
+
+def test_fullsize_knn_graph_1m(A):
+    # the k-NN graph of the 1M x 128 workload: all 1M database vectors
+    # searched with k = 10 in one call (the benchmark's configuration),
+    # sampled rows checked against the oracle
+    print("full size: k-NN graph, 1M x 128 queries against the 1M index, k 10", flush=True)
+    w = G.gmm1m(keep_vectors=True)
+    gw = G.Workload("knn_graph_n1m_d128_k10", w.index, w.vectors, w.nprobe, 10)
+    search_and_check(A, gw, sample=24)
