@@ -16,6 +16,13 @@ rules below say when a device result counts as the oracle's result:
 3. Distances.  Every returned id's distance is within tau relative of the
    oracle's distance for that id (tau = 1e-4 float32 tables, 1e-2 fp16).
 
+Inner-product metric: rules 1-3 on the negated scores (so that rows ascend),
+with absolute bands in place of the relative ones (a score can be near zero):
+delta_c(q) = 4 gamma_{d+2} |x_q| max_l |c_l| for the probes, and for ids and
+scores delta_s(q) = 4 gamma_{d+m+2} |x_q| (max_l |c_l| + sum_j max_v |C_j[v]|),
+a forward-error bound of the float32 score <x, c_l> + sum_j <x_j, C_j[v_j]>
+(Cauchy-Schwarz on each term), times two.
+
 Index building (assignment and encoding of database vectors):
 
 4. Lists.  A device list may differ from the oracle's (the nearest centroid)
@@ -40,6 +47,7 @@ k-means (Lloyd's algorithm on the device):
 from __future__ import annotations
 
 import dataclasses
+import math
 
 import numpy as np
 
@@ -76,7 +84,7 @@ def _get(index, name):
     return index[name] if isinstance(index, dict) else getattr(index, name)
 
 
-def check_probes(index, queries, gpu_probes, oracle_probes, report: Report):
+def check_probes(index, queries, gpu_probes, oracle_probes, report: Report, ip=False):
     """Rule 1.  Returns the list of query rows whose probe set differs."""
     cent = np.asarray(_get(index, "centroids"), dtype=np.float32)
     nlist, d = cent.shape
@@ -91,10 +99,15 @@ def check_probes(index, queries, gpu_probes, oracle_probes, report: Report):
         if g == o:
             continue
         nprobe = len(oracle_probes[qi])
-        allp, alld = O.coarse(queries[qi], cent, nlist)
-        dist_of = {int(p): float(v) for p, v in zip(allp, alld)}
         x2 = float(np.sum(np.asarray(queries[qi], dtype=np.float64) ** 2))
-        delta = 4.0 * gamma(d + 2) * (x2 + cmax)
+        if ip:
+            allp, ips = O.coarse_ip(queries[qi], cent, nlist)
+            alld = -ips
+            delta = 4.0 * gamma(d + 2) * math.sqrt(x2 * cmax)
+        else:
+            allp, alld = O.coarse(queries[qi], cent, nlist)
+            delta = 4.0 * gamma(d + 2) * (x2 + cmax)
+        dist_of = {int(p): float(v) for p, v in zip(allp, alld)}
         edge = float(alld[nprobe - 1])
         for lst in g ^ o:
             if lst not in dist_of or abs(dist_of[lst] - edge) > delta:
@@ -172,14 +185,16 @@ def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None,
 
 def compare_search(index, queries, nprobe, k, gpu_d, gpu_i, gpu_probes=None, lut_mode=O.LUT_F64,
                    tau=None, k_extra=32, nthreads=None) -> Report:
-    """Full acceptance check of a device IVF-PQ search against the oracle."""
-    tau = (TAU_F32 if lut_mode == O.LUT_F64 else TAU_F16) if tau is None else tau
+    """Full acceptance check of a device IVF-PQ search against the oracle
+    (lut_mode O.IP: the inner-product metric, scores in decreasing order)."""
+    ip = lut_mode == O.IP
+    tau = (TAU_F32 if lut_mode in (O.LUT_F64, O.IP) else TAU_F16) if tau is None else tau
     queries = np.ascontiguousarray(queries, dtype=np.float32)
     rep = Report(nq=len(queries))
     kx = k + k_extra
     od, oi, op = O.search(index, queries, nprobe, kx, lut_mode=lut_mode, nthreads=nthreads)
     if gpu_probes is not None:
-        differ = check_probes(index, queries, gpu_probes, op, rep)
+        differ = check_probes(index, queries, gpu_probes, op, rep, ip=ip)
         if differ:
             rep.queries_reprobed = len(differ)
             sub = np.asarray(differ)
@@ -205,10 +220,21 @@ def compare_search(index, queries, nprobe, k, gpu_d, gpu_i, gpu_probes=None, lut
         if ok.any():
             vals, _ = O.entry_distances(index, queries[row], pos[ok], lut_mode=lut_mode)
             for j, v in zip(np.flatnonzero(ok), vals):
-                out[j] = v
+                out[j] = -v if ip else v
         return out
 
-    check_results(gpu_d, gpu_i, od, oi, k, tau, rep, lookup=lookup)
+    if ip:
+        cent = np.asarray(_get(index, "centroids"), dtype=np.float64)
+        books = np.asarray(_get(index, "codebooks"), dtype=np.float64)
+        d, m = cent.shape[1], books.shape[0]
+        cmax = float(np.sqrt(np.max(np.sum(cent ** 2, axis=1))))
+        bsum = float(np.sum(np.sqrt(np.max(np.sum(books ** 2, axis=2), axis=1))))
+        xn = np.sqrt(np.sum(queries.astype(np.float64) ** 2, axis=1))
+        abs_tol = 4.0 * gamma(d + m + 2) * xn * (cmax + bsum)
+        check_results(-np.asarray(gpu_d, dtype=np.float64), gpu_i, -od, oi, k, 0.0, rep,
+                      lookup=lookup, abs_tol=abs_tol)
+    else:
+        check_results(gpu_d, gpu_i, od, oi, k, tau, rep, lookup=lookup)
     return rep
 
 

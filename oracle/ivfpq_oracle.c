@@ -29,6 +29,15 @@
  * vectors, full sort by (distance, id)), the textbook definition of the
  * k-NN problem stated in the same page's problem statement.
  *
+ * Inner-product metric (ORACLE_IP; the conventions of "Support HNSW Search
+ * using GPUs", Search kernel section: inner product, larger is better, the
+ * kernel ranks by the negated value and flips the sign on output): the lists probed are those of largest <x, c_l> (ties to the smaller
+ * list number), the tables T_j(v) = <x_j, C_j[v]> depend on the query only,
+ * and an entry of list l with code c scores <x, c_l> + sum_j T_j(c_j), the
+ * inner product of x with the reconstructed vector c_l + (C_j[c_j])_j.  The
+ * candidates are sorted by (score decreasing, id); missing ones are padded
+ * (-inf, -1).
+ *
  * Queries are independent; the search and brute-force entry points run them
  * on a pool of POSIX threads, one query at a time per thread.
  */
@@ -40,6 +49,7 @@
 
 #define ORACLE_LUT_F64 0
 #define ORACLE_LUT_F16 1
+#define ORACLE_IP 2 /* inner-product metric, double-precision tables */
 
 typedef struct {
     double key;
@@ -107,6 +117,51 @@ int oracle_coarse(const float *x, const float *centroids, int d, int nlist, int 
     return 0;
 }
 
+static double dot(const float *a, const float *b, int n)
+{
+    double s = 0.0;
+    for (int t = 0; t < n; t++)
+        s += (double)a[t] * (double)b[t];
+    return s;
+}
+
+/* Inner-product step 1: the nprobe lists of largest <x, c_l> (ties to the
+ * smaller list number); ips, when not NULL, receives their inner products. */
+int oracle_coarse_ip(const float *x, const float *centroids, int d, int nlist, int nprobe,
+                     int32_t *probes, double *ips)
+{
+    if (nprobe < 1 || nprobe > nlist)
+        return -1;
+    pair_t *all = (pair_t *)malloc(sizeof(pair_t) * (size_t)nlist);
+    if (!all)
+        return -2;
+    for (int l = 0; l < nlist; l++) {
+        all[l].key = -dot(x, centroids + (size_t)l * d, d);
+        all[l].id = l;
+    }
+    qsort(all, (size_t)nlist, sizeof(pair_t), cmp_pair);
+    for (int p = 0; p < nprobe; p++) {
+        probes[p] = (int32_t)all[p].id;
+        if (ips)
+            ips[p] = -all[p].key;
+    }
+    free(all);
+    return 0;
+}
+
+/* Inner-product tables: T_j(v) = <x_j, C_j[v]> over the dsub dims of
+ * sub-vector j (the same for every list). */
+int oracle_lut_ip(const float *x, const float *codebooks, int d, int m, double *lut)
+{
+    if (m < 1 || d % m)
+        return -1;
+    int dsub = d / m;
+    for (int j = 0; j < m; j++)
+        for (int v = 0; v < 256; v++)
+            lut[j * 256 + v] = dot(x + j * dsub, codebooks + ((size_t)j * 256 + v) * dsub, dsub);
+    return 0;
+}
+
 /* Steps 2-3: the m x 256 table for query x and the list with centroid c.
  * codebooks is [m][256][dsub] float. */
 int oracle_lut(const float *x, const float *c, const float *codebooks, int d, int m, int lut_mode,
@@ -157,8 +212,17 @@ int oracle_entry_distances(const float *x, const float *centroids, const float *
     double *lut = (double *)malloc(sizeof(double) * (size_t)m * 256);
     if (!lut)
         return -2;
+    if (lut_mode == ORACLE_IP && oracle_lut_ip(x, codebooks, d, m, lut)) {
+        free(lut);
+        return -1;
+    }
     for (int64_t i = 0; i < n; i++) {
-        int rc = oracle_lut(x, centroids + (size_t)lists[i] * d, codebooks, d, m, lut_mode, lut);
+        const float *c = centroids + (size_t)lists[i] * d;
+        if (lut_mode == ORACLE_IP) {
+            out[i] = dot(x, c, d) + adc_one(lut, code_rows + (size_t)i * m, m);
+            continue;
+        }
+        int rc = oracle_lut(x, c, codebooks, d, m, lut_mode, lut);
         if (rc) {
             free(lut);
             return rc;
@@ -209,9 +273,11 @@ static int search_one(search_job_t *J, int64_t q)
         free(lut);
         return -2;
     }
+    const int ip = J->lut_mode == ORACLE_IP;
     if (J->probes_in) {
         memcpy(probes, J->probes_in + (size_t)q * J->nprobe, sizeof(int32_t) * (size_t)J->nprobe);
-    } else if (oracle_coarse(x, J->centroids, J->d, J->nlist, J->nprobe, probes, NULL)) {
+    } else if (ip ? oracle_coarse_ip(x, J->centroids, J->d, J->nlist, J->nprobe, probes, NULL)
+                  : oracle_coarse(x, J->centroids, J->d, J->nlist, J->nprobe, probes, NULL)) {
         free(probes);
         free(lut);
         return -1;
@@ -228,18 +294,28 @@ static int search_one(search_job_t *J, int64_t q)
         return -2;
     }
     int64_t n = 0;
+    if (ip)
+        oracle_lut_ip(x, J->codebooks, J->d, J->m, lut);
     for (int p = 0; p < J->nprobe; p++) {
         int l = probes[p];
-        oracle_lut(x, J->centroids + (size_t)l * J->d, J->codebooks, J->d, J->m, J->lut_mode, lut);
+        const float *c = J->centroids + (size_t)l * J->d;
+        double base = 0.0;
+        if (ip)
+            base = dot(x, c, J->d);
+        else
+            oracle_lut(x, c, J->codebooks, J->d, J->m, J->lut_mode, lut);
         for (int64_t e = J->list_offsets[l]; e < J->list_offsets[l + 1]; e++) {
-            cand[n].key = adc_one(lut, J->codes + (size_t)e * J->m, J->m);
+            double r = adc_one(lut, J->codes + (size_t)e * J->m, J->m);
+            /* inner product: sort by the negated score, so that larger comes first */
+            cand[n].key = ip ? -(base + r) : r;
             cand[n].id = J->ids[e];
             n++;
         }
     }
     qsort(cand, (size_t)n, sizeof(pair_t), cmp_pair);
     for (int i = 0; i < J->k; i++) {
-        J->out_dist[(size_t)q * J->k + i] = i < n ? cand[i].key : INFINITY;
+        J->out_dist[(size_t)q * J->k + i] =
+            i < n ? (ip ? -cand[i].key : cand[i].key) : (ip ? -INFINITY : INFINITY);
         J->out_ids[(size_t)q * J->k + i] = i < n ? cand[i].id : -1;
     }
     if (J->out_probes)

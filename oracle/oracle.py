@@ -21,6 +21,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 LUT_F64 = 0
 LUT_F16 = 1
+IP = 2        # inner-product metric (double-precision tables), passed as lut_mode
 
 _lib = None
 
@@ -48,12 +49,15 @@ def lib():
         L.oracle_round_binary16.restype = ctypes.c_double
         L.oracle_coarse.argtypes = [P, P, i32, i32, i32, P, P]
         L.oracle_lut.argtypes = [P, P, P, i32, i32, i32, P]
+        L.oracle_coarse_ip.argtypes = [P, P, i32, i32, i32, P, P]
+        L.oracle_lut_ip.argtypes = [P, P, i32, i32, P]
         L.oracle_search.argtypes = [P, P, P, P, P, i32, i32, i32, P, i64, i32, i32, i32, P, P, P,
                                     P, i32]
         L.oracle_entry_distances.argtypes = [P, P, P, i32, i32, i32, P, P, i64, P]
         L.oracle_bruteforce.argtypes = [P, P, i64, i32, P, i64, i32, P, P, i32]
         L.oracle_bruteforce_bf16.argtypes = [P, i64, i32, P, i64, i32, P, P, i32]
-        for f in ("oracle_coarse", "oracle_lut", "oracle_search", "oracle_entry_distances",
+        for f in ("oracle_coarse", "oracle_lut", "oracle_coarse_ip", "oracle_lut_ip",
+                  "oracle_search", "oracle_entry_distances",
                   "oracle_bruteforce",
                   "oracle_bruteforce_bf16"):
             getattr(L, f).restype = ctypes.c_int
@@ -114,6 +118,31 @@ def coarse(x, centroids, nprobe):
     if rc:
         raise ValueError(f"oracle_coarse failed ({rc})")
     return probes, dists
+
+
+def coarse_ip(x, centroids, nprobe):
+    """Inner-product coarse step: the nprobe lists of largest <x, c_l>
+    (ties to the smaller list number) and those inner products."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    c = np.ascontiguousarray(centroids, dtype=np.float32)
+    probes = np.empty(nprobe, dtype=np.int32)
+    ips = np.empty(nprobe, dtype=np.float64)
+    rc = lib().oracle_coarse_ip(_p(x), _p(c), c.shape[1], c.shape[0], nprobe, _p(probes), _p(ips))
+    if rc:
+        raise ValueError(f"oracle_coarse_ip failed ({rc})")
+    return probes, ips
+
+
+def lut_ip(x, codebooks):
+    """Inner-product tables T_j(v) = <x_j, C_j[v]> (float64 [m, 256])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = np.ascontiguousarray(codebooks, dtype=np.float32)
+    m = b.shape[0]
+    out = np.empty((m, 256), dtype=np.float64)
+    rc = lib().oracle_lut_ip(_p(x), _p(b), x.shape[0], m, _p(out))
+    if rc:
+        raise ValueError(f"oracle_lut_ip failed ({rc})")
+    return out
 
 
 def lut(x, centroid, codebooks, lut_mode=LUT_F64):

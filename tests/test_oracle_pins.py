@@ -500,3 +500,88 @@ def test_kmeans_checker_accepts_oracle_and_rejects_perturbations():
     bad[i] = int(O.coarse(x[i], c0, 10)[0][-1])
     assert not check.compare_kmeans_round(x, c0, bad, c1, counts).ok()
     assert not check.compare_kmeans_round(x, c0, a, c1, counts + 1).ok()
+
+
+# ---------------------------------------------------------------------------
+# inner-product metric
+# ---------------------------------------------------------------------------
+
+def test_ip_coarse_matches_numpy_argsort():
+    rng = np.random.default_rng(71)
+    c = rng.standard_normal((300, 24)).astype(np.float32)
+    c[17] = c[5]                                       # an exact tie: 5 before 17
+    for _ in range(5):
+        x = rng.standard_normal(24).astype(np.float32)
+        ip = c.astype(np.float64) @ x.astype(np.float64)
+        order = np.argsort(-ip, kind="stable")
+        probes, ips = O.coarse_ip(x, c, 40)
+        assert np.array_equal(probes, order[:40])
+        np.testing.assert_allclose(ips, ip[order[:40]], rtol=1e-14)
+    x = c[5] * 3
+    probes, _ = O.coarse_ip(x, c, 2)
+    assert probes.tolist() == [5, 17]
+
+
+@pytest.mark.parametrize("nlist,d,m,n", [(4, 8, 2, 300), (6, 12, 4, 500), (5, 16, 16, 200)])
+def test_ip_scores_equal_inner_product_with_reconstruction(nlist, d, m, n):
+    idx, rng = random_idx(2 + nlist * d, nlist, d, m, n)
+    q = rng.standard_normal((4, d)).astype(np.float32)
+    score, ids, _ = O.search(idx, q, nlist, n, lut_mode=O.IP)     # every list, every entry
+    recon = reconstruct(idx)
+    pos_of = np.empty(n, dtype=np.int64)
+    pos_of[idx["ids"]] = np.arange(n)
+    for r in range(len(q)):
+        expl = recon[pos_of[ids[r]]] @ q[r].astype(np.float64)
+        np.testing.assert_allclose(score[r], expl, rtol=1e-10, atol=1e-12)
+        assert np.all(np.diff(score[r]) <= 0)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_ip_pq_exact_integer_equals_bruteforce(seed):
+    # integer data, every list probed: the scores are exact integers and the
+    # result must be the brute-force maximum inner product, ties by id
+    idx, db, q = pq_exact(seed)
+    k = 25
+    score, ids, _ = O.search(idx, q, len(idx["list_sizes"]), k, lut_mode=O.IP)
+    pos_of = np.empty(len(db), dtype=np.int64)
+    pos_of[idx["ids"]] = np.arange(len(db))
+    for r in range(len(q)):
+        s = db.astype(np.float64) @ q[r].astype(np.float64)
+        order = sorted(range(len(db)), key=lambda i: (-s[pos_of[i]], i))[:k]
+        assert ids[r].tolist() == order
+        assert score[r].tolist() == [s[pos_of[i]] for i in order]
+
+
+def test_ip_padding_and_entry_scores():
+    idx, rng = random_idx(73, 4, 8, 2, 30)
+    q = rng.standard_normal((2, 8)).astype(np.float32)
+    score, ids, probes = O.search(idx, q, 1, 50, lut_mode=O.IP)
+    for r in range(2):
+        valid = int(np.sum(ids[r] >= 0))
+        assert valid == idx["list_sizes"][probes[r][0]]
+        assert np.all(np.isneginf(score[r][valid:])) and np.all(ids[r][valid:] == -1)
+    pos_of = np.empty(30, dtype=np.int64)
+    pos_of[idx["ids"]] = np.arange(30)
+    got, _ = O.entry_distances(idx, q[0], pos_of[ids[0][:3]], lut_mode=O.IP)
+    np.testing.assert_allclose(got, score[0][:3], rtol=1e-14)
+
+
+def test_ip_checker_accepts_oracle_and_rejects_perturbations():
+    idx, rng = random_idx(74, 8, 16, 4, 2000)
+    q = rng.standard_normal((6, 16)).astype(np.float32)
+    s, i, p = O.search(idx, q, 3, 20, lut_mode=O.IP)
+    rep = check.compare_search(idx, q, 3, 20, s.astype(np.float32), i, p, lut_mode=O.IP)
+    assert rep.ok(), rep.failures
+    far_s, far_i, _ = O.search(idx, q[:1], 3, 2000, lut_mode=O.IP)
+    bad = i.copy()
+    bad[0, 5] = far_i[0][int(np.sum(far_i[0] >= 0)) - 1]        # the lowest-scoring entry
+    assert not check.compare_search(idx, q, 3, 20, s.astype(np.float32), bad, p,
+                                    lut_mode=O.IP).ok()
+    ss = s.astype(np.float32).copy()
+    ss[1, 3] += 1e-3
+    ss[1] = -np.sort(-ss[1])
+    assert not check.compare_search(idx, q, 3, 20, ss, i, p, lut_mode=O.IP).ok()
+    pp = p.copy()
+    pp[2, 0] = int(O.coarse_ip(q[2], idx["centroids"], 8)[0][-1])
+    assert not check.compare_search(idx, q, 3, 20, s.astype(np.float32), i, pp,
+                                    lut_mode=O.IP).ok()
