@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libivfpq.so")
 
 OK, E_INVALID_ARG, E_IO, E_FORMAT, E_NO_DEVICE, E_OUT_OF_MEMORY, E_DEVICE = range(7)
+METRIC_L2, METRIC_IP = 0, 1
 LUT_F32, LUT_F16 = 0, 1
 MODE_NORMAL, MODE_SCAN_ONLY = 0, 1
 
@@ -30,7 +31,7 @@ class IVFPQError(RuntimeError):
 class SearchParams(ctypes.Structure):
     _fields_ = [("nprobe", ctypes.c_int32), ("k", ctypes.c_int32), ("lut", ctypes.c_int32),
                 ("mode", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("metric", ctypes.c_int32)]
 
 
 class Info(ctypes.Structure):
@@ -242,10 +243,13 @@ def _stream_ptr(stream) -> ctypes.c_void_p:
 
 def ivfpq_search_ex(index: Index, queries: torch.Tensor, nprobe: int, k: int, lut: str = "f32",
                     mode: int = MODE_NORMAL, chunk_len: int = 0, return_probes: bool = False,
-                    out=None, stream=None):
+                    out=None, stream=None, metric: str = "l2"):
     """Asynchronous device search on the current (or given) torch stream.
+    metric "l2" (squared L2, ascending) or "ip" (inner product, descending).
 
     Returns (distances [nq,k] float32, ids [nq,k] int64[, probes [nq,nprobe] int32])."""
+    if metric not in ("l2", "ip"):
+        raise ValueError("metric must be 'l2' or 'ip'")
     q = _dev(queries, torch.float32)
     nq = q.shape[0]
     if out is None:
@@ -255,7 +259,8 @@ def ivfpq_search_ex(index: Index, queries: torch.Tensor, nprobe: int, k: int, lu
             if return_probes else None
     else:
         dist, ids, probes = out
-    p = SearchParams(nprobe, k, LUT_F16 if lut == "f16" else LUT_F32, mode, chunk_len, 0)
+    p = SearchParams(nprobe, k, LUT_F16 if lut == "f16" else LUT_F32, mode, chunk_len,
+                     METRIC_IP if metric == "ip" else METRIC_L2)
     _check(lib().ivfpq_search_ex(index.handle, ctypes.byref(p), ctypes.c_void_p(q.data_ptr()),
                                  nq, ctypes.c_void_p(dist.data_ptr()),
                                  ctypes.c_void_p(ids.data_ptr()),

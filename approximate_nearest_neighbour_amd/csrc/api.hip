@@ -330,6 +330,10 @@ ivfpq_status check_params(const ivfpq_index *ix, const ivfpq_search_params *p, i
         return fail(IVFPQ_E_INVALID_ARG, "unknown mode");
     if (p->chunk_len < 0)
         return fail(IVFPQ_E_INVALID_ARG, "chunk_len must be >= 0");
+    if (p->metric != IVFPQ_METRIC_L2 && p->metric != IVFPQ_METRIC_IP)
+        return fail(IVFPQ_E_INVALID_ARG, "unknown metric");
+    if (p->metric == IVFPQ_METRIC_IP && p->lut != IVFPQ_LUT_F32)
+        return fail(IVFPQ_E_INVALID_ARG, "the inner-product metric uses float32 tables");
     return IVFPQ_OK;
 }
 
@@ -589,8 +593,9 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
         return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const DeviceIndex &dx = idx->dx;
+    const bool ip = p->metric == IVFPQ_METRIC_IP;
     if (scan_lds_bytes(dx.d, dx.m, p->nprobe, p->lut == IVFPQ_LUT_F16, kw_of(p->k) / 64,
-                       dx.m % 2 == 0 ? 2 : 1) > 160 * 1024)
+                       !ip && dx.m % 2 == 0 ? 2 : 1) > 160 * 1024)
         return fail(IVFPQ_E_INVALID_ARG, "tables of this m and precision exceed the LDS");
     // workspace: probes | plan arrays | partial top-k of the work items
     SearchPlan pl;
@@ -626,7 +631,7 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
 
     prof_record(idx, 0, true, st);
     hipError_t e =
-        launch_coarse(dx, queries_dev, nq, p->nprobe, ws + o_coarse, probes, nullptr, st);
+        launch_coarse(dx, queries_dev, nq, p->nprobe, ws + o_coarse, probes, nullptr, st, ip);
     prof_record(idx, 0, false, st);
     if (e != hipSuccess)
         return fail(IVFPQ_E_DEVICE, std::string("coarse kernel: ") + hipGetErrorString(e));
@@ -638,6 +643,7 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
     a.lut = p->lut;
     a.mode = p->mode;
     a.chunk_len = p->chunk_len;
+    a.metric = ip ? 1 : 0;
     a.out_d = distances_dev;
     a.out_i = ids_dev;
     a.probes = probes;

@@ -37,6 +37,7 @@ struct SearchArgs {
     int chunk_len;
     float *out_d;
     int64_t *out_i;
+    int metric = 0;  // 0 squared L2, 1 inner product
     int32_t *probes; // [nq][nprobe] (workspace or caller buffer)
     float *probe_d;  // [nq][nprobe] or nullptr
 };
@@ -56,10 +57,13 @@ struct SearchPlan {
 };
 
 // Each launcher enqueues on `stream` and returns the launch status.
+// ip: rank the lists by -<x, c_l> (inner-product metric) instead of |x - c_l|^2
 hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
-                         void *ws, int32_t *probes, float *probe_d, hipStream_t stream);
+                         void *ws, int32_t *probes, float *probe_d, hipStream_t stream,
+                         bool ip = false);
 hipError_t launch_coarse_valu(const DeviceIndex &ix, const float *queries, int64_t nq,
-                              int nprobe, int32_t *probes, float *probe_d, hipStream_t stream);
+                              int nprobe, int32_t *probes, float *probe_d, hipStream_t stream,
+                              bool ip = false);
 size_t coarse_ws_bytes(const DeviceIndex &ix, int64_t nq, int nprobe);
 hipError_t launch_centroid_blocks(const DeviceIndex &ix, hipStream_t stream);
 hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
     const float *__restrict__ queries, int64_t nq, int d, int nblk, int nprobe,
     const float *__restrict__ cblk, const float *__restrict__ cnorm_pad, int splits,
     float *__restrict__ part_d, uint32_t *__restrict__ part_p, uint32_t *__restrict__ qbound,
-    int32_t *__restrict__ probes, float *__restrict__ probe_d)
+    int32_t *__restrict__ probes, float *__restrict__ probe_d, int ip)
 {
     constexpr int TQ = 16 * RG, THREADS = 1024, MW = 8, QS = TQ / 8, KW = 64 * NW;
     static_assert(4 * RG / RPW == MW, "eight matrix waves");
@@ -165,7 +165,10 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = (rg0 + g) * 16 + 4 * (lane >> 4) + r;
-                    dtile[row * 64 + cbk * 16 + col] = xr[g][r] + cc - 2.f * acc[r];
+                    // inner-product metric: -<x, c>, padding centroids (norm
+                    // +inf) kept out the same way
+                    dtile[row * 64 + cbk * 16 + col] =
+                        ip ? (cc == INFINITY ? INFINITY : -acc[r]) : xr[g][r] + cc - 2.f * acc[r];
                 }
             }
         };
@@ -357,7 +360,7 @@ size_t coarse_ws_bytes(const DeviceIndex &ix, int64_t nq, int nprobe)
 template <int NW, int RG, int RPW, int KD>
 static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *queries, int64_t nq,
                                       int nprobe, int splits, void *ws, int32_t *probes,
-                                      float *probe_d, hipStream_t stream)
+                                      float *probe_d, hipStream_t stream, bool ip)
 {
     constexpr int TQ = 16 * RG;
     const size_t lds = (size_t)TQ * (4 * KD + 1) * 4 + TQ * 4 + 2 * TQ * 64 * 4 + TQ * 512;
@@ -382,7 +385,8 @@ static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *querie
     }
     const dim3 grid((unsigned)((nq + TQ - 1) / TQ), (unsigned)splits);
     hipLaunchKernelGGL(kern, grid, dim3(1024), lds, stream, queries, nq, ix.d, ix.nblk, nprobe,
-                       ix.cblk, ix.cnorm_pad, splits, part_d, part_p, qbound, probes, probe_d);
+                       ix.cblk, ix.cnorm_pad, splits, part_d, part_p, qbound, probes, probe_d,
+                       ip ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;
@@ -396,34 +400,35 @@ static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *querie
 template <int NW>
 static hipError_t coarse_mfma_k(const DeviceIndex &ix, const float *queries, int64_t nq,
                                 int nprobe, int rg, int splits, void *ws, int32_t *probes,
-                                float *probe_d, hipStream_t stream)
+                                float *probe_d, hipStream_t stream, bool ip)
 {
     switch (ix.d4) {
     case 8:
         return rg == 4 ? coarse_mfma_variant<NW, 4, 2, 8>(ix, queries, nq, nprobe, splits, ws,
-                                                          probes, probe_d, stream)
+                                                          probes, probe_d, stream, ip)
                        : coarse_mfma_variant<NW, 2, 1, 8>(ix, queries, nq, nprobe, splits, ws,
-                                                          probes, probe_d, stream);
+                                                          probes, probe_d, stream, ip);
     case 16:
         return rg == 4 ? coarse_mfma_variant<NW, 4, 2, 16>(ix, queries, nq, nprobe, splits, ws,
-                                                           probes, probe_d, stream)
+                                                           probes, probe_d, stream, ip)
                        : coarse_mfma_variant<NW, 2, 1, 16>(ix, queries, nq, nprobe, splits, ws,
-                                                           probes, probe_d, stream);
+                                                           probes, probe_d, stream, ip);
     case 24:
         return rg == 4 ? coarse_mfma_variant<NW, 4, 2, 24>(ix, queries, nq, nprobe, splits, ws,
-                                                           probes, probe_d, stream)
+                                                           probes, probe_d, stream, ip)
                        : coarse_mfma_variant<NW, 2, 1, 24>(ix, queries, nq, nprobe, splits, ws,
-                                                           probes, probe_d, stream);
+                                                           probes, probe_d, stream, ip);
     case 32:
         return coarse_mfma_variant<NW, 2, 1, 32>(ix, queries, nq, nprobe, splits, ws, probes,
-                                                 probe_d, stream);
+                                                 probe_d, stream, ip);
     default:
         return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
-                         void *ws, int32_t *probes, float *probe_d, hipStream_t stream)
+                         void *ws, int32_t *probes, float *probe_d, hipStream_t stream,
+                         bool ip)
 {
     if (nq == 0)
         return hipSuccess;
@@ -433,12 +438,13 @@ hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq
     // the matrix-core form keeps a tile's B operand in registers (d up to 128)
     // and four register top-k per wave (nprobe up to 128)
     if (nw > 2 || ix.d4 > 32)
-        return launch_coarse_valu(ix, queries, nq, nprobe, probes, probe_d, stream);
+        return launch_coarse_valu(ix, queries, nq, nprobe, probes, probe_d, stream, ip);
     int rg, splits;
     coarse_shape(nq, ix.nblk, ix.d4, &rg, &splits);
     if (nw == 1)
-        return coarse_mfma_k<1>(ix, queries, nq, nprobe, rg, splits, ws, probes, probe_d, stream);
-    return coarse_mfma_k<2>(ix, queries, nq, nprobe, rg, splits, ws, probes, probe_d, stream);
+        return coarse_mfma_k<1>(ix, queries, nq, nprobe, rg, splits, ws, probes, probe_d, stream,
+                                ip);
+    return coarse_mfma_k<2>(ix, queries, nq, nprobe, rg, splits, ws, probes, probe_d, stream, ip);
 }
 
 } // namespace ivfpq

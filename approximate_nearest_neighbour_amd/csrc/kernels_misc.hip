@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kBlock) void coarse_kernel(const float *__restrict_
                                                         int nlist, int nprobe,
                                                         const float *__restrict__ centroids,
                                                         int32_t *__restrict__ probes,
-                                                        float *__restrict__ probe_d)
+                                                        float *__restrict__ probe_d, int ip)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int dpad = (d + 3) & ~3;
@@ -90,7 +90,12 @@ __global__ __launch_bounds__(kBlock) void coarse_kernel(const float *__restrict_
         if (l < nlist) {
             const float *c = centroids + (size_t)l * d;
             float acc = 0.f;
-            if ((d & 3) == 0) {
+            if (ip) {
+                // inner-product metric: lists ranked by -<x, c_l>
+                for (int t = 0; t < d; ++t)
+                    acc = fmaf(x[t], c[t], acc);
+                acc = -acc;
+            } else if ((d & 3) == 0) {
                 for (int t = 0; t < d; t += 4) {
                     const float4 cv = *reinterpret_cast<const float4 *>(c + t);
                     float df = x[t] - cv.x;
@@ -230,7 +235,7 @@ static hipError_t set_lds(K kernel, size_t bytes)
 
 template <int NW>
 static hipError_t coarse_nw(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
-                            int32_t *probes, float *probe_d, hipStream_t stream)
+                            int32_t *probes, float *probe_d, hipStream_t stream, bool ip)
 {
     const size_t lds = (size_t)((ix.d + 3) & ~3) * 4 + 16 + (size_t)(kWaves - 1) * 64 * NW * 8 +
                        (size_t)kWaves * 512;
@@ -239,21 +244,22 @@ static hipError_t coarse_nw(const DeviceIndex &ix, const float *queries, int64_t
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)nq), dim3(kBlock), lds, stream, queries, ix.d,
-                       ix.nlist, nprobe, ix.centroids, probes, probe_d);
+                       ix.nlist, nprobe, ix.centroids, probes, probe_d, ip ? 1 : 0);
     return hipGetLastError();
 }
 
 hipError_t launch_coarse_valu(const DeviceIndex &ix, const float *queries, int64_t nq,
-                              int nprobe, int32_t *probes, float *probe_d, hipStream_t stream)
+                              int nprobe, int32_t *probes, float *probe_d, hipStream_t stream,
+                              bool ip)
 {
     if (nq == 0)
         return hipSuccess;
     switch (nw_for(nprobe)) {
-    case 1: return coarse_nw<1>(ix, queries, nq, nprobe, probes, probe_d, stream);
-    case 2: return coarse_nw<2>(ix, queries, nq, nprobe, probes, probe_d, stream);
-    case 4: return coarse_nw<4>(ix, queries, nq, nprobe, probes, probe_d, stream);
-    case 8: return coarse_nw<8>(ix, queries, nq, nprobe, probes, probe_d, stream);
-    default: return coarse_nw<16>(ix, queries, nq, nprobe, probes, probe_d, stream);
+    case 1: return coarse_nw<1>(ix, queries, nq, nprobe, probes, probe_d, stream, ip);
+    case 2: return coarse_nw<2>(ix, queries, nq, nprobe, probes, probe_d, stream, ip);
+    case 4: return coarse_nw<4>(ix, queries, nq, nprobe, probes, probe_d, stream, ip);
+    case 8: return coarse_nw<8>(ix, queries, nq, nprobe, probes, probe_d, stream, ip);
+    default: return coarse_nw<16>(ix, queries, nq, nprobe, probes, probe_d, stream, ip);
     }
 }
 

@@ -130,6 +130,8 @@ struct ScanArgs {
     uint32_t *part_p;
     float *out_d;
     int64_t *out_i;
+    int ip;      // inner-product metric (tables of the run-time shape)
+    float osign; // sign of the reported values: +1 squared L2, -1 inner product
 };
 
 // A code row of M bytes read with the widest loads its size allows.
@@ -227,7 +229,12 @@ struct Piece {
 // is the same.  The sums now cancel where |x - c_l - C(code)| is small
 // against |x - c_l| and |C(code)|: float32 rounding of order 1e-7 of those
 // norms, against the same order of the result in the difference form.
-template <int M, int DSUB, int G, int NW, bool F16, bool SO, bool PRE>
+//
+// IP (M == 0): inner-product metric.  The scan ranks entries by the negated
+// score, -(<x, c_l> + sum_j <x_j, C_j[v_j]>): table entries are
+// -<x_j, C_j[v]>, and -<x, c_l> (computed per piece) is added to the entries
+// of sub-quantizer 0.  The reported values are negated back.
+template <int M, int DSUB, int G, int NW, bool F16, bool SO, bool PRE, bool IP = false>
 // Register budget: 128 VGPRs, i.e. four waves per SIMD, so that two
 // workgroups of eight waves share a CU and their table-build and scan
 // phases overlap.
@@ -275,6 +282,7 @@ void scan_items_kernel(ScanArgs a)
     const int v = tid & 255, g = tid >> 8;
 
     static_assert(!PRE || M > 0, "decomposed tables need a compile-time shape");
+    static_assert(!IP || (M == 0 && !PRE), "inner-product tables use the run-time shape");
     // codebook slice in registers (difference form) or the query term (PRE)
     float cb[(M > 0 && !PRE) ? JG * DSUB : 1];
     float t2[PRE ? JG : 1];
@@ -289,7 +297,17 @@ void scan_items_kernel(ScanArgs a)
     // rs: the piece's residual (difference form) or, in rs[0], |x - c_l|^2
     // (PRE); list: the piece's list
     auto build = [&](const float *rs, int list, void *lut) {
-        if constexpr (PRE) {
+        if constexpr (IP) {
+            const float cst = rs[0];
+            for (int j = 0; j < m; ++j) {
+                const float *cw = a.codebooks + ((size_t)j * 256 + v) * dsub;
+                float acc = 0.f;
+                for (int s = 0; s < dsub; ++s)
+                    acc = fmaf(xs[j * dsub + s], cw[s], acc);
+                Table<F16>::put(lut, j * 256 + v, j == 0 ? cst - acc : -acc);
+            }
+            (void)list;
+        } else if constexpr (PRE) {
             const float cst = rs[0];
             const float *t1l = a.t1 + (size_t)list * M * 256;
 #pragma unroll
@@ -331,19 +349,24 @@ void scan_items_kernel(ScanArgs a)
     // word)
     auto residual_group = [&](int grp, int b) {
         const int pn = group_size(grp);
-        if constexpr (PRE) {
+        if constexpr (PRE || IP) {
+            // PRE: |x - c_l|^2; IP: -<x, c_l>
             for (int p = wave; p < pn; p += WAVES) {
                 const float *c = a.centroids + (size_t)pieces[grp * PG + p].list * d;
                 float acc = 0.f;
                 for (int t = lane; t < d; t += 64) {
-                    const float df = xs[t] - c[t];
-                    acc = fmaf(df, df, acc);
+                    if constexpr (IP) {
+                        acc = fmaf(xs[t], c[t], acc);
+                    } else {
+                        const float df = xs[t] - c[t];
+                        acc = fmaf(df, df, acc);
+                    }
                 }
 #pragma unroll
                 for (int sh = 32; sh >= 1; sh >>= 1)
                     acc += __shfl_xor(acc, sh);
                 if (lane == 0)
-                    rsbuf(b, p)[0] = acc;
+                    rsbuf(b, p)[0] = IP ? -acc : acc;
             }
         } else {
             for (int i = tid; i < pn * d; i += THREADS) {
@@ -606,7 +629,7 @@ void scan_items_kernel(ScanArgs a)
                     for (int r = 0; r < NW; ++r) {
                         const int e = r * 64 + lane;
                         if (e < a.k) {
-                            a.out_d[q * a.k + e] = sel.wk[r];
+                            a.out_d[q * a.k + e] = a.osign * sel.wk[r];
                             a.out_i[q * a.k + e] =
                                 sel.wv[r] == kSentinel ? -1 : a.ids[sel.wv[r]];
                         }
@@ -634,7 +657,7 @@ __global__ __launch_bounds__(256) void merge_items_kernel(const uint32_t *__rest
                                                           const float *__restrict__ part_d,
                                                           const uint32_t *__restrict__ part_p,
                                                           const int64_t *__restrict__ ids, int k,
-                                                          float *__restrict__ out_d,
+                                                          float osign, float *__restrict__ out_d,
                                                           int64_t *__restrict__ out_i)
 {
     __shared__ __align__(16) float mk[3 * 64 * NW];
@@ -655,7 +678,7 @@ __global__ __launch_bounds__(256) void merge_items_kernel(const uint32_t *__rest
         for (int r = 0; r < NW; ++r) {
             const int e = r * 64 + lane;
             if (e < k) {
-                out_d[q * k + e] = sel.wk[r];
+                out_d[q * k + e] = osign * sel.wk[r];
                 out_i[q * k + e] = sel.wv[r] == kSentinel ? -1 : ids[sel.wv[r]];
             }
         }
@@ -707,10 +730,10 @@ size_t scan_lds_bytes(int d, int m, int nprobe, bool f16, int nw, int g)
     return o_tab + (table > merge ? table : merge);
 }
 
-template <int M, int DSUB, int G, int NW, bool F16, bool SO, bool PRE = false>
+template <int M, int DSUB, int G, int NW, bool F16, bool SO, bool PRE = false, bool IP = false>
 static hipError_t scan_variant(const ScanArgs &a, const SearchPlan &pl, hipStream_t stream)
 {
-    auto kern = scan_items_kernel<M, DSUB, G, NW, F16, SO, PRE>;
+    auto kern = scan_items_kernel<M, DSUB, G, NW, F16, SO, PRE, IP>;
     const size_t lds = scan_lds_bytes(a.d, a.m, a.nprobe, F16, NW, G);
     if (lds > 160 * 1024)
         return hipErrorInvalidValue;
@@ -755,6 +778,9 @@ template <int NW>
 static hipError_t scan_nw(const ScanArgs &a, const SearchPlan &pl, int f16, int so,
                           hipStream_t stream)
 {
+    if (a.ip) // inner product: float32 tables of the run-time shape
+        return so ? scan_variant<0, 0, 1, NW, false, true, false, true>(a, pl, stream)
+                  : scan_variant<0, 0, 1, NW, false, false, false, true>(a, pl, stream);
     if (a.m == 4 && a.dsub == 8)
         return scan_shape<4, 8, 1, NW>(a, pl, f16, so, stream);
     if (a.m == 16 && a.dsub == 8)
@@ -771,7 +797,8 @@ static hipError_t merge_nw(const SearchArgs &s, const SearchPlan &pl, const Devi
                            hipStream_t stream)
 {
     hipLaunchKernelGGL(merge_items_kernel<NW>, dim3((unsigned)s.nq), dim3(256), 0, stream,
-                       pl.item_base, pl.part_d, pl.part_p, ix.ids, s.k, s.out_d, s.out_i);
+                       pl.item_base, pl.part_d, pl.part_p, ix.ids, s.k,
+                       s.metric ? -1.f : 1.f, s.out_d, s.out_i);
     return hipGetLastError();
 }
 
@@ -850,7 +877,7 @@ hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     a.pg = tables_per_group(ix.m, s.lut != 0);
     a.centroids = ix.centroids;
     a.codebooks = ix.codebooks;
-    a.t1 = ix.t1;
+    a.t1 = s.metric ? nullptr : ix.t1;
     a.list_off = ix.list_off;
     a.codes = ix.codes;
     a.ids = ix.ids;
@@ -865,6 +892,8 @@ hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     a.part_p = pl.part_p;
     a.out_d = s.out_d;
     a.out_i = s.out_i;
+    a.ip = s.metric;
+    a.osign = s.metric ? -1.f : 1.f;
     switch (nw_of(s.k)) {
     case 1: return scan_nw<1>(a, pl, s.lut, s.mode, stream);
     case 2: return scan_nw<2>(a, pl, s.lut, s.mode, stream);

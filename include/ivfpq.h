@@ -57,6 +57,16 @@ typedef enum {
 
 typedef enum { IVFPQ_LUT_F32 = 0, IVFPQ_LUT_F16 = 1 } ivfpq_lut_type;
 
+/* Ranking metric of a search.  IVFPQ_METRIC_L2: squared L2 distance, smaller
+ * is better, rows ascending, padding (+INFINITY, -1).  IVFPQ_METRIC_IP: inner
+ * product, larger is better, rows descending, padding (-INFINITY, -1): the
+ * lists probed are the nprobe of largest <x, c_l> and an entry of list l with
+ * code v scores <x, c_l> + sum_j <x_j, C_j[v_j]>, the inner product of the
+ * query with the entry's reconstruction (the conventions of "Support HNSW
+ * Search using GPUs", Search kernel section: the kernels rank by the negated
+ * value and flip its sign on output).  Float32 tables only. */
+typedef enum { IVFPQ_METRIC_L2 = 0, IVFPQ_METRIC_IP = 1 } ivfpq_metric;
+
 typedef enum {
     IVFPQ_MODE_NORMAL = 0,
     /* benchmark only: the scan computes every distance but keeps just the
@@ -75,7 +85,7 @@ typedef struct {
     int32_t lut;  /* ivfpq_lut_type */
     int32_t mode; /* ivfpq_mode */
     int32_t chunk_len;
-    int32_t reserved;
+    int32_t metric; /* ivfpq_metric (0 = squared L2) */
 } ivfpq_search_params;
 
 typedef struct {
