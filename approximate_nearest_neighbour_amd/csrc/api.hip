@@ -595,7 +595,7 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
     const DeviceIndex &dx = idx->dx;
     const bool ip = p->metric == IVFPQ_METRIC_IP;
     if (scan_lds_bytes(dx.d, dx.m, p->nprobe, p->lut == IVFPQ_LUT_F16, kw_of(p->k) / 64,
-                       !ip && dx.m % 2 == 0 ? 2 : 1) > 160 * 1024)
+                       dx.m % 2 == 0 ? 2 : 1) > 160 * 1024)
         return fail(IVFPQ_E_INVALID_ARG, "tables of this m and precision exceed the LDS");
     // workspace: probes | plan arrays | partial top-k of the work items
     SearchPlan pl;

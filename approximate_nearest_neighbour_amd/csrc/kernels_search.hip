@@ -230,10 +230,11 @@ struct Piece {
 // against |x - c_l| and |C(code)|: float32 rounding of order 1e-7 of those
 // norms, against the same order of the result in the difference form.
 //
-// IP (M == 0): inner-product metric.  The scan ranks entries by the negated
-// score, -(<x, c_l> + sum_j <x_j, C_j[v_j]>): table entries are
-// -<x_j, C_j[v]>, and -<x, c_l> (computed per piece) is added to the entries
-// of sub-quantizer 0.  The reported values are negated back.
+// IP: inner-product metric.  The scan ranks entries by the negated score,
+// -(<x, c_l> + sum_j <x_j, C_j[v_j]>): table entries are -<x_j, C_j[v]>, and
+// -<x, c_l> (computed per piece) is added to the entries of sub-quantizer 0.
+// With a compile-time shape the query term is held in registers as in PRE
+// (no list term, no codebook slice).  The reported values are negated back.
 template <int M, int DSUB, int G, int NW, bool F16, bool SO, bool PRE, bool IP = false>
 // Register budget: 128 VGPRs, i.e. four waves per SIMD, so that two
 // workgroups of eight waves share a CU and their table-build and scan
@@ -282,11 +283,13 @@ void scan_items_kernel(ScanArgs a)
     const int v = tid & 255, g = tid >> 8;
 
     static_assert(!PRE || M > 0, "decomposed tables need a compile-time shape");
-    static_assert(!IP || (M == 0 && !PRE), "inner-product tables use the run-time shape");
-    // codebook slice in registers (difference form) or the query term (PRE)
-    float cb[(M > 0 && !PRE) ? JG * DSUB : 1];
-    float t2[PRE ? JG : 1];
-    if constexpr (M > 0 && !PRE) {
+    static_assert(!IP || !PRE, "one table form at a time");
+    // codebook slice in registers (difference form) or the query term (PRE,
+    // IP with a compile-time shape)
+    constexpr bool QT = M > 0 && (PRE || IP);
+    float cb[(M > 0 && !QT) ? JG * DSUB : 1];
+    float t2[QT ? JG : 1];
+    if constexpr (M > 0 && !QT) {
 #pragma unroll
         for (int jj = 0; jj < JG; ++jj)
 #pragma unroll
@@ -297,7 +300,15 @@ void scan_items_kernel(ScanArgs a)
     // rs: the piece's residual (difference form) or, in rs[0], |x - c_l|^2
     // (PRE); list: the piece's list
     auto build = [&](const float *rs, int list, void *lut) {
-        if constexpr (IP) {
+        if constexpr (IP && M > 0) {
+            const float cst = rs[0];
+#pragma unroll
+            for (int jj = 0; jj < JG; ++jj) {
+                const int j = g * JG + jj;
+                Table<F16>::put(lut, j * 256 + v, j == 0 ? t2[jj] + cst : t2[jj]);
+            }
+            (void)list;
+        } else if constexpr (IP) {
             const float cst = rs[0];
             for (int j = 0; j < m; ++j) {
                 const float *cw = a.codebooks + ((size_t)j * 256 + v) * dsub;
@@ -449,7 +460,7 @@ void scan_items_kernel(ScanArgs a)
         }
         __syncthreads();
         np = __builtin_amdgcn_readfirstlane((int)misc[1]);
-        if constexpr (PRE) {
+        if constexpr (QT) {
             // the query term of this thread's sub-quantizers and code value
             // (the codebook pointer made opaque here: loads the compiler
             // could hoist out of the item loop would keep the codebook
@@ -466,7 +477,7 @@ void scan_items_kernel(ScanArgs a)
 #pragma unroll
                 for (int s = 0; s < DSUB; ++s)
                     acc = fmaf(xs[j * DSUB + s], cw[s], acc);
-                t2[jj] = -2.f * acc;
+                t2[jj] = (PRE ? -2.f : -1.f) * acc;
                 // materialised here (the compiler would otherwise recompute
                 // it in every table build and keep the codebook values live)
                 __asm__ volatile("" : "+v"(t2[jj]));
@@ -758,6 +769,9 @@ template <int M, int DSUB, int G, int NW>
 static hipError_t scan_shape(const ScanArgs &a, const SearchPlan &pl, int f16, int so,
                              hipStream_t stream)
 {
+    if (a.ip) // inner product: float32 tables
+        return so ? scan_variant<M, DSUB, G, NW, false, true, false, true>(a, pl, stream)
+                  : scan_variant<M, DSUB, G, NW, false, false, false, true>(a, pl, stream);
     if constexpr (M == 16 && DSUB == 8) {
         if (a.t1) {
             if (so)
@@ -778,9 +792,6 @@ template <int NW>
 static hipError_t scan_nw(const ScanArgs &a, const SearchPlan &pl, int f16, int so,
                           hipStream_t stream)
 {
-    if (a.ip) // inner product: float32 tables of the run-time shape
-        return so ? scan_variant<0, 0, 1, NW, false, true, false, true>(a, pl, stream)
-                  : scan_variant<0, 0, 1, NW, false, false, false, true>(a, pl, stream);
     if (a.m == 4 && a.dsub == 8)
         return scan_shape<4, 8, 1, NW>(a, pl, f16, so, stream);
     if (a.m == 16 && a.dsub == 8)

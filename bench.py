@@ -536,6 +536,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ivfpq_n1m_d128_m16_nlist1024")
     ap.add_argument("--lut", choices=["f32", "f16"], default="f32")
+    ap.add_argument("--metric", choices=["l2", "ip"], default="l2",
+                    help="ranking metric of the IVF-PQ search (squared L2 or inner product)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parity-queries", type=int, default=200)
@@ -582,7 +584,8 @@ def main():
            torch.empty((nq, w.nprobe), dtype=torch.int32, device=dev))
 
     def step():
-        A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=args.lut, return_probes=True, out=out)
+        A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=args.lut, return_probes=True, out=out,
+                          metric=args.metric)
 
     if args.copy_calibration_mib:
         # known traffic for the counters: a fill writes N bytes, a sum reads N
@@ -615,15 +618,19 @@ def main():
 
     # k-select cost: same scan with the top-k replaced by a running minimum
     so = (torch.empty((nq, w.k), dtype=torch.float32, device=dev), out[1], out[2])
-    A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=args.lut, mode=1, out=so, return_probes=True)
+    A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=args.lut, mode=1, out=so, return_probes=True,
+                      metric=args.metric)
     A.ivfpq_profile_begin(ix, args.steps)
     for _ in range(args.steps):
-        A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=args.lut, mode=1, out=so, return_probes=True)
+        A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=args.lut, mode=1, out=so, return_probes=True,
+                          metric=args.metric)
     torch.cuda.synchronize()
     scan_only_ms = A.ivfpq_profile_end(ix)["scan_ms"] / args.steps
 
-    host_qps = host_pointer_qps(lambda: A.ivfpq_search(ix, w.queries, w.nprobe, w.k), nq)
-    log(f"host-pointer entry point: {host_qps:.0f} queries/s (PCIe copies included)")
+    host_qps = None
+    if args.metric == "l2":   # the host-pointer entry point ranks by squared L2
+        host_qps = host_pointer_qps(lambda: A.ivfpq_search(ix, w.queries, w.nprobe, w.k), nq)
+        log(f"host-pointer entry point: {host_qps:.0f} queries/s (PCIe copies included)")
     read_gbs = measured_read_gbs(torch, A)
     log(f"measured streaming read: {read_gbs:.0f} GB/s")
 
@@ -631,7 +638,7 @@ def main():
     step()
     torch.cuda.synchronize()
     pn = min(args.parity_queries, nq)
-    lut_mode = O.LUT_F16 if args.lut == "f16" else O.LUT_F64
+    lut_mode = O.IP if args.metric == "ip" else (O.LUT_F16 if args.lut == "f16" else O.LUT_F64)
     rep = check.compare_search(w.index, w.queries[:pn], w.nprobe, w.k, out[0][:pn].cpu().numpy(),
                                out[1][:pn].cpu().numpy(), out[2][:pn].cpu().numpy(),
                                lut_mode=lut_mode)
@@ -659,10 +666,10 @@ def main():
                  "synthetic (seeded Gaussian mixture, CPU-built IVF-PQ index)"),
         "config": {"workload": w.name, "n": int(w.index.ntotal), "d": w.index.d,
                    "nlist": w.index.nlist, "m": w.index.m, "nq": nq, "nprobe": w.nprobe,
-                   "k": w.k, "lut": args.lut},
+                   "k": w.k, "lut": args.lut, "metric": args.metric},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic(w.name, args.lut),
+                     "traffic": stored_traffic(w.name, args.lut) if args.metric == "l2" else None,
                      "kernel": "scan_kernel", "kernel_ms": scan_ms,
                      "algorithmic_bytes_per_launch": code_bytes,
                      "measured_read_gbs": read_gbs, "frac_of_measured_read": achieved / read_gbs},
