@@ -330,7 +330,7 @@ static void coarse_shape(int64_t nq, int nblk, int d4, int *rg, int *splits)
     *rg = nblk >= 1024 && d4 <= 24 ? 4 : 2;
     const int64_t wgs = (nq + 16 * *rg - 1) / (16 * *rg);
     const int ntile = (nblk + 3) / 4;
-    const int64_t want = (int64_t)coarse_cu_count() * 4; // one resident per CU, ~4 rounds
+    const int64_t want = (int64_t)coarse_cu_count() * 4; // one resident per CU, ~4 waves of workgroups
     int s = (int)((want + wgs - 1) / wgs);
     s = s < 1 ? 1 : s;
     s = s > ntile ? ntile : s;

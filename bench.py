@@ -364,14 +364,14 @@ KMEANS_WORKLOAD = "kmeans_n262144_d128_k1024"
 def bench_kmeans(args):
     """k-means on the device at the 1M x 128 workload's coarse training shape:
     262,144 of its vectors (seeded sample), 1,024 centers initialised with
-    1,024 distinct sampled vectors; one step = one call of 10 Lloyd rounds."""
+    1,024 distinct sampled vectors; one step = one call of 10 Lloyd iterations."""
     import torch
     import approximate_nearest_neighbour_amd as A
     from approximate_nearest_neighbour_amd import datagen as G
     from oracle import check
     from oracle import oracle as O
 
-    rounds = 10
+    iters = 10
     t0 = time.time()
     w = G.gmm1m(keep_vectors=True)
     rng = np.random.default_rng(2003)
@@ -384,9 +384,9 @@ def bench_kmeans(args):
     n, d = xs.shape
     k = init.shape[0]
 
-    def step(iters=rounds):
+    def step(count=iters):
         c.copy_(c0)
-        return A.ivfpq_kmeans_ex(x, c, iters)
+        return A.ivfpq_kmeans_ex(x, c, count)
 
     for _ in range(args.warmup):
         step()
@@ -396,28 +396,28 @@ def bench_kmeans(args):
         step()
     torch.cuda.synchronize()
     ms_step = 1e3 * (time.perf_counter() - t) / args.steps
-    ms_round = ms_step / rounds
-    flops = 2.0 * n * k * d                       # the assignment's x.c per round
-    achieved = flops / (ms_round * 1e-3) / 1e12
-    log(f"step {ms_step:.3f} ms = {rounds} rounds, {ms_round:.3f} ms per round")
-    # parity: the first round, checked in full against the oracle
+    ms_iter = ms_step / iters
+    flops = 2.0 * n * k * d                       # the assignment's x.c per iteration
+    achieved = flops / (ms_iter * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms = {iters} iterations, {ms_iter:.3f} ms per iteration")
+    # parity: the first iteration, checked in full against the oracle
     a1, n1 = step(1)
-    rep = check.compare_kmeans_round(xs, init, a1.cpu().numpy(), c.cpu().numpy(), n1.cpu().numpy())
-    log("parity (round 1)", rep.summary())
+    rep = check.compare_kmeans_iteration(xs, init, a1.cpu().numpy(), c.cpu().numpy(), n1.cpu().numpy())
+    log("parity (iteration 1)", rep.summary())
     cpu = None
     if not args.no_cpu_baseline:
         threads = O.default_threads()
         t = time.perf_counter()
         O.kmeans(xs, init, 1, nthreads=threads)
         wall = time.perf_counter() - t
-        cpu = dict(value=1.0 / wall, unit="rounds/s", cores=threads, kind="oracle",
-                   sample=f"one round over all {n} vectors (assignment in double precision, "
+        cpu = dict(value=1.0 / wall, unit="iterations/s", cores=threads, kind="oracle",
+                   sample=f"one iteration over all {n} vectors (assignment in double precision, "
                           f"full sort per vector; double-precision means), {wall:.1f} s wall")
         log("cpu baseline", cpu)
     res = {
-        "metric": "k-means (Lloyd) rounds per second",
-        "value": 1e3 / ms_round,
-        "unit": "rounds/s",
+        "metric": "k-means (Lloyd) iterations per second",
+        "value": 1e3 / ms_iter,
+        "unit": "iterations/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -427,11 +427,11 @@ def bench_kmeans(args):
         "vs_baseline": None,
         "dtype": "fp32 (double-precision sums)",
         "data": "synthetic (seeded Gaussian mixture sample)",
-        "config": {"workload": KMEANS_WORKLOAD, "n": n, "d": d, "k": k, "rounds_per_step": rounds},
+        "config": {"workload": KMEANS_WORKLOAD, "n": n, "d": d, "k": k, "iterations_per_step": iters},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "one round (coarse assignment + update), assignment flops",
-                     "kernel_ms": ms_round, "algorithmic_flops_per_launch": flops},
+                     "kernel": "one iteration (coarse assignment + update), assignment flops",
+                     "kernel_ms": ms_iter, "algorithmic_flops_per_launch": flops},
         "cpu_baseline": cpu,
         "parity": rep.summary(),
     }

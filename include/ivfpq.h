@@ -194,16 +194,16 @@ ivfpq_status ivfpq_assign_encode_ex(const ivfpq_index *idx, const float *vectors
  * floating point value format for reducing shared memory bank conflict in ANN
  * search", IVFPQ section, index-building step 1; run it on the residuals of
  * one sub-vector to train a sub-quantizer's 256 codewords).  Each of `iters`
- * rounds assigns every vector to its nearest center (the coarse step with
+ * iterations assigns every vector to its nearest center (the coarse step with
  * nprobe = 1: squared L2 through the float32 norm expansion on the matrix
  * cores) and then moves every center to the mean of its vectors (sums in
  * double precision, the mean rounded to float32); a center with no vector
  * keeps its value.
  *
  * vectors_dev [n][d] float32 row-major; centers_dev [k][d] float32: the
- * initial centers on entry, the centers after the last round on return.
+ * initial centers on entry, the centers after the last iteration on return.
  * assign_dev [n] int32 and counts_dev [k] int32, when not NULL, receive the
- * last round's assignment and cluster sizes.  On the current device and
+ * last iteration's assignment and cluster sizes.  On the current device and
  * `stream`; scratch is allocated and freed inside, and the call returns after
  * the device work is done.  iters = 0 changes nothing; n = 0 leaves the centers
  * as they are.  Errors: IVFPQ_E_INVALID_ARG (n outside [0, 2^31), d outside

@@ -38,7 +38,7 @@ Index building (assignment and encoding of database vectors):
 
 k-means (Lloyd's algorithm on the device):
 
-6. One round.  The device assignment obeys rule 4 against the round's input
+6. One iteration.  The device assignment obeys rule 4 against the iteration's input
    centers; with that assignment the oracle's update (double-precision means)
    gives the counts exactly, and each device center equals the float32
    rounding of the oracle's mean or its float32 neighbour on the other side
@@ -349,9 +349,9 @@ class KmeansReport:
                     failures=len(self.failures))
 
 
-def compare_kmeans_round(vectors, centers_in, gpu_assign, gpu_centers, gpu_counts=None,
+def compare_kmeans_iteration(vectors, centers_in, gpu_assign, gpu_centers, gpu_counts=None,
                          nthreads=None) -> KmeansReport:
-    """Rule 6: one device round (assignment + update) from centers_in."""
+    """Rule 6: one device iteration (assignment + update) from centers_in."""
     x = np.ascontiguousarray(vectors, dtype=np.float32)
     c0 = np.ascontiguousarray(centers_in, dtype=np.float32)
     ga = np.asarray(gpu_assign).reshape(-1).astype(np.int64)

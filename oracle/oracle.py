@@ -319,8 +319,8 @@ def nearest_lists(vectors, centers, nthreads=None):
 
 def kmeans(vectors, init, iters, nthreads=None):
     """Lloyd's algorithm from the given float32 initial centers: `iters`
-    rounds of assignment (``nearest_lists``) then update
-    (``kmeans_update``).  Returns (centers float32 [k, d], the last round's
+    iterations of assignment (``nearest_lists``) then update
+    (``kmeans_update``).  Returns (centers float32 [k, d], the last iteration's
     assignment int32 [n], its counts int64 [k])."""
     c = np.ascontiguousarray(init, dtype=np.float32)
     a = np.zeros(len(vectors), dtype=np.int32)

@@ -7,7 +7,7 @@ be the nearest codeword of the oracle's table of the device's list up to the
 float32 forward-error bound, so codes are equal wherever the decision is not
 a near-tie.  Exact ties must go to the smaller codeword.
 
-k-means (ivfpq_kmeans_ex, rule 6): each device round's assignment obeys the
+k-means (ivfpq_kmeans_ex, rule 6): each device iteration's assignment obeys the
 coarse tie band against its input centers, its counts equal the oracle's
 for that assignment, and every center equals the float32 rounding of the
 oracle's double-precision mean or the float32 neighbour across it.
@@ -200,32 +200,32 @@ def mixture(seed, n, d, ncomp, spread=0.5):
     (777, 60, 7),
     (1, 4, 1),
 ])
-def test_kmeans_one_round(dev, n, d, k):
-    say(f"k-means round n={n} d={d} k={k}")
+def test_kmeans_one_iteration(dev, n, d, k):
+    say(f"k-means iteration n={n} d={d} k={k}")
     x, rng = mixture(200 + d + k, n, d, max(k // 4, 2))
     init = x[rng.choice(n, k, replace=k > n)]
     c1, a, cnt = gpu_kmeans(x, init, 1)
-    rep = check.compare_kmeans_round(x, init, a, c1, cnt)
+    rep = check.compare_kmeans_iteration(x, init, a, c1, cnt)
     say("k-means parity", rep.summary())
     assert rep.ok(), rep.failures[:5]
 
 
-def test_kmeans_chained_rounds(dev):
-    # four rounds, each its own call and each checked against the oracle's
-    # round from the same input centers
+def test_kmeans_chained_iterations(dev):
+    # four iterations, each its own call and each checked against the
+    # oracle's iteration from the same input centers
     x, rng = mixture(61, 6000, 48, 20)
     c = x[rng.choice(6000, 64, replace=False)]
     for r in range(4):
-        say(f"k-means chained round {r}")
+        say(f"k-means chained iteration {r}")
         c_next, a, cnt = gpu_kmeans(x, c, 1)
-        rep = check.compare_kmeans_round(x, c, a, c_next, cnt)
+        rep = check.compare_kmeans_iteration(x, c, a, c_next, cnt)
         assert rep.ok(), (r, rep.failures[:5])
         c = c_next
 
 
-def test_kmeans_rounds_in_one_call_match_the_oracle(dev):
-    # separated clusters, one initial center in each: every round's
-    # assignment is unambiguous, so five rounds in one call must give the
+def test_kmeans_iterations_in_one_call_match_the_oracle(dev):
+    # separated clusters, one initial center in each: every
+    # iteration's assignment is unambiguous, so five iterations in one call must give the
     # oracle's assignment and counts, and its centers up to the float32
     # neighbour of each exact mean
     rng = np.random.default_rng(62)
@@ -234,7 +234,7 @@ def test_kmeans_rounds_in_one_call_match_the_oracle(dev):
     lab = rng.integers(0, k, 8000)
     x = (true[lab] + rng.standard_normal((8000, d))).astype(np.float32)
     init = x[[int(np.flatnonzero(lab == c)[0]) for c in range(k)]]
-    say("k-means five rounds")
+    say("k-means five iterations")
     c, a, cnt = gpu_kmeans(x, init, 5)
     oc, oa, ocnt = O.kmeans(x, init, 5)
     assert np.array_equal(a, oa) and np.array_equal(cnt, ocnt)
@@ -244,7 +244,7 @@ def test_kmeans_rounds_in_one_call_match_the_oracle(dev):
 def test_kmeans_edge_cases_and_errors(dev):
     x, rng = mixture(63, 100, 16, 4)
     init = x[:5].copy()
-    c, a, cnt = gpu_kmeans(x, init, 0)                 # no rounds: nothing changes
+    c, a, cnt = gpu_kmeans(x, init, 0)                 # no iterations: nothing changes
     assert np.array_equal(c, init) and np.all(a == -1) and np.all(cnt == 0)
     c, a, cnt = gpu_kmeans(np.zeros((0, 16), np.float32), init, 3)
     assert np.array_equal(c, init) and np.all(cnt == 0)
@@ -262,15 +262,15 @@ def test_kmeans_edge_cases_and_errors(dev):
 
 
 @pytest.mark.slow
-def test_kmeans_fullsize_round(dev):
-    # one round at the 1M workload's coarse training shape (262,144 sampled
+def test_kmeans_fullsize_iteration(dev):
+    # one iteration at the 1M workload's coarse training shape (262,144 sampled
     # vectors, 1,024 centers, d 128), checked in full
-    say("k-means full size: 262,144 x 128, k 1024, one round")
+    say("k-means full size: 262,144 x 128, k 1024, one iteration")
     w = G.gmm1m(keep_vectors=True)
     rng = np.random.default_rng(64)
     x = w.vectors[np.sort(rng.choice(len(w.vectors), 262_144, replace=False))]
     init = x[rng.choice(len(x), 1024, replace=False)]
     c1, a, cnt = gpu_kmeans(x, init, 1)
-    rep = check.compare_kmeans_round(x, init, a, c1, cnt)
+    rep = check.compare_kmeans_iteration(x, init, a, c1, cnt)
     say("k-means parity", rep.summary())
     assert rep.ok(), rep.failures[:5]

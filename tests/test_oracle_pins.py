@@ -487,19 +487,19 @@ def test_kmeans_checker_accepts_oracle_and_rejects_perturbations():
     c0 = x[:10].copy()
     a, _ = O.nearest_lists(x, c0)
     c1, means, counts = O.kmeans_update(x, a, c0)
-    assert check.compare_kmeans_round(x, c0, a, c1, counts).ok()
+    assert check.compare_kmeans_iteration(x, c0, a, c1, counts).ok()
     other = c1.copy()
     c, t = 3, 2
     other[c, t] = np.nextafter(c1[c, t], np.float32(np.inf if means[c, t] > c1[c, t] else -np.inf))
-    assert check.compare_kmeans_round(x, c0, a, other, counts).ok()      # the other neighbour
+    assert check.compare_kmeans_iteration(x, c0, a, other, counts).ok()      # the other neighbour
     far = c1.copy()
     far[c, t] = np.nextafter(c1[c, t], np.float32(-np.inf if means[c, t] > c1[c, t] else np.inf))
-    assert not check.compare_kmeans_round(x, c0, a, far, counts).ok()
+    assert not check.compare_kmeans_iteration(x, c0, a, far, counts).ok()
     bad = a.copy()
     i = int(np.argmax([np.sum((x[j] - c0[a[j]]) ** 2) for j in range(300)]))
     bad[i] = int(O.coarse(x[i], c0, 10)[0][-1])
-    assert not check.compare_kmeans_round(x, c0, bad, c1, counts).ok()
-    assert not check.compare_kmeans_round(x, c0, a, c1, counts + 1).ok()
+    assert not check.compare_kmeans_iteration(x, c0, bad, c1, counts).ok()
+    assert not check.compare_kmeans_iteration(x, c0, a, c1, counts + 1).ok()
 
 
 # ---------------------------------------------------------------------------
