@@ -6,6 +6,7 @@ The search runs in hand-written HIP kernels behind the C ABI of
 (``datagen``: seeded generators, CPU index builder, index file).
 """
 from .binding import (IVFPQError, FlatIndex, Index, ivfpq_assign_encode_ex,  # noqa: F401
+                      ivfpq_build_index_ex, ivfpq_index_export,
                       ivfpq_compute_luts_ex,
                       ivfpq_coarse_ex, ivfpq_flat_free, ivfpq_flat_load_bf16,
                       ivfpq_flat_profile_begin, ivfpq_flat_profile_end, ivfpq_flat_search_bf16,

@@ -67,6 +67,7 @@ class FlatTimings(ctypes.Structure):
 EXPORTS = ("ivfpq_validate_index_file", "ivfpq_validate_host_index", "ivfpq_load_index",
            "ivfpq_load_index_host", "ivfpq_free_index", "ivfpq_index_info", "ivfpq_search",
            "ivfpq_search_ex", "ivfpq_coarse_ex", "ivfpq_assign_encode_ex", "ivfpq_kmeans_ex",
+           "ivfpq_build_index_ex", "ivfpq_index_export",
            "ivfpq_compute_luts_ex",
            "ivfpq_select_topk_ex",
            "ivfpq_profile_begin",
@@ -100,6 +101,8 @@ def lib():
             "ivfpq_coarse_ex": ([P, P, i64, i32, P, P, P], st),
             "ivfpq_assign_encode_ex": ([P, P, i64, P, P, P], st),
             "ivfpq_kmeans_ex": ([P, i64, i32, i32, i32, P, P, P, P], st),
+            "ivfpq_build_index_ex": ([P, P, i64, i32, i32, i32, P, P, i32, P], st),
+            "ivfpq_index_export": ([P, P, P, P, P, P], st),
             "ivfpq_compute_luts_ex": ([P, P, i64, P, i32, i32, P, P], st),
             "ivfpq_select_topk_ex": ([P, i64, i64, i32, P, P, P], st),
             "ivfpq_profile_begin": ([P, i32], st),
@@ -208,6 +211,47 @@ def ivfpq_load_index_host(index, device: int = 0) -> Index:
     h = ctypes.c_void_p()
     _check(lib().ivfpq_load_index_host(ctypes.byref(s), device, ctypes.byref(h)))
     return Index(h)
+
+
+def ivfpq_build_index_ex(vectors: torch.Tensor, centroids: torch.Tensor,
+                         codebooks: torch.Tensor, ids: torch.Tensor = None,
+                         device: int = 0) -> Index:
+    """Build an index on the device from device tensors: vectors [n, d]
+    float32, centroids [nlist, d] float32, codebooks [m, 256, d/m] float32,
+    ids [n] int64 (None: row numbers)."""
+    x = _dev(vectors, torch.float32)
+    c = _dev(centroids, torch.float32)
+    b = _dev(codebooks, torch.float32)
+    if x.dim() != 2 or c.dim() != 2 or b.dim() != 3 or c.shape[1] != x.shape[1] or \
+            b.shape[1] != 256 or b.shape[0] * b.shape[2] != x.shape[1]:
+        raise ValueError("expected vectors [n, d], centroids [nlist, d], codebooks [m, 256, d/m]")
+    idp = 0
+    if ids is not None:
+        ids = _dev(ids, torch.int64)
+        if ids.shape != (x.shape[0],):
+            raise ValueError("expected ids [n]")
+        idp = ids.data_ptr()
+    h = ctypes.c_void_p()
+    _check(lib().ivfpq_build_index_ex(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(idp),
+                                      x.shape[0], x.shape[1], c.shape[0], b.shape[0],
+                                      ctypes.c_void_p(c.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                      device, ctypes.byref(h)))
+    return Index(h)
+
+
+def ivfpq_index_export(index: Index) -> dict:
+    """The index's arrays in host memory: centroids, codebooks, list_sizes,
+    codes (list-major) and ids (numpy arrays, the host index layout)."""
+    i = index.info
+    d, nlist, m, n = i["d"], i["nlist"], i["m"], i["ntotal"]
+    out = dict(centroids=np.empty((nlist, d), np.float32),
+               codebooks=np.empty((m, 256, d // m), np.float32),
+               list_sizes=np.empty(nlist, np.int64), codes=np.empty((n, m), np.uint8),
+               ids=np.empty(n, np.int64))
+    _check(lib().ivfpq_index_export(index.handle, *(_np_ptr(out[k]) for k in
+                                                    ("centroids", "codebooks", "list_sizes",
+                                                     "codes", "ids"))))
+    return out
 
 
 def ivfpq_free_index(index: Index) -> None:

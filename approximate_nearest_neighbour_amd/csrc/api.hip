@@ -821,6 +821,127 @@ ivfpq_status ivfpq_kmeans_ex(const float *vectors_dev, int64_t n, int d, int k, 
     return s;
 }
 
+ivfpq_status ivfpq_build_index_ex(const float *vectors_dev, const int64_t *ids_dev, int64_t n,
+                                  int d, int nlist, int m, const float *centroids_dev,
+                                  const float *codebooks_dev, int device, ivfpq_index **out)
+{
+    if (!out)
+        return fail(IVFPQ_E_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (n < 0 || n > (int64_t)0x7FFFFFFF)
+        return fail(IVFPQ_E_INVALID_ARG, "n must be in [0, 2^31)");
+    if (check_shape(d, nlist, m, 8, n) != IVFPQ_OK) {
+        const std::string msg = g_err;
+        return fail(IVFPQ_E_INVALID_ARG, msg);
+    }
+    if (!centroids_dev || !codebooks_dev || (n > 0 && !vectors_dev))
+        return fail(IVFPQ_E_INVALID_ARG, "a required device pointer is NULL");
+    ivfpq_status s = device_check(device);
+    if (s)
+        return s;
+    DeviceGuard g(device);
+    if (!g.ok)
+        return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
+    std::vector<int64_t> no_sizes((size_t)nlist, 0);
+    ivfpq_index *ix = nullptr;
+    if ((s = alloc_index(device, d, nlist, m, n, no_sizes.data(), &ix)))
+        return s;
+    DeviceIndex &dx = ix->dx;
+    if (hipMemcpy(dx.centroids, centroids_dev, (size_t)nlist * d * 4, hipMemcpyDeviceToDevice) !=
+            hipSuccess ||
+        hipMemcpy(dx.codebooks, codebooks_dev, (size_t)d * 256 * 4, hipMemcpyDeviceToDevice) !=
+            hipSuccess ||
+        launch_centroid_blocks(dx, nullptr) != hipSuccess) {
+        release(ix);
+        return fail(IVFPQ_E_DEVICE, "centroid or codebook upload failed");
+    }
+    if (n > 0) {
+        // scratch: lists, codes in input order, sort keys and permutation,
+        // list counts, the sort's own scratch
+        void *lists = nullptr, *codes = nullptr, *keys = nullptr, *perm_in = nullptr,
+             *perm_out = nullptr, *counts = nullptr, *tmp = nullptr;
+        size_t tmp_bytes = 0;
+        std::vector<uint32_t> counts_h((size_t)nlist);
+        bool okay = dev_alloc(&lists, (size_t)n * 4) == hipSuccess &&
+                    dev_alloc(&codes, (size_t)n * m) == hipSuccess &&
+                    dev_alloc(&keys, (size_t)n * 4) == hipSuccess &&
+                    dev_alloc(&perm_in, (size_t)n * 4) == hipSuccess &&
+                    dev_alloc(&perm_out, (size_t)n * 4) == hipSuccess &&
+                    dev_alloc(&counts, (size_t)nlist * 4) == hipSuccess;
+        s = okay ? ensure_ws(ix, coarse_ws_bytes(dx, n, 1))
+                 : fail(IVFPQ_E_OUT_OF_MEMORY, "build scratch allocation failed");
+        auto li = static_cast<int32_t *>(lists);
+        auto co = static_cast<uint8_t *>(codes);
+        auto ke = static_cast<int32_t *>(keys);
+        auto pi = static_cast<int32_t *>(perm_in);
+        auto po = static_cast<int32_t *>(perm_out);
+        auto cn = static_cast<uint32_t *>(counts);
+        if (s == IVFPQ_OK &&
+            (launch_coarse(dx, vectors_dev, n, 1, ix->ws, li, nullptr, nullptr) != hipSuccess ||
+             launch_encode(dx, vectors_dev, n, li, co, nullptr) != hipSuccess ||
+             launch_list_layout(li, n, nlist, m, co, ids_dev, cn, ke, pi, po, nullptr, &tmp_bytes,
+                                dx.codes, dx.ids, nullptr) != hipSuccess))
+            s = fail(IVFPQ_E_DEVICE, "assignment or encoding kernels failed");
+        if (s == IVFPQ_OK && dev_alloc(&tmp, tmp_bytes) != hipSuccess)
+            s = fail(IVFPQ_E_OUT_OF_MEMORY, "sort scratch allocation failed");
+        if (s == IVFPQ_OK &&
+            (launch_list_layout(li, n, nlist, m, co, ids_dev, cn, ke, pi, po, tmp, &tmp_bytes,
+                                dx.codes, dx.ids, nullptr) != hipSuccess ||
+             hipDeviceSynchronize() != hipSuccess ||
+             hipMemcpy(counts_h.data(), cn, (size_t)nlist * 4, hipMemcpyDeviceToHost) !=
+                 hipSuccess))
+            s = fail(IVFPQ_E_DEVICE, "list layout failed");
+        for (void *p : {lists, codes, keys, perm_in, perm_out, counts, tmp})
+            if (p)
+                (void)hipFree(p);
+        if (s != IVFPQ_OK) {
+            release(ix);
+            return s;
+        }
+        // list offsets (host copy and device array) from the counts
+        int64_t mx = 0;
+        for (int l = 0; l < nlist; ++l) {
+            ix->host_off[l + 1] = ix->host_off[l] + counts_h[l];
+            mx = (int64_t)counts_h[l] > mx ? (int64_t)counts_h[l] : mx;
+        }
+        dx.max_list = mx;
+        if ((int64_t)ix->host_off[nlist] != n) {
+            release(ix);
+            return fail(IVFPQ_E_DEVICE, "an entry was assigned outside the lists");
+        }
+        COPY_OR_FAIL(dx.list_off, ix->host_off.data(), ((size_t)nlist + 1) * 4);
+    }
+    if ((s = finish_load(ix)))
+        return s;
+    *out = ix;
+    return ok();
+}
+
+ivfpq_status ivfpq_index_export(const ivfpq_index *idx, float *centroids, float *codebooks,
+                                int64_t *list_sizes, uint8_t *codes, int64_t *ids)
+{
+    if (!idx)
+        return fail(IVFPQ_E_INVALID_ARG, "index handle is NULL");
+    DeviceGuard g(idx->device);
+    if (!g.ok)
+        return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
+    const DeviceIndex &dx = idx->dx;
+    if (list_sizes)
+        for (int l = 0; l < dx.nlist; ++l)
+            list_sizes[l] = (int64_t)idx->host_off[l + 1] - (int64_t)idx->host_off[l];
+    if ((centroids && hipMemcpy(centroids, dx.centroids, (size_t)dx.nlist * dx.d * 4,
+                                hipMemcpyDeviceToHost) != hipSuccess) ||
+        (codebooks && hipMemcpy(codebooks, dx.codebooks, (size_t)dx.d * 256 * 4,
+                                hipMemcpyDeviceToHost) != hipSuccess) ||
+        (codes && dx.ntotal > 0 &&
+         hipMemcpy(codes, dx.codes, (size_t)dx.ntotal * dx.m, hipMemcpyDeviceToHost) !=
+             hipSuccess) ||
+        (ids && dx.ntotal > 0 &&
+         hipMemcpy(ids, dx.ids, (size_t)dx.ntotal * 8, hipMemcpyDeviceToHost) != hipSuccess))
+        return fail(IVFPQ_E_DEVICE, "device to host copy failed");
+    return ok();
+}
+
 ivfpq_status ivfpq_compute_luts_ex(const ivfpq_index *idx, const float *queries_dev, int64_t nq,
                                    const int32_t *probes_dev, int nprobe, int lut,
                                    float *luts_dev, void *stream)

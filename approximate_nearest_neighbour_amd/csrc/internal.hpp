@@ -75,6 +75,14 @@ hipError_t launch_list_term(const DeviceIndex &ix, hipStream_t stream);
 // PQ codes of n vectors (x [n][d]) given their lists (index building)
 hipError_t launch_encode(const DeviceIndex &ix, const float *x, int64_t n, const int32_t *lists,
                          uint8_t *codes, hipStream_t stream);
+// list-major layout of n encoded entries (index building): counts [nlist],
+// keys_out, perm_in, perm_out [n] scratch; sort_tmp == nullptr asks for the
+// sort's scratch size in *sort_tmp_bytes
+hipError_t launch_list_layout(const int32_t *lists, int64_t n, int nlist, int m,
+                              const uint8_t *codes_in, const int64_t *ids_in, uint32_t *counts,
+                              int32_t *keys_out, int32_t *perm_in, int32_t *perm_out,
+                              void *sort_tmp, size_t *sort_tmp_bytes, uint8_t *codes_out,
+                              int64_t *ids_out, hipStream_t stream);
 // k-means update step: centers = means of their assigned vectors (sums [k][d]
 // double and counts [k] are scratch / output)
 hipError_t launch_kmeans_update(const float *x, int64_t n, int d, const int32_t *assign, int k,

@@ -16,6 +16,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <hipcub/hipcub.hpp>
+
 namespace ivfpq {
 
 // Workgroup: 64 vectors (vector v0 + l in lane l of every wave); its four
@@ -192,6 +194,90 @@ hipError_t launch_kmeans_update(const float *x, int64_t n, int d, const int32_t 
         return e;
     hipLaunchKernelGGL(kmeans_finalize_kernel, dim3((unsigned)((nsum + 255) / 256)), dim3(256), 0,
                        stream, centers, sums, counts, k, d);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// list-major layout of encoded entries: "Custom 8-bit floating point value
+// format for reducing shared memory bank conflict in ANN search", IVFPQ
+// section, index-building step 4 (the codes are stored with their cluster
+// membership); "Billion-scale similarity search with GPUs", IVFADC section
+// (the codes of a list are stored contiguously).  Entries keep their input
+// order inside a list (a stable sort by list number).
+// ---------------------------------------------------------------------------
+
+__global__ void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
+__global__ void iota_kernel(int32_t *__restrict__ p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = (int32_t)i;
+}
+
+__global__ void list_count_kernel(const int32_t *__restrict__ lists, int64_t n, int nlist,
+                                  uint32_t *__restrict__ counts)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const int l = lists[i];
+        if ((unsigned)l < (unsigned)nlist)
+            atomicAdd(counts + l, 1u);
+    }
+}
+
+// Position p of the layout takes entry perm[p]: its code row and its id (the
+// row number when no ids are given).
+__global__ void gather_entries_kernel(const int32_t *__restrict__ perm, int64_t n, int m,
+                                      const uint8_t *__restrict__ codes_in,
+                                      const int64_t *__restrict__ ids_in,
+                                      uint8_t *__restrict__ codes_out,
+                                      int64_t *__restrict__ ids_out)
+{
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= n)
+        return;
+    const int64_t src = perm[p];
+    for (int j = 0; j < m; ++j)
+        codes_out[p * m + j] = codes_in[src * m + j];
+    ids_out[p] = ids_in ? ids_in[src] : src;
+}
+
+hipError_t launch_list_layout(const int32_t *lists, int64_t n, int nlist, int m,
+                              const uint8_t *codes_in, const int64_t *ids_in, uint32_t *counts,
+                              int32_t *keys_out, int32_t *perm_in, int32_t *perm_out,
+                              void *sort_tmp, size_t *sort_tmp_bytes, uint8_t *codes_out,
+                              int64_t *ids_out, hipStream_t stream)
+{
+    int bits = 1;
+    while (bits < 31 && (1ll << bits) < (int64_t)nlist)
+        ++bits;
+    if (!sort_tmp) // size query
+        return hipcub::DeviceRadixSort::SortPairs(nullptr, *sort_tmp_bytes, lists, keys_out,
+                                                  perm_in, perm_out, (int)n, 0, bits, stream);
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    const unsigned cblocks = (unsigned)((nlist + 255) / 256);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(cblocks), dim3(256), 0, stream, counts,
+                       (int64_t)nlist);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n == 0)
+        return e;
+    hipLaunchKernelGGL(list_count_kernel, dim3(blocks), dim3(256), 0, stream, lists, n, nlist,
+                       counts);
+    hipLaunchKernelGGL(iota_kernel, dim3(blocks), dim3(256), 0, stream, perm_in, n);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    e = hipcub::DeviceRadixSort::SortPairs(sort_tmp, *sort_tmp_bytes, lists, keys_out, perm_in,
+                                           perm_out, (int)n, 0, bits, stream);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(gather_entries_kernel, dim3(blocks), dim3(256), 0, stream, perm_out, n, m,
+                       codes_in, ids_in, codes_out, ids_out);
     return hipGetLastError();
 }
 

@@ -213,6 +213,36 @@ ivfpq_status ivfpq_kmeans_ex(const float *vectors_dev, int64_t n, int d, int k, 
                              float *centers_dev, int32_t *assign_dev, int32_t *counts_dev,
                              void *stream);
 
+/* Index building: an index built on `device` from n database vectors in
+ * device memory and trained centroids and codebooks (device memory too, for
+ * instance from ivfpq_kmeans_ex).  Each vector goes to the list of its nearest
+ * centroid and is PQ-encoded on its residual (ivfpq_assign_encode_ex); the
+ * entries are then laid out list after list, keeping their input order inside
+ * a list ("Custom 8-bit floating point value format for reducing shared memory
+ * bank conflict in ANN search", IVFPQ section, index-building steps 1-4;
+ * "Billion-scale similarity search with GPUs", IVFADC section: the codes of a
+ * list are stored contiguously).
+ *
+ * vectors_dev [n][d] float32; ids_dev [n] int64 or NULL (the ids are then the
+ * row numbers 0..n-1); centroids_dev [nlist][d] float32; codebooks_dev
+ * [m][256][d/m] float32.  The library copies what it keeps; the caller keeps
+ * ownership of its buffers.  The call returns when the index is ready (it
+ * synchronises the device).  Errors: IVFPQ_E_INVALID_ARG (NULL out or pointer,
+ * n outside [0, 2^31), a shape ivfpq_load_index would reject), IVFPQ_E_NO_DEVICE,
+ * IVFPQ_E_OUT_OF_MEMORY, IVFPQ_E_DEVICE. */
+ivfpq_status ivfpq_build_index_ex(const float *vectors_dev, const int64_t *ids_dev, int64_t n,
+                                  int d, int nlist, int m, const float *centroids_dev,
+                                  const float *codebooks_dev, int device, ivfpq_index **out);
+
+/* Copy an index back to host memory (for saving it, or checking it): any
+ * pointer may be NULL to skip that array.  Sizes from ivfpq_index_info:
+ * centroids [nlist][d] float32, codebooks [m][256][d/m] float32, list_sizes
+ * [nlist] int64, codes [ntotal][m] uint8 (list after list), ids [ntotal]
+ * int64.  Blocking.  Errors: IVFPQ_E_INVALID_ARG (NULL handle),
+ * IVFPQ_E_NO_DEVICE, IVFPQ_E_DEVICE. */
+ivfpq_status ivfpq_index_export(const ivfpq_index *idx, float *centroids, float *codebooks,
+                                int64_t *list_sizes, uint8_t *codes, int64_t *ids);
+
 /* The table step alone (device buffers, asynchronous, for verification): for
  * each query q and each of its nprobe lists probes_dev[q][p], writes the
  * m x 256 table F_j(v) to luts_dev[q][p][j][v] as float32 (values of the fp16

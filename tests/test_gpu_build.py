@@ -274,3 +274,144 @@ def test_kmeans_fullsize_iteration(dev):
     rep = check.compare_kmeans_iteration(x, init, a, c1, cnt)
     say("k-means parity", rep.summary())
     assert rep.ok(), rep.failures[:5]
+
+
+# ---------------------------------------------------------------------------
+# index built on the device (list-major layout of the encoded entries)
+# ---------------------------------------------------------------------------
+
+def gpu_build(x, cent, books, ids=None):
+    t = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
+    ix = A.ivfpq_build_index_ex(t(x), t(cent), t(books),
+                                None if ids is None else t(ids, torch.int64))
+    return ix
+
+
+def test_build_index_exact_layout(dev):
+    # vectors made of known codewords around far-apart centroids, in random
+    # order with random ids: the layout must be the stable list-major order
+    rng = np.random.default_rng(91)
+    nlist, d, m, n = 16, 32, 8, 5000
+    base = G.random_index(rng, nlist, d, m, np.full(nlist, 1), scale=10.0, codebook_scale=0.1)
+    lst = rng.integers(0, nlist, n)
+    code = rng.integers(0, 256, (n, m))
+    x = (base.centroids[lst] +
+         np.concatenate([base.codebooks[j][code[:, j]] for j in range(m)], axis=1)).astype(np.float32)
+    ids = rng.permutation(10 * n)[:n].astype(np.int64)
+    say("build exact layout")
+    ix = gpu_build(x, base.centroids, base.codebooks, ids)
+    got = A.ivfpq_index_export(ix)
+    order = np.argsort(lst, kind="stable")
+    assert np.array_equal(got["list_sizes"], np.bincount(lst, minlength=nlist))
+    assert np.array_equal(got["codes"], code[order].astype(np.uint8))
+    assert np.array_equal(got["ids"], ids[order])
+    assert np.array_equal(got["centroids"], base.centroids)
+    assert np.array_equal(got["codebooks"], base.codebooks)
+    info = A.ivfpq_index_info(ix)
+    assert info["ntotal"] == n and info["max_list"] == int(np.bincount(lst).max())
+    ix.close()
+
+
+def test_build_index_trained_and_round_trip(dev):
+    # the 10,000 x 32 workload's vectors with its trained centroids and
+    # codebooks: every entry's list and code obey the encode rules, ids are
+    # the row numbers in increasing order inside each list, and the exported
+    # index loaded back searches exactly like the built one
+    w = G.gmm_workload("t", 1, 10_000, 32, 16, 0.3, 100, 16, 4, 4, 10)
+    say("build trained index")
+    ix = gpu_build(w.vectors, w.index.centroids, w.index.codebooks)
+    got = A.ivfpq_index_export(ix)
+    owner = np.repeat(np.arange(16), got["list_sizes"])
+    rows = got["ids"]
+    assert sorted(rows.tolist()) == list(range(10_000))
+    for l in range(16):
+        r = rows[owner == l]
+        assert np.all(np.diff(r) > 0)
+    lists = np.empty(10_000, np.int32)
+    codes = np.empty((10_000, 4), np.uint8)
+    lists[rows] = owner
+    codes[rows] = got["codes"]
+    rep = check.compare_encode(w.vectors, w.index.centroids, w.index.codebooks, lists, codes)
+    say("build parity", rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    host = G.HostIndex(got["centroids"], got["codebooks"], got["list_sizes"], got["codes"],
+                       got["ids"])
+    ix2 = A.ivfpq_load_index_host(host)
+    q = torch.from_numpy(w.queries).cuda()
+    d1, i1 = A.ivfpq_search_ex(ix, q, 4, 10)
+    d2, i2 = A.ivfpq_search_ex(ix2, q, 4, 10)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2) and torch.equal(i1, i2)
+    rep = check.compare_search(host, w.queries, 4, 10, d1.cpu().numpy(), i1.cpu().numpy())
+    assert rep.ok(), rep.failures[:5]
+    ix.close()
+    ix2.close()
+
+
+def test_build_index_empty_and_errors(dev):
+    rng = np.random.default_rng(92)
+    base = G.random_index(rng, 8, 16, 4, np.full(8, 1))
+    ix = gpu_build(np.zeros((0, 16), np.float32), base.centroids, base.codebooks)
+    assert A.ivfpq_index_info(ix)["ntotal"] == 0
+    dd, ii = A.ivfpq_search_ex(ix, torch.zeros((3, 16), device="cuda"), 2, 5)
+    torch.cuda.synchronize()
+    assert torch.all(ii == -1) and torch.all(torch.isinf(dd))
+    ix.close()
+    with pytest.raises(ValueError):
+        gpu_build(np.zeros((4, 16), np.float32), base.centroids[:, :8], base.codebooks)
+    from approximate_nearest_neighbour_amd import binding as B
+    import ctypes
+    h = ctypes.c_void_p()
+    c = torch.from_numpy(base.centroids).cuda()
+    b = torch.from_numpy(base.codebooks).cuda()
+    L = B.lib()
+    assert L.ivfpq_build_index_ex(None, None, 4, 16, 8, 4, c.data_ptr(), b.data_ptr(), 0,
+                                  ctypes.byref(h)) == B.E_INVALID_ARG
+    assert L.ivfpq_build_index_ex(None, None, 0, 16, 8, 5, c.data_ptr(), b.data_ptr(), 0,
+                                  ctypes.byref(h)) == B.E_INVALID_ARG   # m does not divide d
+    assert L.ivfpq_build_index_ex(None, None, 0, 16, 8, 4, None, b.data_ptr(), 0,
+                                  ctypes.byref(h)) == B.E_INVALID_ARG
+    assert L.ivfpq_build_index_ex(None, None, 0, 16, 8, 4, c.data_ptr(), b.data_ptr(), 0,
+                                  None) == B.E_INVALID_ARG
+    assert L.ivfpq_index_export(None, None, None, None, None, None) == B.E_INVALID_ARG
+
+
+def test_device_pipeline_train_build_search(dev):
+    # the whole index on the device: coarse k-means, PQ codebooks by k-means
+    # on each sub-vector of the residuals, the build, then a search checked
+    # against the oracle on the exported index
+    x, rng = mixture(93, 20_000, 32, 40, spread=0.3)
+    nlist, m = 32, 4
+    xt = torch.from_numpy(x).cuda()
+    cent = xt[torch.from_numpy(rng.choice(20_000, nlist, replace=False)).cuda()].clone()
+    assign, _ = A.ivfpq_kmeans_ex(xt, cent, 8)
+    resid = xt - cent[assign.long()]
+    books = torch.empty((m, 256, 32 // m), device="cuda")
+    for j in range(m):
+        sub = resid[:, j * 8:(j + 1) * 8].contiguous()
+        books[j] = sub[torch.from_numpy(rng.choice(20_000, 256, replace=False)).cuda()]
+        A.ivfpq_kmeans_ex(sub, books[j], 8)
+    say("device pipeline: build")
+    ix = A.ivfpq_build_index_ex(xt, cent, books.contiguous())
+    got = A.ivfpq_index_export(ix)
+    host = G.HostIndex(got["centroids"], got["codebooks"], got["list_sizes"], got["codes"],
+                       got["ids"])
+    q = x[rng.choice(20_000, 50, replace=False)] + 0.05
+    d, i, p = A.ivfpq_search_ex(ix, torch.from_numpy(q.astype(np.float32)).cuda(), 4, 20,
+                                return_probes=True)
+    torch.cuda.synchronize()
+    rep = check.compare_search(host, q.astype(np.float32), 4, 20, d.cpu().numpy(),
+                               i.cpu().numpy(), p.cpu().numpy())
+    say("device pipeline parity", rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    # the encoding of every vector obeys the encode rules for the trained books
+    lists = np.empty(20_000, np.int32)
+    codes = np.empty((20_000, m), np.uint8)
+    owner = np.repeat(np.arange(nlist), got["list_sizes"])
+    lists[got["ids"]] = owner
+    codes[got["ids"]] = got["codes"]
+    sample = np.sort(rng.choice(20_000, 2000, replace=False))
+    rep = check.compare_encode(x[sample], got["centroids"], got["codebooks"], lists[sample],
+                               codes[sample])
+    assert rep.ok(), rep.failures[:5]
+    ix.close()
