@@ -36,7 +36,7 @@ def workload(name: str):
               "ivfpq_zipf_n1000000000_d96_m8_nlist262144": G.zipf_workload}
     if name not in makers:
         raise SystemExit(f"unknown workload {name}; choose from "
-                         f"{sorted(makers) + [FLAT_WORKLOAD, ENCODE_WORKLOAD, KMEANS_WORKLOAD, KNN_GRAPH_WORKLOAD]}")
+                         f"{sorted(makers) + EXTRA_WORKLOADS}")
     return makers[name]()
 
 
@@ -402,7 +402,8 @@ def bench_kmeans(args):
     log(f"step {ms_step:.3f} ms = {iters} iterations, {ms_iter:.3f} ms per iteration")
     # parity: the first iteration, checked in full against the oracle
     a1, n1 = step(1)
-    rep = check.compare_kmeans_iteration(xs, init, a1.cpu().numpy(), c.cpu().numpy(), n1.cpu().numpy())
+    rep = check.compare_kmeans_iteration(xs, init, a1.cpu().numpy(), c.cpu().numpy(),
+                                         n1.cpu().numpy())
     log("parity (iteration 1)", rep.summary())
     cpu = None
     if not args.no_cpu_baseline:
@@ -427,13 +428,102 @@ def bench_kmeans(args):
         "vs_baseline": None,
         "dtype": "fp32 (double-precision sums)",
         "data": "synthetic (seeded Gaussian mixture sample)",
-        "config": {"workload": KMEANS_WORKLOAD, "n": n, "d": d, "k": k, "iterations_per_step": iters},
+        "config": {"workload": KMEANS_WORKLOAD, "n": n, "d": d, "k": k,
+                   "iterations_per_step": iters},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
                      "kernel": "one iteration (coarse assignment + update), assignment flops",
                      "kernel_ms": ms_iter, "algorithmic_flops_per_launch": flops},
         "cpu_baseline": cpu,
         "parity": rep.summary(),
+    }
+    print(json.dumps(res), flush=True)
+
+
+BUILD_WORKLOAD = "build_n1m_d128_m16_nlist1024"
+
+
+def bench_build(args):
+    """Index built on the device: the 1M x 128 workload's 1M vectors with its
+    trained centroids (nlist 1024) and codebooks (m 16), assigned, encoded and
+    laid out list-major by one ivfpq_build_index_ex call (scratch allocation
+    and the final synchronisation included): one step = one build."""
+    import torch
+    import approximate_nearest_neighbour_amd as A
+    from approximate_nearest_neighbour_amd import datagen as G
+    from oracle import check
+    from oracle import oracle as O
+
+    t0 = time.time()
+    w = G.gmm1m(keep_vectors=True)
+    log(f"workload {BUILD_WORKLOAD}: built in {time.time() - t0:.1f} s")
+    x = torch.from_numpy(w.vectors).cuda()
+    cent = torch.from_numpy(w.index.centroids).cuda()
+    books = torch.from_numpy(w.index.codebooks).cuda()
+    n, d = x.shape
+    nlist, m = cent.shape[0], books.shape[0]
+    for _ in range(args.warmup):
+        A.ivfpq_build_index_ex(x, cent, books).close()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(args.steps):
+        ix = A.ivfpq_build_index_ex(x, cent, books)
+        ix.close()
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t) / args.steps
+    flops = 2.0 * n * nlist * d + 3.0 * n * m * 256 * (d // m)
+    achieved = flops / (ms_step * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms per build of {n} vectors")
+    ix = A.ivfpq_build_index_ex(x, cent, books)
+    got = A.ivfpq_index_export(ix)
+    ix.close()
+    owner = np.repeat(np.arange(nlist), got["list_sizes"])
+    lists = np.empty(n, np.int32)
+    codes = np.empty((n, m), np.uint8)
+    lists[got["ids"]] = owner
+    codes[got["ids"]] = got["codes"]
+    layout_ok = bool(np.all(np.diff(got["ids"])[np.diff(owner) == 0] > 0))
+    rng = np.random.default_rng(2005)
+    rows = np.sort(rng.choice(n, 256, replace=False))
+    rep = check.compare_encode(w.vectors[rows], w.index.centroids, w.index.codebooks,
+                               lists[rows], codes[rows])
+    summary = dict(rep.summary(), layout_stable=layout_ok)
+    log("parity", summary)
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = O.default_threads()
+        cnt = int(min(n, 16 * threads))
+        t = time.perf_counter()
+        O.assign_encode(w.vectors[:cnt], w.index.centroids, w.index.codebooks, nthreads=threads)
+        per_v = (time.perf_counter() - t) / cnt
+        cnt = int(min(n, max(cnt, args.cpu_seconds / max(per_v, 1e-9))))
+        t = time.perf_counter()
+        O.assign_encode(w.vectors[:cnt], w.index.centroids, w.index.codebooks, nthreads=threads)
+        wall = time.perf_counter() - t
+        cpu = dict(value=cnt / wall, unit="vectors/s", cores=threads, kind="oracle",
+                   sample=f"assignment and encoding of the first {cnt} of {n} vectors "
+                          f"(double precision; the layout is a sort), {wall:.1f} s wall")
+        log("cpu baseline", cpu)
+    res = {
+        "metric": "database vectors indexed per second (assignment, encoding, list-major layout)",
+        "value": n / (ms_step * 1e-3),
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded Gaussian mixture, CPU-trained centroids and codebooks)",
+        "config": {"workload": BUILD_WORKLOAD, "n": n, "d": d, "nlist": nlist, "m": m},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "whole build call (assignment and encoding flops)",
+                     "kernel_ms": ms_step, "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": cpu,
+        "parity": summary,
     }
     print(json.dumps(res), flush=True)
 
@@ -529,6 +619,10 @@ def bench_knn_graph(args):
     ix.close()
 
 
+EXTRA_WORKLOADS = [FLAT_WORKLOAD, ENCODE_WORKLOAD, KMEANS_WORKLOAD, KNN_GRAPH_WORKLOAD,
+                   BUILD_WORKLOAD]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -571,6 +665,8 @@ def main():
         return bench_kmeans(args)
     if args.workload == KNN_GRAPH_WORKLOAD:
         return bench_knn_graph(args)
+    if args.workload == BUILD_WORKLOAD:
+        return bench_build(args)
 
     t0 = time.time()
     w = workload(args.workload)
