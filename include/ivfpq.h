@@ -226,8 +226,9 @@ ivfpq_status ivfpq_kmeans_ex(const float *vectors_dev, int64_t n, int d, int k, 
  * vectors_dev [n][d] float32; ids_dev [n] int64 or NULL (the ids are then the
  * row numbers 0..n-1); centroids_dev [nlist][d] float32; codebooks_dev
  * [m][256][d/m] float32.  The library copies what it keeps; the caller keeps
- * ownership of its buffers.  The call returns when the index is ready (it
- * synchronises the device).  Errors: IVFPQ_E_INVALID_ARG (NULL out or pointer,
+ * ownership of its buffers.  Its kernels run on the null stream, so buffers
+ * written on another stream must be complete before the call; it returns when
+ * the index is ready (it synchronises the device).  Errors: IVFPQ_E_INVALID_ARG (NULL out or pointer,
  * n outside [0, 2^31), a shape ivfpq_load_index would reject), IVFPQ_E_NO_DEVICE,
  * IVFPQ_E_OUT_OF_MEMORY, IVFPQ_E_DEVICE. */
 ivfpq_status ivfpq_build_index_ex(const float *vectors_dev, const int64_t *ids_dev, int64_t n,
