@@ -30,7 +30,9 @@ def sample_rows(nq, count, seed):
     return np.array(sorted(rows))
 
 
-def search_and_check(A, w, lut="f32", sample=16):
+def search_and_check(A, w, lut="f32", sample=16, giant=0):
+    """giant: also check this many rows whose probes include a list of more
+    than 10^6 entries (the longest lists of a skewed index)."""
     t = time.time()
     ix = A.ivfpq_load_index_host(w.index, device=0)
     q = torch.from_numpy(w.queries).cuda()
@@ -39,6 +41,12 @@ def search_and_check(A, w, lut="f32", sample=16):
     print(f"  {w.name} lut={lut}: searched {len(w.queries)} queries "
           f"({time.time() - t:.1f} s incl. upload)", flush=True)
     rows = sample_rows(len(w.queries), sample, 11)
+    if giant:
+        big = np.flatnonzero(np.asarray(w.index.list_sizes) > 1_000_000)
+        hits = np.flatnonzero(np.isin(p.cpu().numpy(), big).any(axis=1))
+        print(f"  {len(hits)} queries probe one of the {len(big)} lists above 10^6 entries; "
+              f"checking {min(giant, len(hits))} of them", flush=True)
+        rows = np.unique(np.concatenate([rows, hits[:giant]]))
     rep = check.compare_search(w.index, w.queries[rows], w.nprobe, w.k, d.cpu().numpy()[rows],
                                i.cpu().numpy()[rows], p.cpu().numpy()[rows],
                                lut_mode=O.LUT_F16 if lut == "f16" else O.LUT_F64)
@@ -72,7 +80,7 @@ def test_fullsize_zipf_1b(A):
     print("full size: 1B entries, d 96, nlist 262144 (Zipf), m 8, nprobe 128, k 100",
           flush=True)
     w = G.zipf_workload()
-    search_and_check(A, w)
+    search_and_check(A, w, giant=2)
 
 
 def test_fullsize_flat_bf16(A):
