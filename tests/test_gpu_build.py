@@ -415,3 +415,18 @@ def test_device_pipeline_train_build_search(dev):
                                codes[sample])
     assert rep.ok(), rep.failures[:5]
     ix.close()
+
+
+@pytest.mark.parametrize("nlist,d,m,n", [(4, 128, 64, 700), (1, 16, 4, 1), (3, 8, 8, 65)])
+def test_build_and_encode_edge_shapes(dev, nlist, d, m, n):
+    # 64 sub-quantizers of 2 dims, a single vector in a single list, dsub 1
+    say(f"build edge nlist={nlist} d={d} m={m} n={n}")
+    index, x = shape_case(500 + m, nlist, d, m, n)
+    lists, codes, _ = assert_encode_parity(index, x)
+    ix = gpu_build(x, index.centroids, index.codebooks)
+    got = A.ivfpq_index_export(ix)
+    order = np.argsort(lists, kind="stable")
+    assert np.array_equal(got["list_sizes"], np.bincount(lists, minlength=nlist))
+    assert np.array_equal(got["ids"], order)
+    assert np.array_equal(got["codes"], codes[order])
+    ix.close()
