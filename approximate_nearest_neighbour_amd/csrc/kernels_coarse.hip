@@ -294,6 +294,191 @@ __global__ __launch_bounds__(64) void coarse_merge_kernel(const float *__restric
     }
 }
 
+// nprobe = 1 (the nearest list of every vector: assignment when an index
+// is built, k-means): the same products and the same distance expression as
+// above, but a lane keeps the smallest distance of each of its rows (its
+// column of every tile) in registers, so there is no selection role, no
+// distance tile in LDS and no barrier inside the sweep.  Eight matrix waves
+// (4 column blocks x 2 row groups of RPW*16 rows), two workgroups per CU.
+// Lane minima meet across the 16 columns of a block by shuffles, across the
+// 4 blocks in LDS, across centroid splits in coarse_argmin_merge_kernel.
+// Equal distances go to the smaller centroid number (a lane sweeps its
+// centroids in increasing order and keeps the first; elsewhere the smaller
+// number wins), so the result is the first minimum, as argmin defines it.
+__device__ __forceinline__ void argmin_take(float &bv, int32_t &bi, float ov, int32_t oi)
+{
+    if (ov < bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+    }
+}
+
+template <int RG, int RPW, int KD>
+__global__ __launch_bounds__(256 * RG / RPW) __attribute__((amdgpu_waves_per_eu(4)))
+void coarse_argmin_kernel(const float *__restrict__ queries, int64_t nq, int d, int nblk,
+                          const float *__restrict__ cblk, const float *__restrict__ cnorm_pad,
+                          int splits, float *__restrict__ part_d, int32_t *__restrict__ part_i,
+                          int32_t *__restrict__ probes, float *__restrict__ probe_d, int ip)
+{
+    constexpr int TQ = 16 * RG, THREADS = 256 * RG / RPW;
+    static_assert(THREADS == 512, "eight matrix waves");
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int xs = 4 * KD + 1; // odd stride: the 16 rows of an A read hit 16 banks
+    float *xt = reinterpret_cast<float *>(smem);            // [TQ][xs]
+    float *xn = xt + TQ * xs;                                // [TQ]
+    float *md = xn + TQ;                                     // [TQ][4] block minima
+    int32_t *mi = reinterpret_cast<int32_t *>(md + TQ * 4);  // [TQ][4] their centroids
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cbk = wave & 3, rg0 = RPW * (wave >> 2);
+    const int64_t q0 = (int64_t)blockIdx.x * TQ;
+    const int split = blockIdx.y;
+    const int ntile = (nblk + 3) / 4;
+    const int t0 = (int)((int64_t)ntile * split / splits);
+    const int t1 = (int)((int64_t)ntile * (split + 1) / splits);
+
+    for (int i = tid; i < TQ * 4 * KD; i += THREADS) {
+        const int row = i / (4 * KD), col = i % (4 * KD);
+        const int64_t q = q0 + row;
+        xt[row * xs + col] = (q < nq && col < d) ? queries[q * d + col] : 0.f;
+    }
+    __syncthreads();
+    if (tid < TQ) {
+        float acc = 0.f;
+        for (int c = 0; c < 4 * KD; ++c)
+            acc = fmaf(xt[tid * xs + c], xt[tid * xs + c], acc);
+        xn[tid] = acc;
+    }
+    __syncthreads();
+
+    float a[RPW][KD];
+#pragma unroll
+    for (int g = 0; g < RPW; ++g) {
+        const float *ap = xt + ((rg0 + g) * 16 + (lane & 15)) * xs + (lane >> 4);
+#pragma unroll
+        for (int s = 0; s < KD; ++s)
+            a[g][s] = ap[4 * s];
+    }
+    float xr[RPW][4];
+#pragma unroll
+    for (int g = 0; g < RPW; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            xr[g][r] = xn[(rg0 + g) * 16 + 4 * (lane >> 4) + r];
+    float bv[RPW][4];
+    int32_t bi[RPW][4];
+#pragma unroll
+    for (int g = 0; g < RPW; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            bv[g][r] = INFINITY;
+            bi[g][r] = INT32_MAX; // no centroid yet
+        }
+
+    // B operand and |c|^2 of a tile, loaded one tile ahead
+    float b0[KD], b1[KD], c0 = INFINITY, c1 = INFINITY;
+    auto load_b = [&](int tile, float (&b)[KD], float &cn) {
+        tile = tile < t1 ? tile : t1 - 1;
+        const float4 *bp =
+            reinterpret_cast<const float4 *>(cblk) + (size_t)(tile * 4 + cbk) * (KD / 4) * 64 + lane;
+#pragma unroll
+        for (int s4 = 0; s4 < KD / 4; ++s4) {
+            const float4 v = bp[(size_t)s4 * 64];
+            b[4 * s4] = v.x;
+            b[4 * s4 + 1] = v.y;
+            b[4 * s4 + 2] = v.z;
+            b[4 * s4 + 3] = v.w;
+        }
+        cn = cnorm_pad[(tile * 4 + cbk) * 16 + (lane & 15)];
+    };
+    // tile `tile` with operand bc, the next tile's operand loaded into bn
+    auto step = [&](int tile, const float (&bc)[KD], float cc, float (&bn)[KD], float &cnext) {
+        load_b(tile + 1, bn, cnext);
+        __builtin_amdgcn_sched_barrier(0);
+        const int32_t cid = (tile * 4 + cbk) * 16 + (lane & 15);
+#pragma unroll
+        for (int g = 0; g < RPW; ++g) {
+            v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KD; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][s], bc[s], acc, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float dist =
+                    ip ? (cc == INFINITY ? INFINITY : -acc[r]) : xr[g][r] + cc - 2.f * acc[r];
+                if (dist < bv[g][r]) {
+                    bv[g][r] = dist;
+                    bi[g][r] = cid;
+                }
+            }
+        }
+    };
+    if (t0 < t1)
+        load_b(t0, b0, c0);
+    for (int t = t0; t < t1; t += 2) {
+        step(t, b0, c0, b1, c1);
+        if (t + 1 < t1)
+            step(t + 1, b1, c1, b0, c0);
+    }
+
+    // the 16 columns of the block: lanes 16h .. 16h+15 hold the same rows
+#pragma unroll
+    for (int g = 0; g < RPW; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int sh = 1; sh < 16; sh <<= 1) {
+                const float ov = __shfl_xor(bv[g][r], sh);
+                const int32_t oi = __shfl_xor(bi[g][r], sh);
+                argmin_take(bv[g][r], bi[g][r], ov, oi);
+            }
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int g = 0; g < RPW; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = (rg0 + g) * 16 + 4 * (lane >> 4) + r;
+                md[row * 4 + cbk] = bv[g][r];
+                mi[row * 4 + cbk] = bi[g][r];
+            }
+    }
+    __syncthreads();
+    if (tid < TQ && q0 + tid < nq) {
+        float v = md[tid * 4];
+        int32_t i = mi[tid * 4];
+#pragma unroll
+        for (int c = 1; c < 4; ++c)
+            argmin_take(v, i, md[tid * 4 + c], mi[tid * 4 + c]);
+        const int64_t q = q0 + tid;
+        if (splits == 1) {
+            probes[q] = i == INT32_MAX ? 0 : i;
+            if (probe_d)
+                probe_d[q] = v;
+        } else {
+            part_d[q * splits + split] = v;
+            part_i[q * splits + split] = i;
+        }
+    }
+}
+
+// The splits' minima of each query, in split order (one thread per query).
+__global__ __launch_bounds__(256) void coarse_argmin_merge_kernel(
+    const float *__restrict__ part_d, const int32_t *__restrict__ part_i, int64_t nq, int splits,
+    int32_t *__restrict__ probes, float *__restrict__ probe_d)
+{
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= nq)
+        return;
+    float v = part_d[q * splits];
+    int32_t i = part_i[q * splits];
+    for (int s = 1; s < splits; ++s)
+        argmin_take(v, i, part_d[q * splits + s], part_i[q * splits + s]);
+    probes[q] = i == INT32_MAX ? 0 : i;
+    if (probe_d)
+        probe_d[q] = v;
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -345,8 +530,29 @@ __global__ void coarse_bound_init_kernel(uint32_t *__restrict__ qbound, int64_t 
         qbound[i] = float_order_key(INFINITY);
 }
 
+// nprobe = 1: 64 queries per workgroup (two row groups per wave) while the
+// two A operands fit the registers (K-steps <= 16), else 32; the split keeps
+// about four rounds of two resident workgroups per CU.
+static void argmin_shape(int64_t nq, int nblk, int d4, int *rg, int *splits)
+{
+    *rg = d4 <= 16 ? 4 : 2;
+    const int64_t wgs = (nq + 16 * *rg - 1) / (16 * *rg);
+    const int ntile = (nblk + 3) / 4;
+    const int64_t want = (int64_t)coarse_cu_count() * 8;
+    int s = (int)((want + wgs - 1) / wgs);
+    s = s < 1 ? 1 : s;
+    s = s > ntile ? ntile : s;
+    s = s > 64 ? 64 : s;
+    *splits = s;
+}
+
 size_t coarse_ws_bytes(const DeviceIndex &ix, int64_t nq, int nprobe)
 {
+    if (nprobe == 1 && ix.d4 <= 32) {
+        int rg, splits;
+        argmin_shape(nq, ix.nblk, ix.d4, &rg, &splits);
+        return splits > 1 ? (size_t)nq * splits * 8 : 0;
+    }
     int nw = 1;
     while (nw * 64 < nprobe)
         nw *= 2;
@@ -426,6 +632,51 @@ static hipError_t coarse_mfma_k(const DeviceIndex &ix, const float *queries, int
     }
 }
 
+template <int RG, int RPW, int KD>
+static hipError_t coarse_argmin_variant(const DeviceIndex &ix, const float *queries, int64_t nq,
+                                        int splits, void *ws, int32_t *probes, float *probe_d,
+                                        hipStream_t stream, bool ip)
+{
+    constexpr int TQ = 16 * RG;
+    const size_t lds = (size_t)TQ * (4 * KD + 1) * 4 + TQ * 4 + TQ * 4 * 8;
+    float *part_d = static_cast<float *>(ws);
+    int32_t *part_i = reinterpret_cast<int32_t *>(part_d + (size_t)nq * splits);
+    const dim3 grid((unsigned)((nq + TQ - 1) / TQ), (unsigned)splits);
+    hipLaunchKernelGGL((coarse_argmin_kernel<RG, RPW, KD>), grid, dim3(256 * RG / RPW), lds,
+                       stream, queries, nq, ix.d, ix.nblk, ix.cblk, ix.cnorm_pad, splits, part_d,
+                       part_i, probes, probe_d, ip ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1)
+        return e;
+    hipLaunchKernelGGL(coarse_argmin_merge_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256),
+                       0, stream, part_d, part_i, nq, splits, probes, probe_d);
+    return hipGetLastError();
+}
+
+static hipError_t launch_coarse_argmin(const DeviceIndex &ix, const float *queries, int64_t nq,
+                                       void *ws, int32_t *probes, float *probe_d,
+                                       hipStream_t stream, bool ip)
+{
+    int rg, splits;
+    argmin_shape(nq, ix.nblk, ix.d4, &rg, &splits);
+    switch (ix.d4) {
+    case 8:
+        return coarse_argmin_variant<4, 2, 8>(ix, queries, nq, splits, ws, probes, probe_d,
+                                              stream, ip);
+    case 16:
+        return coarse_argmin_variant<4, 2, 16>(ix, queries, nq, splits, ws, probes, probe_d,
+                                               stream, ip);
+    case 24:
+        return coarse_argmin_variant<2, 1, 24>(ix, queries, nq, splits, ws, probes, probe_d,
+                                               stream, ip);
+    case 32:
+        return coarse_argmin_variant<2, 1, 32>(ix, queries, nq, splits, ws, probes, probe_d,
+                                               stream, ip);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
                          void *ws, int32_t *probes, float *probe_d, hipStream_t stream,
                          bool ip)
@@ -435,6 +686,8 @@ hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq
     int nw = 1;
     while (nw * 64 < nprobe)
         nw *= 2;
+    if (nprobe == 1 && ix.d4 <= 32)
+        return launch_coarse_argmin(ix, queries, nq, ws, probes, probe_d, stream, ip);
     // the matrix-core form keeps a tile's B operand in registers (d up to 128)
     // and four register top-k per wave (nprobe up to 128)
     if (nw > 2 || ix.d4 > 32)

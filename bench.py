@@ -306,7 +306,7 @@ def bench_encode(args):
         f"encode {encode_ms:.3f} ms")
     if coarse_ms >= encode_ms:
         roof = {"bound": "mfma", "achieved": coarse_flops / (coarse_ms * 1e-3) / 1e12,
-                "kernel": "coarse_mfma_kernel (nprobe 1)", "kernel_ms": coarse_ms,
+                "kernel": "coarse_argmin_kernel (nprobe 1)", "kernel_ms": coarse_ms,
                 "algorithmic_flops_per_launch": coarse_flops}
     else:
         roof = {"bound": "alu", "achieved": encode_flops / (encode_ms * 1e-3) / 1e12,
