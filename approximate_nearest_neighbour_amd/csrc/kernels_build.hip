@@ -220,15 +220,27 @@ __global__ void iota_kernel(int32_t *__restrict__ p, int64_t n)
         p[i] = (int32_t)i;
 }
 
-__global__ void list_count_kernel(const int32_t *__restrict__ lists, int64_t n, int nlist,
-                                  uint32_t *__restrict__ counts)
+// Entries per list from the sorted list numbers: the distance between the
+// first positions holding a number >= l and >= l + 1 (binary searches; one
+// thread per list, no contended counters).
+__global__ void list_count_sorted_kernel(const int32_t *__restrict__ keys, int64_t n, int nlist,
+                                         uint32_t *__restrict__ counts)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) {
-        const int l = lists[i];
-        if ((unsigned)l < (unsigned)nlist)
-            atomicAdd(counts + l, 1u);
-    }
+    const int l = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (l >= nlist)
+        return;
+    auto first_at_least = [&](int v) {
+        int64_t lo = 0, hi = n;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (keys[mid] < v)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        return lo;
+    };
+    counts[l] = (uint32_t)(first_at_least(l + 1) - first_at_least(l));
 }
 
 // Position p of the layout takes entry perm[p]: its code row and its id (the
@@ -262,20 +274,21 @@ hipError_t launch_list_layout(const int32_t *lists, int64_t n, int nlist, int m,
                                                   perm_in, perm_out, (int)n, 0, bits, stream);
     const unsigned blocks = (unsigned)((n + 255) / 256);
     const unsigned cblocks = (unsigned)((nlist + 255) / 256);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(cblocks), dim3(256), 0, stream, counts,
-                       (int64_t)nlist);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || n == 0)
-        return e;
-    hipLaunchKernelGGL(list_count_kernel, dim3(blocks), dim3(256), 0, stream, lists, n, nlist,
-                       counts);
+    if (n == 0) {
+        hipLaunchKernelGGL(zero_u32_kernel, dim3(cblocks), dim3(256), 0, stream, counts,
+                           (int64_t)nlist);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(iota_kernel, dim3(blocks), dim3(256), 0, stream, perm_in, n);
-    if ((e = hipGetLastError()) != hipSuccess)
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
         return e;
     e = hipcub::DeviceRadixSort::SortPairs(sort_tmp, *sort_tmp_bytes, lists, keys_out, perm_in,
                                            perm_out, (int)n, 0, bits, stream);
     if (e != hipSuccess)
         return e;
+    hipLaunchKernelGGL(list_count_sorted_kernel, dim3(cblocks), dim3(256), 0, stream, keys_out, n,
+                       nlist, counts);
     hipLaunchKernelGGL(gather_entries_kernel, dim3(blocks), dim3(256), 0, stream, perm_out, n, m,
                        codes_in, ids_in, codes_out, ids_out);
     return hipGetLastError();
