@@ -508,19 +508,36 @@ hipError_t launch_centroid_blocks(const DeviceIndex &ix, hipStream_t stream)
 
 // Row groups per workgroup (16 queries each) and the centroid split: many
 // centroids -> 4 row groups (fewer passes over the centroid array) when the
-// registers allow it (1024 threads leave 128 per lane); the split keeps
-// about 4 workgroup-waves per SIMD busy.
+// registers allow it (1024 threads leave 128 per lane).  The split starts
+// from about four rounds of workgroups over the CUs (one 16-wave workgroup
+// resident per CU); a last round that fills only part of the chip costs as
+// much as a full one, so among s0 .. 2 s0 splits the one with the fewest
+// rounds x tiles per workgroup is taken (1% per extra split against it: more
+// splits mean more selection and merge work).
 static void coarse_shape(int64_t nq, int nblk, int d4, int *rg, int *splits)
 {
     *rg = nblk >= 1024 && d4 <= 24 ? 4 : 2;
     const int64_t wgs = (nq + 16 * *rg - 1) / (16 * *rg);
     const int ntile = (nblk + 3) / 4;
-    const int64_t want = (int64_t)coarse_cu_count() * 4; // one resident per CU, ~4 waves of workgroups
-    int s = (int)((want + wgs - 1) / wgs);
-    s = s < 1 ? 1 : s;
-    s = s > ntile ? ntile : s;
-    s = s > 64 ? 64 : s;
-    *splits = s;
+    const int64_t slots = coarse_cu_count();
+    const int smax = ntile < 64 ? ntile : 64;
+    int s0 = (int)((slots * 4 + wgs - 1) / wgs);
+    s0 = s0 < 1 ? 1 : s0;
+    s0 = s0 > smax ? smax : s0;
+    auto cost = [&](int s) {
+        const int64_t rounds = (wgs * s + slots - 1) / slots;
+        return (double)rounds * ((ntile + s - 1) / s) * (1.0 + 0.01 * (s - s0));
+    };
+    int best = s0;
+    double bc = cost(s0);
+    for (int s = s0 + 1; s <= 2 * s0 && s <= smax; ++s) {
+        const double c = cost(s);
+        if (c < bc) {
+            bc = c;
+            best = s;
+        }
+    }
+    *splits = best;
 }
 
 __global__ void coarse_bound_init_kernel(uint32_t *__restrict__ qbound, int64_t nq)
