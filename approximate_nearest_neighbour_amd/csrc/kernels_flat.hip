@@ -627,9 +627,31 @@ static hipError_t gemm_variant(const FlatDevice &fx, const uint16_t *q, int64_t 
             return e;
     }
     const int64_t qg = (nq + TQ - 1) / TQ;
-    // about 10 workgroups per CU in all (2-3 resident per CU)
-    int64_t splits = ((int64_t)flat_cu_count() * 10 + qg - 1) / qg;
-    splits = splits < 1 ? 1 : splits > p.nseg ? p.nseg : splits;
+    // about 10 workgroups per CU in all; a last round of workgroups that
+    // fills only part of the chip costs as much as a full one, so among half
+    // to twice that many segment splits the one with the fewest rounds x
+    // segments per workgroup is taken (rounds from the resident workgroups
+    // per CU the runtime reports; ties to fewer splits)
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    const int64_t resident = (int64_t)per_cu * flat_cu_count();
+    int64_t s0 = ((int64_t)flat_cu_count() * 10 + qg - 1) / qg;
+    s0 = s0 < 1 ? 1 : s0 > p.nseg ? p.nseg : s0;
+    auto cost = [&](int64_t sp) {
+        return (double)((qg * sp + resident - 1) / resident) * (double)((p.nseg + sp - 1) / sp) *
+               (1.0 + 0.002 * (double)sp);
+    };
+    int64_t splits = s0;
+    double best = cost(s0);
+    for (int64_t sp = s0 / 2 > 1 ? s0 / 2 : 1; sp <= 2 * s0 && sp <= p.nseg; ++sp) {
+        const double c = cost(sp);
+        if (c < best) {
+            best = c;
+            splits = sp;
+        }
+    }
     hipLaunchKernelGGL(kern, dim3((unsigned)qg, (unsigned)splits), dim3(256), lds, stream, q, nq,
                        fx.d, fx.vec, fx.norms, fx.n, p.ntile, p.seg, p.nseg, (int)splits, slots,
                        p.nslot, tuq, p.cap, cnt, cand_d, cand_p);
