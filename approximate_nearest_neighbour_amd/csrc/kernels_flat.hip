@@ -346,27 +346,35 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *red)
 }
 
 constexpr int kKthBins = 2048; // 8 per thread
+// slot minima per thread, held in registers: nslot <= 256 * kKthPer = 16,128
+// (the plan keeps nslot <= 16,000)
+constexpr int kKthPer = 63;
 
 // Pass 2: per query an upper bound v of the k-th smallest of its nslot slot
 // minima with at least k minima <= v: a 2048-bin histogram of the finite
-// minima over [min, max] (count and largest member per bin); v = the largest
-// member of the bins up to the one that holds the k-th.  Then the collect
-// threshold tu = v + slack (+inf when fewer than k minima are finite).
+// minima over [min, max]; v = the largest minimum in the bins up to the one
+// that holds the k-th.  Then the collect threshold tu = v + slack (+inf when
+// fewer than k minima are finite).  Each thread reads its minima once and
+// keeps them in registers for the histogram and the final maximum.
 __global__ __launch_bounds__(256) void flat_kth_kernel(const uint16_t *__restrict__ queries, int d,
                                                        const float *__restrict__ slots,
                                                        int64_t nslot, int k, float ymax,
                                                        float *__restrict__ tuq)
 {
-    __shared__ uint32_t cnt[kKthBins], bmax[kKthBins];
+    __shared__ uint32_t cnt[kKthBins];
     __shared__ float redf[8];
     __shared__ uint32_t redu[8];
     const int64_t q = blockIdx.x;
     const int tid = threadIdx.x;
     const float *sq = slots + q * nslot;
+    float vals[kKthPer];
     float lo = INFINITY, hi = -INFINITY;
     uint32_t fin = 0;
-    for (int64_t i = tid; i < nslot; i += 256) {
-        const float v = sq[i];
+#pragma unroll
+    for (int j = 0; j < kKthPer; ++j) {
+        const int64_t i = tid + (int64_t)256 * j;
+        const float v = i < nslot ? sq[i] : INFINITY;
+        vals[j] = v;
         if (v < INFINITY) {
             lo = fminf(lo, v);
             hi = fmaxf(hi, v);
@@ -383,20 +391,17 @@ __global__ __launch_bounds__(256) void flat_kth_kernel(const uint16_t *__restric
         v = lo;
     } else {
         const float scale = kKthBins / (hi - lo);
-        for (int b = tid; b < kKthBins; b += 256) {
+        auto bin_of = [&](float x) {
+            int b = (int)((x - lo) * scale);
+            return b < 0 ? 0 : b >= kKthBins ? kKthBins - 1 : b;
+        };
+        for (int b = tid; b < kKthBins; b += 256)
             cnt[b] = 0;
-            bmax[b] = 0;
-        }
         __syncthreads();
-        for (int64_t i = tid; i < nslot; i += 256) {
-            const float x = sq[i];
-            if (x < INFINITY) {
-                int b = (int)((x - lo) * scale);
-                b = b < 0 ? 0 : b >= kKthBins ? kKthBins - 1 : b;
-                atomicAdd(&cnt[b], 1u);
-                atomicMax(&bmax[b], float_order_key(x));
-            }
-        }
+#pragma unroll
+        for (int j = 0; j < kKthPer; ++j)
+            if (vals[j] < INFINITY)
+                atomicAdd(&cnt[bin_of(vals[j])], 1u);
         __syncthreads();
         // thread t owns bins 8t..8t+7: local sums, block prefix, find the bin
         uint32_t local = 0;
@@ -424,13 +429,12 @@ __global__ __launch_bounds__(256) void flat_kth_kernel(const uint16_t *__restric
         }
         __syncthreads();
         const int bsel = (int)redu[4];
-        // largest member of bins 0..bsel
+        // largest finite minimum in bins 0..bsel
         float m = -INFINITY;
-        for (int j = 0; j < 8; ++j) {
-            const int b = 8 * tid + j;
-            if (b <= bsel && cnt[b])
-                m = fmaxf(m, float_from_order_key(bmax[b]));
-        }
+#pragma unroll
+        for (int j = 0; j < kKthPer; ++j)
+            if (vals[j] < INFINITY && bin_of(vals[j]) <= bsel)
+                m = fmaxf(m, vals[j]);
         v = block_max(m, redf);
     }
     if (tid == 0) {
@@ -731,6 +735,8 @@ hipError_t launch_flat_stage(const FlatDevice &fx, const uint16_t *q, int64_t nq
         }
     }
     case 1: { // k-th slot minimum -> collect threshold
+        if (p.nslot > (int64_t)256 * kKthPer)
+            return hipErrorInvalidValue;
         if (p.ntile == 0)
             return hipSuccess;
         hipLaunchKernelGGL(flat_kth_kernel, dim3((unsigned)nq), dim3(256), 0, stream, q, fx.d,
