@@ -177,7 +177,8 @@ ivfpq_status ivfpq_coarse_ex(const ivfpq_index *idx, const float *queries_dev, i
  *
  * vectors_dev [n][d] float32 row-major.  lists_dev [n] int32 receives the
  * list of smallest |x - c_l|^2 (the coarse distances of a search, float32
- * through the norm expansion; equal distances to the smaller list number);
+ * through the norm expansion; with d <= 128 equal distances go to the
+ * smaller list number, above that to any of the tied lists);
  * codes_dev [n][m] uint8 receives, for each sub-quantizer j, the codeword v
  * of smallest F_j(v) = sum_s (r[j dsub + s] - C_j[v][s])^2 with r = x - c_list
  * (float32, evaluated as the search evaluates its tables; ties to the smaller
@@ -197,7 +198,8 @@ ivfpq_status ivfpq_assign_encode_ex(const ivfpq_index *idx, const float *vectors
  * one sub-vector to train a sub-quantizer's 256 codewords).  Each of `iters`
  * iterations assigns every vector to its nearest center (the coarse step with
  * nprobe = 1: squared L2 through the float32 norm expansion on the matrix
- * cores, equal distances to the smaller center number) and then moves every center to the mean of its vectors (sums in
+ * cores; with d <= 128 equal distances go to the smaller center number)
+ * and then moves every center to the mean of its vectors (sums in
  * double precision, the mean rounded to float32); a center with no vector
  * keeps its value.
  *
