@@ -430,3 +430,32 @@ def test_build_and_encode_edge_shapes(dev, nlist, d, m, n):
     assert np.array_equal(got["ids"], order)
     assert np.array_equal(got["codes"], codes[order])
     ix.close()
+
+
+@pytest.mark.slow
+def test_build_fullsize_1m(dev):
+    # all 1M vectors of the 1M x 128 workload built into an index on the
+    # device (the benchmark's configuration): the layout must be exactly the
+    # stable list-major order of the device's own assignment and codes, and
+    # searches on the built index must match the oracle's on that index
+    say("build full size: 1M x 128, nlist 1024, m 16")
+    w = G.gmm1m(keep_vectors=True)
+    lists, codes = gpu_encode(w.index, w.vectors)
+    ix = gpu_build(w.vectors, w.index.centroids, w.index.codebooks)
+    got = A.ivfpq_index_export(ix)
+    order = np.argsort(lists, kind="stable")
+    assert np.array_equal(got["list_sizes"], np.bincount(lists, minlength=len(w.index.list_sizes)))
+    assert np.array_equal(got["ids"], order)
+    assert np.array_equal(got["codes"], codes[order])
+    say("layout exact; searching the built index")
+    q = w.queries[:12]
+    s, i, p = A.ivfpq_search_ex(ix, torch.from_numpy(q).cuda(), w.nprobe, w.k,
+                                return_probes=True)
+    torch.cuda.synchronize()
+    built = G.HostIndex(got["centroids"], got["codebooks"], got["list_sizes"].astype(np.int64),
+                        got["codes"], got["ids"])
+    rep = check.compare_search(built, q, w.nprobe, w.k, s.cpu().numpy(), i.cpu().numpy(),
+                               p.cpu().numpy())
+    say("search parity on the built index", rep.summary())
+    ix.close()
+    assert rep.ok(), rep.failures[:5]
