@@ -1,7 +1,8 @@
 """Full-size IVF-PQ parity: the benchmark shapes (1M x 128 / m 16, 10M x 96 /
 m 32, 1B entries / m 8 with Zipf lists), all 10,000 queries searched in the
-launch configuration the benchmark times, a sample of the queries checked
-against the oracle (exact, double precision) one by one."""
+launch configuration the benchmark times (the 10M and 1B shapes also with the
+inner-product metric), a sample of the queries checked against the oracle
+(exact, double precision) one by one."""
 import time
 
 import numpy as np
@@ -30,29 +31,35 @@ def sample_rows(nq, count, seed):
     return np.array(sorted(rows))
 
 
-def search_and_check(A, w, lut="f32", sample=16, giant=0):
-    """giant: also check this many rows whose probes include a list of more
+def search_and_check(A, w, runs=(("f32", "l2"),), sample=16, giant=0):
+    """runs: (table type, metric) pairs searched on one upload of the index.
+    giant: also check this many rows whose probes include a list of more
     than 10^6 entries (the longest lists of a skewed index)."""
     t = time.time()
     ix = A.ivfpq_load_index_host(w.index, device=0)
     q = torch.from_numpy(w.queries).cuda()
-    d, i, p = A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=lut, return_probes=True)
-    torch.cuda.synchronize()
-    print(f"  {w.name} lut={lut}: searched {len(w.queries)} queries "
-          f"({time.time() - t:.1f} s incl. upload)", flush=True)
-    rows = sample_rows(len(w.queries), sample, 11)
-    if giant:
-        big = np.flatnonzero(np.asarray(w.index.list_sizes) > 1_000_000)
-        hits = np.flatnonzero(np.isin(p.cpu().numpy(), big).any(axis=1))
-        print(f"  {len(hits)} queries probe one of the {len(big)} lists above 10^6 entries; "
-              f"checking {min(giant, len(hits))} of them", flush=True)
-        rows = np.unique(np.concatenate([rows, hits[:giant]]))
-    rep = check.compare_search(w.index, w.queries[rows], w.nprobe, w.k, d.cpu().numpy()[rows],
-                               i.cpu().numpy()[rows], p.cpu().numpy()[rows],
-                               lut_mode=O.LUT_F16 if lut == "f16" else O.LUT_F64)
-    print(f"  parity {rep.summary()}", flush=True)
+    print(f"  {w.name}: index uploaded ({time.time() - t:.1f} s)", flush=True)
+    for lut, metric in runs:
+        t = time.time()
+        d, i, p = A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=lut, metric=metric,
+                                    return_probes=True)
+        torch.cuda.synchronize()
+        print(f"  {w.name} lut={lut} metric={metric}: searched {len(w.queries)} queries "
+              f"({time.time() - t:.1f} s)", flush=True)
+        rows = sample_rows(len(w.queries), sample, 11)
+        if giant:
+            big = np.flatnonzero(np.asarray(w.index.list_sizes) > 1_000_000)
+            hits = np.flatnonzero(np.isin(p.cpu().numpy(), big).any(axis=1))
+            print(f"  {len(hits)} queries probe one of the {len(big)} lists above 10^6 "
+                  f"entries; checking {min(giant, len(hits))} of them", flush=True)
+            rows = np.unique(np.concatenate([rows, hits[:giant]]))
+        mode = O.IP if metric == "ip" else O.LUT_F16 if lut == "f16" else O.LUT_F64
+        rep = check.compare_search(w.index, w.queries[rows], w.nprobe, w.k,
+                                   d.cpu().numpy()[rows], i.cpu().numpy()[rows],
+                                   p.cpu().numpy()[rows], lut_mode=mode)
+        print(f"  parity {rep.summary()}", flush=True)
+        assert rep.ok(), rep.failures[:5]
     ix.close()
-    assert rep.ok(), rep.failures[:5]
 
 
 def test_fullsize_gmm_1m(A):
@@ -72,15 +79,17 @@ def test_fullsize_10m_shape(A):
     index = G.random_index(rng, nlist, 96, 32, sizes, codebook_scale=0.3)
     queries = rng.standard_normal((10_000, 96), dtype=np.float32)
     w = G.Workload("ivfpq_shape_n10m_d96_m32_nlist4096", index, queries, 64, 100)
-    search_and_check(A, w, "f32")
-    search_and_check(A, w, "f16")
+    # float32 and binary16 tables, and the inner-product metric
+    search_and_check(A, w, runs=(("f32", "l2"), ("f16", "l2"), ("f32", "ip")))
 
 
 def test_fullsize_zipf_1b(A):
     print("full size: 1B entries, d 96, nlist 262144 (Zipf), m 8, nprobe 128, k 100",
           flush=True)
     w = G.zipf_workload()
-    search_and_check(A, w, giant=2)
+    # squared L2 and the inner-product metric (the lists were built for L2,
+    # which the metric does not assume)
+    search_and_check(A, w, runs=(("f32", "l2"), ("f32", "ip")), giant=2)
 
 
 def test_fullsize_flat_bf16(A):
