@@ -87,9 +87,9 @@ def test_fullsize_zipf_1b(A):
     print("full size: 1B entries, d 96, nlist 262144 (Zipf), m 8, nprobe 128, k 100",
           flush=True)
     w = G.zipf_workload()
-    # squared L2 and the inner-product metric (the lists were built for L2,
-    # which the metric does not assume)
-    search_and_check(A, w, runs=(("f32", "l2"), ("f32", "ip")), giant=2)
+    # squared L2 (float32 and binary16 tables) and the inner-product metric
+    # (the lists were built for L2, which the metric does not assume)
+    search_and_check(A, w, runs=(("f32", "l2"), ("f16", "l2"), ("f32", "ip")), giant=2)
 
 
 def test_fullsize_flat_bf16(A):
