@@ -3,6 +3,7 @@
 // per-kernel event timing.  Declarations and conventions: include/ivfpq.h.
 #include "../../include/ivfpq.h"
 #include "internal.hpp"
+#include "plan.hpp"
 
 #include <hip/hip_runtime.h>
 
@@ -32,13 +33,23 @@ ivfpq_status ok()
     return IVFPQ_OK;
 }
 
-// Test hook: IVFPQ_TEST_FAIL_ALLOC=n makes the n-th device allocation of the
-// process fail (1-based), to exercise the out-of-memory paths.
+// Test hook: IVFPQ_TEST_FAIL_ALLOC=n makes the n-th device allocation
+// (1-based) counted from the moment the variable took its current value fail,
+// to exercise the out-of-memory paths.  The count restarts whenever the
+// variable's value changes (unset counts as a value), so a long-running test
+// process can aim at "the n-th allocation from now"; the value is read as its
+// leading integer, so "3:a" and "3:b" both mean 3 and still restart the count.
 int g_alloc_count = 0;
+std::string g_alloc_env;
 
 hipError_t dev_alloc(void **p, size_t bytes)
 {
     const char *env = std::getenv("IVFPQ_TEST_FAIL_ALLOC");
+    const std::string now = env ? env : "";
+    if (now != g_alloc_env) {
+        g_alloc_env = now;
+        g_alloc_count = 0;
+    }
     ++g_alloc_count;
     if (env && std::atoi(env) == g_alloc_count) {
         *p = nullptr;
@@ -82,19 +93,6 @@ int kw_of(int k)
     return kw;
 }
 
-// Work items per query: as many as a 1 GiB partial top-k buffer holds, 2 to
-// 64.  With heavy-tailed list sizes a query that probes the largest lists
-// holds many times the average work; cutting it into more items keeps the
-// largest item small against the work per workgroup (the persistent
-// workgroups otherwise wait on one long item at the end).
-uint32_t items_per_query(int64_t nq, int k)
-{
-    const double per = (1024.0 * 1024 * 1024) / ((double)(nq > 0 ? nq : 1) * kw_of(k) * 8);
-    if (per < 2)
-        return 2;
-    return per > 64 ? 64u : (uint32_t)per;
-}
-
 } // namespace
 
 struct ivfpq_index {
@@ -108,8 +106,7 @@ struct ivfpq_index {
     bool profiling = false;
     int prof_max = 0;
     int prof_calls = 0;
-    int64_t prof_entries = 0;
-    int64_t prof_items = 0;
+    unsigned long long *prof_counts = nullptr; // device: [entries scanned, work items]
     std::vector<EventPair> prof_events; // [call][stage]
     std::vector<int> prof_used;         // [call][stage] 0/1
     std::vector<uint32_t> host_off;     // list offsets (host copy)
@@ -202,6 +199,7 @@ void release(ivfpq_index *ix)
     (void)hipFree(d.ids);
     (void)hipFree(d.t1);
     (void)hipFree(ix->ws);
+    (void)hipFree(ix->prof_counts);
     for (auto &e : ix->prof_events) {
         if (e.start)
             (void)hipEventDestroy(e.start);
@@ -600,7 +598,7 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
     // workspace: probes | plan arrays | partial top-k of the work items
     SearchPlan pl;
     pl.target = p->chunk_len > 0 ? (uint32_t)p->chunk_len : kDefaultChunk;
-    pl.imax = items_per_query(nq, p->k);
+    pl.imax = items_per_query(nq, kw_of(p->k));
     pl.max_items = nq * (int64_t)pl.imax;
     const size_t kw = (size_t)kw_of(p->k);
     size_t off = 0;
@@ -628,6 +626,8 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
     pl.counter = reinterpret_cast<uint32_t *>(ws + o_counter);
     pl.part_d = reinterpret_cast<float *>(ws + o_pd);
     pl.part_p = reinterpret_cast<uint32_t *>(ws + o_pp);
+    const bool recording = idx->profiling && idx->prof_calls < idx->prof_max;
+    pl.prof = recording ? idx->prof_counts : nullptr;
 
     prof_record(idx, 0, true, st);
     hipError_t e =
@@ -665,10 +665,8 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
         if (e != hipSuccess)
             return fail(IVFPQ_E_DEVICE, std::string("merge kernel: ") + hipGetErrorString(e));
     }
-    if (idx->profiling && idx->prof_calls < idx->prof_max) {
+    if (recording)
         idx->prof_calls++;
-        idx->prof_items += nq;
-    }
     return ok();
 }
 
@@ -1008,12 +1006,18 @@ ivfpq_status ivfpq_profile_begin(ivfpq_index *idx, int max_calls)
             return fail(IVFPQ_E_DEVICE, "event creation failed");
         idx->prof_events.push_back(e);
     }
+    if (!idx->prof_counts && dev_alloc(reinterpret_cast<void **>(&idx->prof_counts),
+                                       2 * sizeof(unsigned long long)) != hipSuccess) {
+        (void)hipGetLastError();
+        idx->prof_counts = nullptr;
+        return fail(IVFPQ_E_OUT_OF_MEMORY, "profile counter allocation failed");
+    }
+    if (hipMemset(idx->prof_counts, 0, 2 * sizeof(unsigned long long)) != hipSuccess)
+        return fail(IVFPQ_E_DEVICE, "profile counter reset failed");
     idx->prof_used.assign(need, 0);
     idx->profiling = true;
     idx->prof_max = max_calls;
     idx->prof_calls = 0;
-    idx->prof_entries = 0;
-    idx->prof_items = 0;
     return ok();
 }
 
@@ -1048,8 +1052,13 @@ ivfpq_status ivfpq_profile_end(ivfpq_index *idx, ivfpq_timings *out)
         }
     }
     out->calls = idx->prof_calls;
-    out->scanned_entries = idx->prof_entries;
-    out->work_items = idx->prof_items;
+    unsigned long long counts[2] = {0, 0};
+    if (idx->prof_counts && (hipDeviceSynchronize() != hipSuccess ||
+                             hipMemcpy(counts, idx->prof_counts, sizeof counts,
+                                       hipMemcpyDeviceToHost) != hipSuccess))
+        return fail(IVFPQ_E_DEVICE, "profile counter read failed");
+    out->scanned_entries = (int64_t)counts[0];
+    out->work_items = (int64_t)counts[1];
     idx->profiling = false;
     return ok();
 }

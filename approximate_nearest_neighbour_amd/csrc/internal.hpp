@@ -54,6 +54,9 @@ struct SearchPlan {
     uint32_t *qbound = nullptr, *counter = nullptr;
     float *part_d = nullptr;   // [max_items][kw]
     uint32_t *part_p = nullptr; // [max_items][kw]
+    // when not null: [0] += entries of the probed lists, [1] += work items
+    // (profiling)
+    unsigned long long *prof = nullptr;
 };
 
 // Each launcher enqueues on `stream` and returns the launch status.

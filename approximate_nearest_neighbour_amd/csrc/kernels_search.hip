@@ -37,6 +37,7 @@
 // no cancellation, every entry and every sum is a sum of non-negative terms.
 #include "common.hpp"
 #include "internal.hpp"
+#include "plan.hpp"
 
 namespace ivfpq {
 
@@ -52,32 +53,43 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ p
                                                    uint32_t *__restrict__ qchunk,
                                                    uint32_t *__restrict__ qcount,
                                                    uint32_t *__restrict__ qbound,
-                                                   uint32_t *__restrict__ counter)
+                                                   uint32_t *__restrict__ counter,
+                                                   unsigned long long *__restrict__ prof)
 {
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (q == 0)
         *counter = 0;
+    uint64_t e = 0;
+    if (q < nq) {
+        for (int p = 0; p < nprobe; ++p) {
+            const int l = probes[q * nprobe + p];
+            if ((unsigned)l < (unsigned)nlist)
+                e += list_off[l + 1] - list_off[l];
+        }
+    }
+    if (prof) {
+        // entries scanned, one atomic per wave
+        uint64_t w = e;
+#pragma unroll
+        for (int sh = 32; sh >= 1; sh >>= 1)
+            w += __shfl_xor(w, sh);
+        if ((threadIdx.x & 63) == 0 && w)
+            atomicAdd(prof, (unsigned long long)w);
+    }
     if (q >= nq)
         return;
-    uint64_t e = 0;
-    for (int p = 0; p < nprobe; ++p) {
-        const int l = probes[q * nprobe + p];
-        if ((unsigned)l < (unsigned)nlist)
-            e += list_off[l + 1] - list_off[l];
-    }
     const uint32_t total = (uint32_t)e;
-    uint32_t chunk = (total + imax - 1) / imax;
-    chunk = chunk > target ? chunk : target;
-    uint32_t count = (total + chunk - 1) / chunk;
+    const QueryPlan qp = plan_query(total, target, imax);
     qtotal[q] = total;
-    qchunk[q] = chunk;
-    qcount[q] = count > 0 ? count : 1;
+    qchunk[q] = qp.chunk;
+    qcount[q] = qp.count;
     qbound[q] = float_order_key(INFINITY);
 }
 
 // Exclusive prefix sum of qcount into base[0..nq]; one workgroup of 1024.
 __global__ __launch_bounds__(1024) void item_scan_kernel(const uint32_t *__restrict__ qcount,
-                                                         int64_t nq, uint32_t *__restrict__ base)
+                                                         int64_t nq, uint32_t *__restrict__ base,
+                                                         unsigned long long *__restrict__ prof)
 {
     __shared__ uint32_t wsum[16];
     __shared__ uint32_t carry_s;
@@ -103,8 +115,11 @@ __global__ __launch_bounds__(1024) void item_scan_kernel(const uint32_t *__restr
             carry_s = before + incl;
         __syncthreads();
     }
-    if (tid == 0)
+    if (tid == 0) {
         base[nq] = carry_s;
+        if (prof)
+            atomicAdd(prof + 1, (unsigned long long)carry_s);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -415,10 +430,8 @@ void scan_items_kernel(ScanArgs a)
         const int64_t q = lo;
         const uint32_t first = a.item_base[q];
         const uint32_t count = a.item_base[q + 1] - first;
-        const uint32_t chunk = a.qchunk[q];
-        const uint32_t start = (item - first) * chunk;
-        const uint32_t total = a.qtotal[q];
-        const uint32_t stop = start + chunk < total ? start + chunk : total;
+        uint32_t start, stop;
+        item_range(item - first, a.qchunk[q], a.qtotal[q], &start, &stop);
 
         for (int t = tid; t < d; t += THREADS)
             xs[t] = a.queries[q * d + t];
@@ -437,15 +450,12 @@ void scan_items_kernel(ScanArgs a)
                     }
                 }
                 const uint32_t incl = wave_inclusive_sum(sz);
-                const uint32_t lo_e = acc + incl - sz, hi_e = acc + incl;
-                const bool take = sz > 0 && lo_e < stop && hi_e > start;
+                Piece pc;
+                const bool take = piece_of(acc + incl - sz, acc + incl, start, stop, &pc.b, &pc.e);
                 const uint64_t mask = wave_ballot(take);
                 if (take) {
                     const int slot = (int)np + mbcnt64(mask);
-                    Piece pc;
                     pc.list = l;
-                    pc.b = (start > lo_e ? start : lo_e) - lo_e;
-                    pc.e = (stop < hi_e ? stop : hi_e) - lo_e;
                     pieces[slot] = pc;
                 }
                 np += (uint32_t)__popcll(mask);
@@ -758,9 +768,7 @@ static hipError_t scan_variant(const ScanArgs &a, const SearchPlan &pl, hipStrea
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256 * G, lds) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
-    int64_t grid = (int64_t)per_cu * cu_count();
-    if (grid > pl.max_items)
-        grid = pl.max_items > 0 ? pl.max_items : 1;
+    const int64_t grid = scan_grid(per_cu, cu_count(), pl.max_items);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256 * G), lds, stream, a);
     return hipGetLastError();
 }
@@ -862,12 +870,12 @@ hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     const unsigned blocks = (unsigned)((s.nq + 255) / 256);
     hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(256), 0, stream, s.probes, s.nprobe, s.nq,
                        ix.nlist, ix.list_off, pl.target, pl.imax, pl.qtotal, pl.qchunk, pl.qcount,
-                       pl.qbound, pl.counter);
+                       pl.qbound, pl.counter, pl.prof);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(item_scan_kernel, dim3(1), dim3(1024), 0, stream, pl.qcount, s.nq,
-                       pl.item_base);
+                       pl.item_base, pl.prof);
     return hipGetLastError();
 }
 

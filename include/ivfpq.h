@@ -16,12 +16,17 @@
  * Conventions, all calls:
  *  - every call returns an ivfpq_status; no exception crosses the ABI;
  *    ivfpq_last_error() gives a message for the last failing call on the
- *    calling thread;
+ *    calling thread (an unsupported request is an explicit error, not a
+ *    silent fallback: "Support HNSW Search using GPUs", API section);
  *  - distances are squared L2, smaller is better, each result row sorted
  *    ascending; a row with fewer than k candidates is padded with
- *    (+INFINITY, -1);
- *  - arguments are validated on the host before any device work; on error
- *    the output buffers are left unspecified;
+ *    (+INFINITY, -1) (the +infinity sentinel of the k-selection section of
+ *    "Billion-scale similarity search with GPUs"; the -1 id of the sentinel
+ *    handling in "Support HNSW Search using GPUs", Search kernel section);
+ *  - arguments are validated on the host before any device work ("Support
+ *    HNSW Search using GPUs", graph conversion section: the structure is
+ *    checked before the GPU dereferences it); on error the output buffers
+ *    are left unspecified;
  *  - inputs must be finite (documented precondition, not checked);
  *  - one search at a time per index handle (the handle owns a workspace).
  *
@@ -75,10 +80,16 @@ typedef enum {
     IVFPQ_MODE_SCAN_ONLY = 1
 } ivfpq_mode;
 
-/* Search parameters.  nprobe in [1, nlist]; k in [1, 1024]; lut selects the
- * table precision (float32, or float32 computed then stored as IEEE binary16
- * round-to-nearest-even; sums are float32 in both).  chunk_len: maximum
- * entries one work item scans (0 = automatic). */
+/* Search parameters ("Billion-scale similarity search with GPUs", IVFADC
+ * section: nprobe is the number tau of lists probed, k the results kept; the
+ * k-selection section bounds k near 1024).  nprobe in [1, nlist]; k in
+ * [1, 1024]; lut selects the table precision (float32, or float32 computed
+ * then stored as IEEE binary16 round-to-nearest-even; sums are float32 in
+ * both).  chunk_len: the target number of entries of one scan work item
+ * (0 = automatic, 131072).  It is a minimum, not a cap: a query whose probed
+ * lists hold E entries gets ceil(E / max(chunk_len, ceil(E / imax))) items,
+ * imax (2..64) chosen from nq and k, so long queries get larger items.  The
+ * result does not depend on it. */
 typedef struct {
     int32_t nprobe;
     int32_t k;
@@ -120,15 +131,23 @@ typedef struct {
     double scan_ms;     /* LUT + code scan + first-pass select */
     double merge_ms;    /* cross-item merge + id gather */
     double total_ms;    /* first kernel start to last kernel end */
-    int64_t scanned_entries; /* entries scanned (sum over calls) */
-    int64_t work_items;      /* scan work items (sum over calls) */
+    int64_t scanned_entries; /* entries of the probed lists, i.e. entries scanned
+                                (sum over calls; counted on the device) */
+    int64_t work_items;      /* scan work items (sum over calls; counted on the device) */
 } ivfpq_timings;
 
-/* Host-only check of an index file's header and size (no GPU needed).
- * IVFPQ_E_IO if unreadable, IVFPQ_E_FORMAT if malformed or truncated. */
+/* Host-only check of an index file's header and size (no GPU needed): the
+ * validation "Support HNSW Search using GPUs" (graph conversion section) asks
+ * for before a structure reaches the device.  The file layout is the index
+ * of "Custom 8-bit floating point value format for reducing shared memory
+ * bank conflict in ANN search", IVFPQ section, index-building step 4 (lists,
+ * codes, codebooks saved).  IVFPQ_E_IO if unreadable, IVFPQ_E_FORMAT if the
+ * magic, nbits, d % m, the list sizes or the length is wrong. */
 ivfpq_status ivfpq_validate_index_file(const char *path);
 
-/* Host-only check of host index arrays (no GPU needed). */
+/* Host-only check of host index arrays (no GPU needed), as
+ * ivfpq_validate_index_file: IVFPQ_E_INVALID_ARG for a NULL pointer,
+ * IVFPQ_E_FORMAT for a bad shape or list sizes that do not sum to ntotal. */
 ivfpq_status ivfpq_validate_host_index(const ivfpq_host_index *src);
 
 /* Read an index file and upload it to GPU `device`.  Codes and centroids stay
@@ -140,19 +159,34 @@ ivfpq_status ivfpq_load_index(const char *path, int device, ivfpq_index **out);
 /* As ivfpq_load_index, from host arrays (copied). */
 ivfpq_status ivfpq_load_index_host(const ivfpq_host_index *src, int device, ivfpq_index **out);
 
-/* Release the handle and its device memory.  NULL is allowed. */
+/* Release the handle and its device memory.  NULL is allowed.  The device
+ * index is search-only ("Support HNSW Search using GPUs", API section: the
+ * GPU index is built from a host index and not copied back into one); the
+ * handle owns every device allocation it made, and this frees all of them. */
 void ivfpq_free_index(ivfpq_index *idx);
 
+/* Shape and device footprint of a loaded index (host-only read of the
+ * handle): d, nlist, m, nbits, ntotal, the longest list, the device and the
+ * bytes of device memory the handle holds.  IVFPQ_E_INVALID_ARG for NULL. */
 ivfpq_status ivfpq_index_info(const ivfpq_index *idx, ivfpq_info *out);
 
-/* Blocking search with host buffers: queries [nq][d] float32 row-major in,
+/* Blocking search with host buffers (the search of "Custom 8-bit floating
+ * point value format for reducing shared memory bank conflict in ANN search",
+ * IVFPQ section, search steps 1-5): queries [nq][d] float32 row-major in,
  * distances [nq][k] float32 and ids [nq][k] int64 out.  Copies queries to the
  * device and results back (PCIe included).  nq = 0 is a no-op. */
 ivfpq_status ivfpq_search(const ivfpq_index *idx, const float *queries, int64_t nq, int nprobe,
                           int k, float *distances, int64_t *ids);
 
 /* Asynchronous search with device buffers on `stream` (a hipStream_t; NULL =
- * the null stream).  queries_dev [nq][d] float32, distances_dev [nq][k] float32,
+ * the null stream).  The path of "Billion-scale similarity search with
+ * GPUs", IVFADC section: coarse distances and the nprobe nearest lists, a
+ * table per (query, list), the scan of the lists' codes summing m table
+ * entries per entry, a first k-selection per piece of work and a second one
+ * across a query's pieces; the tables and sums are those of Eq. (1) of the
+ * IVFPQ section of "Custom 8-bit floating point value format for reducing
+ * shared memory bank conflict in ANN search".  params: see
+ * ivfpq_search_params (its metric picks squared L2 or inner product).  queries_dev [nq][d] float32, distances_dev [nq][k] float32,
  * ids_dev [nq][k] int64; probes_dev, when not NULL, receives the probed list
  * numbers [nq][nprobe] int32 in ascending coarse distance.  No host
  * synchronisation happens between the kernels; the call returns once they are
@@ -161,7 +195,10 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *idx, const ivfpq_search_params *
                              const float *queries_dev, int64_t nq, float *distances_dev,
                              int64_t *ids_dev, int32_t *probes_dev, void *stream);
 
-/* The coarse step alone (device buffers, asynchronous): for each query the
+/* The coarse step alone (device buffers, asynchronous; the coarse quantizer
+ * q1 of "Billion-scale similarity search with GPUs", IVFADC section, and
+ * search step 1 of the IVFPQ section of "Custom 8-bit floating point value
+ * format for reducing shared memory bank conflict in ANN search"): for each query the
  * nprobe lists of smallest |x - c_l|^2, ascending: probes_dev [nq][nprobe]
  * int32 and, when not NULL, coarse_dist_dev [nq][nprobe] float32. */
 ivfpq_status ivfpq_coarse_ex(const ivfpq_index *idx, const float *queries_dev, int64_t nq,
@@ -265,8 +302,12 @@ ivfpq_status ivfpq_compute_luts_ex(const ivfpq_index *idx, const float *queries_
 ivfpq_status ivfpq_select_topk_ex(const float *keys_dev, int64_t rows, int64_t n, int k,
                                   float *out_dist_dev, int32_t *out_pos_dev, void *stream);
 
-/* Start summing per-kernel times (HIP events on the search stream, no host
- * synchronisation during searches).  Up to max_calls searches are recorded. */
+/* Measurement support (not part of the search path): start summing
+ * per-kernel times (HIP events on the search stream, no host
+ * synchronisation during searches) and counting the entries and work items
+ * scanned (device counters).  Up to max_calls searches are recorded.
+ * Errors: IVFPQ_E_INVALID_ARG (NULL handle, max_calls outside [1, 100000]),
+ * IVFPQ_E_OUT_OF_MEMORY, IVFPQ_E_DEVICE. */
 ivfpq_status ivfpq_profile_begin(ivfpq_index *idx, int max_calls);
 
 /* Wait for the recorded searches, write the sums to *out, stop recording. */
@@ -320,7 +361,7 @@ ivfpq_status ivfpq_flat_search_bf16(const ivfpq_flat *f, const uint16_t *queries
 ivfpq_status ivfpq_flat_profile_begin(ivfpq_flat *f, int max_calls);
 ivfpq_status ivfpq_flat_profile_end(ivfpq_flat *f, ivfpq_flat_timings *out);
 
-/* ---- measurement support ------------------------------------------------
+/* ---- measurement support ---------------------------------------------- */
 
 /* Reference streaming read for the bandwidth roofline (not part of the search
  * path): reads the `bytes` bytes at data_dev (device memory, 16-byte aligned;
@@ -334,9 +375,13 @@ ivfpq_status ivfpq_stream_read(const void *data_dev, size_t bytes, uint32_t *sin
                                int sink_words, void *stream);
 
 /* Message for the last failing call on this thread ("" if none); valid until
- * the next call on this thread. */
+ * the next call on this thread.  (Errors are reported, never hidden behind a
+ * fallback: "Support HNSW Search using GPUs", API section.)  The string is
+ * owned by the library. */
 const char *ivfpq_last_error(void);
 
+/* A fixed English name of a status code ("unknown status" for a value outside
+ * the enum); a static string owned by the library. */
 const char *ivfpq_status_string(ivfpq_status s);
 
 #ifdef __cplusplus

@@ -360,13 +360,30 @@ def bruteforce_bf16(db_bits, query_bits, k, nthreads=None):
 # recall (two readings of the pages' measures)
 # ---------------------------------------------------------------------------
 
-def recall_1_at_k(found_ids, true_ids):
-    """Fraction of queries whose true nearest neighbour is among the k found."""
-    return float(np.mean([t[0] in set(f.tolist()) for f, t in zip(found_ids, true_ids)]))
+def recall_1_at_k(found_ids, true_ids, n=None):
+    """R@n ("Billion-scale similarity search with GPUs", experiments section):
+    the fraction of queries whose true nearest neighbour (column 0 of
+    true_ids) is among the first n ids found (n defaults to every column of
+    found_ids).  A padding id (-1) never counts."""
+    found = np.asarray(found_ids)
+    true = np.asarray(true_ids)
+    n = found.shape[1] if n is None else n
+    hits = [int(t[0]) >= 0 and int(t[0]) in set(f[:n].tolist()) for f, t in zip(found, true)]
+    return float(np.mean(hits)) if hits else 0.0
 
 
-def recall_k_at_k(found_ids, true_ids):
-    """Mean fraction of the k found that are among the true k nearest."""
-    k = found_ids.shape[1]
-    return float(np.mean([len(set(f.tolist()) & set(t.tolist())) / k
-                          for f, t in zip(found_ids, true_ids)]))
+def recall_k_at_k(found_ids, true_ids, k=None):
+    """The intersection measure of the same section: for each query the
+    number of the first k ids found that are among the true k nearest,
+    divided by k, averaged over the queries (k defaults to every column of
+    found_ids; only the first k columns of true_ids count).  Padding ids (-1)
+    never count."""
+    found = np.asarray(found_ids)
+    true = np.asarray(true_ids)
+    k = found.shape[1] if k is None else k
+    fr = []
+    for f, t in zip(found, true):
+        tk = set(int(v) for v in t[:k].tolist() if v >= 0)
+        fk = set(int(v) for v in f[:k].tolist() if v >= 0)
+        fr.append(len(fk & tk) / k)
+    return float(np.mean(fr)) if fr else 0.0

@@ -585,3 +585,57 @@ def test_ip_checker_accepts_oracle_and_rejects_perturbations():
     pp[2, 0] = int(O.coarse_ip(q[2], idx["centroids"], 8)[0][-1])
     assert not check.compare_search(idx, q, 3, 20, s.astype(np.float32), i, pp,
                                     lut_mode=O.IP).ok()
+
+
+# ---------------------------------------------------------------------------
+# recall measures ("Billion-scale similarity search with GPUs", experiments
+# section: R@n, the fraction of queries whose true nearest neighbour is among
+# the first n results, and the intersection measure, the fraction of the k
+# found that are among the true k nearest), worked by hand
+# ---------------------------------------------------------------------------
+
+# four queries, three ids found each (-1 = padding); the truth lists five
+# neighbours per query, nearest first, so that a measure reading past k
+# columns of the truth or one that tests the wrong membership changes value
+RECALL_FOUND = np.array([[5, 3, 9], [1, 2, 4], [7, 8, 6], [0, -1, -1]])
+RECALL_TRUE = np.array([[3, 5, 2, 9, 4], [9, 1, 2, 4, 0], [8, 6, 7, 1, 2], [4, 0, 1, 2, 3]])
+
+
+def test_recall_at_n_hand_worked():
+    # true nearest: 3, 9, 8, 4.  Found in the first n:
+    #   n = 1: 5, 1, 7, 0        -> none                      -> 0
+    #   n = 2: {5,3} {1,2} {7,8} {0} -> q0 and q2             -> 1/2
+    #   n = 3: adds 9, 4, 6      -> still q0 and q2           -> 1/2
+    assert O.recall_1_at_k(RECALL_FOUND, RECALL_TRUE, n=1) == 0.0
+    assert O.recall_1_at_k(RECALL_FOUND, RECALL_TRUE, n=2) == 0.5
+    assert O.recall_1_at_k(RECALL_FOUND, RECALL_TRUE) == 0.5
+    # (the reversed membership test, "the first id found is among the true
+    # ones", would give 1 at n = 1: 5, 1, 7 and 0 are all in their truth rows)
+
+
+def test_recall_intersection_hand_worked():
+    # |found ∩ true[:3]| per query: {5,3,9}∩{3,5,2} = 2, {1,2,4}∩{9,1,2} = 2,
+    # {7,8,6}∩{8,6,7} = 3, {0}∩{4,0,1} = 1 -> (2 + 2 + 3 + 1) / (4 * 3) = 2/3
+    assert abs(O.recall_k_at_k(RECALL_FOUND, RECALL_TRUE) - 2.0 / 3.0) < 1e-15
+    # against all five true neighbours it would be (3 + 3 + 3 + 1) / 12
+    # k = 1: 5 vs 3, 1 vs 9, 7 vs 8, 0 vs 4 -> 0
+    assert O.recall_k_at_k(RECALL_FOUND, RECALL_TRUE, k=1) == 0.0
+    # k = 2: {5,3}∩{3,5} = 2, {1,2}∩{9,1} = 1, {7,8}∩{8,6} = 1, {0}∩{4,0} = 1 -> 5/8
+    assert O.recall_k_at_k(RECALL_FOUND, RECALL_TRUE, k=2) == 5 / 8
+    # padding never matches padding
+    pad = np.array([[-1, -1, -1]])
+    assert O.recall_k_at_k(pad, pad) == 0.0 and O.recall_1_at_k(pad, pad) == 0.0
+
+
+def test_recall_on_bruteforce_neighbours():
+    # the exact neighbours of a small set found again with one of them
+    # replaced: recall drops by exactly one id out of k for that query
+    rng = np.random.default_rng(11)
+    db = rng.standard_normal((300, 6)).astype(np.float32)
+    q = rng.standard_normal((20, 6)).astype(np.float32)
+    _, ti = O.bruteforce(db, q, 10)
+    fi = ti.copy()
+    fi[3, 9] = -1                       # the 10th of query 3 lost
+    fi[7, 0] = next(j for j in range(300) if j not in set(ti[7].tolist()))  # nearest of q7 wrong
+    assert abs(O.recall_k_at_k(fi, ti) - (1 - 2 / 200)) < 1e-12
+    assert O.recall_1_at_k(fi, ti) == 19 / 20
