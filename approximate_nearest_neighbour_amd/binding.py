@@ -38,7 +38,7 @@ class Info(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("nlist", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("nbits", ctypes.c_int32), ("ntotal", ctypes.c_int64),
                 ("max_list", ctypes.c_int64), ("device", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("device_bytes", ctypes.c_int64)]
+                ("flags", ctypes.c_int32), ("device_bytes", ctypes.c_int64)]
 
 
 class HostIndexStruct(ctypes.Structure):

@@ -570,6 +570,7 @@ ivfpq_status ivfpq_index_info(const ivfpq_index *idx, ivfpq_info *out)
     out->ntotal = idx->dx.ntotal;
     out->max_list = idx->dx.max_list;
     out->device = idx->device;
+    out->flags = idx->dx.t1 ? IVFPQ_INDEX_DECOMPOSED_TABLES : 0;
     out->device_bytes = idx->device_bytes;
     return ok();
 }

@@ -896,7 +896,9 @@ hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     a.pg = tables_per_group(ix.m, s.lut != 0);
     a.centroids = ix.centroids;
     a.codebooks = ix.codebooks;
-    a.t1 = s.metric ? nullptr : ix.t1;
+    // decomposed tables for squared L2 with float32 tables only: binary16
+    // storage would round entries the size of |x - c_l|^2 instead of F_j
+    a.t1 = (s.metric || s.lut) ? nullptr : ix.t1;
     a.list_off = ix.list_off;
     a.codes = ix.codes;
     a.ids = ix.ids;

@@ -6,7 +6,11 @@ index, queries and outputs resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--lut f32|f16]
 
-Synthetic data only (seeded Gaussian mixtures, CPU-built index).
+The default workload is the largest single-GPU configuration, the 1B-entry
+index with Zipf(1.1) list sizes (nlist 262,144, d 96, m 8, nprobe 128, k 100,
+10,000 queries; 8 GB of codes and 8 GB of ids in HBM).  Other workloads:
+the 1M and 10M Gaussian-mixture indexes, the exact bf16 flat search, index
+building, k-means and the k-NN graph.  Synthetic data only (seeded).
 """
 from __future__ import annotations
 
@@ -29,11 +33,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+ZIPF_WORKLOAD = "ivfpq_zipf_n1000000000_d96_m8_nlist262144"
+# the Infinity Cache (MALL) of an MI355X: a code array this small stays cache
+# resident across searches, so its code-byte rate is an effective rate, not
+# an HBM one
+MALL_BYTES = 256 << 20
+# lists this long make a query's scan many times the mean (1B Zipf index)
+GIANT_LIST = 1_000_000
+
+
 def workload(name: str):
     from approximate_nearest_neighbour_amd import datagen as G
-    makers = {"ivfpq_n1m_d128_m16_nlist1024": G.gmm1m, "ivfpq_tiny_n10k_d32_m4": G.tiny,
-              "ivfpq_n10m_d96_m32_nlist4096": G.gmm10m,
-              "ivfpq_zipf_n1000000000_d96_m8_nlist262144": G.zipf_workload}
+    makers = {"ivfpq_n1m_d128_m16_nlist1024": lambda: G.gmm1m(keep_vectors=True),
+              "ivfpq_tiny_n10k_d32_m4": G.tiny,
+              "ivfpq_n10m_d96_m32_nlist4096": lambda: G.gmm10m(keep_vectors=True),
+              ZIPF_WORKLOAD: G.zipf_workload}
     if name not in makers:
         raise SystemExit(f"unknown workload {name}; choose from "
                          f"{sorted(makers) + EXTRA_WORKLOADS}")
@@ -139,8 +153,34 @@ def scanned_entries(index, probes: np.ndarray) -> int:
     return int(index.list_sizes[probes.astype(np.int64)].sum())
 
 
-def cpu_baseline(w, lut_mode, budget_s: float):
-    """The oracle, as it stands, on a bounded leading sample of the queries."""
+def giant_list_queries(index, probes: np.ndarray) -> np.ndarray:
+    """Rows whose probes include a list of more than GIANT_LIST entries."""
+    big = index.list_sizes[probes.astype(np.int64)] > GIANT_LIST
+    return np.flatnonzero(big.any(axis=1))
+
+
+def recall_report(w, found_ids, nsample: int = 200, seed: int = 2005):
+    """1-recall@k (R@k) and k-recall@k (intersection) of the search against
+    the oracle's exact brute force over the database vectors, on a seeded
+    sample of the queries (the two measures of "Billion-scale similarity
+    search with GPUs", experiments section)."""
+    from oracle import oracle as O
+    if w.vectors is None:
+        return None
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(len(w.queries), min(nsample, len(w.queries)), replace=False))
+    # the generated indexes give database row r the id r
+    _, true_ids = O.bruteforce(w.vectors, w.queries[rows], w.k)
+    found = found_ids[rows]
+    return {"queries": int(len(rows)), "k": int(w.k),
+            "recall_1_at_k": O.recall_1_at_k(found, true_ids),
+            "recall_k_at_k": O.recall_k_at_k(found, true_ids)}
+
+
+def cpu_baseline(w, lut_mode, budget_s: float, probes=None):
+    """The oracle, as it stands, on a bounded leading sample of the queries
+    (their natural mix: on the 1B Zipf index about 4% of the queries probe a
+    list above 10^6 entries, and the sample holds them at that rate)."""
     from oracle import oracle as O
     threads = O.default_threads()
     probe_n = min(len(w.queries), max(threads, 16))
@@ -152,8 +192,12 @@ def cpu_baseline(w, lut_mode, budget_s: float):
     od, oi, op = O.search(w.index, w.queries[:n], w.nprobe, w.k, lut_mode=lut_mode,
                           nthreads=threads)
     wall = time.perf_counter() - t
+    extra = ""
+    if probes is not None:
+        g = int(np.sum(giant_list_queries(w.index, probes[:n]) < n))
+        extra = f" ({g} of them probe a list above {GIANT_LIST:,} entries)"
     return dict(value=n / wall, unit="queries/s", cores=threads, kind="oracle",
-                sample=f"first {n} of {len(w.queries)} queries, full search (fp64), "
+                sample=f"first {n} of {len(w.queries)} queries{extra}, full search (fp64), "
                        f"{wall:.1f} s wall"), (n, od, oi, op)
 
 
@@ -607,8 +651,10 @@ def bench_knn_graph(args):
         "data": "synthetic (seeded Gaussian mixture, CPU-built IVF-PQ index)",
         "config": {"workload": KNN_GRAPH_WORKLOAD, "n": nq, "d": w.index.d,
                    "nlist": w.index.nlist, "m": w.index.m, "nprobe": nprobe, "k": k},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "scan_kernel",
+        "roofline": {"bound": "hbm" if int(w.index.ntotal) * w.index.m > MALL_BYTES
+                     else "effective", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "scan_items_kernel",
                      "kernel_ms": scan_ms, "algorithmic_bytes_per_launch": code_bytes},
         "cpu_baseline": cpu,
         "stages_ms": {"coarse": coarse_ms, "scan": scan_ms},
@@ -628,7 +674,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="ivfpq_n1m_d128_m16_nlist1024")
+    ap.add_argument("--workload", default=ZIPF_WORKLOAD)
     ap.add_argument("--lut", choices=["f32", "f16"], default="f32")
     ap.add_argument("--metric", choices=["l2", "ip"], default="l2",
                     help="ranking metric of the IVF-PQ search (squared L2 or inner product)")
@@ -730,20 +776,34 @@ def main():
     read_gbs = measured_read_gbs(torch, A)
     log(f"measured streaming read: {read_gbs:.0f} GB/s")
 
-    # parity on a sample of the timed configuration
+    # parity on a sample of the timed configuration: the leading queries plus
+    # (1B Zipf index) up to 8 queries that probe a list above 10^6 entries
     step()
     torch.cuda.synchronize()
     pn = min(args.parity_queries, nq)
+    rows = np.arange(pn)
+    giants = giant_list_queries(w.index, probes)
+    rows = np.unique(np.concatenate([rows, giants[giants >= pn][:8]])).astype(np.int64)
     lut_mode = O.IP if args.metric == "ip" else (O.LUT_F16 if args.lut == "f16" else O.LUT_F64)
-    rep = check.compare_search(w.index, w.queries[:pn], w.nprobe, w.k, out[0][:pn].cpu().numpy(),
-                               out[1][:pn].cpu().numpy(), out[2][:pn].cpu().numpy(),
-                               lut_mode=lut_mode)
-    log("parity", rep.summary())
+    decomposed = bool(A.ivfpq_index_info(ix)["flags"] & 1) and args.lut == "f32" \
+        and args.metric == "l2"
+    rep = check.compare_search(w.index, w.queries[rows], w.nprobe, w.k,
+                               out[0].cpu().numpy()[rows], out[1].cpu().numpy()[rows],
+                               out[2].cpu().numpy()[rows], lut_mode=lut_mode,
+                               decomposed=decomposed)
+    log("parity", rep.summary(), f"({len(rows) - pn} giant-list queries among {len(rows)})")
+    recall = None
+    if args.metric == "l2":
+        recall = recall_report(w, out[1].cpu().numpy())
+        if recall:
+            log("recall", recall)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu, _ = cpu_baseline(w, lut_mode, args.cpu_seconds)
+        cpu, _ = cpu_baseline(w, lut_mode, args.cpu_seconds, probes=probes)
         log("cpu baseline", cpu)
+    code_array = int(w.index.ntotal) * w.index.m
+    bound = "hbm" if code_array > MALL_BYTES else "effective"
 
     res = {
         "metric": METRIC,
@@ -763,16 +823,18 @@ def main():
         "config": {"workload": w.name, "n": int(w.index.ntotal), "d": w.index.d,
                    "nlist": w.index.nlist, "m": w.index.m, "nq": nq, "nprobe": w.nprobe,
                    "k": w.k, "lut": args.lut, "metric": args.metric},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"bound": bound, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": stored_traffic(w.name, args.lut) if args.metric == "l2" else None,
-                     "kernel": "scan_kernel", "kernel_ms": scan_ms,
+                     "kernel": "scan_items_kernel", "kernel_ms": scan_ms,
                      "algorithmic_bytes_per_launch": code_bytes,
+                     "code_array_bytes": code_array,
                      "measured_read_gbs": read_gbs, "frac_of_measured_read": achieved / read_gbs},
         "cpu_baseline": cpu,
         "stages_ms": {"coarse": coarse_ms, "scan": scan_ms, "scan_only": scan_only_ms,
                       "kselect_overhead": scan_ms / scan_only_ms - 1 if scan_only_ms else None},
         "host_pointer_qps": host_qps,
+        "recall": recall,
         "parity": rep.summary(),
     }
     print(json.dumps(res), flush=True)

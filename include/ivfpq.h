@@ -99,12 +99,21 @@ typedef struct {
     int32_t metric; /* ivfpq_metric (0 = squared L2) */
 } ivfpq_search_params;
 
+/* ivfpq_info.flags: the squared-L2 scan of this index with float32 tables
+ * builds its tables from a list term precomputed at load plus a query term
+ * (the decomposition of "Billion-scale similarity search with GPUs", IVFADC
+ * section); their float32 error near a zero distance is larger than the
+ * difference form's (bounded by the sum of the terms' magnitudes times a few
+ * units of round-off).  Binary16 tables and the inner product always use the
+ * direct form. */
+#define IVFPQ_INDEX_DECOMPOSED_TABLES 1
+
 typedef struct {
     int32_t d, nlist, m, nbits;
     int64_t ntotal;
     int64_t max_list; /* longest inverted list */
     int32_t device;
-    int32_t reserved;
+    int32_t flags;        /* IVFPQ_INDEX_* bits */
     int64_t device_bytes; /* device memory held by the index */
 } ivfpq_info;
 

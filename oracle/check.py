@@ -14,7 +14,28 @@ rules below say when a device result counts as the oracle's result:
    distance; no duplicates; distances non-decreasing; the padding (+inf, -1)
    matches.
 3. Distances.  Every returned id's distance is within tau relative of the
-   oracle's distance for that id (tau = 1e-4 float32 tables, 1e-2 fp16).
+   oracle's distance for that id (tau = 1e-4 float32 tables, 1e-2 fp16),
+   plus an absolute term for the residual's rounding: the device forms
+   r = fl(x - c_l) in float32 (search step 2 of the IVFPQ section of "Custom
+   8-bit floating point value format for reducing shared memory bank conflict
+   in ANN search"), |fl(r_s) - r_s| <= u |x_s - c_s|, and squaring
+   (r_s - C_s) turns that into |R^ - R| <= 2 u X sqrt(R) + u^2 X^2 beyond the
+   relative error of the table arithmetic, X = |x - c_l|.  The checker allows
+   twice that with X the largest |x - c_l| over the row's probed lists and R
+   the row's k-th oracle distance (an upper bound for every returned id).
+   It matters only near R = 0 (a query on a reconstruction), where no
+   relative bound can hold.
+   Decomposed tables (the list-term/query-term split of the IVFADC section of
+   "Billion-scale similarity search with GPUs"): the device computes
+   F_j(v) = fl(fl(t1 + t2) [+ |x - c_l|^2 for j = 0]) with
+   t1 = |C_j[v]|^2 + 2 <c_l,j, C_j[v]> (double precision, rounded once) and
+   t2 = -2 fl(<x_j, C_j[v]>), then sums the m entries in float32.  Each term
+   is bounded by |t1| <= B_j^2 + 2 |c_l,j| B_j and |t2| <= 2 |x_j| B_j
+   (B_j = max_v |C_j[v]|, Cauchy-Schwarz), so
+   |R^ - R| <= gamma_{dsub+m+4} (sum_j (B_j^2 + 2 (|c_l,j| + |x_j|) B_j)
+   + |x - c_l|^2) + gamma_{d+2} |x - c_l|^2; the checker allows twice that,
+   maximised over the row's probed lists.  Unlike the difference form this
+   cancels: near R = 0 the error is of the order of u times the norms.
 
 Inner-product metric: rules 1-3 on the negated scores (so that rows ascend),
 with absolute bands in place of the relative ones (a score can be near zero):
@@ -183,10 +204,43 @@ def check_results(gpu_d, gpu_i, ora_d, ora_i, k, tau, report: Report, rows=None,
                 report.max_rel_err = max(report.max_rel_err, err / abs(ref))
 
 
+def l2_abs_tol(index, queries, probes, kth, decomposed=False):
+    """Absolute term of rule 3 per query row (squared L2): the residual's
+    float32 rounding, and with decomposed tables their forward-error bound
+    (the module docstring derives both); maximised over the row's probed
+    lists.  kth: the row's k-th oracle distance."""
+    u = 2.0 ** -24
+    cent = np.asarray(_get(index, "centroids"), dtype=np.float64)
+    books = np.asarray(_get(index, "codebooks"), dtype=np.float64)
+    d, m = cent.shape[1], books.shape[0]
+    dsub = d // m
+    bj = np.sqrt(np.max(np.sum(books ** 2, axis=2), axis=1))          # [m]
+    q = np.asarray(queries, dtype=np.float64)
+    out = np.zeros(len(q))
+    for r in range(len(q)):
+        ls = np.asarray(probes[r], dtype=np.int64)
+        ls = ls[(ls >= 0) & (ls < len(cent))]
+        if len(ls) == 0:
+            continue
+        c = cent[ls]                                                    # [p][d]
+        x2 = np.sum((q[r] - c) ** 2, axis=1)                           # |x - c_l|^2
+        rk = max(float(kth[r]), 0.0) if np.isfinite(kth[r]) else 0.0
+        tol = 2.0 * (2.0 * u * np.sqrt(x2) * np.sqrt(rk) + u * u * x2)
+        if decomposed:
+            cj = np.sqrt(np.sum(c.reshape(len(ls), m, dsub) ** 2, axis=2))    # [p][m]
+            xj = np.sqrt(np.sum(q[r].reshape(m, dsub) ** 2, axis=1))          # [m]
+            terms = np.sum(bj ** 2 + 2.0 * (cj + xj) * bj, axis=1)             # [p]
+            tol = tol + 2.0 * (gamma(dsub + m + 4) * (terms + x2) + gamma(d + 2) * x2)
+        out[r] = float(np.max(tol))
+    return out
+
+
 def compare_search(index, queries, nprobe, k, gpu_d, gpu_i, gpu_probes=None, lut_mode=O.LUT_F64,
-                   tau=None, k_extra=32, nthreads=None) -> Report:
+                   tau=None, k_extra=32, nthreads=None, decomposed=False) -> Report:
     """Full acceptance check of a device IVF-PQ search against the oracle
-    (lut_mode O.IP: the inner-product metric, scores in decreasing order)."""
+    (lut_mode O.IP: the inner-product metric, scores in decreasing order).
+    decomposed: the device built its tables from the per-list term (squared
+    L2 only); rule 3's absolute term then includes their error bound."""
     ip = lut_mode == O.IP
     tau = (TAU_F32 if lut_mode in (O.LUT_F64, O.IP) else TAU_F16) if tau is None else tau
     queries = np.ascontiguousarray(queries, dtype=np.float32)
@@ -234,7 +288,10 @@ def compare_search(index, queries, nprobe, k, gpu_d, gpu_i, gpu_probes=None, lut
         check_results(-np.asarray(gpu_d, dtype=np.float64), gpu_i, -od, oi, k, 0.0, rep,
                       lookup=lookup, abs_tol=abs_tol)
     else:
-        check_results(gpu_d, gpu_i, od, oi, k, tau, rep, lookup=lookup)
+        kth = np.array([row[min(k, int(np.sum(np.isfinite(row)))) - 1]
+                        if np.any(np.isfinite(row)) else 0.0 for row in od[:, :k]])
+        abs_tol = l2_abs_tol(index, queries, probes_used, kth, decomposed=decomposed)
+        check_results(gpu_d, gpu_i, od, oi, k, tau, rep, lookup=lookup, abs_tol=abs_tol)
     return rep
 
 

@@ -639,3 +639,116 @@ def test_recall_on_bruteforce_neighbours():
     fi[7, 0] = next(j for j in range(300) if j not in set(ti[7].tolist()))  # nearest of q7 wrong
     assert abs(O.recall_k_at_k(fi, ti) - (1 - 2 / 200)) < 1e-12
     assert O.recall_1_at_k(fi, ti) == 19 / 20
+
+
+# ---------------------------------------------------------------------------
+# absolute error terms of rule 3 near a zero distance: a float32 evaluation
+# (numpy float32, the device's order of operations) of both table forms for
+# queries placed on a reconstruction must stay inside half of each band (the
+# checker allows twice the bound), and the checker must accept an error
+# inside the band and reject one past it
+# ---------------------------------------------------------------------------
+
+def _rand_index(rng, nlist, d, m, sizes, codebook_scale=1.0):
+    sizes = np.asarray(sizes, dtype=np.int64)
+    n = int(sizes.sum())
+    return dict(centroids=rng.standard_normal((nlist, d)).astype(np.float32),
+                codebooks=(codebook_scale * rng.standard_normal((m, 256, d // m)))
+                .astype(np.float32),
+                list_sizes=sizes, codes=rng.integers(0, 256, (n, m), dtype=np.uint8),
+                ids=rng.permutation(n).astype(np.int64))
+
+
+def _f32_difference_form(x, c, books, codes):
+    """sum_j sum_s (fl(x - c)_s - C)^2 in float32, s and j ascending."""
+    m, _, dsub = books.shape
+    r = (x.astype(np.float32) - c.astype(np.float32)).astype(np.float32)
+    tot = np.float32(0)
+    for j in range(m):
+        e = np.float32(0)
+        for s in range(dsub):
+            df = np.float32(r[j * dsub + s] - books[j, codes[j], s])
+            e = np.float32(e + np.float32(df * df))
+        tot = np.float32(tot + e)
+    return float(tot)
+
+
+def _f32_decomposed_form(x, c, books, codes):
+    """fl(fl(t1 + t2) [+ |x - c|^2]) per sub-quantizer, t1 from double."""
+    m, _, dsub = books.shape
+    x32 = x.astype(np.float32)
+    cst = np.float32(0)
+    for t in range(len(x)):
+        df = np.float32(x32[t] - np.float32(c[t]))
+        cst = np.float32(cst + np.float32(df * df))
+    tot = np.float32(0)
+    for j in range(m):
+        cw = books[j, codes[j]].astype(np.float64)
+        t1 = np.float32(np.dot(cw, cw) + 2.0 * np.dot(c[j * dsub:(j + 1) * dsub]
+                                                       .astype(np.float64), cw))
+        acc = np.float32(0)
+        for s in range(dsub):
+            acc = np.float32(acc + np.float32(x32[j * dsub + s] * np.float32(cw[s])))
+        e = np.float32(t1 + np.float32(np.float32(-2.0) * acc))
+        if j == 0:
+            e = np.float32(e + cst)
+        tot = np.float32(tot + e)
+    return float(tot)
+
+
+@pytest.mark.parametrize("m,dsub", [(16, 8), (8, 12), (4, 8)])
+def test_l2_bands_bound_float32_evaluations_near_zero(m, dsub):
+    rng = np.random.default_rng(17 + m)
+    d, nlist, n = m * dsub, 6, 60
+    idx = _rand_index(rng, nlist, d, m, [10] * nlist, codebook_scale=0.5)
+    off = np.concatenate([[0], np.cumsum(idx["list_sizes"])])
+    worst_diff = worst_dec = 0.0
+    for t in range(12):
+        pos = int(rng.integers(0, n))
+        l = int(np.searchsorted(off, pos, side="right") - 1)
+        code = idx["codes"][pos]
+        recon = idx["centroids"][l].astype(np.float64) + np.concatenate(
+            [idx["codebooks"][j, code[j]] for j in range(m)]).astype(np.float64)
+        eps = [0.0, 1e-6, 1e-4, 1e-2][t % 4]
+        x = (recon + eps * rng.standard_normal(d)).astype(np.float32)
+        exact, _ = O.entry_distances(idx, x, np.array([pos]))
+        exact = float(exact[0])
+        kth = np.array([exact])
+        b_diff = check.l2_abs_tol(idx, x[None], [[l]], kth)[0] / 2
+        b_dec = check.l2_abs_tol(idx, x[None], [[l]], kth, decomposed=True)[0] / 2
+        rel = check.gamma(dsub + m + 2) * exact
+        e_diff = abs(_f32_difference_form(x, idx["centroids"][l], idx["codebooks"], code) - exact)
+        e_dec = abs(_f32_decomposed_form(x, idx["centroids"][l], idx["codebooks"], code) - exact)
+        assert e_diff <= b_diff + rel, (eps, e_diff, b_diff)
+        assert e_dec <= b_dec + rel, (eps, e_dec, b_dec)
+        worst_diff = max(worst_diff, e_diff)
+        worst_dec = max(worst_dec, e_dec)
+    # the decomposed form really does lose to cancellation near zero
+    assert worst_dec > 10 * worst_diff
+
+
+def test_checker_band_near_zero_accepts_and_rejects():
+    rng = np.random.default_rng(23)
+    m, dsub, nlist = 8, 4, 4
+    idx = _rand_index(rng, nlist, m * dsub, m, [40] * nlist, codebook_scale=0.5)
+    pos = 7
+    code = idx["codes"][pos]
+    x = (idx["centroids"][0].astype(np.float64) + np.concatenate(
+        [idx["codebooks"][j, code[j]] for j in range(m)])).astype(np.float32)[None]
+    k = 10
+    od, oi, op = O.search(idx, x, nlist, k)
+    base = od.astype(np.float32)
+    kth = od[:, k - 1]
+    checked = 0
+    for decomposed in (False, True):
+        band = check.l2_abs_tol(idx, x, op, kth, decomposed=decomposed)[0]
+        assert band > 0
+        for scale, ok in ((0.5, True), (3.0, False)):
+            g = base.copy()
+            g[0, 0] = np.float32(od[0, 0] + scale * band + check.TAU_F32 * od[0, 0])
+            if g[0, 0] > g[0, 1]:      # keep the row ascending (and the ids with it)
+                continue
+            rep = check.compare_search(idx, x, nlist, k, g, oi, op, decomposed=decomposed)
+            assert rep.ok() == ok, (decomposed, scale, rep.failures[:2])
+            checked += 1
+    assert checked == 4
