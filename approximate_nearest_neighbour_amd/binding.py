@@ -66,7 +66,7 @@ class FlatTimings(ctypes.Structure):
 
 EXPORTS = ("ivfpq_validate_index_file", "ivfpq_validate_host_index", "ivfpq_load_index",
            "ivfpq_load_index_host", "ivfpq_free_index", "ivfpq_index_info", "ivfpq_search",
-           "ivfpq_search_ex", "ivfpq_coarse_ex", "ivfpq_assign_encode_ex", "ivfpq_kmeans_ex",
+           "ivfpq_search_ex", "ivfpq_search_noalloc_ex", "ivfpq_coarse_ex", "ivfpq_assign_encode_ex", "ivfpq_kmeans_ex",
            "ivfpq_build_index_ex", "ivfpq_index_export",
            "ivfpq_compute_luts_ex",
            "ivfpq_select_topk_ex",
@@ -98,6 +98,7 @@ def lib():
             "ivfpq_index_info": ([P, P], st),
             "ivfpq_search": ([P, P, i64, i32, i32, P, P], st),
             "ivfpq_search_ex": ([P, P, P, i64, P, P, P, P], st),
+            "ivfpq_search_noalloc_ex": ([P, P, P, i64, P, P, P, P], st),
             "ivfpq_coarse_ex": ([P, P, i64, i32, P, P, P], st),
             "ivfpq_assign_encode_ex": ([P, P, i64, P, P, P], st),
             "ivfpq_kmeans_ex": ([P, i64, i32, i32, i32, P, P, P, P], st),
@@ -287,9 +288,11 @@ def _stream_ptr(stream) -> ctypes.c_void_p:
 
 def ivfpq_search_ex(index: Index, queries: torch.Tensor, nprobe: int, k: int, lut: str = "f32",
                     mode: int = MODE_NORMAL, chunk_len: int = 0, return_probes: bool = False,
-                    out=None, stream=None, metric: str = "l2"):
+                    out=None, stream=None, metric: str = "l2", noalloc: bool = False):
     """Asynchronous device search on the current (or given) torch stream.
     metric "l2" (squared L2, ascending) or "ip" (inner product, descending).
+    noalloc: call ivfpq_search_noalloc_ex (workspace in the library's fixed
+    device scratch; pass `out` too so that nothing is allocated here either).
 
     Returns (distances [nq,k] float32, ids [nq,k] int64[, probes [nq,nprobe] int32])."""
     if metric not in ("l2", "ip"):
@@ -305,11 +308,12 @@ def ivfpq_search_ex(index: Index, queries: torch.Tensor, nprobe: int, k: int, lu
         dist, ids, probes = out
     p = SearchParams(nprobe, k, LUT_F16 if lut == "f16" else LUT_F32, mode, chunk_len,
                      METRIC_IP if metric == "ip" else METRIC_L2)
-    _check(lib().ivfpq_search_ex(index.handle, ctypes.byref(p), ctypes.c_void_p(q.data_ptr()),
-                                 nq, ctypes.c_void_p(dist.data_ptr()),
-                                 ctypes.c_void_p(ids.data_ptr()),
-                                 ctypes.c_void_p(probes.data_ptr() if probes is not None else 0),
-                                 _stream_ptr(stream)))
+    fn = lib().ivfpq_search_noalloc_ex if noalloc else lib().ivfpq_search_ex
+    _check(fn(index.handle, ctypes.byref(p), ctypes.c_void_p(q.data_ptr()),
+              nq, ctypes.c_void_p(dist.data_ptr()),
+              ctypes.c_void_p(ids.data_ptr()),
+              ctypes.c_void_p(probes.data_ptr() if probes is not None else 0),
+              _stream_ptr(stream)))
     return (dist, ids, probes) if return_probes else (dist, ids)
 
 

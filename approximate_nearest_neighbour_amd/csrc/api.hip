@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -575,11 +576,79 @@ ivfpq_status ivfpq_index_info(const ivfpq_index *idx, ivfpq_info *out)
     return ok();
 }
 
-ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params *p,
-                             const float *queries_dev, int64_t nq, float *distances_dev,
-                             int64_t *ids_dev, int32_t *probes_dev, void *stream)
+} // extern "C"
+
+namespace {
+
+// Workspace of one search, byte offsets: probes (unless the caller passes a
+// buffer) | plan arrays | coarse scratch | partial top-k of the work items
+// (imax items per query; a query with one item writes its rows from the
+// scan, so imax = 1 needs no partials).
+struct WsLayout {
+    size_t probes, total, chunk, count, base, bound, counter, coarse, pd, pp, bytes;
+};
+
+WsLayout ws_layout(const DeviceIndex &dx, int64_t nq, int nprobe, int k, uint32_t imax,
+                   bool own_probes)
 {
-    ivfpq_index *idx = const_cast<ivfpq_index *>(cidx);
+    WsLayout o{};
+    size_t off = 0;
+    auto carve = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return at;
+    };
+    o.probes = own_probes ? carve((size_t)nq * nprobe * 4) : 0;
+    o.total = carve((size_t)nq * 4);
+    o.chunk = carve((size_t)nq * 4);
+    o.count = carve((size_t)nq * 4);
+    o.base = carve(((size_t)nq + 1) * 4);
+    o.bound = carve((size_t)nq * 4);
+    o.counter = carve(4);
+    o.coarse = carve(coarse_ws_bytes(dx, nq, nprobe));
+    const size_t part = imax > 1 ? (size_t)nq * imax * (size_t)kw_of(k) * 4 : 0;
+    o.pd = carve(part);
+    o.pp = carve(part);
+    o.bytes = off;
+    return o;
+}
+
+// Fixed device scratch of the allocation-free search (ivfpq_search_noalloc_ex):
+// one array per GPU, created with the code object and held until the process
+// ends.  Host code never uses the array's name as an address: its device
+// address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and kept in g_scratch.
+constexpr size_t kScratchBytes = IVFPQ_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's scratch address (the caller has made `device` current).
+hipError_t scratch_address(int device, unsigned char **out)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    ScratchSlot &sl = g_scratch[device];
+    std::call_once(sl.once, [&] {
+        sl.err = hipGetSymbolAddress(&sl.ptr, HIP_SYMBOL(scratch));
+    });
+    *out = static_cast<unsigned char *>(sl.ptr);
+    return sl.err;
+}
+
+// The search behind ivfpq_search_ex (workspace owned by the handle, grown on
+// demand) and ivfpq_search_noalloc_ex (workspace in the fixed scratch; no
+// allocation of any kind).
+ivfpq_status search_impl(ivfpq_index *idx, const ivfpq_search_params *p, const float *queries_dev,
+                         int64_t nq, float *distances_dev, int64_t *ids_dev, int32_t *probes_dev,
+                         void *stream, bool noalloc)
+{
     ivfpq_status s = check_params(idx, p, nq);
     if (s)
         return s;
@@ -596,43 +665,48 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
     if (scan_lds_bytes(dx.d, dx.m, p->nprobe, p->lut == IVFPQ_LUT_F16, kw_of(p->k) / 64,
                        dx.m % 2 == 0 ? 2 : 1) > 160 * 1024)
         return fail(IVFPQ_E_INVALID_ARG, "tables of this m and precision exceed the LDS");
-    // workspace: probes | plan arrays | partial top-k of the work items
     SearchPlan pl;
     pl.target = p->chunk_len > 0 ? (uint32_t)p->chunk_len : kDefaultChunk;
     pl.imax = items_per_query(nq, kw_of(p->k));
+    WsLayout o = ws_layout(dx, nq, p->nprobe, p->k, pl.imax, !probes_dev);
+    unsigned char *ws = nullptr;
+    if (noalloc) {
+        // as many items per query as the fixed scratch holds (down to one)
+        while (o.bytes > kScratchBytes && pl.imax > 1) {
+            pl.imax = pl.imax > 2 ? pl.imax / 2 : 1;
+            o = ws_layout(dx, nq, p->nprobe, p->k, pl.imax, !probes_dev);
+        }
+        if (o.bytes > kScratchBytes)
+            return fail(IVFPQ_E_INVALID_ARG,
+                        "the batch needs " + std::to_string(o.bytes) +
+                            " bytes of workspace, more than the allocation-free search's "
+                            "fixed scratch of " + std::to_string(kScratchBytes) +
+                            " bytes: split it into smaller batches");
+        if (scratch_address(idx->device, &ws) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return fail(IVFPQ_E_DEVICE, "cannot find the device address of the fixed scratch");
+        }
+    } else {
+        if ((s = ensure_ws(idx, o.bytes)))
+            return s;
+        ws = static_cast<unsigned char *>(idx->ws);
+    }
     pl.max_items = nq * (int64_t)pl.imax;
-    const size_t kw = (size_t)kw_of(p->k);
-    size_t off = 0;
-    auto carve = [&](size_t bytes) {
-        const size_t at = off;
-        off += (bytes + 255) & ~(size_t)255;
-        return at;
-    };
-    const size_t o_probes = probes_dev ? 0 : carve((size_t)nq * p->nprobe * 4);
-    const size_t o_total = carve((size_t)nq * 4), o_chunk = carve((size_t)nq * 4);
-    const size_t o_count = carve((size_t)nq * 4), o_base = carve(((size_t)nq + 1) * 4);
-    const size_t o_bound = carve((size_t)nq * 4), o_counter = carve(4);
-    const size_t o_coarse = carve(coarse_ws_bytes(dx, nq, p->nprobe));
-    const size_t o_pd = carve((size_t)pl.max_items * kw * 4);
-    const size_t o_pp = carve((size_t)pl.max_items * kw * 4);
-    if ((s = ensure_ws(idx, off)))
-        return s;
-    unsigned char *ws = static_cast<unsigned char *>(idx->ws);
-    int32_t *probes = probes_dev ? probes_dev : reinterpret_cast<int32_t *>(ws + o_probes);
-    pl.qtotal = reinterpret_cast<uint32_t *>(ws + o_total);
-    pl.qchunk = reinterpret_cast<uint32_t *>(ws + o_chunk);
-    pl.qcount = reinterpret_cast<uint32_t *>(ws + o_count);
-    pl.item_base = reinterpret_cast<uint32_t *>(ws + o_base);
-    pl.qbound = reinterpret_cast<uint32_t *>(ws + o_bound);
-    pl.counter = reinterpret_cast<uint32_t *>(ws + o_counter);
-    pl.part_d = reinterpret_cast<float *>(ws + o_pd);
-    pl.part_p = reinterpret_cast<uint32_t *>(ws + o_pp);
+    int32_t *probes = probes_dev ? probes_dev : reinterpret_cast<int32_t *>(ws + o.probes);
+    pl.qtotal = reinterpret_cast<uint32_t *>(ws + o.total);
+    pl.qchunk = reinterpret_cast<uint32_t *>(ws + o.chunk);
+    pl.qcount = reinterpret_cast<uint32_t *>(ws + o.count);
+    pl.item_base = reinterpret_cast<uint32_t *>(ws + o.base);
+    pl.qbound = reinterpret_cast<uint32_t *>(ws + o.bound);
+    pl.counter = reinterpret_cast<uint32_t *>(ws + o.counter);
+    pl.part_d = reinterpret_cast<float *>(ws + o.pd);
+    pl.part_p = reinterpret_cast<uint32_t *>(ws + o.pp);
     const bool recording = idx->profiling && idx->prof_calls < idx->prof_max;
     pl.prof = recording ? idx->prof_counts : nullptr;
 
     prof_record(idx, 0, true, st);
     hipError_t e =
-        launch_coarse(dx, queries_dev, nq, p->nprobe, ws + o_coarse, probes, nullptr, st, ip);
+        launch_coarse(dx, queries_dev, nq, p->nprobe, ws + o.coarse, probes, nullptr, st, ip);
     prof_record(idx, 0, false, st);
     if (e != hipSuccess)
         return fail(IVFPQ_E_DEVICE, std::string("coarse kernel: ") + hipGetErrorString(e));
@@ -669,6 +743,26 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params 
     if (recording)
         idx->prof_calls++;
     return ok();
+}
+
+} // namespace
+
+extern "C" {
+
+ivfpq_status ivfpq_search_ex(const ivfpq_index *cidx, const ivfpq_search_params *p,
+                             const float *queries_dev, int64_t nq, float *distances_dev,
+                             int64_t *ids_dev, int32_t *probes_dev, void *stream)
+{
+    return search_impl(const_cast<ivfpq_index *>(cidx), p, queries_dev, nq, distances_dev,
+                       ids_dev, probes_dev, stream, false);
+}
+
+ivfpq_status ivfpq_search_noalloc_ex(const ivfpq_index *cidx, const ivfpq_search_params *p,
+                                     const float *queries_dev, int64_t nq, float *distances_dev,
+                                     int64_t *ids_dev, int32_t *probes_dev, void *stream)
+{
+    return search_impl(const_cast<ivfpq_index *>(cidx), p, queries_dev, nq, distances_dev,
+                       ids_dev, probes_dev, stream, true);
 }
 
 ivfpq_status ivfpq_search(const ivfpq_index *idx, const float *queries, int64_t nq, int nprobe,

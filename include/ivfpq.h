@@ -204,6 +204,27 @@ ivfpq_status ivfpq_search_ex(const ivfpq_index *idx, const ivfpq_search_params *
                              const float *queries_dev, int64_t nq, float *distances_dev,
                              int64_t *ids_dev, int32_t *probes_dev, void *stream);
 
+/* Allocation-free search, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and kernels as ivfpq_search_ex, but the
+ * workspace (probes unless probes_dev is given, the work plan, the coarse
+ * step's scratch and the partial top-k of the work items) lives in a fixed
+ * device array of IVFPQ_NOALLOC_SCRATCH_BYTES per GPU, created with the
+ * library's code object and held until the process ends; the call allocates
+ * and frees nothing (no hipMalloc, no library routine that allocates).
+ * Items per query are reduced (64 down to 1) until the workspace fits; a
+ * batch that does not fit even then (about nq * (4 nprobe + 8 nprobe-rounded
+ * coarse partials + 24) bytes) is rejected with IVFPQ_E_INVALID_ARG before
+ * any device work: split it.  Every call on a GPU uses that GPU's single
+ * array, so calls that overlap on one GPU (two streams, two threads, two
+ * handles) race and must be serialised by the caller; the array keeps the
+ * last call's contents, and the kernels set everything they read before
+ * reading it. */
+#define IVFPQ_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+ivfpq_status ivfpq_search_noalloc_ex(const ivfpq_index *idx, const ivfpq_search_params *params,
+                                     const float *queries_dev, int64_t nq, float *distances_dev,
+                                     int64_t *ids_dev, int32_t *probes_dev, void *stream);
+
 /* The coarse step alone (device buffers, asynchronous; the coarse quantizer
  * q1 of "Billion-scale similarity search with GPUs", IVFADC section, and
  * search step 1 of the IVFPQ section of "Custom 8-bit floating point value
