@@ -39,6 +39,8 @@
 #include "internal.hpp"
 #include "plan.hpp"
 
+#include <cstdlib>
+
 namespace ivfpq {
 
 // ---------------------------------------------------------------------------
@@ -147,6 +149,7 @@ struct ScanArgs {
     int64_t *out_i;
     int ip;      // inner-product metric (tables of the run-time shape)
     float osign; // sign of the reported values: +1 squared L2, -1 inner product
+    uint32_t wide_min; // pieces of at least this many entries get a replicated table
 };
 
 // A code row of M bytes read with the widest loads its size allows.
@@ -186,10 +189,34 @@ struct CodeRow {
     }
 };
 
-// R = sum_{j<M} F_j(code[j]), j ascending, for the M code bytes in the M/4
-// words w.  The M table reads are all issued before the first add (they are
-// independent), so one entry costs one LDS round trip rather than M of them.
-template <int M, bool F16>
+// Sum of M values: j ascending, or (TREE, M a power of two) as a balanced
+// pairwise tree, ((t0 + t1) + (t2 + t3)) + ...  The tree gives the same bits
+// for any order t[k] = F_{k ^ s} (each node adds the same two values, and a
+// float sum of two values does not depend on their order), which the
+// replicated-table scan relies on.
+template <int M, bool TREE>
+__device__ __forceinline__ float sum_terms(float (&t)[M])
+{
+    if constexpr (TREE) {
+#pragma unroll
+        for (int w = 1; w < M; w *= 2)
+#pragma unroll
+            for (int j = 0; j < M; j += 2 * w)
+                t[j] = t[j] + t[j + w];
+        return t[0];
+    } else {
+        float r = t[0];
+#pragma unroll
+        for (int j = 1; j < M; ++j)
+            r += t[j];
+        return r;
+    }
+}
+
+// R = sum_{j<M} F_j(code[j]) for the M code bytes in the M/4 words w.  The M
+// table reads are all issued before the first add (they are independent), so
+// one entry costs one LDS round trip rather than M of them.
+template <int M, bool F16, bool TREE = false>
 __device__ __forceinline__ float adc_words(const uint32_t *w, const void *lut)
 {
     float t[M];
@@ -198,11 +225,7 @@ __device__ __forceinline__ float adc_words(const uint32_t *w, const void *lut)
         const uint32_t c = (w[j >> 2] >> (8 * (j & 3))) & 255u;
         t[j] = Table<F16>::get(lut, j * 256 + (int)c);
     }
-    float r = t[0];
-#pragma unroll
-    for (int j = 1; j < M; ++j)
-        r += t[j];
-    return r;
+    return sum_terms<M, TREE>(t);
 }
 
 // Run-time m (any m, byte loads when m % 4 != 0).
@@ -268,17 +291,44 @@ void scan_items_kernel(ScanArgs a)
     const int dpad = (d + 3) & ~3;
     const size_t tbytes = (size_t)m * 256 * (F16 ? 2 : 4);
 
+    static_assert(!PRE || M > 0, "decomposed tables need a compile-time shape");
+    static_assert(!IP || !PRE, "one table form at a time");
+    // codebook slice in registers (difference form) or the query term (PRE,
+    // IP with a compile-time shape)
+    constexpr bool QT = M > 0 && (PRE || IP);
+
+    // Row tables (m 8, float32 difference form): both table buffers share a
+    // 64 KiB region at LDS offset 0 of 256 rows (code value c) x 256 bytes,
+    // buffer b in bytes [128 b, 128 b + 128) of every row, so that a table
+    // address is (c << 8) | byte0 and one v_perm_b32 assembles it from the
+    // code byte and a per-lane column byte.  In step t of an entry lane l
+    // reads sub-quantizer j = s ^ t, s = (l & 31) >> 2 (it byte-permutes its
+    // code row once so that the code of step t sits in byte t):
+    //  * a group of up to 4 short pieces: table p in columns 8p .. 8p + 7,
+    //    column 8p + j, one copy (a half-wave's lanes meet at most 4 to a
+    //    bank, about what random 8-bit indices into one table give);
+    //  * a long piece (at least a.wide_min entries) alone in the buffer: four
+    //    copies, column 4j + r holding copy r of sub-quantizer j; lane l reads
+    //    copy l & 3, i.e. column (l & 31) ^ 4t: the 32 lanes of a half-wave
+    //    read 32 different banks whatever the codes ("Custom 8-bit floating
+    //    point value format for reducing shared memory bank conflict in ANN
+    //    search", bank-conflict analysis: random 8-bit indices into one table
+    //    collide in the banks; replication spreads them).
+    constexpr bool WIDE = M == 8 && !F16 && !QT && G == 2;
+
     // Pieces (list, entry range) are handled in groups of PG: one barrier per
     // group, tables of the next group built while the current one is
     // scanned (two buffers of PG tables, two of PG residuals).
     const int PG = a.pg;
     // LDS layout by byte offsets from smem (pointer arithmetic on the LDS
-    // array keeps every access a DS instruction)
-    const uint32_t o_misc = (1u + 2u * (uint32_t)PG) * dpad * 4u;
+    // array keeps every access a DS instruction).  Row tables come first, at
+    // offset 0; otherwise the tables come last.
+    const uint32_t o_base = WIDE ? 2u * (uint32_t)PG * (uint32_t)tbytes : 0u;
+    const uint32_t o_misc = o_base + (1u + 2u * (uint32_t)PG) * dpad * 4u;
     const uint32_t o_pieces = o_misc + 64u;
     const uint32_t o_stage = (o_pieces + (uint32_t)a.nprobe * (uint32_t)sizeof(Piece) + 15u) & ~15u;
-    const uint32_t o_tab = o_stage + WAVES * 512u;
-    float *xs = reinterpret_cast<float *>(smem);
+    const uint32_t o_tab = WIDE ? 0u : o_stage + WAVES * 512u;
+    float *xs = reinterpret_cast<float *>(smem + o_base);
     // misc: [0] item [1] pieces [2] min bound [4 .. 4+WAVES) per-wave rank values
     uint32_t *misc = reinterpret_cast<uint32_t *>(smem + o_misc);
     uint32_t *pub = misc + 4;
@@ -286,7 +336,10 @@ void scan_items_kernel(ScanArgs a)
     unsigned char *tab = smem + o_tab;
     auto rsbuf = [&](int b, int p) { return xs + dpad + (b * PG + p) * dpad; };
     auto tabp = [&](int b, int p) {
-        return reinterpret_cast<void *>(tab + (size_t)(b * PG + p) * tbytes);
+        if constexpr (WIDE)   // the row-table buffer's first byte, plus the table's columns
+            return reinterpret_cast<void *>(tab + 128 * b + 32 * p);
+        else
+            return reinterpret_cast<void *>(tab + (size_t)(b * PG + p) * tbytes);
     };
     float *mk = reinterpret_cast<float *>(tab);
     uint32_t *mv = reinterpret_cast<uint32_t *>(mk + (WAVES - 1) * 64 * NW);
@@ -295,13 +348,26 @@ void scan_items_kernel(ScanArgs a)
     // the wave number is the same in all lanes: say so, so that what derives
     // from it (piece rotation, loop bounds) is scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int v = tid & 255, g = tid >> 8;
 
-    static_assert(!PRE || M > 0, "decomposed tables need a compile-time shape");
-    static_assert(!IP || !PRE, "one table form at a time");
-    // codebook slice in registers (difference form) or the query term (PRE,
-    // IP with a compile-time shape)
-    constexpr bool QT = M > 0 && (PRE || IP);
+    // thread -> (group g, codeword v); with WIDE a half-wave holds 16
+    // threads of each group, and thread v holds sub-quantizer
+    // g * JG + ((jj + v) % JG) in register slot jj, so that the 16-byte stores
+    // of a half-wave's replicated entries cover all 32 banks
+    const int v = WIDE ? ((tid & 15) | ((tid >> 5) << 4)) : (tid & 255);
+    const int g = WIDE ? ((tid >> 4) & 1) : (tid >> 8);
+    auto jsub = [&](int jj) { return WIDE ? g * JG + ((jj + v) & (JG - 1)) : g * JG + jj; };
+
+    // byte selectors of v_perm_b32 that move code byte t ^ s of a lane's
+    // 8-byte row into byte t (s = (l & 31) >> 2), low and high word
+    uint32_t perm_lo = 0, perm_hi = 0;
+    if constexpr (WIDE) {
+        const uint32_t sx = (uint32_t)((lane & 31) >> 2);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            perm_lo |= ((uint32_t)t ^ sx) << (8 * t);
+            perm_hi |= ((uint32_t)(t + 4) ^ sx) << (8 * t);
+        }
+    }
     float cb[(M > 0 && !QT) ? JG * DSUB : 1];
     float t2[QT ? JG : 1];
     if constexpr (M > 0 && !QT) {
@@ -309,12 +375,12 @@ void scan_items_kernel(ScanArgs a)
         for (int jj = 0; jj < JG; ++jj)
 #pragma unroll
             for (int s = 0; s < DSUB; ++s)
-                cb[jj * DSUB + s] = a.codebooks[((size_t)(g * JG + jj) * 256 + v) * DSUB + s];
+                cb[jj * DSUB + s] = a.codebooks[((size_t)jsub(jj) * 256 + v) * DSUB + s];
     }
 
     // rs: the piece's residual (difference form) or, in rs[0], |x - c_l|^2
-    // (PRE); list: the piece's list
-    auto build = [&](const float *rs, int list, void *lut) {
+    // (PRE); list: the piece's list; wide: the replicated layout
+    auto build = [&](const float *rs, int list, void *lut, bool wide) {
         if constexpr (IP && M > 0) {
             const float cst = rs[0];
 #pragma unroll
@@ -323,6 +389,7 @@ void scan_items_kernel(ScanArgs a)
                 Table<F16>::put(lut, j * 256 + v, j == 0 ? t2[jj] + cst : t2[jj]);
             }
             (void)list;
+            (void)wide;
         } else if constexpr (IP) {
             const float cst = rs[0];
             for (int j = 0; j < m; ++j) {
@@ -347,14 +414,20 @@ void scan_items_kernel(ScanArgs a)
         } else if constexpr (M > 0) {
 #pragma unroll
             for (int jj = 0; jj < JG; ++jj) {
-                const int j = g * JG + jj;
+                const int j = jsub(jj);
                 float acc = 0.f;
 #pragma unroll
                 for (int s = 0; s < DSUB; ++s) {
                     const float df = rs[j * DSUB + s] - cb[jj * DSUB + s];
                     acc = fmaf(df, df, acc);
                 }
-                Table<F16>::put(lut, j * 256 + v, acc);
+                unsigned char *row = reinterpret_cast<unsigned char *>(lut) + (v << 8);
+                if (WIDE && wide)   // the four copies of (j, v): one 16-byte store
+                    *reinterpret_cast<float4 *>(row + 16 * j) = make_float4(acc, acc, acc, acc);
+                else if (WIDE)      // row table, one copy
+                    *reinterpret_cast<float *>(row + 4 * j) = acc;
+                else
+                    Table<F16>::put(lut, j * 256 + v, acc);
             }
         } else {
             for (int j = 0; j < m; ++j) {
@@ -368,8 +441,17 @@ void scan_items_kernel(ScanArgs a)
             }
         }
     };
-    int np = 0;
-    auto group_size = [&](int grp) { return np - grp * PG < PG ? np - grp * PG : PG; };
+    // Pieces of an item: nn narrow ones in slots [0, nn), taken PG to a group
+    // (ngn groups), then nw wide ones, one per group, in slots counted down
+    // from nprobe - 1.
+    int nn = 0, nw = 0, ngn = 0;
+    auto group_size = [&](int grp) {
+        return grp >= ngn ? 1 : (nn - grp * PG < PG ? nn - grp * PG : PG);
+    };
+    auto group_wide = [&](int grp) { return grp >= ngn; };
+    auto piece_index = [&](int grp, int p) {
+        return grp >= ngn ? a.nprobe - 1 - (grp - ngn) : grp * PG + p;
+    };
     // residuals x - c_l of the pieces of group grp into residual buffer b
     // (PRE: their squared norms, one wave per piece, into the buffer's first
     // word)
@@ -378,7 +460,7 @@ void scan_items_kernel(ScanArgs a)
         if constexpr (PRE || IP) {
             // PRE: |x - c_l|^2; IP: -<x, c_l>
             for (int p = wave; p < pn; p += WAVES) {
-                const float *c = a.centroids + (size_t)pieces[grp * PG + p].list * d;
+                const float *c = a.centroids + (size_t)pieces[piece_index(grp, p)].list * d;
                 float acc = 0.f;
                 for (int t = lane; t < d; t += 64) {
                     if constexpr (IP) {
@@ -397,15 +479,16 @@ void scan_items_kernel(ScanArgs a)
         } else {
             for (int i = tid; i < pn * d; i += THREADS) {
                 const int p = i / d, t = i - p * d;
-                const float *c = a.centroids + (size_t)pieces[grp * PG + p].list * d;
+                const float *c = a.centroids + (size_t)pieces[piece_index(grp, p)].list * d;
                 rsbuf(b, p)[t] = xs[t] - c[t];
             }
         }
     };
     auto build_group = [&](int grp, int b) {
         const int pn = group_size(grp);
+        const bool wide = group_wide(grp);
         for (int p = 0; p < pn; ++p)
-            build(rsbuf(b, p), pieces[grp * PG + p].list, tabp(b, p));
+            build(rsbuf(b, p), pieces[piece_index(grp, p)].list, tabp(b, p), wide);
     };
 
     const uint32_t total_items = a.item_base[a.nq];
@@ -437,7 +520,7 @@ void scan_items_kernel(ScanArgs a)
             xs[t] = a.queries[q * d + t];
         // pieces of [start, stop) of the query's concatenated probed lists
         if (wave == 0) {
-            uint32_t acc = 0, np = 0;
+            uint32_t acc = 0, cn = 0, cw = 0;
             for (int p0 = 0; p0 < a.nprobe; p0 += 64) {
                 const int p = p0 + lane;
                 int l = -1;
@@ -452,24 +535,30 @@ void scan_items_kernel(ScanArgs a)
                 const uint32_t incl = wave_inclusive_sum(sz);
                 Piece pc;
                 const bool take = piece_of(acc + incl - sz, acc + incl, start, stop, &pc.b, &pc.e);
-                const uint64_t mask = wave_ballot(take);
+                const bool wide = WIDE && take && pc.e - pc.b >= a.wide_min;
+                const uint64_t mn = wave_ballot(take && !wide), mw = wave_ballot(wide);
                 if (take) {
-                    const int slot = (int)np + mbcnt64(mask);
                     pc.list = l;
+                    const int slot = wide ? a.nprobe - 1 - (int)(cw + mbcnt64(mw))
+                                          : (int)(cn + mbcnt64(mn));
                     pieces[slot] = pc;
                 }
-                np += (uint32_t)__popcll(mask);
+                cn += (uint32_t)__popcll(mn);
+                cw += (uint32_t)__popcll(mw);
                 acc += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
             }
             if (lane == 0) {
-                misc[1] = np;
+                misc[1] = cn;
+                misc[3] = cw;
                 misc[2] = a.qbound[q];
             }
             if (lane < WAVES)
                 pub[lane] = float_order_key(INFINITY);
         }
         __syncthreads();
-        np = __builtin_amdgcn_readfirstlane((int)misc[1]);
+        nn = __builtin_amdgcn_readfirstlane((int)misc[1]);
+        nw = __builtin_amdgcn_readfirstlane((int)misc[3]);
+        ngn = (nn + PG - 1) / PG;
         if constexpr (QT) {
             // the query term of this thread's sub-quantizers and code value
             // (the codebook pointer made opaque here: loads the compiler
@@ -503,7 +592,7 @@ void scan_items_kernel(ScanArgs a)
                  (a.k + WAVES - 1) / WAVES);
         float sink = INFINITY, published = INFINITY;
 
-        const int ng = (np + PG - 1) / PG;
+        const int ng = ngn + nw;
         if (ng > 0) {
             residual_group(0, 0);
             __syncthreads();
@@ -520,8 +609,9 @@ void scan_items_kernel(ScanArgs a)
             if constexpr (!SO)
                 sel.bound(read_bound(&misc[2]));
             const int pn = group_size(grp);
+            const bool gwide = group_wide(grp);
             for (int pp = 0; pp < pn; ++pp) {
-            const int pi = grp * PG + pp;
+            const int pi = piece_index(grp, pp);
             void *lut = tabp(grp & 1, pp);
             // the wave that starts a piece rotates, so that a group of short
             // lists spreads over the waves
@@ -544,13 +634,55 @@ void scan_items_kernel(ScanArgs a)
                 constexpr uint32_t WSTRIDE = SPAN * WAVES;   // entries per workgroup-step
                 constexpr size_t PSTEP = (size_t)WSTRIDE * M;
                 using Row = CodeRow<M * EPL>;
+                // row tables: byte 0 of the address of step t (its column
+                // and buffer half), four steps per word
+                uint32_t zlo = 0, zhi = 0;
+                if constexpr (WIDE) {
+                    const uint32_t l5 = (uint32_t)(lane & 31), sx = l5 >> 2;
+                    const uint32_t col0 =
+                        (uint32_t)(reinterpret_cast<unsigned char *>(lut) - tab);  // 128 b + 32 p
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const uint32_t z = gwide ? ((col0 & 128u) | ((l5 << 2) ^ (uint32_t)(t << 4)))
+                                                 : (col0 | (((uint32_t)t ^ sx) << 2));
+                        if (t < 4)
+                            zlo |= z << (8 * t);
+                        else
+                            zhi |= z << (8 * (t - 4));
+                    }
+                }
                 // FULL: every entry of the step exists (no per-lane bound)
                 auto consume = [&](auto full, const Row &row, uint32_t first, uint32_t limit) {
                     constexpr bool FULL = decltype(full)::value;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) {
                         const uint32_t i = first + e;
-                        float r = adc_words<M, F16>(row.w + e * (M / 4), lut);
+                        float r;
+                        if constexpr (WIDE) {
+                            // code of sub-quantizer t ^ s into byte t (s = (l & 31) >> 2)
+                            const uint32_t lo = row.w[2 * e], hi = row.w[2 * e + 1];
+                            const uint32_t nl = __builtin_amdgcn_perm(hi, lo, perm_lo);
+                            const uint32_t nh = __builtin_amdgcn_perm(hi, lo, perm_hi);
+                            float tv[8];
+#pragma unroll
+                            for (int t = 0; t < 8; ++t) {
+                                // address = (c << 8) | z_t: byte 1 <- code byte t & 3 of
+                                // the permuted word, byte 0 <- byte t & 3 of z, bytes 2-3 <- 0
+                                const uint32_t SEL = (uint32_t)(t & 3) |
+                                                         ((uint32_t)(4 + (t & 3)) << 8) |
+                                                         (0x0cu << 16) | (0x0cu << 24);
+                                const uint32_t ad = __builtin_amdgcn_perm(t < 4 ? nl : nh,
+                                                                          t < 4 ? zlo : zhi, SEL);
+                                // the row tables sit at LDS address 0: read through an
+                                // LDS pointer made from the address itself (a DS read with
+                                // no add for the array base)
+                                tv[t] = *reinterpret_cast<const __attribute__((address_space(3))) float *>(
+                                    (uintptr_t)ad);
+                            }
+                            r = sum_terms<8, true>(tv);
+                        } else {
+                            r = adc_words<M, F16>(row.w + e * (M / 4), lut);
+                        }
                         if constexpr (!FULL)
                             r = i < limit ? r : INFINITY;
                         if constexpr (SO)
@@ -729,6 +861,17 @@ static int cu_count()
             n = 256;
     }
     return n;
+}
+
+// Pieces of at least this many entries get the replicated table of the m 8
+// scan (its build writes four copies of every entry, which a short piece's
+// lookups do not repay); IVFPQ_SCAN_WIDE_MIN overrides it, read at every
+// search (tuning, and tests that force either table form).
+static uint32_t wide_min_entries()
+{
+    const char *e = std::getenv("IVFPQ_SCAN_WIDE_MIN");
+    const long long x = e ? std::atoll(e) : 4096;
+    return x < 1 ? 1u : (x > 0x7FFFFFFFll ? 0x7FFFFFFFu : (uint32_t)x);
 }
 
 // Tables per group: as many as 32 KiB holds (1..8), two groups resident.
@@ -915,6 +1058,7 @@ hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     a.out_i = s.out_i;
     a.ip = s.metric;
     a.osign = s.metric ? -1.f : 1.f;
+    a.wide_min = wide_min_entries();
     switch (nw_of(s.k)) {
     case 1: return scan_nw<1>(a, pl, s.lut, s.mode, stream);
     case 2: return scan_nw<2>(a, pl, s.lut, s.mode, stream);

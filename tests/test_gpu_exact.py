@@ -152,6 +152,23 @@ def test_exact_l2(m, dsub, lut):
     assert_exact(idx, q[:1], nlist, 10, d, i, p)
 
 
+@pytest.mark.parametrize("wide_min", ["1", "300", "100000000"])
+def test_exact_l2_m8_table_forms(monkeypatch, wide_min):
+    """The (m 8, dsub 12) scan with every piece in the replicated table form
+    (wide_min 1), a mix of both forms (300: lists of this index hold about
+    600 entries, cut into pieces of any size by the items), and none."""
+    monkeypatch.setenv("IVFPQ_SCAN_WIDE_MIN", wide_min)
+    idx, q = exact_case(8, 12, seed=812)
+    nlist = idx.nlist
+    for nprobe, k, chunk in [(nlist, 100, 0), (nlist, 100, 256), (nlist, 100, 700), (3, 100, 0),
+                             (nlist, 1, 64), (2, 1024, 0)]:
+        say(f"exact l2 m=8 dsub=12 wide_min={wide_min} nprobe={nprobe} k={k} chunk={chunk}")
+        d, i, p = run(idx, q, nprobe, k, chunk_len=chunk)
+        assert_exact(idx, q, nprobe, k, d, i, p)
+        if nprobe == nlist:
+            assert np.all(d[0::3, 0] == 0.0)
+
+
 @pytest.mark.parametrize("m,dsub", SHAPES)
 def test_exact_inner_product(m, dsub):
     idx, q = exact_case(m, dsub, seed=7 * m + dsub)

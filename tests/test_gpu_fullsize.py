@@ -32,32 +32,39 @@ def sample_rows(nq, count, seed):
 
 
 def search_and_check(A, w, runs=(("f32", "l2"),), sample=16, giant=0):
-    """runs: (table type, metric) pairs searched on one upload of the index.
-    giant: also check this many rows whose probes include a list of more
-    than 10^6 entries (the longest lists of a skewed index)."""
+    """runs: (table type, metric[, sample, giant]) searched on one upload of
+    the index; sample rows are checked against the oracle, plus (giant)
+    rows whose probes include a list of more than 10^6 entries (the longest
+    lists of a skewed index)."""
     t = time.time()
     ix = A.ivfpq_load_index_host(w.index, device=0)
     q = torch.from_numpy(w.queries).cuda()
     print(f"  {w.name}: index uploaded ({time.time() - t:.1f} s)", flush=True)
-    for lut, metric in runs:
+    for run in runs:
+        lut, metric = run[:2]
+        n_sample, n_giant = (run[2], run[3]) if len(run) > 2 else (sample, giant)
         t = time.time()
         d, i, p = A.ivfpq_search_ex(ix, q, w.nprobe, w.k, lut=lut, metric=metric,
                                     return_probes=True)
         torch.cuda.synchronize()
         print(f"  {w.name} lut={lut} metric={metric}: searched {len(w.queries)} queries "
               f"({time.time() - t:.1f} s)", flush=True)
-        rows = sample_rows(len(w.queries), sample, 11)
-        if giant:
+        rows = sample_rows(len(w.queries), n_sample, 11)
+        if n_giant:
             big = np.flatnonzero(np.asarray(w.index.list_sizes) > 1_000_000)
             hits = np.flatnonzero(np.isin(p.cpu().numpy(), big).any(axis=1))
             print(f"  {len(hits)} queries probe one of the {len(big)} lists above 10^6 "
-                  f"entries; checking {min(giant, len(hits))} of them", flush=True)
-            rows = np.unique(np.concatenate([rows, hits[:giant]]))
+                  f"entries; checking {min(n_giant, len(hits))} of them", flush=True)
+            rows = np.unique(np.concatenate([rows, hits[:n_giant]]))
         mode = O.IP if metric == "ip" else O.LUT_F16 if lut == "f16" else O.LUT_F64
+        t = time.time()
+        decomposed = bool(A.ivfpq_index_info(ix)["flags"] & 1) and lut == "f32" \
+            and metric == "l2"
         rep = check.compare_search(w.index, w.queries[rows], w.nprobe, w.k,
                                    d.cpu().numpy()[rows], i.cpu().numpy()[rows],
-                                   p.cpu().numpy()[rows], lut_mode=mode)
-        print(f"  parity {rep.summary()}", flush=True)
+                                   p.cpu().numpy()[rows], lut_mode=mode, decomposed=decomposed)
+        print(f"  parity {rep.summary()} on {len(rows)} rows ({time.time() - t:.1f} s)",
+              flush=True)
         assert rep.ok(), rep.failures[:5]
     ix.close()
 
@@ -89,7 +96,8 @@ def test_fullsize_zipf_1b(A):
     w = G.zipf_workload()
     # squared L2 (float32 and binary16 tables) and the inner-product metric
     # (the lists were built for L2, which the metric does not assume)
-    search_and_check(A, w, runs=(("f32", "l2"), ("f16", "l2"), ("f32", "ip")), giant=2)
+    search_and_check(A, w, runs=(("f32", "l2", 200, 40), ("f16", "l2", 48, 8),
+                                 ("f32", "ip", 48, 8)))
 
 
 def test_fullsize_flat_bf16(A):

@@ -178,3 +178,4 @@ def test_large_totals_do_not_wrap(driver):
     assert sum(it["stop"] - it["start"] for it in q["items"]) == 3_000_000_000
     mid = [it for it in q["items"] if len(it["pieces"]) == 2]
     assert len(mid) == 1 and mid[0]["pieces"][0][2] == 1_500_000_007
+
