@@ -585,7 +585,8 @@ namespace {
 // (imax items per query; a query with one item writes its rows from the
 // scan, so imax = 1 needs no partials).
 struct WsLayout {
-    size_t probes, total, chunk, count, base, bound, counter, coarse, pd, pp, bytes;
+    size_t probes, total, chunk, count, base, bound, counter, order_q, order_r, rank_n, coarse,
+        pd, pp, bytes;
 };
 
 WsLayout ws_layout(const DeviceIndex &dx, int64_t nq, int nprobe, int k, uint32_t imax,
@@ -605,6 +606,9 @@ WsLayout ws_layout(const DeviceIndex &dx, int64_t nq, int nprobe, int k, uint32_
     o.base = carve(((size_t)nq + 1) * 4);
     o.bound = carve((size_t)nq * 4);
     o.counter = carve(4);
+    o.order_q = carve((size_t)nq * imax * 4);
+    o.order_r = carve((size_t)nq * imax * 4);
+    o.rank_n = carve((size_t)imax * 4);
     o.coarse = carve(coarse_ws_bytes(dx, nq, nprobe));
     const size_t part = imax > 1 ? (size_t)nq * imax * (size_t)kw_of(k) * 4 : 0;
     o.pd = carve(part);
@@ -699,6 +703,9 @@ ivfpq_status search_impl(ivfpq_index *idx, const ivfpq_search_params *p, const f
     pl.item_base = reinterpret_cast<uint32_t *>(ws + o.base);
     pl.qbound = reinterpret_cast<uint32_t *>(ws + o.bound);
     pl.counter = reinterpret_cast<uint32_t *>(ws + o.counter);
+    pl.item_q = reinterpret_cast<uint32_t *>(ws + o.order_q);
+    pl.item_r = reinterpret_cast<uint32_t *>(ws + o.order_r);
+    pl.rank_n = reinterpret_cast<uint32_t *>(ws + o.rank_n);
     pl.part_d = reinterpret_cast<float *>(ws + o.pd);
     pl.part_p = reinterpret_cast<uint32_t *>(ws + o.pp);
     const bool recording = idx->profiling && idx->prof_calls < idx->prof_max;

@@ -52,6 +52,9 @@ struct SearchPlan {
     int64_t max_items = 0; // nq * imax
     uint32_t *qtotal = nullptr, *qchunk = nullptr, *qcount = nullptr, *item_base = nullptr;
     uint32_t *qbound = nullptr, *counter = nullptr;
+    // scan order of the items, rank-major: position i holds query item_q[i]'s
+    // item number item_r[i]; rank_n[r] = queries with more than r items
+    uint32_t *item_q = nullptr, *item_r = nullptr, *rank_n = nullptr;
     float *part_d = nullptr;   // [max_items][kw]
     uint32_t *part_p = nullptr; // [max_items][kw]
     // when not null: [0] += entries of the probed lists, [1] += work items

@@ -124,6 +124,77 @@ __global__ __launch_bounds__(1024) void item_scan_kernel(const uint32_t *__restr
     }
 }
 
+// Scan order of the work items, rank-major: item 0 of every query (queries
+// in order), then item 1 of every query that has one, and so on.  The items
+// of one query then start at different times, and a later one begins with
+// the bound its query's earlier items have published (their k-th values
+// bound the query's), so its k-selection admits few candidates; with the
+// items of a query side by side in the order, all of them would start from
+// an empty top-k at once.  Two kernels, one workgroup per rank r < imax:
+// the number of queries with more than r items, then the positions.
+__global__ __launch_bounds__(1024) void rank_count_kernel(const uint32_t *__restrict__ qcount,
+                                                          int64_t nq, uint32_t *__restrict__ rank_n)
+{
+    __shared__ uint32_t wsum[16];
+    const uint32_t r = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t c = 0;
+    for (int64_t i = tid; i < nq; i += 1024)
+        c += qcount[i] > r ? 1u : 0u;
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1)
+        c += (uint32_t)__shfl_xor((int)c, sh);
+    if (lane == 0)
+        wsum[wave] = c;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < 16; ++w)
+            t += wsum[w];
+        rank_n[r] = t;
+    }
+}
+
+__global__ __launch_bounds__(1024) void rank_order_kernel(const uint32_t *__restrict__ qcount,
+                                                          int64_t nq,
+                                                          const uint32_t *__restrict__ rank_n,
+                                                          uint32_t *__restrict__ item_q,
+                                                          uint32_t *__restrict__ item_r)
+{
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t carry_s;
+    const uint32_t r = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid == 0) {
+        uint32_t b = 0;
+        for (uint32_t s = 0; s < r; ++s)
+            b += rank_n[s];
+        carry_s = b;
+    }
+    __syncthreads();
+    for (int64_t s = 0; s < nq; s += 1024) {
+        const int64_t i = s + tid;
+        const uint32_t v = (i < nq && qcount[i] > r) ? 1u : 0u;
+        const uint32_t incl = wave_inclusive_sum(v);
+        if (lane == 63)
+            wsum[wave] = incl;
+        __syncthreads();
+        uint32_t before = carry_s;
+        for (int w = 0; w < wave; ++w)
+            before += wsum[w];
+        if (v) {
+            item_q[before + incl - 1] = (uint32_t)i;
+            item_r[before + incl - 1] = r;
+        }
+        __syncthreads();
+        if (tid == 1023)
+            carry_s = before + incl;
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // scan
 // ---------------------------------------------------------------------------
@@ -139,7 +210,7 @@ struct ScanArgs {
     const uint8_t *codes;
     const int64_t *ids;
     const int32_t *probes;
-    const uint32_t *qtotal, *qchunk, *item_base;
+    const uint32_t *qtotal, *qchunk, *item_base, *item_q, *item_r;
     uint32_t *qbound;
     uint32_t *counter;
     int64_t nq;
@@ -501,20 +572,14 @@ void scan_items_kernel(ScanArgs a)
         const uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane((int)misc[0]);
         if (item >= total_items)
             break;
-        // the query owning this item: last q with item_base[q] <= item
-        int64_t lo = 0, hi = a.nq - 1;
-        while (lo < hi) {
-            const int64_t mid = (lo + hi + 1) >> 1;
-            if (a.item_base[mid] <= item)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        const int64_t q = lo;
+        // the query and item number at this position of the scan order
+        const int64_t q = (int64_t)__builtin_amdgcn_readfirstlane((int)a.item_q[item]);
+        const uint32_t rk = (uint32_t)__builtin_amdgcn_readfirstlane((int)a.item_r[item]);
         const uint32_t first = a.item_base[q];
         const uint32_t count = a.item_base[q + 1] - first;
+        const uint32_t slot = first + rk; // the item's partial top-k
         uint32_t start, stop;
-        item_range(item - first, a.qchunk[q], a.qtotal[q], &start, &stop);
+        item_range(rk, a.qchunk[q], a.qtotal[q], &start, &stop);
 
         for (int t = tid; t < d; t += THREADS)
             xs[t] = a.queries[q * d + t];
@@ -704,6 +769,11 @@ void scan_items_kernel(ScanArgs a)
                         // this step leaves the next step's load in flight
                         Row nxt;
                         nxt.load(more ? p + PSTEP : p);
+                        // keep the next step's loads ahead of this step's scan:
+                        // the scheduler would otherwise sink them below it into
+                        // the current step's registers, and every step would
+                        // wait for its own load with nothing in flight
+                        __builtin_amdgcn_sched_barrier(0);
                         consume(std::true_type{}, cur, s0 + lane * EPL, 0u);
                         s0 = n0;
                         p += PSTEP;
@@ -790,7 +860,7 @@ void scan_items_kernel(ScanArgs a)
                 } else {
 #pragma unroll
                     for (int r = 0; r < NW; ++r) {
-                        const size_t e = (size_t)item * (64 * NW) + r * 64 + lane;
+                        const size_t e = (size_t)slot * (64 * NW) + r * 64 + lane;
                         a.part_d[e] = sel.wk[r];
                         a.part_p[e] = sel.wv[r];
                     }
@@ -1019,6 +1089,16 @@ hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
         return e;
     hipLaunchKernelGGL(item_scan_kernel, dim3(1), dim3(1024), 0, stream, pl.qcount, s.nq,
                        pl.item_base, pl.prof);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(rank_count_kernel, dim3(pl.imax), dim3(1024), 0, stream, pl.qcount, s.nq,
+                       pl.rank_n);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(rank_order_kernel, dim3(pl.imax), dim3(1024), 0, stream, pl.qcount, s.nq,
+                       pl.rank_n, pl.item_q, pl.item_r);
     return hipGetLastError();
 }
 
@@ -1049,6 +1129,8 @@ hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     a.qtotal = pl.qtotal;
     a.qchunk = pl.qchunk;
     a.item_base = pl.item_base;
+    a.item_q = pl.item_q;
+    a.item_r = pl.item_r;
     a.qbound = pl.qbound;
     a.counter = pl.counter;
     a.nq = s.nq;
