@@ -84,7 +84,7 @@ constexpr int kStages = 4; // coarse, worklist, scan, merge
 // Minimum entries per scan work item when the caller passes chunk_len = 0.
 // Large items amortise the top-k warm-up (every wave of an item starts from an
 // empty queue); the imax cap still splits long queries across workgroups.
-constexpr uint32_t kDefaultChunk = 131072;
+constexpr uint32_t kDefaultChunk = 262144;
 
 int kw_of(int k)
 {

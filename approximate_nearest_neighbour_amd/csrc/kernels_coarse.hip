@@ -60,20 +60,61 @@ __global__ void centroid_blocks_kernel(const float *__restrict__ c, int d, int d
     }
 }
 
-// Workgroup of 16 waves in two roles, pipelined over the tiles of its range
-// (one barrier per tile, distance tiles double-buffered in LDS):
+// Distance tiles pass between the two roles of the coarse kernel through a
+// ring of kRing buffers in LDS with two counters per buffer, instead of a
+// workgroup barrier per tile: the roles take about as long per tile, and a
+// barrier made each wait for the other's slower tiles.  Counters only grow:
+// a matrix wave adds 1 to produced[b] once its part of a tile is in buffer b
+// (8 parts per tile), a selection wave adds 1 to consumed[b] once it has
+// read its rows (8 readers).  Waits are bounded: a wait that takes more than
+// 2^22 polls sets `broken`, and from then on every wait returns at once (the
+// kernel then ends with wrong probes instead of hanging; never expected).
+constexpr int kRing = 4;
+
+__device__ __forceinline__ void ring_wait(const uint32_t *ctr, uint32_t target, uint32_t *broken)
+{
+    uint32_t n = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        if (__hip_atomic_load(broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u)
+            break;
+        if (++n > (1u << 22)) {
+            __hip_atomic_store(broken, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    // the buffer's LDS accesses stay after the wait
+    __asm__ volatile("" ::: "memory");
+}
+
+// Count this wave's LDS writes (or reads) of a buffer once they are complete;
+// the wait covers LDS operations only, so global loads in flight (the next
+// tile's B operand) stay in flight.
+__device__ __forceinline__ void ring_signal(uint32_t *ctr)
+{
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Workgroup of 16 waves in two roles over the tiles of its range, meeting in
+// the ring of distance tiles:
 //  * 8 matrix waves: wave w computes column block w%4 of row groups
-//    RPW*(w/4) .. +RPW of tile t+1 (A operand of its rows in registers, the
-//    next tile's B operand prefetched) and writes |x|^2 + |c|^2 - 2 x.c;
+//    RPW*(w/4) .. +RPW of a tile (A operand of its rows in registers, the
+//    next tile's B operand prefetched) and writes |x|^2 + |c|^2 - 2 x.c:
+//    the accumulators start at |x|^2 + |c|^2 and the A operand holds -2 x,
+//    so the products are added onto the norms and the result goes to LDS
+//    as it is (inner product: they start at 0 and A holds -x, giving
+//    -<x, c>);
 //  * 8 selection waves: each owns QS = TQ/8 queries and pushes their 64
-//    distances of tile t into its register top-k (WaveTopK).
+//    distances of a tile into its register top-k (WaveTopK).
 // So the matrix cores and the selection run at the same time on every SIMD.
-template <int NW, int RG, int RPW, int KD>
+template <int NW, int RG, int RPW, int KD, bool IP>
 __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
     const float *__restrict__ queries, int64_t nq, int d, int nblk, int nprobe,
     const float *__restrict__ cblk, const float *__restrict__ cnorm_pad, int splits,
     float *__restrict__ part_d, uint32_t *__restrict__ part_p, uint32_t *__restrict__ qbound,
-    int32_t *__restrict__ probes, float *__restrict__ probe_d, int ip)
+    uint32_t *__restrict__ pslot, int32_t *__restrict__ probes, float *__restrict__ probe_d)
 {
     constexpr int TQ = 16 * RG, THREADS = 1024, MW = 8, QS = TQ / 8, KW = 64 * NW;
     static_assert(4 * RG / RPW == MW, "eight matrix waves");
@@ -81,8 +122,11 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
     const int xs = 4 * KD + 1; // odd stride: the 16 rows of an A read hit 16 banks
     float *xt = reinterpret_cast<float *>(smem);                      // [TQ][xs]
     float *xn = xt + TQ * xs;                                          // [TQ]
-    float *dt = xn + TQ;                                               // [2][TQ][64]
-    uint32_t *stage = reinterpret_cast<uint32_t *>(dt + 2 * TQ * 64); // [TQ][128]
+    float *dt = xn + TQ;                                                   // [kRing][TQ][64]
+    uint32_t *stage = reinterpret_cast<uint32_t *>(dt + kRing * TQ * 64); // [TQ][128]
+    uint32_t *produced = stage + TQ * 128;                                 // [kRing]
+    uint32_t *consumed = produced + kRing;                                 // [kRing]
+    uint32_t *broken = consumed + kRing;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
@@ -107,19 +151,25 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
             acc = fmaf(xt[tid * xs + c], xt[tid * xs + c], acc);
         xn[tid] = acc;
     }
+    if (tid < 2 * kRing + 1)
+        produced[tid] = 0u; // produced, consumed, broken
     __syncthreads();
 
-    // The two roles run separate loops with the same barriers (1 + tiles), so
-    // each keeps only its own registers live.
+    // The two roles run separate loops, so each keeps only its own registers
+    // live.
     if (matrix) {
         // A layout of 16x16x4: lane l supplies row l%16, K-index l/16 of each step
+        // (scaled by -2, or -1 for the inner product: exact; the sign flip is
+        // an integer operation, as a float negation here was folded into
+        // the operands at the cost of a second copy of A)
         float a[RPW][KD];
 #pragma unroll
         for (int g = 0; g < RPW; ++g) {
             const float *ap = xt + ((rg0 + g) * 16 + (lane & 15)) * xs + (lane >> 4);
 #pragma unroll
             for (int s = 0; s < KD; ++s)
-                a[g][s] = ap[4 * s];
+                a[g][s] = IP ? __int_as_float(__float_as_int(ap[4 * s]) ^ (int)0x80000000)
+                             : -2.f * ap[4 * s];
         }
         // |x|^2 of the 4*RPW query rows this lane holds in the D layout
         float xr[RPW][4];
@@ -146,99 +196,131 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
             }
             cn = cnorm_pad[(tile * 4 + cbk) * 16 + (lane & 15)];
         };
-        // tile `tile` into LDS buffer tile&1, prefetching the next tile
+        // tile `tile` into its ring buffer, prefetching the next tile's B
+        // operand; the buffer is taken once the selection waves have read
+        // the tile that held it kRing tiles before
         auto multiply = [&](int tile, const float (&bc)[KD], float cc, float (&bn)[KD],
                             float &cnext) {
             const int col = lane & 15;
             load_b(tile + 1, bn, cnext);
             // keep the next tile's loads ahead of this tile's MFMAs (the
-            // scheduler would otherwise sink them to the barrier)
+            // scheduler would otherwise sink them below)
             __builtin_amdgcn_sched_barrier(0);
-            float *dtile = dt + (tile & 1) * TQ * 64;
+            const int rb = (tile - t0) % kRing;
+            const uint32_t visit = (uint32_t)((tile - t0) / kRing);
+            if (visit > 0)
+                ring_wait(&consumed[rb], 8u * visit, broken);
+            float *dtile = dt + rb * TQ * 64;
+            // inner product: a padding centroid (norm +inf) starts at +inf
+            const float ic = cc == INFINITY ? INFINITY : 0.f;
 #pragma unroll
             for (int g = 0; g < RPW; ++g) {
-                v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+                v4f acc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[r] = IP ? ic : xr[g][r] + cc;
 #pragma unroll
                 for (int s = 0; s < KD; ++s)
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g][s], bc[s], acc, 0, 0, 0);
                 // D layout of 16x16x4: lane l holds rows 4*(l/16) + r of column l%16
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = (rg0 + g) * 16 + 4 * (lane >> 4) + r;
-                    // inner-product metric: -<x, c>, padding centroids (norm
-                    // +inf) kept out the same way
-                    dtile[row * 64 + cbk * 16 + col] =
-                        ip ? (cc == INFINITY ? INFINITY : -acc[r]) : xr[g][r] + cc - 2.f * acc[r];
-                }
+                for (int r = 0; r < 4; ++r)
+                    dtile[((rg0 + g) * 16 + 4 * (lane >> 4) + r) * 64 + cbk * 16 + col] = acc[r];
             }
+            ring_signal(&produced[rb]);
         };
-        if (t0 < t1) {
+        if (t0 < t1)
             load_b(t0, b0, c0);
-            multiply(t0, b0, c0, b1, c1);
-        }
-        lds_barrier();
-        // iteration t: produce tile t+1 while the selection waves consume t
         int t = t0;
-        for (; t + 2 < t1; t += 2) {
+        for (; t + 1 < t1; t += 2) {
+            multiply(t, b0, c0, b1, c1);
             multiply(t + 1, b1, c1, b0, c0);
-            lds_barrier();
-            multiply(t + 2, b0, c0, b1, c1);
-            lds_barrier();
         }
-        for (; t < t1; ++t) {
-            if (t + 1 < t1)
-                multiply(t + 1, b1, c1, b0, c0);
-            lds_barrier();
-        }
+        if (t < t1)
+            multiply(t, b0, c0, b1, c1);
         return;
     }
 
+    // Splits of a query share two bounds on its k-th smallest distance:
+    //  * each split's k-th value (its k values are at most that), the
+    //    smallest over the splits kept by an atomic min per query;
+    //  * each split's rk-th value, rk = ceil(k / splits), in a slot of its
+    //    own: every split has rk values at most its slot, so the union of the
+    //    splits has >= k values at most the largest slot (+inf until every
+    //    split has published), a far tighter bound early in the sweep.
+    // Every 8 tiles a wave publishes its queries' values and loads the shared
+    // ones, which it applies a tile later (the loads complete meanwhile).
+    // Values only decrease, so a stale load is a weaker bound, never a wrong
+    // one.  Lane i of a selection wave handles query i for the k-th value;
+    // the slots of query i, split s are loaded by lane i + 8 (s % 8), two
+    // loads for up to 16 splits (more splits use the first bound only).
+    const int rk = splits > 1 ? (nprobe + splits - 1) / splits : nprobe;
     WaveTopK<NW> sel[QS];
 #pragma unroll
     for (int i = 0; i < QS; ++i)
-        sel[i].init(nprobe, stage + (sw * QS + i) * 128);
-    lds_barrier();
-    // Splits of a query share a bound: each split's k-th value is >= the
-    // query's k-th, so the smallest of them filters every split.  Every 8
-    // tiles a wave publishes its k-th values (atomic min, no wait) and reads
-    // the shared ones, which it applies a tile later (the loads complete
-    // meanwhile).
-    // Lane i of a selection wave handles query i of the wave here: one
-    // atomic and one load per exchange, the loaded value kept in a vector
-    // register until it is applied (so nothing waits for it).
+        sel[i].init(nprobe, stage + (sw * QS + i) * 128, rk);
     int64_t ql = q0 + sw * QS + (lane < QS ? lane : 0);
     const bool qvalid = lane < QS && ql < nq;
     ql = ql < nq ? ql : nq - 1; // the loads stay unconditional
+    const bool use_slots = splits > 1 && splits <= 16;
+    const int64_t qs = q0 + sw * QS + (lane & 7);
+    const bool slot_q = (lane & 7) < QS && qs < nq;
+    const int s_lo = lane >> 3, s_hi = 8 + (lane >> 3);
+    const uint32_t *ps_lo = pslot + (slot_q && s_lo < splits ? qs * splits + s_lo : 0);
+    const uint32_t *ps_hi = pslot + (slot_q && s_hi < splits ? qs * splits + s_hi : 0);
+    const bool lo_ok = slot_q && s_lo < splits, hi_ok = slot_q && s_hi < splits;
     uint32_t nb = float_order_key(INFINITY);
+    uint32_t nu0 = 0u, nu1 = 0u; // order key 0 is below every float: neutral for max
     bool pending = false;
     for (int t = t0; t < t1; ++t) {
         if (pending) {
+            uint32_t u = nu0 > nu1 ? nu0 : nu1;
+            uint32_t o = xor_lane<8>(u);
+            u = u > o ? u : o;
+            o = xor_lane<16>(u);
+            u = u > o ? u : o;
+            o = xor_lane<32>(u);
+            u = u > o ? u : o;
+            u = use_slots ? u : float_order_key(INFINITY);
+            const uint32_t b = nb < u ? nb : u;
 #pragma unroll
             for (int i = 0; i < QS; ++i)
-                sel[i].bound(
-                    float_from_order_key((uint32_t)__builtin_amdgcn_readlane((int)nb, i)));
+                sel[i].bound(float_from_order_key((uint32_t)__builtin_amdgcn_readlane((int)b, i)));
             pending = false;
         }
         // all reads first (one LDS round trip), then the selections
-        const float *dtile = dt + (t & 1) * TQ * 64;
+        const int rb = (t - t0) % kRing;
+        ring_wait(&produced[rb], 8u * (uint32_t)((t - t0) / kRing + 1), broken);
+        const float *dtile = dt + rb * TQ * 64;
         float cand[QS];
 #pragma unroll
         for (int i = 0; i < QS; ++i)
             cand[i] = dtile[(sw * QS + i) * 64 + lane];
+        ring_signal(&consumed[rb]);
 #pragma unroll
         for (int i = 0; i < QS; ++i)
             sel[i].push(cand[i], (uint32_t)(t * 64 + lane));
         if (splits > 1 && ((t - t0) & 7) == 7) {
-            float mine = INFINITY;
+            float mine = INFINITY, mpart = INFINITY;
 #pragma unroll
-            for (int i = 0; i < QS; ++i)
+            for (int i = 0; i < QS; ++i) {
                 mine = lane == i ? sel[i].kth : mine;
+                mpart = lane == i ? sel[i].part : mpart;
+            }
             if (qvalid && mine < INFINITY)
                 atomicMin(qbound + ql, float_order_key(mine));
+            if (use_slots && qvalid)
+                __hip_atomic_store(pslot + ql * splits + split, float_order_key(mpart),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             nb = __hip_atomic_load(qbound + ql, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (use_slots) {
+                nu0 = __hip_atomic_load(ps_lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                nu1 = __hip_atomic_load(ps_hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                nu0 = lo_ok ? nu0 : 0u;
+                nu1 = hi_ok ? nu1 : 0u;
+            }
             pending = true;
         }
-        lds_barrier();
     }
 #pragma unroll
     for (int i = 0; i < QS; ++i) {
@@ -540,10 +622,11 @@ static void coarse_shape(int64_t nq, int nblk, int d4, int *rg, int *splits)
     *splits = best;
 }
 
-__global__ void coarse_bound_init_kernel(uint32_t *__restrict__ qbound, int64_t nq)
+// Shared bounds of the splits: per query, then per (query, split) slot.
+__global__ void coarse_bound_init_kernel(uint32_t *__restrict__ qbound, int64_t n)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < nq)
+    if (i < n)
         qbound[i] = float_order_key(INFINITY);
 }
 
@@ -577,7 +660,10 @@ size_t coarse_ws_bytes(const DeviceIndex &ix, int64_t nq, int nprobe)
         return 0;
     int rg, splits;
     coarse_shape(nq, ix.nblk, ix.d4, &rg, &splits);
-    return splits > 1 ? (size_t)nq * splits * 64 * nw * 8 + (size_t)nq * 4 : 0;
+    // partial top-k of every split, the per-query bound, the per-split slots
+    return splits > 1 ? (size_t)nq * splits * 64 * nw * 8 + (size_t)nq * 4 +
+                            (size_t)nq * splits * 4
+                      : 0;
 }
 
 template <int NW, int RG, int RPW, int KD>
@@ -586,8 +672,10 @@ static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *querie
                                       float *probe_d, hipStream_t stream, bool ip)
 {
     constexpr int TQ = 16 * RG;
-    const size_t lds = (size_t)TQ * (4 * KD + 1) * 4 + TQ * 4 + 2 * TQ * 64 * 4 + TQ * 512;
-    auto kern = coarse_mfma_kernel<NW, RG, RPW, KD>;
+    const size_t lds = (size_t)TQ * (4 * KD + 1) * 4 + TQ * 4 + (size_t)kRing * TQ * 64 * 4 +
+                       TQ * 512 + (2 * kRing + 1) * 4;
+    auto kern = ip ? coarse_mfma_kernel<NW, RG, RPW, KD, true>
+                   : coarse_mfma_kernel<NW, RG, RPW, KD, false>;
     if (lds > 160 * 1024)
         return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
@@ -599,17 +687,19 @@ static hipError_t coarse_mfma_variant(const DeviceIndex &ix, const float *querie
     float *part_d = static_cast<float *>(ws);
     uint32_t *part_p = reinterpret_cast<uint32_t *>(part_d + (size_t)nq * splits * 64 * NW);
     uint32_t *qbound = part_p + (size_t)nq * splits * 64 * NW;
+    uint32_t *pslot = qbound + nq;
     if (splits > 1) {
-        hipLaunchKernelGGL(coarse_bound_init_kernel, dim3((unsigned)((nq + 255) / 256)),
-                           dim3(256), 0, stream, qbound, nq);
+        const int64_t n = nq * (1 + (int64_t)splits); // qbound and pslot are contiguous
+        hipLaunchKernelGGL(coarse_bound_init_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
+                           0, stream, qbound, n);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
     const dim3 grid((unsigned)((nq + TQ - 1) / TQ), (unsigned)splits);
     hipLaunchKernelGGL(kern, grid, dim3(1024), lds, stream, queries, nq, ix.d, ix.nblk, nprobe,
-                       ix.cblk, ix.cnorm_pad, splits, part_d, part_p, qbound, probes, probe_d,
-                       ip ? 1 : 0);
+                       ix.cblk, ix.cnorm_pad, splits, part_d, part_p, qbound, pslot, probes,
+                       probe_d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1)
         return e;

@@ -86,7 +86,7 @@ typedef enum {
  * [1, 1024]; lut selects the table precision (float32, or float32 computed
  * then stored as IEEE binary16 round-to-nearest-even; sums are float32 in
  * both).  chunk_len: the target number of entries of one scan work item
- * (0 = automatic, 131072).  It is a minimum, not a cap: a query whose probed
+ * (0 = automatic, 262144).  It is a minimum, not a cap: a query whose probed
  * lists hold E entries gets ceil(E / max(chunk_len, ceil(E / imax))) items,
  * imax (2..64) chosen from nq and k, so long queries get larger items.  The
  * result does not depend on it. */
