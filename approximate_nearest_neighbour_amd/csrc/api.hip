@@ -1251,7 +1251,7 @@ ivfpq_status ivfpq_flat_search_bf16_ex(const ivfpq_flat *cf, const uint16_t *que
         return fail(IVFPQ_E_NO_DEVICE, "cannot select device");
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const FlatDevice &fx = f->fx;
-    const FlatPlan plan = flat_plan(fx.n, k, nq);
+    const FlatPlan plan = flat_plan(fx.n, k, nq, fx.dp);
     const size_t per_q = flat_ws_bytes(plan, 1);
     // test hook: IVFPQ_TEST_FLAT_WS_BYTES=n caps the workspace (forces chunks)
     size_t budget = kFlatWsBudget;

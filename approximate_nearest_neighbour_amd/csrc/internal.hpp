@@ -122,9 +122,10 @@ struct FlatPlan {
     int seg = 1;
     int64_t nseg = 0, nslot = 0;
     uint32_t cap = 0;
+    int dp = 0; // padded row length (bf16)
 };
 
-FlatPlan flat_plan(int64_t n, int k, int64_t nq);
+FlatPlan flat_plan(int64_t n, int k, int64_t nq, int dp);
 size_t flat_ws_bytes(const FlatPlan &p, int64_t nq);
 hipError_t launch_flat_pack(const uint16_t *src, int64_t n, int d, int dp, int64_t npad,
                             uint16_t *dst, float *norms, hipStream_t stream);

@@ -5,23 +5,33 @@
 // gives the result; here bf16 x bf16 products with float32 sums on the
 // matrix cores, v_mfma_f32_16x16x32_bf16).
 //
-// The distance matrix is never stored.  Four passes per batch of queries:
+// The distance matrix is never stored.  Passes per batch of queries:
 //
-//  1. minima:  the GEMM over every 64-row tile; per query, each lane keeps the
-//              running minimum of u = |y|^2 - 2 x.y over the rows it sees in
-//              a segment of G tiles (16 rows per tile: its column in each of
-//              the 4 column blocks) and writes it out per segment: P = 16 *
-//              segments "slot minima" per query, each the value of a
-//              distinct row.
+//  0. prep:    the A operand, each query times -2 in bfloat16 (exact),
+//              padded to whole K-steps, and |x|^2 in float32.
+//  1. minima:  the GEMM over every 64-row tile.  The accumulators start at
+//              |y|^2 and the A operand holds -2x, so the matrix cores give
+//              u = |y|^2 - 2 x.y itself; per query, each lane keeps the
+//              running minimum of u over the rows it sees in a segment of G
+//              tiles (16 rows per tile: its column c in each of the 4 column
+//              blocks) and writes it out per segment: P = 16 * segments
+//              "slot minima" per query, slot (segment, c) covering 4 G rows.
 //  2. kth:     a value v with at least k slot minima <= v, close above the
 //              k-th smallest (histogram of the minima).  Those k slot rows
 //              are distinct rows with u <= v, so the k-th smallest distance is
 //              at most |x|^2 + v (plus rounding).  tu = v + slack, slack =
-//              2^-20 (|x|^2 + max |y|^2), covers the float32 rounding of u and
-//              of the distance.
-//  3. collect: the GEMM again; rows with u <= tu (a superset of the true top
-//              k, about k rows) are appended with their distance to the
-//              query's candidate buffer (capacity C).
+//              2^-20 (|x|^2 + max |y|^2), covers the float32 rounding of the
+//              distance |x|^2 + u.
+//  3. collect: only slots whose minimum is <= tu can hold a row with
+//              u <= tu.  Per segment, the queries are listed by hot slot and
+//              the slot's rows multiplied again, 16 queries at a time, with
+//              the same operands, start value and K order as in pass 1 (the
+//              same u to the bit); rows with u <= tu (a superset of the true
+//              top k, about k rows) are appended with their distance to the
+//              query's candidate buffer (capacity C).  About k of a query's
+//              P slots are hot, so this pass does a few percent of the
+//              GEMM's work.  (A second full GEMM with the bound test, the
+//              earlier form, remains behind a test switch for comparison.)
 //  4. select:  exact top-k of each buffer (four-wave register selection).
 //              A query whose candidates overflowed C (only when very many rows
 //              tie) is redone by `fallback`, an exact streaming selection over
@@ -29,6 +39,8 @@
 //
 #include "common.hpp"
 #include "internal.hpp"
+
+#include <cstdlib>
 
 namespace ivfpq {
 
@@ -70,40 +82,59 @@ __global__ void flat_pack_kernel(const uint16_t *__restrict__ src, int64_t n, in
         norms[i] = i < n ? bf16_row_norm(src + i * d, d) : INFINITY;
 }
 
-// A operand of 16x16x32: lane l supplies row l%16, K-indices 8*(l/16)..+7 of
-// each 32-wide K-step (the B operand uses the same K-split, so the dot
-// product does not depend on how the hardware pairs them).
-template <int KS>
-__device__ __forceinline__ void load_a(const uint16_t *__restrict__ q, int64_t nq, int d,
-                                       int64_t row, int lane, bf16x8 (&a)[KS])
+// Pass 0: qs = -2 x in bfloat16, rows padded to dp with zeros, and
+// qn = |x|^2 in float32.  -2 x is exact: x has at most 8 significant bits and
+// the product only moves the exponent, so the top half of its float32 bits is
+// the value.
+__global__ void flat_query_prep_kernel(const uint16_t *__restrict__ q, int64_t nq, int d, int dp,
+                                       uint16_t *__restrict__ qs, float *__restrict__ qn)
 {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nq * dp) {
+        const int64_t row = i / dp;
+        const int col = (int)(i % dp);
+        uint16_t v = 0;
+        if (col < d)
+            v = (uint16_t)(__float_as_uint(-2.f * bf16_to_float(q[row * d + col])) >> 16);
+        qs[i] = v;
+    }
+    if (i < nq)
+        qn[i] = bf16_row_norm(q + i * d, d);
+}
+
+// A operand of 16x16x32 from the padded -2x rows: lane l supplies row l%16,
+// K-indices 8*(l/16)..+7 of each 32-wide K-step (the B operand uses the same
+// K-split); rows past nq are zero.
+template <int KS>
+__device__ __forceinline__ void load_a(const uint16_t *__restrict__ qs, int64_t nq, int64_t row,
+                                       int lane, bf16x8 (&a)[KS])
+{
+    constexpr int DP = 32 * KS;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        u16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int k = 32 * s + 8 * (lane >> 4) + e;
-            v[e] = (row < nq && k < d) ? q[row * d + k] : (uint16_t)0;
-        }
+        u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (row < nq)
+            v = *reinterpret_cast<const u16x8 *>(qs + row * DP + 32 * s + 8 * (lane >> 4));
         a[s] = __builtin_bit_cast(bf16x8, v);
     }
 }
 
+// u = |y|^2 - 2 x.y of a 16x16 block: the chain starts at |y|^2 of the
+// block's column (yc, the same in the 4 values of a lane) and adds the
+// products of -2x and y, K-steps in order.  Every pass computes u this way,
+// so a row's u is the same value in all of them.
 template <int KS>
-__device__ __forceinline__ v4f mfma_block(const bf16x8 (&a)[KS], const bf16x8 (&b)[KS])
+__device__ __forceinline__ v4f mfma_u(const bf16x8 (&a)[KS], const bf16x8 (&b)[KS], float yc)
 {
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    v4f acc = v4f{yc, yc, yc, yc};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
     return acc;
 }
 
-// u = |y|^2 - 2 x.y: the distance less |x|^2, one instruction per pair.
-__device__ __forceinline__ float flat_u(float yn, float dot) { return fmaf(-2.f, dot, yn); }
-
-// Rounding allowance between u + |x|^2 and the float32 distance (both from
-// the same dot product): 16 units of 2^-24 of |x|^2 + max |y|^2.
+// Rounding allowance between |x|^2 + v and the float32 distances |x|^2 + u
+// of rows with u <= v: 16 units of 2^-24 of |x|^2 + max |y|^2.
 __device__ __forceinline__ float flat_slack(float xn, float ymax)
 {
     return 0x1p-20f * (xn + ymax);
@@ -124,10 +155,11 @@ constexpr int kFlatStage = 1024;
 template <int KS, int RB, int PASS>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(PASS == kPassCollect ? 3 : 1))) void flat_gemm_kernel(
-    const uint16_t *__restrict__ queries, int64_t nq, int d, const uint16_t *__restrict__ db,
-    const float *__restrict__ dbn, int64_t n, int64_t ntile, int seg, int64_t nseg, int splits,
-    float *__restrict__ slots, int64_t nslot, const float *__restrict__ tuq, uint32_t cap,
-    uint32_t *__restrict__ cnt, float *__restrict__ cand_d, uint32_t *__restrict__ cand_p)
+    const uint16_t *__restrict__ qs, const float *__restrict__ qn, int64_t nq,
+    const uint16_t *__restrict__ db, const float *__restrict__ dbn, int64_t n, int64_t ntile,
+    int seg, int64_t nseg, int splits, float *__restrict__ slots, int64_t nslot,
+    const float *__restrict__ tuq, uint32_t cap, uint32_t *__restrict__ cnt,
+    float *__restrict__ cand_d, uint32_t *__restrict__ cand_p)
 {
     constexpr int DP = 32 * KS, TQ = 64 * RB, RS = DP + 8; // LDS row stride (bf16), +16 B
     constexpr int CHUNKS = 64 * DP / 8 / 256;              // 16-byte pieces per thread per tile
@@ -153,7 +185,7 @@ __attribute__((amdgpu_waves_per_eu(PASS == kPassCollect ? 3 : 1))) void flat_gem
     if (PASS == kPassCollect) {
         for (int r = tid; r < TQ; r += 256) {
             const int64_t q = q0 + r;
-            xn[r] = q < nq ? bf16_row_norm(queries + q * d, d) : 0.f;
+            xn[r] = q < nq ? qn[q] : 0.f;
             tq[r] = q < nq ? tuq[q] : -INFINITY;
         }
         if (tid == 0)
@@ -182,7 +214,7 @@ __attribute__((amdgpu_waves_per_eu(PASS == kPassCollect ? 3 : 1))) void flat_gem
     bf16x8 a[RB][KS];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-        load_a<KS>(queries, nq, d, q0 + (wave * RB + rb) * 16 + (lane & 15), lane, a[rb]);
+        load_a<KS>(qs, nq, q0 + (wave * RB + rb) * 16 + (lane & 15), lane, a[rb]);
 
     u16x8 stg[CHUNKS];
     float ystg = INFINITY;
@@ -229,26 +261,38 @@ __attribute__((amdgpu_waves_per_eu(PASS == kPassCollect ? 3 : 1))) void flat_gem
     for (int64_t t = t0; t < t1; ++t) {
         const int buf = (int)(t - t0) & 1;
         fetch(t + 1);
-        // not unrolled: the compiler would keep all four blocks' operands live
-#pragma unroll 1
-        for (int cb = 0; cb < 4; ++cb) {
+        // u of this wave's row blocks and column block cb of the tile
+        auto block_u = [&](int cb, v4f (&acc)[RB]) {
             bf16x8 b[KS];
             const uint16_t *bp = bt + (buf * 64 + cb * 16 + (lane & 15)) * RS + 8 * (lane >> 4);
 #pragma unroll
             for (int s = 0; s < KS; ++s)
                 b[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(bp + 32 * s));
             const float ycol = yn[buf * 64 + cb * 16 + (lane & 15)];
-            v4f acc[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                acc[rb] = mfma_block<KS>(a[rb], b);
-            if (PASS == kPassMinima) {
+                acc[rb] = mfma_u<KS>(a[rb], b, ycol);
+        };
+        if (PASS == kPassMinima) {
+            // column blocks in pairs: one three-way minimum per two values
+#pragma unroll 1
+            for (int cb = 0; cb < 4; cb += 2) {
+                v4f u0[RB], u1[RB];
+                block_u(cb, u0);
+                block_u(cb + 1, u1);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        mn[rb][r] = fminf(mn[rb][r], flat_u(ycol, acc[rb][r]));
-            } else {
+                        mn[rb][r] = fminf(mn[rb][r], fminf(u0[rb][r], u1[rb][r]));
+            }
+        }
+        // not unrolled: the compiler would keep all four blocks' operands live
+#pragma unroll 1
+        for (int cb = 0; cb < (PASS == kPassMinima ? 0 : 4); ++cb) {
+            v4f acc[RB];
+            block_u(cb, acc);
+            {
                 // rows under the bound are rare (about k of n per query): one
                 // scalar test per row block (its 4 rows), then per row
                 const int64_t row = t * 64 + cb * 16 + (lane & 15);
@@ -258,7 +302,7 @@ __attribute__((amdgpu_waves_per_eu(PASS == kPassCollect ? 3 : 1))) void flat_gem
                     bool any = false;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        pass[r] = flat_u(ycol, acc[rb][r]) <= tr[rb][r];
+                        pass[r] = acc[rb][r] <= tr[rb][r];
                         any |= pass[r];
                     }
                     if (!__builtin_amdgcn_ballot_w64(any))
@@ -278,7 +322,7 @@ __attribute__((amdgpu_waves_per_eu(PASS == kPassCollect ? 3 : 1))) void flat_gem
                         base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
                         if (take) {
                             const uint32_t at = base + mbcnt64(mask);
-                            const float dist = flat_distance(xr[rb][r], ycol, acc[rb][r]);
+                            const float dist = xr[rb][r] + acc[rb][r];
                             if (at < (uint32_t)kFlatStage) {
                                 srow[at] = (uint32_t)row;
                                 sdist[at] = dist;
@@ -356,7 +400,7 @@ constexpr int kKthPer = 63;
 // that holds the k-th.  Then the collect threshold tu = v + slack (+inf when
 // fewer than k minima are finite).  Each thread reads its minima once and
 // keeps them in registers for the histogram and the final maximum.
-__global__ __launch_bounds__(256) void flat_kth_kernel(const uint16_t *__restrict__ queries, int d,
+__global__ __launch_bounds__(256) void flat_kth_kernel(const float *__restrict__ qn,
                                                        const float *__restrict__ slots,
                                                        int64_t nslot, int k, float ymax,
                                                        float *__restrict__ tuq)
@@ -437,10 +481,194 @@ __global__ __launch_bounds__(256) void flat_kth_kernel(const uint16_t *__restric
                 m = fmaxf(m, vals[j]);
         v = block_max(m, redf);
     }
-    if (tid == 0) {
-        const float xn = bf16_row_norm(queries + q * d, d);
-        tuq[q] = v + flat_slack(xn, ymax);
+    if (tid == 0)
+        tuq[q] = v + flat_slack(qn[q], ymax);
+}
+
+// Pass 3 by recomputation.  Workgroup (segment sg, queries qb0 ..
+// qb0 + kRecQB): a query is listed under column c when its minimum of slot
+// (sg, c) is <= its bound tu; then each wave takes columns c = w, w + 4, ...
+// and multiplies the listed queries, 16 at a time, by the rows of slot
+// (sg, c): B block j holds the rows t*64 + 16 j + c of the segment's tiles t
+// (tile tb + p in column p), so one slot is 4 blocks of 16 rows, kept in
+// registers while its queries stream through.  Rows with u <= tu are staged
+// in the wave's own LDS area (slots from a ballot, no atomics) and appended
+// to the queries' candidate buffers when it fills and at the end: all of a
+// lane's global atomics for a drain are issued before any is waited on.
+constexpr int kRecQB = 2048;
+constexpr int kRecStage = 384; // staged candidates per wave
+
+template <int U>
+__device__ __forceinline__ void rec_drain(uint32_t m, const uint16_t *sq, const uint32_t *srow,
+                                          const float *sdist, int64_t qb0, uint32_t cap,
+                                          uint32_t *__restrict__ cnt, float *__restrict__ cand_d,
+                                          uint32_t *__restrict__ cand_p)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t at[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t i = u * 64 + lane;
+        at[u] = i < m ? atomicAdd(cnt + qb0 + sq[i], 1u) : cap;
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t i = u * 64 + lane;
+        if (at[u] < cap) {
+            const size_t base = (size_t)(qb0 + sq[i]) * cap + at[u];
+            cand_d[base] = sdist[i];
+            cand_p[base] = srow[i];
+        }
+    }
+}
+
+template <int KS>
+__global__ __launch_bounds__(256) void flat_recompute_kernel(
+    const uint16_t *__restrict__ qs, const float *__restrict__ qn, int64_t nq,
+    const uint16_t *__restrict__ db, const float *__restrict__ dbn, int64_t n, int64_t ntile,
+    int seg, const float *__restrict__ slots, int64_t nslot, const float *__restrict__ tuq,
+    uint32_t cap, uint32_t *__restrict__ cnt, float *__restrict__ cand_d,
+    uint32_t *__restrict__ cand_p)
+{
+    constexpr int DP = 32 * KS;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *count = reinterpret_cast<uint32_t *>(smem);         // [16]
+    uint16_t *list = reinterpret_cast<uint16_t *>(count + 16);    // [16][kRecQB]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
+    // this wave's candidate stage: rows, distances, query (block index)
+    uint32_t *srow = reinterpret_cast<uint32_t *>(list + 16 * kRecQB) + wave * kRecStage;
+    float *sdist = reinterpret_cast<float *>(srow + (4 - wave) * kRecStage) + wave * kRecStage;
+    uint16_t *sq = reinterpret_cast<uint16_t *>(sdist + (4 - wave) * kRecStage) + wave * kRecStage;
+    uint32_t staged = 0; // wave-uniform
+    const int64_t sg = blockIdx.x;
+    const int64_t qb0 = (int64_t)blockIdx.y * kRecQB;
+    const int64_t tb = sg * seg;
+    const int64_t te = tb + seg < ntile ? tb + seg : ntile;
+    if (tid < 16)
+        count[tid] = 0;
+    __syncthreads();
+    // hot (query, column) pairs, listed per column (one LDS atomic per wave
+    // and column for its 64 queries)
+    for (int i0 = wave * 64; i0 < kRecQB; i0 += 256) {
+        const int i = i0 + lane;
+        const int64_t q = qb0 + i;
+        const bool qv = q < nq;
+        float m[16];
+        float tq = -INFINITY;
+        if (qv) {
+            tq = tuq[q];
+            const float4 *sp = reinterpret_cast<const float4 *>(slots + q * nslot + sg * 16);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float4 x = sp[v];
+                m[4 * v] = x.x;
+                m[4 * v + 1] = x.y;
+                m[4 * v + 2] = x.z;
+                m[4 * v + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                m[c] = INFINITY;
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const bool hot = qv && m[c] <= tq;
+            const uint64_t mask = __builtin_amdgcn_ballot_w64(hot);
+            if (mask == 0)
+                continue;
+            uint32_t base = 0;
+            if (lane == 0)
+                base = atomicAdd(&count[c], (uint32_t)__popcll(mask));
+            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+            if (hot)
+                list[c * kRecQB + base + mbcnt64(mask)] = (uint16_t)i;
+        }
+    }
+    __syncthreads();
+    const int p = lane & 15, kq = lane >> 4;
+    const int64_t t = tb + p;
+    const bool tv = t < te;
+    for (int c = wave; c < 16; c += 4) {
+        const uint32_t nc = count[c];
+        if (nc == 0)
+            continue;
+        const uint16_t *lc = list + c * kRecQB;
+        // B operand of the slot: block j, column p = row (tb + p) * 64 + 16 j + c
+        bf16x8 b[4][KS];
+        float yc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t row = t * 64 + 16 * j + c;
+            yc[j] = tv ? dbn[row] : INFINITY;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                if (tv)
+                    v = *reinterpret_cast<const u16x8 *>(db + row * DP + 32 * s + 8 * kq);
+                b[j][s] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+        // the listed queries of a chunk: A operand (query base + p) and, per
+        // D row (query base + 4 kq + r), its bound and |x|^2; the next
+        // chunk's are loaded while this one is multiplied
+        bf16x8 a[KS];
+        int64_t qr[4];
+        float tr[4], xr[4];
+        auto fetch = [&](uint32_t base) {
+            const uint32_t ia = base + p;
+            load_a<KS>(qs, nq, ia < nc ? qb0 + lc[ia] : nq, lane, a);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t ir = base + 4 * kq + r;
+                qr[r] = ir < nc ? qb0 + lc[ir] : -1;
+                tr[r] = qr[r] >= 0 ? tuq[qr[r]] : -INFINITY;
+                xr[r] = qr[r] >= 0 ? qn[qr[r]] : 0.f;
+            }
+        };
+        fetch(0);
+        for (uint32_t base = 0; base < nc; base += 16) {
+            v4f acc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[j] = mfma_u<KS>(a, b[j], yc[j]);
+            const int64_t q_cur[4] = {qr[0], qr[1], qr[2], qr[3]};
+            const float t_cur[4] = {tr[0], tr[1], tr[2], tr[3]};
+            const float x_cur[4] = {xr[0], xr[1], xr[2], xr[3]};
+            if (base + 16 < nc)
+                fetch(base + 16);
+            if (!__builtin_amdgcn_ballot_w64(q_cur[0] >= 0 || q_cur[1] >= 0 || q_cur[2] >= 0 ||
+                                             q_cur[3] >= 0))
+                continue;
+            // rows t*64 + 16 j + c of this lane's column with u <= tu of D row r
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t row = t * 64 + 16 * j + c;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool tk = q_cur[r] >= 0 && tv && row < n && acc[j][r] <= t_cur[r];
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(tk);
+                    if (m == 0)
+                        continue;
+                    const uint32_t nm = (uint32_t)__popcll(m);
+                    if (staged + nm > (uint32_t)kRecStage) {
+                        rec_drain<kRecStage / 64>(staged, sq, srow, sdist, qb0, cap, cnt, cand_d,
+                                                  cand_p);
+                        staged = 0;
+                    }
+                    if (tk) {
+                        const uint32_t at = staged + mbcnt64(m);
+                        srow[at] = (uint32_t)row;
+                        sdist[at] = x_cur[r] + acc[j][r];
+                        sq[at] = (uint16_t)(q_cur[r] - qb0);
+                    }
+                    staged += nm;
+                }
+            }
+        }
+    }
+    rec_drain<kRecStage / 64>(staged, sq, srow, sdist, qb0, cap, cnt, cand_d, cand_p);
 }
 
 constexpr int kFlatSelWaves = 4;
@@ -594,10 +822,11 @@ static int flat_cu_count()
     return cus;
 }
 
-FlatPlan flat_plan(int64_t n, int k, int64_t nq)
+FlatPlan flat_plan(int64_t n, int k, int64_t nq, int dp)
 {
     (void)nq;
     FlatPlan p;
+    p.dp = dp;
     p.ntile = (n + 63) / 64;
     // at most 1000 segments (16000 slot minima per query): about 16 per
     // top-k row at k = 1024, so few top-k rows share a slot
@@ -610,15 +839,16 @@ FlatPlan flat_plan(int64_t n, int k, int64_t nq)
     return p;
 }
 
+// slot minima, bound, counters, candidates, |x|^2 and the -2x rows
 size_t flat_ws_bytes(const FlatPlan &p, int64_t nq)
 {
-    return (size_t)nq * ((size_t)p.nslot * 4 + 12 + (size_t)p.cap * 8) + 256;
+    return (size_t)nq * ((size_t)p.nslot * 4 + 16 + (size_t)p.cap * 8 + (size_t)p.dp * 2) + 512;
 }
 
 template <int KS, int RB, int PASS>
-static hipError_t gemm_variant(const FlatDevice &fx, const uint16_t *q, int64_t nq,
-                               const FlatPlan &p, float *slots, const float *tuq, uint32_t *cnt,
-                               float *cand_d, uint32_t *cand_p, hipStream_t stream)
+static hipError_t gemm_variant(const FlatDevice &fx, const uint16_t *qs, const float *qn,
+                               int64_t nq, const FlatPlan &p, float *slots, const float *tuq,
+                               uint32_t *cnt, float *cand_d, uint32_t *cand_p, hipStream_t stream)
 {
     constexpr int TQ = 64 * RB, DP = 32 * KS;
     const size_t lds = (size_t)TQ * 8 + 128 * 4 + 2 * 64 * (DP + 8) * 2 +
@@ -656,10 +886,36 @@ static hipError_t gemm_variant(const FlatDevice &fx, const uint16_t *q, int64_t 
             splits = sp;
         }
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)qg, (unsigned)splits), dim3(256), lds, stream, q, nq,
-                       fx.d, fx.vec, fx.norms, fx.n, p.ntile, p.seg, p.nseg, (int)splits, slots,
+    hipLaunchKernelGGL(kern, dim3((unsigned)qg, (unsigned)splits), dim3(256), lds, stream, qs, qn,
+                       nq, fx.vec, fx.norms, fx.n, p.ntile, p.seg, p.nseg, (int)splits, slots,
                        p.nslot, tuq, p.cap, cnt, cand_d, cand_p);
     return hipGetLastError();
+}
+
+template <int KS>
+static hipError_t recompute_variant(const FlatDevice &fx, const uint16_t *qs, const float *qn,
+                                    int64_t nq, const FlatPlan &p, const float *slots,
+                                    const float *tuq, uint32_t *cnt, float *cand_d,
+                                    uint32_t *cand_p, hipStream_t stream)
+{
+    const size_t lds = 64 + (size_t)16 * kRecQB * 2 + (size_t)4 * kRecStage * 10;
+    auto kern = flat_recompute_kernel<KS>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+        return e;
+    const dim3 grid((unsigned)p.nseg, (unsigned)((nq + kRecQB - 1) / kRecQB));
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, qs, qn, nq, fx.vec, fx.norms, fx.n,
+                       p.ntile, p.seg, slots, p.nslot, tuq, p.cap, cnt, cand_d, cand_p);
+    return hipGetLastError();
+}
+
+// Test switch: IVFPQ_TEST_FLAT_FULL_COLLECT=1 runs the collect pass as a
+// second full GEMM with the bound test (read on every search).
+static bool flat_full_collect()
+{
+    const char *e = std::getenv("IVFPQ_TEST_FLAT_FULL_COLLECT");
+    return e && e[0] == '1';
 }
 
 template <int NW>
@@ -682,19 +938,22 @@ static hipError_t select_variant(const FlatDevice &fx, const uint16_t *q, int64_
 }
 
 template <int KS>
-static hipError_t gemm_pass(const FlatDevice &fx, const uint16_t *q, int64_t nq,
-                            const FlatPlan &p, float *slots, const float *tuq, uint32_t *cnt,
-                            float *cand_d, uint32_t *cand_p, hipStream_t stream, int pass)
+static hipError_t gemm_pass(const FlatDevice &fx, const uint16_t *qs, const float *qn,
+                            int64_t nq, const FlatPlan &p, float *slots, const float *tuq,
+                            uint32_t *cnt, float *cand_d, uint32_t *cand_p, hipStream_t stream,
+                            int pass)
 {
     // minima pass: four row blocks per wave while the A operand fits the
-    // registers (fewer B reads per product); collect pass: two (its append
-    // path needs the registers, and more waves hide its latency)
+    // registers (fewer B reads per product); full collect pass: two (its
+    // append path needs the registers, and more waves hide its latency)
     constexpr int RBM = KS <= 4 ? 4 : 2;
     if (pass == kPassMinima)
-        return gemm_variant<KS, RBM, kPassMinima>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p,
-                                                  stream);
-    return gemm_variant<KS, 2, kPassCollect>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p,
-                                             stream);
+        return gemm_variant<KS, RBM, kPassMinima>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d,
+                                                  cand_p, stream);
+    if (flat_full_collect())
+        return gemm_variant<KS, 2, kPassCollect>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d,
+                                                 cand_p, stream);
+    return recompute_variant<KS>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d, cand_p, stream);
 }
 
 hipError_t launch_flat_stage(const FlatDevice &fx, const uint16_t *q, int64_t nq, int k,
@@ -709,8 +968,13 @@ hipError_t launch_flat_stage(const FlatDevice &fx, const uint16_t *q, int64_t nq
     uint32_t *over = cnt + nq;
     float *cand_d = reinterpret_cast<float *>(over + nq);
     uint32_t *cand_p = reinterpret_cast<uint32_t *>(cand_d + (size_t)nq * p.cap);
+    float *qn = reinterpret_cast<float *>(cand_p + (size_t)nq * p.cap);
+    uint16_t *qs = reinterpret_cast<uint16_t *>(
+        (reinterpret_cast<uintptr_t>(qn + nq) + 255) & ~(uintptr_t)255);
+    if (fx.dp != p.dp)
+        return hipErrorInvalidValue;
     switch (stage) {
-    case 0:   // clear the counters, slot minima
+    case 0:   // clear the counters, the A operand, slot minima
     case 2: { // collect
         if (stage == 0) {
             hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((2 * nq + 255) / 256)), dim3(256),
@@ -718,19 +982,25 @@ hipError_t launch_flat_stage(const FlatDevice &fx, const uint16_t *q, int64_t nq
             hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
+            const int64_t total = nq * fx.dp;
+            hipLaunchKernelGGL(flat_query_prep_kernel, dim3((unsigned)((total + 255) / 256)),
+                               dim3(256), 0, stream, q, nq, fx.d, fx.dp, qs, qn);
+            e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
         }
         if (p.ntile == 0) // empty database: every row of the result is padding
             return hipSuccess;
         const int pass = stage == 0 ? kPassMinima : kPassCollect;
         switch (fx.dp / 32) {
-        case 1: return gemm_pass<1>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
-        case 2: return gemm_pass<2>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
-        case 3: return gemm_pass<3>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
-        case 4: return gemm_pass<4>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
-        case 5: return gemm_pass<5>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
-        case 6: return gemm_pass<6>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
-        case 7: return gemm_pass<7>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
-        case 8: return gemm_pass<8>(fx, q, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 1: return gemm_pass<1>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 2: return gemm_pass<2>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 3: return gemm_pass<3>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 4: return gemm_pass<4>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 5: return gemm_pass<5>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 6: return gemm_pass<6>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 7: return gemm_pass<7>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
+        case 8: return gemm_pass<8>(fx, qs, qn, nq, p, slots, tuq, cnt, cand_d, cand_p, stream, pass);
         default: return hipErrorInvalidValue;
         }
     }
@@ -739,8 +1009,8 @@ hipError_t launch_flat_stage(const FlatDevice &fx, const uint16_t *q, int64_t nq
             return hipErrorInvalidValue;
         if (p.ntile == 0)
             return hipSuccess;
-        hipLaunchKernelGGL(flat_kth_kernel, dim3((unsigned)nq), dim3(256), 0, stream, q, fx.d,
-                           slots, p.nslot, k, fx.ymax, tuq);
+        hipLaunchKernelGGL(flat_kth_kernel, dim3((unsigned)nq), dim3(256), 0, stream, qn, slots,
+                           p.nslot, k, fx.ymax, tuq);
         return hipGetLastError();
     }
     default: { // 3: select, 4: fallback

@@ -88,12 +88,46 @@ def test_flat_chunked_batches_match(A, monkeypatch):
     rng = np.random.default_rng(5)
     db, q = uniform_bits(rng, 4000, 32), uniform_bits(rng, 70, 32)
     full = run(A, db, q, 20)
-    per_query = 16 * 63 * 4 + 12 + 4096 * 8  # slot minima, counters, candidates
+    # slot minima, bound and counters, candidates, -2x row
+    per_query = 16 * 63 * 4 + 16 + 4096 * 8 + 32 * 2
     monkeypatch.setenv("IVFPQ_TEST_FLAT_WS_BYTES", str(per_query * 16 + 300))
     chunked = run(A, db, q, 20)
     assert np.array_equal(full[0], chunked[0])
     rep = check.compare_flat(db, q, 20, *chunked)
     assert rep.ok(), rep.failures[:5]
+
+
+RECOMPUTE_SHAPES = [  # more than one query block (2048), ragged segments, k = 1024
+    (20000, 128, 300, 1024),
+    (70001, 96, 129, 257),
+    (5003, 100, 2500, 100),
+    (3000, 256, 20, 64),
+    (1, 4, 3, 5),
+]
+
+
+@pytest.mark.parametrize("n,d,nq,k", RECOMPUTE_SHAPES)
+def test_flat_recompute_equals_full_collect(A, monkeypatch, n, d, nq, k):
+    # The collect pass recomputes only the slots whose minimum is under the
+    # bound; the earlier form (a second full GEMM with the bound test, behind
+    # a test switch) must give the same k distances to the bit, and the same
+    # rows wherever a distance is not tied with another row's.
+    print(f"flat recompute vs full collect n={n} d={d} nq={nq} k={k}", flush=True)
+    rng = np.random.default_rng(n + 13 * d + nq)
+    db, q = uniform_bits(rng, n, d), uniform_bits(rng, nq, d)
+    gd, gi = run(A, db, q, k)
+    monkeypatch.setenv("IVFPQ_TEST_FLAT_FULL_COLLECT", "1")
+    fd, fi = run(A, db, q, k)
+    monkeypatch.delenv("IVFPQ_TEST_FLAT_FULL_COLLECT")
+    assert np.array_equal(gd.view(np.uint32), fd.view(np.uint32))
+    for row in range(nq):
+        vals, counts = np.unique(gd[row], return_counts=True)
+        single = set(vals[counts == 1].tolist())
+        for j in range(k):
+            if gd[row, j] in single and gd[row, j] != gd[row, -1]:
+                assert gi[row, j] == fi[row, j], (row, j)
+    rep = check.compare_flat(db, q, k, gd, gi)
+    assert rep.ok(), (rep.summary(), rep.failures[:5])
 
 
 def test_flat_empty_database_and_host_api(A):
