@@ -142,6 +142,11 @@ __device__ __forceinline__ float flat_slack(float xn, float ymax)
 
 enum FlatPass { kPassMinima = 0, kPassCollect = 1 };
 
+// Candidate counters one per 128-byte line: the appends of the many
+// workgroups that share a block of queries would otherwise queue on the few
+// lines that hold the block's counters.
+constexpr int kCntStride = 32;
+
 // Passes 1 and 3 (GEMM over every tile).  Workgroup: 4 waves, TQ = 64*RB
 // queries (wave w: row blocks w*RB..), tiles [t0, t1) made of whole
 // segments of `seg` tiles.  Tiles are staged in LDS (double buffer, one
@@ -193,7 +198,7 @@ __attribute__((amdgpu_waves_per_eu(PASS == kPassCollect ? 3 : 1))) void flat_gem
     }
     // one candidate into its query's buffer (the global append)
     auto append = [&](int64_t q, uint32_t row, float dist) {
-        const uint32_t slot = atomicAdd(cnt + q, 1u);
+        const uint32_t slot = atomicAdd(cnt + q * kCntStride, 1u);
         if (slot < cap) {
             cand_d[(size_t)q * cap + slot] = dist;
             cand_p[(size_t)q * cap + slot] = row;
@@ -485,6 +490,21 @@ __global__ __launch_bounds__(256) void flat_kth_kernel(const float *__restrict__
         tuq[q] = v + flat_slack(qn[q], ymax);
 }
 
+// Wave-wide inclusive prefix sum in DPP (no LDS round trips): row_shr by 1, 2,
+// 4, 8 inside each 16-lane row (lanes shifted in from outside read 0), then
+// row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and
+// row_bcast:31 adds lane 31's sum to rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+    return v;
+}
+
 // Pass 3 by recomputation.  Workgroup (segment sg, queries qb0 ..
 // qb0 + kRecQB): a query is listed under column c when its minimum of slot
 // (sg, c) is <= its bound tu; then each wave takes columns c = w, w + 4, ...
@@ -509,7 +529,7 @@ __device__ __forceinline__ void rec_drain(uint32_t m, const uint16_t *sq, const 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t i = u * 64 + lane;
-        at[u] = i < m ? atomicAdd(cnt + qb0 + sq[i], 1u) : cap;
+        at[u] = i < m ? atomicAdd(cnt + (qb0 + sq[i]) * kCntStride, 1u) : cap;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -638,34 +658,53 @@ __global__ __launch_bounds__(256) void flat_recompute_kernel(
             const float x_cur[4] = {xr[0], xr[1], xr[2], xr[3]};
             if (base + 16 < nc)
                 fetch(base + 16);
-            if (!__builtin_amdgcn_ballot_w64(q_cur[0] >= 0 || q_cur[1] >= 0 || q_cur[2] >= 0 ||
-                                             q_cur[3] >= 0))
-                continue;
-            // rows t*64 + 16 j + c of this lane's column with u <= tu of D row r
+            // rows t*64 + 16 j + c of this lane's column with u <= tu of D
+            // row r: bit 4 j + r of `take`
+            uint32_t take = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t row = t * 64 + 16 * j + c;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool tk = q_cur[r] >= 0 && tv && row < n && acc[j][r] <= t_cur[r];
-                    const uint64_t m = __builtin_amdgcn_ballot_w64(tk);
-                    if (m == 0)
-                        continue;
-                    const uint32_t nm = (uint32_t)__popcll(m);
-                    if (staged + nm > (uint32_t)kRecStage) {
-                        rec_drain<kRecStage / 64>(staged, sq, srow, sdist, qb0, cap, cnt, cand_d,
-                                                  cand_p);
-                        staged = 0;
-                    }
-                    if (tk) {
-                        const uint32_t at = staged + mbcnt64(m);
-                        srow[at] = (uint32_t)row;
-                        sdist[at] = x_cur[r] + acc[j][r];
-                        sq[at] = (uint16_t)(q_cur[r] - qb0);
-                    }
-                    staged += nm;
-                }
+                for (int r = 0; r < 4; ++r)
+                    take |= (q_cur[r] >= 0 && tv && row < n && acc[j][r] <= t_cur[r])
+                                ? 1u << (4 * j + r)
+                                : 0u;
             }
+            if (!__builtin_amdgcn_ballot_w64(take != 0))
+                continue;
+            // each lane's takes go to consecutive stage entries: offsets from
+            // a prefix sum over the wave
+            const uint32_t mine = (uint32_t)__popc(take);
+            const uint32_t incl = wave_scan_dpp(mine);
+            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+            if (staged + total > (uint32_t)kRecStage) {
+                rec_drain<kRecStage / 64>(staged, sq, srow, sdist, qb0, cap, cnt, cand_d, cand_p);
+                staged = 0;
+            }
+            uint32_t at = staged + incl - mine;
+            while (take) {
+                const int bit = __builtin_ctz(take);
+                take &= take - 1;
+                const int j = bit >> 2, r = bit & 3;
+                float v = acc[0][0];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        v = (jj == j && rr == r) ? acc[jj][rr] : v;
+                float xv = x_cur[0];
+                int64_t qv = q_cur[0];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    xv = rr == r ? x_cur[rr] : xv;
+                    qv = rr == r ? q_cur[rr] : qv;
+                }
+                srow[at] = (uint32_t)(t * 64 + 16 * j + c);
+                sdist[at] = xv + v;
+                sq[at] = (uint16_t)(qv - qb0);
+                ++at;
+            }
+            staged += total;
         }
     }
     rec_drain<kRecStage / 64>(staged, sq, srow, sdist, qb0, cap, cnt, cand_d, cand_p);
@@ -689,7 +728,7 @@ __global__ __launch_bounds__(64 * kFlatSelWaves) void flat_select_kernel(
     const int64_t q = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
-    const uint32_t c = cnt[q];
+    const uint32_t c = cnt[q * kCntStride];
     if (c > cap) {
         if (tid == 0)
             over[q] = 1u;
@@ -839,10 +878,13 @@ FlatPlan flat_plan(int64_t n, int k, int64_t nq, int dp)
     return p;
 }
 
-// slot minima, bound, counters, candidates, |x|^2 and the -2x rows
+// slot minima, bound, counter line, overflow flag, candidates, |x|^2 and the
+// -2x rows (+ alignment)
 size_t flat_ws_bytes(const FlatPlan &p, int64_t nq)
 {
-    return (size_t)nq * ((size_t)p.nslot * 4 + 16 + (size_t)p.cap * 8 + (size_t)p.dp * 2) + 512;
+    return (size_t)nq * ((size_t)p.nslot * 4 + 12 + 4 * kCntStride + (size_t)p.cap * 8 +
+                         (size_t)p.dp * 2) +
+           640;
 }
 
 template <int KS, int RB, int PASS>
@@ -964,8 +1006,9 @@ hipError_t launch_flat_stage(const FlatDevice &fx, const uint16_t *q, int64_t nq
         return hipSuccess;
     float *slots = static_cast<float *>(ws);
     float *tuq = slots + (size_t)nq * p.nslot;
-    uint32_t *cnt = reinterpret_cast<uint32_t *>(tuq + nq);
-    uint32_t *over = cnt + nq;
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(
+        (reinterpret_cast<uintptr_t>(tuq + nq) + 127) & ~(uintptr_t)127); // [nq][kCntStride]
+    uint32_t *over = cnt + (size_t)nq * kCntStride;
     float *cand_d = reinterpret_cast<float *>(over + nq);
     uint32_t *cand_p = reinterpret_cast<uint32_t *>(cand_d + (size_t)nq * p.cap);
     float *qn = reinterpret_cast<float *>(cand_p + (size_t)nq * p.cap);
@@ -977,8 +1020,9 @@ hipError_t launch_flat_stage(const FlatDevice &fx, const uint16_t *q, int64_t nq
     case 0:   // clear the counters, the A operand, slot minima
     case 2: { // collect
         if (stage == 0) {
-            hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((2 * nq + 255) / 256)), dim3(256),
-                               0, stream, cnt, 2 * nq, 0u);
+            const int64_t nfill = nq * (kCntStride + 1); // counters and overflow flags
+            hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nfill + 255) / 256)), dim3(256),
+                               0, stream, cnt, nfill, 0u);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;

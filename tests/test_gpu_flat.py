@@ -88,8 +88,8 @@ def test_flat_chunked_batches_match(A, monkeypatch):
     rng = np.random.default_rng(5)
     db, q = uniform_bits(rng, 4000, 32), uniform_bits(rng, 70, 32)
     full = run(A, db, q, 20)
-    # slot minima, bound and counters, candidates, -2x row
-    per_query = 16 * 63 * 4 + 16 + 4096 * 8 + 32 * 2
+    # slot minima, bound, counter line, flag, |x|^2, candidates, -2x row
+    per_query = 16 * 63 * 4 + 12 + 128 + 4096 * 8 + 32 * 2
     monkeypatch.setenv("IVFPQ_TEST_FLAT_WS_BYTES", str(per_query * 16 + 300))
     chunked = run(A, db, q, 20)
     assert np.array_equal(full[0], chunked[0])
