@@ -14,14 +14,17 @@
 //   s = 4, 16: ds_swizzle bit-mask mode (xor inside 32-lane halves)
 //   s = 32   : ds_bpermute
 // The networks are bitonic: sort of 2^n elements in n(n+1)/2 steps, merge of
-// a bitonic sequence of 2^n elements in n steps.  Every lane executes the same
-// instruction stream whatever the data.
+// a bitonic sequence of 2^n elements in n steps; their step tables and lane
+// masks are in network.hpp (shared with a host check of the same tables).
+// Every lane executes the same instruction stream whatever the data.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <utility>
+
+#include "network.hpp"
 
 namespace ivfpq {
 
@@ -69,22 +72,6 @@ __device__ __forceinline__ void cx_lane_mask(float &k, uint32_t &v)
     v = take ? pv : v;
 }
 
-// Lanes of register r that keep the smaller key in a bitonic step (pairs
-// (e, e ^ S), blocks of B elements ascending when ((e & B) == 0) != DESC;
-// B == 0: the whole array ascending).
-constexpr uint64_t keep_min_mask(int S, int B, bool DESC, int r)
-{
-    uint64_t m = 0;
-    for (int l = 0; l < 64; ++l) {
-        const int e = r * 64 + l;
-        const bool lower = (l & S) == 0;
-        const bool up = B == 0 ? !DESC : (((e & B) == 0) != DESC);
-        if (lower == up)
-            m |= 1ull << l;
-    }
-    return m;
-}
-
 // The lane compare-exchanges of one bitonic step, register by register.
 template <int S, int B, bool DESC, int R, int... RR>
 __device__ __forceinline__ void cx_lanes(float (&k)[R], uint32_t (&v)[R],
@@ -115,54 +102,38 @@ __device__ __forceinline__ void bitonic_step(float (&k)[R], uint32_t (&v)[R])
         constexpr int RS = S / 64;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            if ((r & RS) == 0) {
-                const int e = r * 64; // block bit B >= 2S >= 128 sits in the register index
-                const bool up = (B == 0) ? !DESC : (((e & B) == 0) != DESC);
-                cx_reg(k[r], v[r], k[r | RS], v[r | RS], up);
-            }
+            // the block bit B >= 2S >= 128 sits in the register index
+            if ((r & RS) == 0)
+                cx_reg(k[r], v[r], k[r | RS], v[r | RS], block_ascending(B, DESC, r));
         }
     } else {
         cx_lanes<S, B, DESC>(k, v, std::make_integer_sequence<int, R>{});
     }
 }
 
-// Bitonic merge (half-cleaner chain S = N/2 .. 1) of a bitonic sequence of
-// N = 64 R elements into ascending order.
-template <int R, int S>
-__device__ __forceinline__ void bitonic_merge_steps(float (&k)[R], uint32_t (&v)[R])
+// The steps of a schedule (network.hpp), in order.
+template <int R, bool DESC, const auto &SCHED, size_t... I>
+__device__ __forceinline__ void run_schedule(float (&k)[R], uint32_t (&v)[R],
+                                             std::index_sequence<I...>)
 {
-    if constexpr (S >= 1) {
-        bitonic_step<R, 0, S, false>(k, v);
-        bitonic_merge_steps<R, S / 2>(k, v);
-    }
+    (bitonic_step<R, SCHED[I].B, SCHED[I].S, DESC>(k, v), ...);
 }
 
+// Bitonic merge (half-cleaner chain S = N/2 .. 1) of a bitonic sequence of
+// N = 64 R elements into ascending order.
 template <int R>
 __device__ __forceinline__ void bitonic_merge_up(float (&k)[R], uint32_t (&v)[R])
 {
-    bitonic_merge_steps<R, 32 * R>(k, v);
+    run_schedule<R, false, kMergeUp<R>>(k, v, std::make_index_sequence<kMergeUp<R>.size()>{});
 }
 
 // Full bitonic sort of a 64-element single-register array.
-template <int B, int S, bool DESC>
-__device__ __forceinline__ void sort64_steps(float (&k)[1], uint32_t (&v)[1])
-{
-    if constexpr (B <= 64) {
-        if constexpr (S >= 1) {
-            bitonic_step<1, (B == 64 ? 0 : B), S, DESC>(k, v);
-            sort64_steps<B, S / 2, DESC>(k, v);
-        } else {
-            sort64_steps<B * 2, B, DESC>(k, v);
-        }
-    }
-}
-
 template <bool DESC>
 __device__ __forceinline__ void sort64(float &key, uint32_t &val)
 {
     float k[1] = {key};
     uint32_t v[1] = {val};
-    sort64_steps<2, 1, DESC>(k, v);
+    run_schedule<1, DESC, kSort64>(k, v, std::make_index_sequence<kSort64.size()>{});
     key = k[0];
     val = v[0];
 }
