@@ -56,8 +56,8 @@ def workload(name: str):
 
 # The sources that define the scan kernel and how a search launches it (work
 # items, workspace): a change to any of them retires stored counter readings.
-SCAN_SOURCES = ("api.hip", "common.hpp", "internal.hpp", "kernels_search.hip", "wave_ops.hpp",
-                "wave_select.hpp")
+SCAN_SOURCES = ("api.hip", "common.hpp", "internal.hpp", "kernels_search.hip", "network.hpp",
+                "plan.hpp", "wave_ops.hpp", "wave_select.hpp")
 
 
 def source_digest() -> str:
