@@ -194,6 +194,7 @@ void release(ivfpq_index *ix)
     (void)hipFree(d.centroids);
     (void)hipFree(d.cblk);
     (void)hipFree(d.cnorm_pad);
+    (void)hipFree(d.cx6);
     (void)hipFree(d.codebooks);
     (void)hipFree(d.list_off);
     (void)hipFree(d.codes);
@@ -266,6 +267,10 @@ ivfpq_status alloc_index(int device, int d, int nlist, int m, int64_t ntotal,
     dx.nblk = ((nlist + 63) / 64) * 4;
     ALLOC_OR_FAIL(dx.cblk, (size_t)dx.nblk * dx.d4 * 64 * 4);
     ALLOC_OR_FAIL(dx.cnorm_pad, (size_t)dx.nblk * 16 * 4);
+    if (coarse_uses_x6(d, nlist)) {
+        dx.x6_kb = (d + 31) / 32;
+        ALLOC_OR_FAIL(dx.cx6, (size_t)dx.nblk * 16 * dx.x6_kb * 32 * 3 * 2);
+    }
     ALLOC_OR_FAIL(dx.codebooks, (size_t)d * 256 * 4);
     ALLOC_OR_FAIL(dx.list_off, ((size_t)nlist + 1) * 4);
     ALLOC_OR_FAIL(dx.codes, (size_t)ntotal * m);
@@ -571,7 +576,8 @@ ivfpq_status ivfpq_index_info(const ivfpq_index *idx, ivfpq_info *out)
     out->ntotal = idx->dx.ntotal;
     out->max_list = idx->dx.max_list;
     out->device = idx->device;
-    out->flags = idx->dx.t1 ? IVFPQ_INDEX_DECOMPOSED_TABLES : 0;
+    out->flags = (idx->dx.t1 ? IVFPQ_INDEX_DECOMPOSED_TABLES : 0) |
+                 (idx->dx.cx6 ? IVFPQ_INDEX_COARSE_SPLIT_BF16 : 0);
     out->device_bytes = idx->device_bytes;
     return ok();
 }

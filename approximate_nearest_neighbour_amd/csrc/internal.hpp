@@ -18,6 +18,11 @@ struct DeviceIndex {
     int nblk = 0;                // 16-centroid blocks, a multiple of 4 (whole 64-wide tiles)
     float *cblk = nullptr;       // centroids in MFMA B-operand order [nblk][d4/4][64][4]
     float *cnorm_pad = nullptr;  // [nblk * 16] |c_l|^2, +inf past nlist
+    // centroids as three bfloat16 parts for the bf16x6 coarse kernel (only
+    // where it runs: d <= 96, nlist >= 16,384; else nullptr):
+    // [nblk/4 tiles][4][x6_kb][3][64][8]
+    uint16_t *cx6 = nullptr;
+    int x6_kb = 0;               // 32-dim K-blocks: ceil(d / 32)
     float *codebooks = nullptr;  // [m][256][dsub]
     uint32_t *list_off = nullptr; // [nlist + 1]
     uint8_t *codes = nullptr;    // [ntotal][m]
@@ -72,6 +77,9 @@ hipError_t launch_coarse_valu(const DeviceIndex &ix, const float *queries, int64
                               bool ip = false);
 size_t coarse_ws_bytes(const DeviceIndex &ix, int64_t nq, int nprobe);
 hipError_t launch_centroid_blocks(const DeviceIndex &ix, hipStream_t stream);
+// whether an index of this shape gets the bfloat16 parts of its centroids
+// (the bf16x6 coarse kernel: d <= 96, nlist >= 16,384)
+bool coarse_uses_x6(int d, int nlist);
 hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
                        hipStream_t stream);
 // Decomposed tables for this index? (compiled shape, list term small enough

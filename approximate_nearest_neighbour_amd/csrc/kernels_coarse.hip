@@ -24,6 +24,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <cstdlib>
+
 namespace ivfpq {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -349,6 +351,335 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Coarse distances as float32-exact products from bfloat16 matrix cores.
+//
+// Each operand is split into three bfloat16 parts, x = x0 + x1 + x2 (each part
+// rounded to nearest from the remainder, so the sum is x itself for float32
+// values of normal range), and x.c is the sum of the six products
+// x2 c0, x0 c2, x1 c1, x1 c0, x0 c1, x0 c0 ("Leveraging the bfloat16 artificial
+// intelligence datatype for higher-precision computations", Henry, Tang and
+// Heinecke, 2019: the split and the dropped small terms).  Every product of
+// two bfloat16 parts is exact in float32; the three dropped products are at
+// most 2^-23 |x_i c_i| together.  v_mfma_f32_16x16x32_bf16 does 8x the K of
+// the float32 16x16x4 instruction in half the cycles, so the six terms take
+// 2.7x fewer matrix cycles than the float32 product.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
+// float32 -> bfloat16 bits, round to nearest even (finite values)
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_value(uint32_t b) { return __uint_as_float(b << 16); }
+
+// x = p0 + p1 + p2, each a bfloat16 rounded from what the previous parts left
+// (the remainders are exact in float32)
+__device__ __forceinline__ void split_bf16x3(float x, uint16_t &p0, uint16_t &p1, uint16_t &p2)
+{
+    const uint32_t b0 = bf16_rne_bits(x);
+    const float r1 = x - bf16_bits_value(b0);
+    const uint32_t b1 = bf16_rne_bits(r1);
+    const float r2 = r1 - bf16_bits_value(b1);
+    p0 = (uint16_t)b0;
+    p1 = (uint16_t)b1;
+    p2 = (uint16_t)bf16_rne_bits(r2);
+}
+
+// Centroid parts in B-operand order of v_mfma_f32_16x16x32_bf16: for tile t
+// (64 centroids), column block cb (16), K-block s (32 dims) and part p, lane l
+// holds centroid 64 t + 16 cb + l%16, dims 32 s + 8 (l/16) .. +7; stored as
+// [t][cb][s][p][l][8] so that a wave reads 1 KiB contiguous per (s, p).  Zero
+// beyond nlist or d.
+__global__ void centroid_x6_kernel(const float *__restrict__ c, int d, int nlist, int64_t ntile,
+                                   int kb, uint16_t *__restrict__ out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= ntile * 4 * kb * 64)
+        return;
+    const int lane = (int)(i & 63);
+    const int64_t rest = i >> 6;
+    const int s = (int)(rest % kb);
+    const int64_t tcb = rest / kb; // 4 t + cb
+    const int64_t row = tcb * 16 + (lane & 15);
+    const int col0 = 32 * s + 8 * (lane >> 4);
+    u16x8_t v0, v1, v2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = (row < nlist && col0 + e < d) ? c[row * d + col0 + e] : 0.f;
+        uint16_t p0, p1, p2;
+        split_bf16x3(x, p0, p1, p2);
+        v0[e] = p0;
+        v1[e] = p1;
+        v2[e] = p2;
+    }
+    uint16_t *o = out + ((tcb * kb + s) * 3) * 512 + lane * 8;
+    *reinterpret_cast<u16x8_t *>(o) = v0;
+    *reinterpret_cast<u16x8_t *>(o + 512) = v1;
+    *reinterpret_cast<u16x8_t *>(o + 1024) = v2;
+}
+
+// Workgroup of 8 waves, 64 queries, a range of 64-centroid tiles:
+//  * 4 matrix waves: wave w computes column block w of every tile for all 64
+//    queries (four row groups, four independent accumulator chains): the A
+//    parts of the 64 queries stay in registers (3 parts x 4 row groups x KB
+//    K-blocks), the B parts of a K-block are reloaded for the next tile right
+//    after their last product here (one tile of latency, no second buffer);
+//    accumulators start at |x|^2 + |c|^2 (0 for the inner product) and A holds
+//    -2x (-x), so the chain's result is the distance;
+//  * 4 selection waves: 16 queries each, a register top-k per query (WaveTopK).
+// The roles meet in the ring of distance tiles (ring_wait / ring_signal) as
+// in the float32 kernel, with 4 writers and 4 readers per tile.
+template <int NW, int KB, bool IP>
+__global__ __launch_bounds__(512) void coarse_x6_kernel(
+    const float *__restrict__ queries, int64_t nq, int d, int nblk, int nprobe,
+    const uint16_t *__restrict__ cx6, const float *__restrict__ cnorm_pad, int splits,
+    float *__restrict__ part_d, uint32_t *__restrict__ part_p, uint32_t *__restrict__ qbound,
+    uint32_t *__restrict__ pslot, int32_t *__restrict__ probes, float *__restrict__ probe_d)
+{
+    constexpr int TQ = 64, THREADS = 512, MW = 4, QS = 16, KW = 64 * NW;
+    constexpr int XS = 32 * KB + 1; // odd stride
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *xt = reinterpret_cast<float *>(smem);                            // [TQ][XS]
+    float *xn = xt + TQ * XS;                                               // [TQ]
+    float *dt = xn + TQ;                                                    // [kRing][TQ][64]
+    uint32_t *stage = reinterpret_cast<uint32_t *>(dt + kRing * TQ * 64);  // [TQ][128]
+    uint32_t *produced = stage + TQ * 128;                                  // [kRing]
+    uint32_t *consumed = produced + kRing;                                  // [kRing]
+    uint32_t *broken = consumed + kRing;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform in the wave
+    const bool matrix = wave < MW;
+    const int64_t q0 = (int64_t)blockIdx.x * TQ;
+    const int split = blockIdx.y;
+    const int ntile = (nblk + 3) / 4;
+    const int t0 = (int)((int64_t)ntile * split / splits);
+    const int t1 = (int)((int64_t)ntile * (split + 1) / splits);
+
+    for (int i = tid; i < TQ * 32 * KB; i += THREADS) {
+        const int row = i / (32 * KB), col = i % (32 * KB);
+        const int64_t q = q0 + row;
+        xt[row * XS + col] = (q < nq && col < d) ? queries[q * d + col] : 0.f;
+    }
+    if (tid < 2 * kRing + 1)
+        produced[tid] = 0u; // produced, consumed, broken
+    __syncthreads();
+    if (tid < TQ) {
+        // |x|^2 in index order over whole groups of 4 dims (the zero padding
+        // adds nothing): the same value as the float32 kernel's
+        float acc = 0.f;
+        for (int c = 0; c < 32 * KB; ++c)
+            acc = fmaf(xt[tid * XS + c], xt[tid * XS + c], acc);
+        xn[tid] = acc;
+    }
+    __syncthreads();
+
+    if (matrix) {
+        const int cb = wave;
+        // A parts: row group g, K-block s: lane l supplies row 16 g + l%16,
+        // dims 32 s + 8 (l/16) .. +7, scaled by -2 (-1 for the inner product)
+        bf16x8_t a0[4][KB], a1[4][KB], a2[4][KB];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int s = 0; s < KB; ++s) {
+                const float *ap = xt + (g * 16 + (lane & 15)) * XS + 32 * s + 8 * (lane >> 4);
+                u16x8_t v0, v1, v2;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = IP ? -ap[e] : -2.f * ap[e];
+                    uint16_t p0, p1, p2;
+                    split_bf16x3(x, p0, p1, p2);
+                    v0[e] = p0;
+                    v1[e] = p1;
+                    v2[e] = p2;
+                }
+                a0[g][s] = __builtin_bit_cast(bf16x8_t, v0);
+                a1[g][s] = __builtin_bit_cast(bf16x8_t, v1);
+                a2[g][s] = __builtin_bit_cast(bf16x8_t, v2);
+            }
+        float xr[4][4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                xr[g][r] = xn[g * 16 + 4 * (lane >> 4) + r];
+        // B parts of one K-block of a tile (past the range: the last tile again,
+        // so the loads stay unconditional)
+        auto b_ptr = [&](int tile, int s, int p) {
+            tile = tile < t1 ? tile : t1 - 1;
+            return reinterpret_cast<const u16x8_t *>(
+                cx6 + ((((size_t)tile * 4 + cb) * KB + s) * 3 + p) * 512 + lane * 8);
+        };
+        bf16x8_t b[KB][3];
+        float cc = INFINITY;
+        if (t0 < t1) {
+#pragma unroll
+            for (int s = 0; s < KB; ++s)
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    b[s][p] = __builtin_bit_cast(bf16x8_t, *b_ptr(t0, s, p));
+            cc = cnorm_pad[((size_t)t0 * 4 + cb) * 16 + (lane & 15)];
+        }
+        for (int tile = t0; tile < t1; ++tile) {
+            const int rb = (tile - t0) % kRing;
+            const uint32_t visit = (uint32_t)((tile - t0) / kRing);
+            v4f acc[4];
+            const float ic = cc == INFINITY ? INFINITY : 0.f;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[g][r] = IP ? ic : xr[g][r] + cc;
+            const int tn = tile + 1;
+            const float cn = cnorm_pad[((size_t)(tn < t1 ? tn : t1 - 1) * 4 + cb) * 16 + (lane & 15)];
+#pragma unroll
+            for (int s = 0; s < KB; ++s) {
+                // small terms first, the leading product last
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[g][s], b[s][0], acc[g], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[g][s], b[s][2], acc[g], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[g][s], b[s][1], acc[g], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[g][s], b[s][0], acc[g], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[g][s], b[s][1], acc[g], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[g][s], b[s][0], acc[g], 0, 0, 0);
+                // this K-block's B parts are done: the next tile's
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    b[s][p] = __builtin_bit_cast(bf16x8_t, *b_ptr(tn, s, p));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            cc = cn;
+            if (visit > 0)
+                ring_wait(&consumed[rb], 4u * visit, broken);
+            float *dtile = dt + rb * TQ * 64;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dtile[(g * 16 + 4 * (lane >> 4) + r) * 64 + cb * 16 + (lane & 15)] = acc[g][r];
+            ring_signal(&produced[rb]);
+        }
+        return;
+    }
+
+    const int sw = wave - MW; // selection wave: queries 16 sw .. 16 sw + 15
+    const int rk = splits > 1 ? (nprobe + splits - 1) / splits : nprobe;
+    WaveTopK<NW> sel[QS];
+#pragma unroll
+    for (int i = 0; i < QS; ++i)
+        sel[i].init(nprobe, stage + (sw * QS + i) * 128, rk);
+    // shared bounds between the splits, as in the float32 kernel: lane i
+    // (< 16) publishes query i's k-th value and its slot value; the slots of
+    // query i, split s, are loaded by lane i + 16 (s % 4), four loads for up
+    // to 16 splits (more splits use the first bound only)
+    int64_t ql = q0 + sw * QS + (lane < QS ? lane : 0);
+    const bool qvalid = lane < QS && ql < nq;
+    ql = ql < nq ? ql : nq - 1;
+    const bool use_slots = splits > 1 && splits <= 16;
+    const int64_t qs = q0 + sw * QS + (lane & 15);
+    const bool slot_q = qs < nq;
+    uint32_t nb = float_order_key(INFINITY);
+    uint32_t nu[4] = {0u, 0u, 0u, 0u}; // order key 0 is below every float
+    bool pending = false;
+    for (int t = t0; t < t1; ++t) {
+        if (pending) {
+            uint32_t u = nu[0];
+#pragma unroll
+            for (int j = 1; j < 4; ++j)
+                u = u > nu[j] ? u : nu[j];
+            uint32_t o = xor_lane<16>(u);
+            u = u > o ? u : o;
+            o = xor_lane<32>(u);
+            u = u > o ? u : o;
+            u = use_slots ? u : float_order_key(INFINITY);
+            const uint32_t bnd = nb < u ? nb : u;
+#pragma unroll
+            for (int i = 0; i < QS; ++i)
+                sel[i].bound(float_from_order_key((uint32_t)__builtin_amdgcn_readlane((int)bnd, i)));
+            pending = false;
+        }
+        const int rb = (t - t0) % kRing;
+        ring_wait(&produced[rb], 4u * (uint32_t)((t - t0) / kRing + 1), broken);
+        const float *dtile = dt + rb * TQ * 64;
+        float cand[QS];
+#pragma unroll
+        for (int i = 0; i < QS; ++i)
+            cand[i] = dtile[(sw * QS + i) * 64 + lane];
+        ring_signal(&consumed[rb]);
+#pragma unroll
+        for (int i = 0; i < QS; ++i)
+            sel[i].push(cand[i], (uint32_t)(t * 64 + lane));
+        if (splits > 1 && ((t - t0) & 7) == 7) {
+            float mine = INFINITY, mpart = INFINITY;
+#pragma unroll
+            for (int i = 0; i < QS; ++i) {
+                mine = lane == i ? sel[i].kth : mine;
+                mpart = lane == i ? sel[i].part : mpart;
+            }
+            if (qvalid && mine < INFINITY)
+                atomicMin(qbound + ql, float_order_key(mine));
+            if (use_slots && qvalid)
+                __hip_atomic_store(pslot + ql * splits + split, float_order_key(mpart),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            nb = __hip_atomic_load(qbound + ql, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (use_slots) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int sj = (lane >> 4) + 4 * j;
+                    const bool ok = slot_q && sj < splits;
+                    const uint32_t *ps = pslot + (ok ? qs * splits + sj : 0);
+                    const uint32_t v =
+                        __hip_atomic_load(ps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    nu[j] = ok ? v : 0u;
+                }
+            }
+            pending = true;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < QS; ++i) {
+        sel[i].flush();
+        const int64_t q = q0 + sw * QS + i;
+        if (q >= nq)
+            continue;
+        if (splits == 1) {
+#pragma unroll
+            for (int r = 0; r < NW; ++r) {
+                const int e = r * 64 + lane;
+                if (e < nprobe) {
+                    probes[q * nprobe + e] = (int32_t)sel[i].wv[r];
+                    if (probe_d)
+                        probe_d[q * nprobe + e] = sel[i].wk[r];
+                }
+            }
+        } else {
+            const size_t base = ((size_t)q * splits + split) * KW;
+#pragma unroll
+            for (int r = 0; r < NW; ++r) {
+                part_d[base + r * 64 + lane] = sel[i].wk[r];
+                part_p[base + r * 64 + lane] = sel[i].wv[r];
+            }
+        }
+    }
+}
+
 // Merge the `splits` sorted partial lists of each query (one wave per query).
 template <int NW>
 __global__ __launch_bounds__(64) void coarse_merge_kernel(const float *__restrict__ part_d,
@@ -578,6 +909,10 @@ static int coarse_cu_count()
     return n;
 }
 
+__global__ void coarse_bound_init_kernel(uint32_t *__restrict__ qbound, int64_t n);
+
+bool coarse_uses_x6(int d, int nlist) { return d <= 96 && nlist >= 16384; }
+
 hipError_t launch_centroid_blocks(const DeviceIndex &ix, hipStream_t stream)
 {
     const int64_t total = (int64_t)ix.nblk * ix.d4 * 64;
@@ -585,7 +920,80 @@ hipError_t launch_centroid_blocks(const DeviceIndex &ix, hipStream_t stream)
     hipLaunchKernelGGL(centroid_blocks_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        stream, ix.centroids, ix.d, ix.d4, ix.nlist, ix.nblk, ix.cblk,
                        ix.cnorm_pad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !ix.cx6)
+        return e;
+    const int64_t ntile = ix.nblk / 4;
+    const int64_t nx = ntile * 4 * ix.x6_kb * 64;
+    hipLaunchKernelGGL(centroid_x6_kernel, dim3((unsigned)((nx + 255) / 256)), dim3(256), 0,
+                       stream, ix.centroids, ix.d, ix.nlist, ntile, ix.x6_kb, ix.cx6);
     return hipGetLastError();
+}
+
+// The bf16x6 kernel for one (NW, KB): the same workgroup grid, splits and
+// workspace as the float32 kernel with four row groups.
+template <int NW, int KB>
+static hipError_t coarse_x6_variant(const DeviceIndex &ix, const float *queries, int64_t nq,
+                                    int nprobe, int splits, void *ws, int32_t *probes,
+                                    float *probe_d, hipStream_t stream, bool ip)
+{
+    constexpr int TQ = 64;
+    const size_t lds = (size_t)TQ * (32 * KB + 1) * 4 + TQ * 4 + (size_t)kRing * TQ * 64 * 4 +
+                       TQ * 512 + (2 * kRing + 1) * 4;
+    auto kern = ip ? coarse_x6_kernel<NW, KB, true> : coarse_x6_kernel<NW, KB, false>;
+    if (lds > 160 * 1024)
+        return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+        return e;
+    float *part_d = static_cast<float *>(ws);
+    uint32_t *part_p = reinterpret_cast<uint32_t *>(part_d + (size_t)nq * splits * 64 * NW);
+    uint32_t *qbound = part_p + (size_t)nq * splits * 64 * NW;
+    uint32_t *pslot = qbound + nq;
+    if (splits > 1) {
+        const int64_t n = nq * (1 + (int64_t)splits);
+        hipLaunchKernelGGL(coarse_bound_init_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
+                           0, stream, qbound, n);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const dim3 grid((unsigned)((nq + TQ - 1) / TQ), (unsigned)splits);
+    hipLaunchKernelGGL(kern, grid, dim3(512), lds, stream, queries, nq, ix.d, ix.nblk, nprobe,
+                       ix.cx6, ix.cnorm_pad, splits, part_d, part_p, qbound, pslot, probes,
+                       probe_d);
+    e = hipGetLastError();
+    if (e != hipSuccess || splits == 1)
+        return e;
+    hipLaunchKernelGGL(coarse_merge_kernel<NW>, dim3((unsigned)nq), dim3(64), 0, stream, part_d,
+                       part_p, nq, splits, nprobe, probes, probe_d);
+    return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t coarse_x6_k(const DeviceIndex &ix, const float *queries, int64_t nq, int nprobe,
+                              int splits, void *ws, int32_t *probes, float *probe_d,
+                              hipStream_t stream, bool ip)
+{
+    switch (ix.x6_kb) {
+    case 1:
+        return coarse_x6_variant<NW, 1>(ix, queries, nq, nprobe, splits, ws, probes, probe_d, stream, ip);
+    case 2:
+        return coarse_x6_variant<NW, 2>(ix, queries, nq, nprobe, splits, ws, probes, probe_d, stream, ip);
+    case 3:
+        return coarse_x6_variant<NW, 3>(ix, queries, nq, nprobe, splits, ws, probes, probe_d, stream, ip);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+// Test switch: IVFPQ_TEST_COARSE_FP32=1 runs the float32 kernel where the
+// bf16x6 one would (read on every call).
+static bool coarse_force_fp32()
+{
+    const char *e = std::getenv("IVFPQ_TEST_COARSE_FP32");
+    return e && e[0] == '1';
 }
 
 // Row groups per workgroup (16 queries each) and the centroid split: many
@@ -801,6 +1209,13 @@ hipError_t launch_coarse(const DeviceIndex &ix, const float *queries, int64_t nq
         return launch_coarse_valu(ix, queries, nq, nprobe, probes, probe_d, stream, ip);
     int rg, splits;
     coarse_shape(nq, ix.nblk, ix.d4, &rg, &splits);
+    // many centroids of up to 96 dims: the bf16x6 kernel (its grid and
+    // workspace are those of the four-row-group float32 kernel)
+    if (ix.cx6 && rg == 4 && !coarse_force_fp32())
+        return nw == 1 ? coarse_x6_k<1>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
+                                        stream, ip)
+                       : coarse_x6_k<2>(ix, queries, nq, nprobe, splits, ws, probes, probe_d,
+                                        stream, ip);
     if (nw == 1)
         return coarse_mfma_k<1>(ix, queries, nq, nprobe, rg, splits, ws, probes, probe_d, stream,
                                 ip);

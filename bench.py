@@ -792,10 +792,11 @@ def main():
     lut_mode = O.IP if args.metric == "ip" else (O.LUT_F16 if args.lut == "f16" else O.LUT_F64)
     decomposed = bool(A.ivfpq_index_info(ix)["flags"] & 1) and args.lut == "f32" \
         and args.metric == "l2"
+    split = bool(A.ivfpq_index_info(ix)["flags"] & 2) and 1 < w.nprobe <= 128
     rep = check.compare_search(w.index, w.queries[rows], w.nprobe, w.k,
                                out[0].cpu().numpy()[rows], out[1].cpu().numpy()[rows],
                                out[2].cpu().numpy()[rows], lut_mode=lut_mode,
-                               decomposed=decomposed)
+                               decomposed=decomposed, split_bf16=split)
     log("parity", rep.summary(), f"({len(rows) - pn} giant-list queries among {len(rows)})")
     recall = None
     if args.metric == "l2":

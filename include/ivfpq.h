@@ -107,6 +107,14 @@ typedef struct {
  * units of round-off).  Binary16 tables and the inner product always use the
  * direct form. */
 #define IVFPQ_INDEX_DECOMPOSED_TABLES 1
+/* ivfpq_info.flags: the top-nprobe coarse step of this index (nprobe 2..128)
+ * forms x.c from three bfloat16 parts of each operand on the bfloat16 matrix
+ * cores (six exact partial products per dimension summed in float32; the
+ * split of "Leveraging the bfloat16 artificial intelligence datatype for
+ * higher-precision computations", Henry, Tang and Heinecke): indexes with
+ * d <= 96 and nlist >= 16,384.  Its forward-error bound counts
+ * 192 ceil(d/32) + d + 2 float32 roundings instead of d + 2. */
+#define IVFPQ_INDEX_COARSE_SPLIT_BF16 2
 
 typedef struct {
     int32_t d, nlist, m, nbits;

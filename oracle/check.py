@@ -9,6 +9,18 @@ rules below say when a device result counts as the oracle's result:
    gamma_n = n u / (1 - n u), u = 2^-24: a forward-error bound of any float32
    evaluation of |x - c|^2 (direct or through the norm expansion), times two.
    Where the sets differ the oracle is re-run on the device's probe set.
+   Split bfloat16 products (split_bf16=True: the device forms x.c from three
+   bfloat16 parts of each operand, x = x0 + x1 + x2 exactly, as six exact
+   partial products per dimension, x2 c0 + x0 c2 + x1 c1 + x1 c0 + x0 c1 +
+   x0 c0, summed in float32 by the matrix cores, "Leveraging the bfloat16
+   artificial intelligence datatype for higher-precision computations",
+   Henry, Tang and Heinecke): the sum has 6 * 32 * ceil(d/32) products and
+   the start value, so a sequential float32 evaluation of it errs by at most
+   gamma_{192 ceil(d/32)} times the sum of the terms' magnitudes (<= 1.01 times
+   those of the float32 expansion), the norms by gamma_d each, and the three
+   dropped products by 2u |x_i c_i|; together within
+   2 gamma_n (|x|^2 + |c|^2) with n = 192 ceil(d/32) + d + 2, so delta_c uses
+   that n in place of d + 2.
 2. Result ids.  The device id set may differ from the oracle's only by ids
    whose oracle distance is within tau * D_o[k-1] of the oracle's k-th
    distance; no duplicates; distances non-decreasing; the padding (+inf, -1)
@@ -105,10 +117,18 @@ def _get(index, name):
     return index[name] if isinstance(index, dict) else getattr(index, name)
 
 
-def check_probes(index, queries, gpu_probes, oracle_probes, report: Report, ip=False):
+def coarse_gamma_n(d: int, split_bf16: bool = False) -> int:
+    """n of the gamma_n in rule 1's band: d + 2 for a float32 evaluation of
+    the norm expansion; 192 ceil(d/32) + d + 2 for split bfloat16 products."""
+    return 192 * ((d + 31) // 32) + d + 2 if split_bf16 else d + 2
+
+
+def check_probes(index, queries, gpu_probes, oracle_probes, report: Report, ip=False,
+                 split_bf16=False):
     """Rule 1.  Returns the list of query rows whose probe set differs."""
     cent = np.asarray(_get(index, "centroids"), dtype=np.float32)
     nlist, d = cent.shape
+    gn = coarse_gamma_n(d, split_bf16)
     cmax = float(np.max(np.sum(cent.astype(np.float64) ** 2, axis=1)))
     differ = []
     for qi in range(len(queries)):
@@ -124,10 +144,10 @@ def check_probes(index, queries, gpu_probes, oracle_probes, report: Report, ip=F
         if ip:
             allp, ips = O.coarse_ip(queries[qi], cent, nlist)
             alld = -ips
-            delta = 4.0 * gamma(d + 2) * math.sqrt(x2 * cmax)
+            delta = 4.0 * gamma(gn) * math.sqrt(x2 * cmax)
         else:
             allp, alld = O.coarse(queries[qi], cent, nlist)
-            delta = 4.0 * gamma(d + 2) * (x2 + cmax)
+            delta = 4.0 * gamma(gn) * (x2 + cmax)
         dist_of = {int(p): float(v) for p, v in zip(allp, alld)}
         edge = float(alld[nprobe - 1])
         for lst in g ^ o:
@@ -236,11 +256,14 @@ def l2_abs_tol(index, queries, probes, kth, decomposed=False):
 
 
 def compare_search(index, queries, nprobe, k, gpu_d, gpu_i, gpu_probes=None, lut_mode=O.LUT_F64,
-                   tau=None, k_extra=32, nthreads=None, decomposed=False) -> Report:
+                   tau=None, k_extra=32, nthreads=None, decomposed=False,
+                   split_bf16=False) -> Report:
     """Full acceptance check of a device IVF-PQ search against the oracle
     (lut_mode O.IP: the inner-product metric, scores in decreasing order).
     decomposed: the device built its tables from the per-list term (squared
-    L2 only); rule 3's absolute term then includes their error bound."""
+    L2 only); rule 3's absolute term then includes their error bound.
+    split_bf16: the device's coarse products came from split bfloat16 parts
+    (rule 1's band with its n)."""
     ip = lut_mode == O.IP
     tau = (TAU_F32 if lut_mode in (O.LUT_F64, O.IP) else TAU_F16) if tau is None else tau
     queries = np.ascontiguousarray(queries, dtype=np.float32)
@@ -248,7 +271,7 @@ def compare_search(index, queries, nprobe, k, gpu_d, gpu_i, gpu_probes=None, lut
     kx = k + k_extra
     od, oi, op = O.search(index, queries, nprobe, kx, lut_mode=lut_mode, nthreads=nthreads)
     if gpu_probes is not None:
-        differ = check_probes(index, queries, gpu_probes, op, rep, ip=ip)
+        differ = check_probes(index, queries, gpu_probes, op, rep, ip=ip, split_bf16=split_bf16)
         if differ:
             rep.queries_reprobed = len(differ)
             sub = np.asarray(differ)

@@ -60,9 +60,11 @@ def search_and_check(A, w, runs=(("f32", "l2"),), sample=16, giant=0):
         t = time.time()
         decomposed = bool(A.ivfpq_index_info(ix)["flags"] & 1) and lut == "f32" \
             and metric == "l2"
+        split = bool(A.ivfpq_index_info(ix)["flags"] & 2) and 1 < w.nprobe <= 128
         rep = check.compare_search(w.index, w.queries[rows], w.nprobe, w.k,
                                    d.cpu().numpy()[rows], i.cpu().numpy()[rows],
-                                   p.cpu().numpy()[rows], lut_mode=mode, decomposed=decomposed)
+                                   p.cpu().numpy()[rows], lut_mode=mode, decomposed=decomposed,
+                                   split_bf16=split)
         print(f"  parity {rep.summary()} on {len(rows)} rows ({time.time() - t:.1f} s)",
               flush=True)
         assert rep.ok(), rep.failures[:5]
