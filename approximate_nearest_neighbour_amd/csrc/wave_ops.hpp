@@ -8,11 +8,16 @@
 // compare-exchange between elements e and e ^ s happens inside one lane when
 // s >= 64 (two registers of the same lane) and across lanes otherwise.
 //
-// Cross-lane exchange by distance:
-//   s = 1, 2 : DPP quad_perm (a VALU operand modifier, no LDS traffic)
+// Cross-lane exchange by distance, all in registers (no LDS round trip: the
+// selection's sorts are latency-bound chains of these steps):
+//   s = 1, 2 : DPP quad_perm
+//   s = 4    : DPP row_half_mirror (l -> l ^ 7 inside 8 lanes) then quad_perm
+//              [3,2,1,0] (l -> l ^ 3): together l ^ 4
 //   s = 8    : DPP row_ror:8 (rotation by 8 inside a 16-lane row == xor 8)
-//   s = 4, 16: ds_swizzle bit-mask mode (xor inside 32-lane halves)
-//   s = 32   : ds_bpermute
+//   s = 16   : v_permlane16_swap of the value with itself: one result holds
+//              rows 0,0,2,2, the other rows 1,1,3,3; a lane of an odd row
+//              takes the first, of an even row the second
+//   s = 32   : v_permlane32_swap likewise (halves lo,lo and hi,hi)
 // The networks are bitonic: sort of 2^n elements in n(n+1)/2 steps, merge of
 // a bitonic sequence of 2^n elements in n steps; their step tables and lane
 // masks are in network.hpp (shared with a host check of the same tables).
@@ -42,10 +47,15 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v)
         return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); // quad_perm 2,3,0,1
     } else if constexpr (S == 8) {
         return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); // row_ror:8
-    } else if constexpr (S == 4 || S == 16) {
-        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (S << 10));
+    } else if constexpr (S == 4) {
+        const int h = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false); // row_half_mirror
+        return (uint32_t)__builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, false);    // quad_perm 3,2,1,0
+    } else if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return __builtin_amdgcn_inverse_ballot_w64(0xFFFF0000FFFF0000ull) ? r[0] : r[1];
     } else {
-        return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, (int)v);
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return __builtin_amdgcn_inverse_ballot_w64(0xFFFFFFFF00000000ull) ? r[0] : r[1];
     }
 }
 
