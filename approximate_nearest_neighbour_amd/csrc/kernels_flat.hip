@@ -279,12 +279,34 @@ __attribute__((amdgpu_waves_per_eu(PASS == kPassCollect ? 3 : 1))) void flat_gem
                 acc[rb] = mfma_u<KS>(a[rb], b, ycol);
         };
         if (PASS == kPassMinima) {
-            // column blocks in pairs: one three-way minimum per two values
-#pragma unroll 1
+            // column blocks in pairs (one three-way minimum per two values),
+            // each block's B operand read from LDS while the previous block
+            // is multiplied
+            auto load_b = [&](int cb, bf16x8 (&b)[KS], float &yc) {
+                const uint16_t *bp =
+                    bt + (buf * 64 + cb * 16 + (lane & 15)) * RS + 8 * (lane >> 4);
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    b[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(bp + 32 * s));
+                yc = yn[buf * 64 + cb * 16 + (lane & 15)];
+            };
+            bf16x8 bA[KS], bB[KS];
+            float yA, yB;
+            load_b(0, bA, yA);
+            load_b(1, bB, yB);
+#pragma unroll
             for (int cb = 0; cb < 4; cb += 2) {
                 v4f u0[RB], u1[RB];
-                block_u(cb, u0);
-                block_u(cb + 1, u1);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    u0[rb] = mfma_u<KS>(a[rb], bA, yA);
+                if (cb + 2 < 4)
+                    load_b(cb + 2, bA, yA);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    u1[rb] = mfma_u<KS>(a[rb], bB, yB);
+                if (cb + 3 < 4)
+                    load_b(cb + 3, bB, yB);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
