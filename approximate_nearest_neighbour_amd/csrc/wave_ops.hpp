@@ -70,16 +70,38 @@ __device__ __forceinline__ float xor_lane(float v)
 // mask: the two comparisons become lane masks, the choice between them three
 // scalar mask operations, and the exchange two selects.  Equal keys never
 // move, so the two lanes of a pair always take consistent decisions.
+//
+// At distance 16 and 32 the row swap hands every lane both elements of its
+// pair, [0] the one of the lane with bit S clear and [1] the other, so both
+// lanes of a pair evaluate the same comparison and take the smaller or the
+// larger element by their mask bit: one compare and two selects instead of
+// two exchanges, two compares and two selects.  Equal keys then keep their
+// places in ascending blocks and trade them in descending ones; either way
+// the pair's (key, value) elements stay whole.
 template <int S, uint64_t KEEP_MIN>
 __device__ __forceinline__ void cx_lane_mask(float &k, uint32_t &v)
 {
-    const float pk = xor_lane<S>(k);
-    const uint32_t pv = xor_lane<S>(v);
-    const uint64_t lt = __builtin_amdgcn_ballot_w64(pk < k);
-    const uint64_t gt = __builtin_amdgcn_ballot_w64(pk > k);
-    const bool take = __builtin_amdgcn_inverse_ballot_w64((lt & KEEP_MIN) | (gt & ~KEEP_MIN));
-    k = take ? pk : k;
-    v = take ? pv : v;
+    if constexpr (S == 16 || S == 32) {
+        const uint32_t ku = __float_as_uint(k);
+        auto kk = S == 16 ? __builtin_amdgcn_permlane16_swap(ku, ku, false, false)
+                          : __builtin_amdgcn_permlane32_swap(ku, ku, false, false);
+        auto vv = S == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                          : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        const float lo = __uint_as_float(kk[0]);
+        const float hi = __uint_as_float(kk[1]);
+        const uint64_t hl = __builtin_amdgcn_ballot_w64(hi < lo);
+        const bool take_hi = __builtin_amdgcn_inverse_ballot_w64(~(hl ^ KEEP_MIN));
+        k = take_hi ? hi : lo;
+        v = take_hi ? vv[1] : vv[0];
+    } else {
+        const float pk = xor_lane<S>(k);
+        const uint32_t pv = xor_lane<S>(v);
+        const uint64_t lt = __builtin_amdgcn_ballot_w64(pk < k);
+        const uint64_t gt = __builtin_amdgcn_ballot_w64(pk > k);
+        const bool take = __builtin_amdgcn_inverse_ballot_w64((lt & KEEP_MIN) | (gt & ~KEEP_MIN));
+        k = take ? pk : k;
+        v = take ? pv : v;
+    }
 }
 
 // The lane compare-exchanges of one bitonic step, register by register.
