@@ -717,12 +717,18 @@ void scan_items_kernel(ScanArgs a)
                     }
                 }
                 // FULL: every entry of the step exists (no per-lane bound)
+                // The lane's EPL entries of a step are all formed first (their
+                // table reads overlap) and then tested against the filter
+                // threshold with one comparison of their minimum: the usual
+                // step has no value under it in any lane and pushes nothing.
+                // Otherwise each entry is pushed in order, as one at a time
+                // would be (the threshold only falls in between, so a skipped
+                // step would have pushed nothing either).
                 auto consume = [&](auto full, const Row &row, uint32_t first, uint32_t limit) {
                     constexpr bool FULL = decltype(full)::value;
+                    float r[EPL];
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) {
-                        const uint32_t i = first + e;
-                        float r;
                         if constexpr (WIDE) {
                             // code of sub-quantizer t ^ s into byte t (s = (l & 31) >> 2)
                             const uint32_t lo = row.w[2 * e], hi = row.w[2 * e + 1];
@@ -744,16 +750,27 @@ void scan_items_kernel(ScanArgs a)
                                 tv[t] = *reinterpret_cast<const __attribute__((address_space(3))) float *>(
                                     (uintptr_t)ad);
                             }
-                            r = sum_terms<8, true>(tv);
+                            r[e] = sum_terms<8, true>(tv);
                         } else {
-                            r = adc_words<M, F16>(row.w + e * (M / 4), lut);
+                            r[e] = adc_words<M, F16>(row.w + e * (M / 4), lut);
                         }
                         if constexpr (!FULL)
-                            r = i < limit ? r : INFINITY;
-                        if constexpr (SO)
-                            sink = fminf(sink, r);
-                        else
-                            sel.push(r, off + i);
+                            r[e] = first + e < limit ? r[e] : INFINITY;
+                    }
+                    if constexpr (SO) {
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e)
+                            sink = fminf(sink, r[e]);
+                    } else {
+                        float mn = r[0];
+#pragma unroll
+                        for (int e = 1; e < EPL; ++e)
+                            mn = fminf(mn, r[e]);
+                        if (sel.any_below(mn)) {
+#pragma unroll
+                            for (int e = 0; e < EPL; ++e)
+                                sel.push(r[e], off + first + e);
+                        }
                     }
                 };
                 uint32_t s0 = pc.b + rank * SPAN;

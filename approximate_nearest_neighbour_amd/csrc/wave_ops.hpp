@@ -65,6 +65,31 @@ __device__ __forceinline__ float xor_lane(float v)
     return __uint_as_float(xor_lane<S>(__float_as_uint(v)));
 }
 
+// The same exchange through the LDS crossbar at distances 4, 16 and 32
+// (ds_swizzle in bit-mask mode, xor inside 32-lane halves; ds_bpermute for
+// 32): a round trip through the LDS pipe but no VALU instruction.  Wide
+// arrays take it: a merge step over many registers has that many independent
+// exchanges in flight, so their latency hides and the VALU is the busy pipe.
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane_lds(uint32_t v)
+{
+    if constexpr (S == 4 || S == 16)
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (S << 10));
+    else if constexpr (S == 32)
+        return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, (int)v);
+    else
+        return xor_lane<S>(v);
+}
+
+#ifndef IVFPQ_LDS_XCHG_MIN_R
+#define IVFPQ_LDS_XCHG_MIN_R 8
+#endif
+#ifndef IVFPQ_LDS_XCHG_S4
+#define IVFPQ_LDS_XCHG_S4 1
+#endif
+// Register count from which a step's lane exchanges go through the LDS.
+constexpr int kLdsExchangeMinR = IVFPQ_LDS_XCHG_MIN_R;
+
 // Compare-exchange of (k, v) with the partner lane at distance S, keep_min
 // (this lane keeps the smaller key) given for all 64 lanes as a compile-time
 // mask: the two comparisons become lane masks, the choice between them three
@@ -78,10 +103,19 @@ __device__ __forceinline__ float xor_lane(float v)
 // two exchanges, two compares and two selects.  Equal keys then keep their
 // places in ascending blocks and trade them in descending ones; either way
 // the pair's (key, value) elements stay whole.
-template <int S, uint64_t KEEP_MIN>
+template <int S, uint64_t KEEP_MIN, bool LDS = false>
 __device__ __forceinline__ void cx_lane_mask(float &k, uint32_t &v)
 {
-    if constexpr (S == 16 || S == 32) {
+    constexpr bool VIA_LDS = LDS && (S == 16 || S == 32 || (S == 4 && IVFPQ_LDS_XCHG_S4));
+    if constexpr (VIA_LDS) {
+        const float pk = __uint_as_float(xor_lane_lds<S>(__float_as_uint(k)));
+        const uint32_t pv = xor_lane_lds<S>(v);
+        const uint64_t lt = __builtin_amdgcn_ballot_w64(pk < k);
+        const uint64_t gt = __builtin_amdgcn_ballot_w64(pk > k);
+        const bool take = __builtin_amdgcn_inverse_ballot_w64((lt & KEEP_MIN) | (gt & ~KEEP_MIN));
+        k = take ? pk : k;
+        v = take ? pv : v;
+    } else if constexpr (S == 16 || S == 32) {
         const uint32_t ku = __float_as_uint(k);
         auto kk = S == 16 ? __builtin_amdgcn_permlane16_swap(ku, ku, false, false)
                           : __builtin_amdgcn_permlane32_swap(ku, ku, false, false);
@@ -109,7 +143,7 @@ template <int S, int B, bool DESC, int R, int... RR>
 __device__ __forceinline__ void cx_lanes(float (&k)[R], uint32_t (&v)[R],
                                          std::integer_sequence<int, RR...>)
 {
-    (cx_lane_mask<S, keep_min_mask(S, B, DESC, RR)>(k[RR], v[RR]), ...);
+    (cx_lane_mask<S, keep_min_mask(S, B, DESC, RR), (R >= kLdsExchangeMinR)>(k[RR], v[RR]), ...);
 }
 
 // In-lane compare-exchange between registers (a holds the lower element).

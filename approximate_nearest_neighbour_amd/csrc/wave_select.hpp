@@ -111,6 +111,12 @@ struct WaveTopK {
     // Tighten the filter with an external bound (another wave's k-th value).
     __device__ __forceinline__ void bound(float ext) { thr = uni(fminf(thr, ext)); }
 
+    // Whether any lane's key would pass the filter now (wave-uniform).
+    __device__ __forceinline__ bool any_below(float key) const
+    {
+        return wave_ballot(key < thr) != 0;
+    }
+
     // One candidate per lane; lanes without a candidate pass key = +inf.
     __device__ __forceinline__ void push(float key, uint32_t val)
     {
