@@ -136,10 +136,12 @@ ivfpq_status check_sizes(const int64_t *sizes, int64_t nlist, int64_t ntotal, in
     for (int64_t l = 0; l < nlist; ++l) {
         if (sizes[l] < 0)
             return fail(IVFPQ_E_FORMAT, "negative list size");
+        // compared with the room left before the addition: a sum that wrapped
+        // around could otherwise come back to ntotal
+        if (sizes[l] > ntotal - sum)
+            return fail(IVFPQ_E_FORMAT, "list sizes exceed ntotal");
         sum += sizes[l];
         mx = sizes[l] > mx ? sizes[l] : mx;
-        if (sum > ntotal)
-            return fail(IVFPQ_E_FORMAT, "list sizes exceed ntotal");
     }
     if (sum != ntotal)
         return fail(IVFPQ_E_FORMAT, "list sizes do not add up to ntotal");
@@ -412,7 +414,11 @@ const char *ivfpq_last_error(void) { return g_err.c_str(); }
 
 const char *ivfpq_status_string(ivfpq_status s)
 {
-    switch (s) {
+    // a C caller may pass any int: read the argument's bytes as one instead
+    // of loading it as the C++ enumeration, whose range ends at 7
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
     case IVFPQ_OK: return "ok";
     case IVFPQ_E_INVALID_ARG: return "invalid argument";
     case IVFPQ_E_IO: return "i/o error";
