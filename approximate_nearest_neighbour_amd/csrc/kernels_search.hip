@@ -881,6 +881,10 @@ void scan_items_kernel(ScanArgs a)
                         a.part_d[e] = sel.wk[r];
                         a.part_p[e] = sel.wv[r];
                     }
+                    // the item's own k-th value (merged over its waves) bounds
+                    // the query's: its items that start later filter against
+                    // it instead of the looser union bound
+                    publish_bound(&a.qbound[q], sel.kth);
                 }
             }
             __syncthreads(); // merge scratch aliases the tables
