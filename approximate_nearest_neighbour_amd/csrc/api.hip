@@ -202,6 +202,7 @@ void release(ivfpq_index *ix)
     (void)hipFree(d.codes);
     (void)hipFree(d.ids);
     (void)hipFree(d.t1);
+    (void)hipFree(d.gbucket);
     (void)hipFree(ix->ws);
     (void)hipFree(ix->prof_counts);
     for (auto &e : ix->prof_events) {
@@ -289,6 +290,26 @@ ivfpq_status alloc_index(int device, int d, int nlist, int m, int64_t ntotal,
 
 ivfpq_status finish_load(ivfpq_index *ix)
 {
+    // region buckets of the giant lists, from the host copy of the list
+    // offsets (the scan order runs the work items that read the same region
+    // of a giant list side by side)
+    {
+        DeviceIndex &dx = ix->dx;
+        std::vector<uint32_t> gb((size_t)dx.nlist, kNoBucket);
+        uint64_t nb = 0;
+        for (int l = 0; l < dx.nlist; ++l) {
+            const uint64_t sz = ix->host_off[l + 1] - ix->host_off[l];
+            if (sz >= kGiantList) {
+                gb[l] = (uint32_t)nb;
+                nb += (sz + kRegion - 1) / kRegion;
+            }
+        }
+        if (nb > 0) {
+            dx.nbucket = (uint32_t)nb;
+            ALLOC_OR_FAIL(dx.gbucket, (size_t)dx.nlist * 4);
+            COPY_OR_FAIL(dx.gbucket, gb.data(), (size_t)dx.nlist * 4);
+        }
+    }
     if (launch_centroid_blocks(ix->dx, nullptr) != hipSuccess ||
         launch_list_term(ix->dx, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         release(ix);
@@ -597,8 +618,8 @@ namespace {
 // (imax items per query; a query with one item writes its rows from the
 // scan, so imax = 1 needs no partials).
 struct WsLayout {
-    size_t probes, total, chunk, count, base, bound, counter, order_q, order_r, rank_n, coarse,
-        pd, pp, bytes;
+    size_t probes, total, chunk, count, base, bound, counter, order_q, order_r, rank_n, rm_q,
+        rm_r, ikey, bcur, coarse, pd, pp, bytes;
 };
 
 WsLayout ws_layout(const DeviceIndex &dx, int64_t nq, int nprobe, int k, uint32_t imax,
@@ -621,6 +642,12 @@ WsLayout ws_layout(const DeviceIndex &dx, int64_t nq, int nprobe, int k, uint32_
     o.order_q = carve((size_t)nq * imax * 4);
     o.order_r = carve((size_t)nq * imax * 4);
     o.rank_n = carve((size_t)imax * 4);
+    if (dx.nbucket > 0) { // the order by giant-list regions
+        o.rm_q = carve((size_t)nq * imax * 4);
+        o.rm_r = carve((size_t)nq * imax * 4);
+        o.ikey = carve((size_t)nq * imax * 4);
+        o.bcur = carve(((size_t)dx.nbucket + 1) * 4);
+    }
     o.coarse = carve(coarse_ws_bytes(dx, nq, nprobe));
     const size_t part = imax > 1 ? (size_t)nq * imax * (size_t)kw_of(k) * 4 : 0;
     o.pd = carve(part);
@@ -718,6 +745,12 @@ ivfpq_status search_impl(ivfpq_index *idx, const ivfpq_search_params *p, const f
     pl.item_q = reinterpret_cast<uint32_t *>(ws + o.order_q);
     pl.item_r = reinterpret_cast<uint32_t *>(ws + o.order_r);
     pl.rank_n = reinterpret_cast<uint32_t *>(ws + o.rank_n);
+    if (dx.nbucket > 0) {
+        pl.rm_q = reinterpret_cast<uint32_t *>(ws + o.rm_q);
+        pl.rm_r = reinterpret_cast<uint32_t *>(ws + o.rm_r);
+        pl.ikey = reinterpret_cast<uint32_t *>(ws + o.ikey);
+        pl.bcur = reinterpret_cast<uint32_t *>(ws + o.bcur);
+    }
     pl.part_d = reinterpret_cast<float *>(ws + o.pd);
     pl.part_p = reinterpret_cast<uint32_t *>(ws + o.pp);
     const bool recording = idx->profiling && idx->prof_calls < idx->prof_max;

@@ -30,7 +30,16 @@ struct DeviceIndex {
     // list term of the decomposed tables (only for the shapes and sizes that
     // use them, else nullptr): t1[l][j][c] = |C_j[c]|^2 + 2 <c_l,j, C_j[c]>
     float *t1 = nullptr;         // [nlist][m][256]
+    // Regions of the giant lists (kGiantList entries or more): list l's
+    // region j (entries [j kRegion, (j + 1) kRegion)) is bucket gbucket[l] + j
+    // of the scan order (kNoBucket for the other lists); nbucket in all.
+    uint32_t *gbucket = nullptr; // [nlist], nullptr when nbucket == 0
+    uint32_t nbucket = 0;
 };
+
+constexpr uint32_t kGiantList = 1u << 20;
+constexpr uint32_t kRegion = 1u << 18;
+constexpr uint32_t kNoBucket = 0xFFFFFFFFu;
 
 struct SearchArgs {
     const float *queries;
@@ -60,6 +69,10 @@ struct SearchPlan {
     // scan order of the items, rank-major: position i holds query item_q[i]'s
     // item number item_r[i]; rank_n[r] = queries with more than r items
     uint32_t *item_q = nullptr, *item_r = nullptr, *rank_n = nullptr;
+    // with giant lists: the rank-major order (rm_q, rm_r), each item's bucket
+    // (ikey) and the buckets' cursors (bcur, nbucket + 1 words); item_q and
+    // item_r then receive the final order (scan_order_kernel)
+    uint32_t *rm_q = nullptr, *rm_r = nullptr, *ikey = nullptr, *bcur = nullptr;
     float *part_d = nullptr;   // [max_items][kw]
     uint32_t *part_p = nullptr; // [max_items][kw]
     // when not null: [0] += entries of the probed lists, [1] += work items

@@ -47,6 +47,19 @@ namespace ivfpq {
 // planning
 // ---------------------------------------------------------------------------
 
+// Region-aligned layout of a query's sequence when the index has giant lists
+// (the scan order groups the work items that read the same region of a
+// giant list; aligned, those items read the same lines in step): the small
+// lists first, in probe order, then, from the next multiple of kRegion, the
+// giant lists in probe order, each taking its size rounded up to a multiple
+// of kRegion (the padding holds no entries and no piece meets it).  Item
+// boundaries, multiples of a chunk that is itself a multiple of kRegion,
+// then fall on region boundaries of every giant list.
+__host__ __device__ inline uint64_t region_round(uint64_t n)
+{
+    return (n + kRegion - 1) / kRegion * kRegion;
+}
+
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ probes, int nprobe,
                                                    int64_t nq, int nlist,
                                                    const uint32_t *__restrict__ list_off,
@@ -56,17 +69,28 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ p
                                                    uint32_t *__restrict__ qcount,
                                                    uint32_t *__restrict__ qbound,
                                                    uint32_t *__restrict__ counter,
-                                                   unsigned long long *__restrict__ prof)
+                                                   unsigned long long *__restrict__ prof,
+                                                   const uint32_t *__restrict__ gbucket,
+                                                   uint32_t *__restrict__ bcur, uint32_t nbucket)
 {
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (q == 0)
         *counter = 0;
-    uint64_t e = 0;
+    if (bcur) // the giant-list buckets' counters (order_* kernels)
+        for (int64_t i = q; i <= (int64_t)nbucket; i += (int64_t)gridDim.x * 256)
+            bcur[i] = 0;
+    uint64_t e = 0, small = 0, giant = 0;
     if (q < nq) {
         for (int p = 0; p < nprobe; ++p) {
             const int l = probes[q * nprobe + p];
-            if ((unsigned)l < (unsigned)nlist)
-                e += list_off[l + 1] - list_off[l];
+            if ((unsigned)l < (unsigned)nlist) {
+                const uint32_t sz = list_off[l + 1] - list_off[l];
+                e += sz;
+                if (gbucket && gbucket[l] != kNoBucket)
+                    giant += region_round(sz);
+                else
+                    small += sz;
+            }
         }
     }
     if (prof) {
@@ -80,8 +104,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ p
     }
     if (q >= nq)
         return;
-    const uint32_t total = (uint32_t)e;
-    const QueryPlan qp = plan_query(total, target, imax);
+    // the query's sequence: its entries (with giant lists, the region-aligned
+    // layout of the scan order)
+    const uint32_t total = (uint32_t)(giant ? region_round(small) + giant : e);
+    const QueryPlan qp = plan_query(total, target, imax, gbucket ? kRegion : 1u);
     qtotal[q] = total;
     qchunk[q] = qp.chunk;
     qcount[q] = qp.count;
@@ -195,6 +221,146 @@ __global__ __launch_bounds__(1024) void rank_order_kernel(const uint32_t *__rest
     }
 }
 
+// Scan order with giant lists (kGiantList entries or more).  The lists
+// nearest to many queries are probed by many of them: at the 1B Zipf shape
+// the regions of the giant lists are read by about 20 work items each, and
+// in rank-major order those reads are spread over the whole scan.  The items
+// past a query's first with a piece of a giant list are therefore taken out
+// of the rank-major order and run after the others, bucket by bucket, a
+// bucket being the region (kRegion entries) of a giant list where the item's
+// largest such piece starts: items that read the same region then run side
+// by side, and all but the first find its lines in the cache.  The other
+// items keep their rank-major order and run first, the first item of every
+// query (its nearest lists) among them, so a query's bound is published
+// before its giant pieces are scanned.  The result does not depend on the
+// order.
+//
+// item_key_kernel: each item's bucket (kNoBucket: none), counted into
+// bcur[bucket + 1] (bcur zeroed by the plan kernel).
+__global__ __launch_bounds__(256) void item_key_kernel(
+    const uint32_t *__restrict__ item_base, int64_t nq, const uint32_t *__restrict__ rm_q,
+    const uint32_t *__restrict__ rm_r, const uint32_t *__restrict__ qchunk,
+    const uint32_t *__restrict__ qtotal, const int32_t *__restrict__ probes, int nprobe,
+    int nlist, const uint32_t *__restrict__ list_off, const uint32_t *__restrict__ gbucket,
+    uint32_t *__restrict__ ikey, uint32_t *__restrict__ bcur)
+{
+    const uint32_t total = item_base[nq];
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)total)
+        return;
+    const int64_t q = rm_q[i];
+    const uint32_t r = rm_r[i];
+    uint32_t start, stop;
+    item_range(r, qchunk[q], qtotal[q], &start, &stop);
+    uint32_t best = 0, key = kNoBucket;
+    // a query's first item (its nearest lists) keeps its rank-major place:
+    // the bound it publishes is the one the query's other items start from
+    if (r > 0) {
+        // the giant lists' offsets in the region-aligned sequence
+        uint64_t acc = 0;
+        for (int p = 0; p < nprobe; ++p) {
+            const int l = probes[q * nprobe + p];
+            if ((unsigned)l < (unsigned)nlist && gbucket[l] == kNoBucket)
+                acc += list_off[l + 1] - list_off[l];
+        }
+        acc = region_round(acc);
+        for (int p = 0; p < nprobe && acc < stop; ++p) {
+            const int l = probes[q * nprobe + p];
+            if ((unsigned)l >= (unsigned)nlist || gbucket[l] == kNoBucket)
+                continue;
+            const uint32_t sz = list_off[l + 1] - list_off[l];
+            uint32_t b, e;
+            if (piece_of((uint32_t)acc, (uint32_t)acc + sz, start, stop, &b, &e) && e - b > best) {
+                best = e - b;
+                key = gbucket[l] + b / kRegion;
+            }
+            acc += region_round(sz);
+        }
+    }
+    ikey[i] = key;
+    if (key != kNoBucket)
+        atomicAdd(&bcur[key + 1], 1u);
+}
+
+// One workgroup: the items without a bucket, compacted in rank-major order to
+// the front of the final order; then bcur[b] becomes the first position of
+// bucket b (an inclusive prefix over bcur[0..nbucket], whose bcur[b + 1]
+// held bucket b's count, plus the number of items placed first).
+__global__ __launch_bounds__(1024) void order_scan_kernel(
+    const uint32_t *__restrict__ item_base, int64_t nq, const uint32_t *__restrict__ rm_q,
+    const uint32_t *__restrict__ rm_r, const uint32_t *__restrict__ ikey,
+    uint32_t *__restrict__ bcur, uint32_t nbucket, uint32_t *__restrict__ item_q,
+    uint32_t *__restrict__ item_r)
+{
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t carry_s;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t total = item_base[nq];
+    if (tid == 0)
+        carry_s = 0;
+    __syncthreads();
+    for (int64_t s = 0; s < total; s += 1024) {
+        const int64_t i = s + tid;
+        const uint32_t v = (i < total && ikey[i] == kNoBucket) ? 1u : 0u;
+        const uint32_t incl = wave_inclusive_sum(v);
+        if (lane == 63)
+            wsum[wave] = incl;
+        __syncthreads();
+        uint32_t before = carry_s;
+        for (int w = 0; w < wave; ++w)
+            before += wsum[w];
+        if (v) {
+            item_q[before + incl - 1] = rm_q[i];
+            item_r[before + incl - 1] = rm_r[i];
+        }
+        __syncthreads();
+        if (tid == 1023)
+            carry_s = before + incl;
+        __syncthreads();
+    }
+    const uint32_t placed = carry_s;
+    __syncthreads();
+    if (tid == 0)
+        carry_s = placed;
+    __syncthreads();
+    for (int64_t s = 0; s <= (int64_t)nbucket; s += 1024) {
+        const int64_t i = s + tid;
+        const uint32_t v = i <= (int64_t)nbucket ? bcur[i] : 0u;
+        const uint32_t incl = wave_inclusive_sum(v);
+        if (lane == 63)
+            wsum[wave] = incl;
+        __syncthreads();
+        uint32_t before = carry_s;
+        for (int w = 0; w < wave; ++w)
+            before += wsum[w];
+        if (i <= (int64_t)nbucket)
+            bcur[i] = before + incl;
+        __syncthreads();
+        if (tid == 1023)
+            carry_s = before + incl;
+        __syncthreads();
+    }
+}
+
+// The items with a bucket, each to the next free position of its bucket.
+__global__ __launch_bounds__(256) void order_scatter_kernel(
+    const uint32_t *__restrict__ item_base, int64_t nq, const uint32_t *__restrict__ rm_q,
+    const uint32_t *__restrict__ rm_r, const uint32_t *__restrict__ ikey,
+    uint32_t *__restrict__ bcur, uint32_t *__restrict__ item_q, uint32_t *__restrict__ item_r)
+{
+    const uint32_t total = item_base[nq];
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)total)
+        return;
+    const uint32_t key = ikey[i];
+    if (key == kNoBucket)
+        return;
+    const uint32_t pos = atomicAdd(&bcur[key], 1u);
+    item_q[pos] = rm_q[i];
+    item_r[pos] = rm_r[i];
+}
+
 // ---------------------------------------------------------------------------
 // scan
 // ---------------------------------------------------------------------------
@@ -221,6 +387,7 @@ struct ScanArgs {
     int ip;      // inner-product metric (tables of the run-time shape)
     float osign; // sign of the reported values: +1 squared L2, -1 inner product
     uint32_t wide_min; // pieces of at least this many entries get a replicated table
+    const uint32_t *gbucket; // giant lists' buckets (region-aligned sequence), or nullptr
 };
 
 // A code row of M bytes read with the widest loads its size allows.
@@ -586,20 +753,37 @@ void scan_items_kernel(ScanArgs a)
         // pieces of [start, stop) of the query's concatenated probed lists
         if (wave == 0) {
             uint32_t acc = 0, cn = 0, cw = 0;
+            // with giant lists (a.gbucket), the region-aligned sequence: small
+            // lists in pass 0, giant ones from the next region in pass 1
+            bool any_giant = false;
+            for (int pass = 0; pass < (a.gbucket ? 2 : 1); ++pass) {
+            if (pass == 1) {
+                if (!any_giant)
+                    break;
+                acc = (uint32_t)region_round(acc);
+            }
             for (int p0 = 0; p0 < a.nprobe; p0 += 64) {
                 const int p = p0 + lane;
                 int l = -1;
                 uint32_t sz = 0, off = 0;
+                bool giant = false;
                 if (p < a.nprobe) {
                     l = a.probes[q * a.nprobe + p];
                     if ((unsigned)l < (unsigned)a.nlist) {
                         off = a.list_off[l];
                         sz = a.list_off[l + 1] - off;
+                        giant = a.gbucket && a.gbucket[l] != kNoBucket;
                     }
                 }
-                const uint32_t incl = wave_inclusive_sum(sz);
+                any_giant = any_giant || wave_ballot(giant) != 0;
+                // this pass's lists: their places in the sequence, their entries
+                const bool mine = giant == (pass == 1);
+                const uint32_t seq = mine ? (giant ? (uint32_t)region_round(sz) : sz) : 0u;
+                sz = mine ? sz : 0u;
+                const uint32_t incl = wave_inclusive_sum(seq);
                 Piece pc;
-                const bool take = piece_of(acc + incl - sz, acc + incl, start, stop, &pc.b, &pc.e);
+                const uint32_t lo = acc + incl - seq;
+                const bool take = piece_of(lo, lo + sz, start, stop, &pc.b, &pc.e);
                 const bool wide = WIDE && take && pc.e - pc.b >= a.wide_min;
                 const uint64_t mn = wave_ballot(take && !wide), mw = wave_ballot(wide);
                 if (take) {
@@ -612,6 +796,7 @@ void scan_items_kernel(ScanArgs a)
                 cw += (uint32_t)__popcll(mw);
                 acc += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
             }
+            } // passes
             if (lane == 0) {
                 misc[1] = cn;
                 misc[3] = cw;
@@ -1098,13 +1283,24 @@ hipError_t launch_list_term(const DeviceIndex &ix, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Whether a search over this index uses the giant-list order and the
+// region-aligned sequences: the index has giant lists and a query's padded
+// sequence (at most nprobe + 1 regions of padding) stays below 2^32 entries.
+static bool giant_order(const DeviceIndex &ix, int nprobe)
+{
+    return ix.nbucket > 0 && ix.gbucket &&
+           (uint64_t)ix.ntotal + (uint64_t)(nprobe + 1) * kRegion < (1ull << 32);
+}
+
 hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
                        hipStream_t stream)
 {
     const unsigned blocks = (unsigned)((s.nq + 255) / 256);
+    const bool reorder = giant_order(ix, s.nprobe) && pl.bcur && pl.rm_q && pl.rm_r && pl.ikey;
     hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(256), 0, stream, s.probes, s.nprobe, s.nq,
                        ix.nlist, ix.list_off, pl.target, pl.imax, pl.qtotal, pl.qchunk, pl.qcount,
-                       pl.qbound, pl.counter, pl.prof);
+                       pl.qbound, pl.counter, pl.prof, reorder ? ix.gbucket : nullptr,
+                       reorder ? pl.bcur : nullptr, ix.nbucket);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -1119,7 +1315,24 @@ hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(rank_order_kernel, dim3(pl.imax), dim3(1024), 0, stream, pl.qcount, s.nq,
-                       pl.rank_n, pl.item_q, pl.item_r);
+                       pl.rank_n, reorder ? pl.rm_q : pl.item_q, reorder ? pl.rm_r : pl.item_r);
+    e = hipGetLastError();
+    if (e != hipSuccess || !reorder)
+        return e;
+    const unsigned iblocks = (unsigned)((pl.max_items + 255) / 256);
+    hipLaunchKernelGGL(item_key_kernel, dim3(iblocks), dim3(256), 0, stream, pl.item_base, s.nq,
+                       pl.rm_q, pl.rm_r, pl.qchunk, pl.qtotal, s.probes, s.nprobe, ix.nlist,
+                       ix.list_off, ix.gbucket, pl.ikey, pl.bcur);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(order_scan_kernel, dim3(1), dim3(1024), 0, stream, pl.item_base, s.nq,
+                       pl.rm_q, pl.rm_r, pl.ikey, pl.bcur, ix.nbucket, pl.item_q, pl.item_r);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(order_scatter_kernel, dim3(iblocks), dim3(256), 0, stream, pl.item_base,
+                       s.nq, pl.rm_q, pl.rm_r, pl.ikey, pl.bcur, pl.item_q, pl.item_r);
     return hipGetLastError();
 }
 
@@ -1146,6 +1359,8 @@ hipError_t launch_scan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     a.list_off = ix.list_off;
     a.codes = ix.codes;
     a.ids = ix.ids;
+    // the plan's layout (launch_plan: the same condition and workspace)
+    a.gbucket = giant_order(ix, s.nprobe) && pl.bcur ? ix.gbucket : nullptr;
     a.probes = s.probes;
     a.qtotal = pl.qtotal;
     a.qchunk = pl.qchunk;

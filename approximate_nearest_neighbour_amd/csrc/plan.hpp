@@ -15,17 +15,21 @@
 namespace ivfpq {
 
 // Entries per item and item count of a query with `total` probed entries:
-// chunk = max(target, ceil(total / imax)), so a query never has more than
-// imax items whatever its lists' sizes; a query with no entries still gets
-// one (empty) item, which writes its padded result.
+// chunk = max(target, ceil(total / imax)) rounded up to a multiple of
+// `align`, so a query never has more than imax items whatever its lists'
+// sizes; a query with no entries still gets one (empty) item, which writes
+// its padded result.
 struct QueryPlan {
     uint32_t chunk, count;
 };
 
-__host__ __device__ inline QueryPlan plan_query(uint32_t total, uint32_t target, uint32_t imax)
+__host__ __device__ inline QueryPlan plan_query(uint32_t total, uint32_t target, uint32_t imax,
+                                                uint32_t align = 1)
 {
     uint32_t chunk = (uint32_t)(((uint64_t)total + imax - 1) / imax);
     chunk = chunk > target ? chunk : target;
+    // a multiple of `align` (item boundaries on region boundaries)
+    chunk = (uint32_t)(((uint64_t)chunk + align - 1) / align * align);
     const uint32_t count = (uint32_t)(((uint64_t)total + chunk - 1) / chunk);
     return QueryPlan{chunk, count > 0 ? count : 1u};
 }

@@ -233,6 +233,45 @@ def test_search_split_into_items(dev, chunk, shape):
     ix.close()
 
 
+@pytest.mark.parametrize("chunk", [0, 65536, 300000])
+def test_search_with_giant_lists(dev, chunk):
+    """Lists of 2^20 entries or more: each query's sequence is laid out with
+    its giant lists on region boundaries (2^18 entries; padding that holds no
+    entries), items are whole regions, and the items past a query's first
+    that cover giant lists run after the others, grouped by the region where
+    their largest giant piece starts ("Billion-scale similarity search with
+    GPUs", IVFADC section: the (query, list) pairs are independent, so their
+    order is free).  Two giant lists (one of them probed by most queries),
+    item targets of 64k (rounded up to one region) and 300k entries (two
+    regions), one item per query, items mixing giant and small lists; the
+    results must pass the checker and not depend on the item size."""
+    nlist, d, m, nq, nprobe, k = 48, 16, 4, 400, 6, 60
+    say("giant lists", chunk)
+    rng = np.random.default_rng(2026 + chunk)
+    sizes = rng.integers(50, 400, nlist).astype(np.int64)
+    sizes[3], sizes[17] = 1_400_000, 1_100_000
+    idx = G.random_index(rng, nlist, d, m, sizes, codebook_scale=0.3)
+    cent = idx.centroids.copy()
+    cent[3] = 0.0  # the list every query finds close
+    idx = G.HostIndex(cent, idx.codebooks, idx.list_sizes, idx.codes, idx.ids)
+    q = (cent[rng.integers(0, nlist, nq)] + 0.5 * rng.standard_normal((nq, d))).astype(np.float32)
+    ix = A.ivfpq_load_index_host(idx)
+    qt = torch.from_numpy(q).to(dev)
+    d1, i1, p1 = A.ivfpq_search_ex(ix, qt, nprobe, k, chunk_len=chunk, return_probes=True)
+    d0, i0 = A.ivfpq_search_ex(ix, qt, nprobe, k, chunk_len=1 << 30)
+    torch.cuda.synchronize()
+    p1 = p1.cpu().numpy()
+    assert np.mean(np.any(p1 == 3, axis=1)) > 0.8 and np.any(p1 == 17)
+    # one item per query (the largest chunk): the same distances
+    assert np.array_equal(d1.cpu().numpy(), d0.cpu().numpy())
+    rows = np.sort(rng.choice(nq, 24, replace=False))
+    rep = check.compare_search(idx, q[rows], nprobe, k, d1.cpu().numpy()[rows],
+                               i1.cpu().numpy()[rows], p1[rows])
+    say("parity", rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    ix.close()
+
+
 def pq_exact(seed, nlist=7, d=16, m=4, n=3000, nq=12):
     rng = np.random.default_rng(seed)
     cent = rng.integers(-3, 4, (nlist, d)).astype(np.float32)
