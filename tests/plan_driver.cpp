@@ -2,7 +2,7 @@
 // the device plan and scan kernels call, run on the CPU.  Reads cases from
 // stdin, prints each query's plan and each item's pieces.
 //
-// input:  T, then per case: nlist nq nprobe kw target per_cu cus,
+// input:  T, then per case: nlist nq nprobe kw target per_cu cus align,
 //         list sizes [nlist], probes [nq * nprobe] (-1 or out of range: none)
 // output: per case "case imax max_items grid", then per query
 //         "query total chunk count" and per item "item start stop npieces
@@ -18,9 +18,9 @@ int main()
     if (std::scanf("%d", &T) != 1)
         return 1;
     for (int t = 0; t < T; ++t) {
-        long long nlist, nq, nprobe, kw, target, per_cu, cus;
-        if (std::scanf("%lld %lld %lld %lld %lld %lld %lld", &nlist, &nq, &nprobe, &kw, &target,
-                       &per_cu, &cus) != 7)
+        long long nlist, nq, nprobe, kw, target, per_cu, cus, align;
+        if (std::scanf("%lld %lld %lld %lld %lld %lld %lld %lld", &nlist, &nq, &nprobe, &kw,
+                       &target, &per_cu, &cus, &align) != 8)
             return 1;
         std::vector<unsigned long long> sizes(nlist);
         for (auto &v : sizes)
@@ -42,7 +42,8 @@ int main()
                     e += sizes[l];
             }
             const uint32_t total = (uint32_t)e;
-            const ivfpq::QueryPlan qp = ivfpq::plan_query(total, (uint32_t)target, imax);
+            const ivfpq::QueryPlan qp =
+                ivfpq::plan_query(total, (uint32_t)target, imax, (uint32_t)align);
             std::printf("query %u %u %u\n", total, qp.chunk, qp.count);
             for (uint32_t i = 0; i < qp.count; ++i) {
                 uint32_t start, stop;

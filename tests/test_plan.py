@@ -37,7 +37,7 @@ def run(driver, cases):
     for c in cases:
         probes = np.asarray(c["probes"], dtype=np.int64)
         lines.append(f"{len(c['sizes'])} {probes.shape[0]} {probes.shape[1]} {c['kw']} "
-                     f"{c['target']} {c['per_cu']} {c['cus']}")
+                     f"{c['target']} {c['per_cu']} {c['cus']} {c.get('align', 1)}")
         lines.append(" ".join(str(int(v)) for v in c["sizes"]))
         lines.append(" ".join(str(int(v)) for v in probes.ravel()))
     out = subprocess.run([driver], input="\n".join(lines) + "\n", capture_output=True,
@@ -76,6 +76,7 @@ def check_case(c, r):
         assert pq["total"] == len(seq)
         assert 1 <= pq["count"] <= r["imax"]
         assert pq["chunk"] >= c["target"] and pq["chunk"] >= 1
+        assert pq["chunk"] % c.get("align", 1) == 0
         if seq:
             assert pq["count"] == -(-len(seq) // pq["chunk"])
         else:
@@ -160,8 +161,11 @@ def test_random_and_skewed_plans(driver):
     cases.append(dict(sizes=rng.integers(0, 30, nl),
                       probes=np.stack([rng.permutation(nl)[:10] for _ in range(1 << 17)]),
                       kw=1024, target=1, per_cu=2, cus=256))
+    # chunks rounded up to whole regions (the scan's region-aligned layout
+    # of queries that probe giant lists): 7, 64 and 2^18 entries
+    cases += [dict(c, align=int(rng.choice([7, 64, 1 << 18]))) for c in cases[:40]]
     r = run(driver, cases)
-    assert r[-1]["imax"] == 2
+    assert r[40]["imax"] == 2
     for c, rr in zip(cases, r):
         check_case(c, rr)
 
