@@ -810,6 +810,11 @@ def main():
         log("cpu baseline", cpu)
     code_array = int(w.index.ntotal) * w.index.m
     bound = "hbm" if code_array > MALL_BYTES else "effective"
+    traffic = stored_traffic(w.name, args.lut) if args.metric == "l2" else None
+    # the measured L2-miss bytes' own rate: below `achieved` when code bytes
+    # are served from L2 (the giant-list order), above it when tables and
+    # staging add reads
+    traffic_gbs = traffic / (scan_ms * 1e-3) / 1e9 if traffic else None
 
     res = {
         "metric": METRIC,
@@ -831,7 +836,9 @@ def main():
                    "k": w.k, "lut": args.lut, "metric": args.metric},
         "roofline": {"bound": bound, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic(w.name, args.lut) if args.metric == "l2" else None,
+                     "traffic": traffic,
+                     "traffic_gbs": traffic_gbs,
+                     "traffic_frac": traffic_gbs / HBM_PEAK_GBS if traffic_gbs else None,
                      "kernel": "scan_items_kernel", "kernel_ms": scan_ms,
                      "algorithmic_bytes_per_launch": code_bytes,
                      "code_array_bytes": code_array,
