@@ -81,6 +81,43 @@ def test_noalloc_equals_search_ex_on_two_calls(metric):
     ix.close()
 
 
+def test_noalloc_with_giant_lists():
+    """An index with lists of 2^20 entries or more: the allocation-free search
+    also carves the giant-list order's arrays (rank-major order, item keys,
+    bucket counters) from the fixed scratch and lays the queries' sequences
+    out region-aligned; two calls in a row (the second smaller) must equal
+    ivfpq_search_ex's rows."""
+    rng = np.random.default_rng(2027)
+    nlist, d, m = 40, 16, 4
+    sizes = rng.integers(50, 400, nlist).astype(np.int64)
+    sizes[5], sizes[11] = 1_300_000, 1_050_000
+    idx = G.random_index(rng, nlist, d, m, sizes, codebook_scale=0.3)
+    cent = idx.centroids.copy()
+    cent[5] = 0.0  # probed by most queries
+    idx = G.HostIndex(cent, idx.codebooks, idx.list_sizes, idx.codes, idx.ids)
+    ix = A.ivfpq_load_index_host(idx)
+    for nq, nprobe, k, chunk in [(600, 6, 50, 0), (150, 4, 20, 65536)]:
+        q = (cent[rng.integers(0, nlist, nq)] + 0.5 * rng.standard_normal((nq, d))).astype(np.float32)
+        qd = torch.from_numpy(q).cuda()
+        out = outputs(nq, nprobe, k)
+        torch.cuda.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        A.ivfpq_search_ex(ix, qd, nprobe, k, chunk_len=chunk, return_probes=True, out=out,
+                          noalloc=True)
+        torch.cuda.synchronize()
+        assert torch.cuda.mem_get_info()[0] == free0
+        d_na, i_na, p_na = (t.cpu().numpy() for t in out)
+        assert np.mean(np.any(p_na == 5, axis=1)) > 0.5
+        d_ref, i_ref, p_ref = (t.cpu().numpy() for t in A.ivfpq_search_ex(
+            ix, qd, nprobe, k, chunk_len=chunk, return_probes=True))
+        assert np.array_equal(p_na, p_ref)
+        same_rows(d_na, i_na, d_ref, i_ref)
+        rows = np.sort(rng.choice(nq, 12, replace=False))
+        rep = check.compare_search(idx, q[rows], nprobe, k, d_na[rows], i_na[rows], p_na[rows])
+        assert rep.ok(), rep.failures[:3]
+    ix.close()
+
+
 def test_noalloc_rejects_a_batch_beyond_the_scratch():
     idx, rng = skewed_index(79)
     ix = A.ivfpq_load_index_host(idx)
