@@ -9,5 +9,5 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (run on the GPU box)")
+    config.addinivalue_line("markers", "gpu: needs an MI355X GPU")
     config.addinivalue_line("markers", "slow: full-size workloads (minutes of host work)")
