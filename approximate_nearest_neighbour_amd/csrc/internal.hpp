@@ -38,7 +38,7 @@ struct DeviceIndex {
 };
 
 constexpr uint32_t kGiantList = 1u << 20;
-constexpr uint32_t kRegion = 1u << 18;
+constexpr uint32_t kRegion = 1u << 19;
 constexpr uint32_t kNoBucket = 0xFFFFFFFFu;
 
 struct SearchArgs {

@@ -90,8 +90,8 @@ typedef enum {
  * lists hold E entries gets ceil(E / max(chunk_len, ceil(E / imax))) items,
  * imax (2..64) chosen from nq and k, so long queries get larger items.  On an
  * index with lists of 2^20 entries or more, the sequence of a query that
- * probes one is laid out with those lists on 2^18-entry boundaries and its
- * item size is rounded up to a multiple of 2^18 entries (the work items that
+ * probes one is laid out with those lists on 2^19-entry boundaries and its
+ * item size is rounded up to a multiple of 2^19 entries (the work items that
  * read the same part of such a list then run together).  The result does
  * not depend on it. */
 typedef struct {

@@ -236,15 +236,15 @@ def test_search_split_into_items(dev, chunk, shape):
 @pytest.mark.parametrize("chunk", [0, 65536, 300000])
 def test_search_with_giant_lists(dev, chunk):
     """Lists of 2^20 entries or more: each query's sequence is laid out with
-    its giant lists on region boundaries (2^18 entries; padding that holds no
+    its giant lists on region boundaries (2^19 entries; padding that holds no
     entries), items are whole regions, and the items past a query's first
     that cover giant lists run after the others, grouped by the region where
     their largest giant piece starts ("Billion-scale similarity search with
     GPUs", IVFADC section: the (query, list) pairs are independent, so their
     order is free).  Two giant lists (one of them probed by most queries),
-    item targets of 64k (rounded up to one region) and 300k entries (two
-    regions), one item per query, items mixing giant and small lists; the
-    results must pass the checker and not depend on the item size."""
+    item targets of 64k and 300k entries (both rounded up to one region),
+    one item per query, items mixing giant and small lists; the results must
+    pass the checker and not depend on the item size."""
     nlist, d, m, nq, nprobe, k = 48, 16, 4, 400, 6, 60
     say("giant lists", chunk)
     rng = np.random.default_rng(2026 + chunk)
