@@ -535,7 +535,8 @@ void scan_items_kernel(ScanArgs a)
     // IP with a compile-time shape)
     constexpr bool QT = M > 0 && (PRE || IP);
 
-    // Row tables (m 8, float32 difference form): both table buffers share a
+    // Row tables (m 8, float32 tables of the difference form or the inner
+    // product; not the decomposed tables): both table buffers share a
     // 64 KiB region at LDS offset 0 of 256 rows (code value c) x 256 bytes,
     // buffer b in bytes [128 b, 128 b + 128) of every row, so that a table
     // address is (c << 8) | byte0 and one v_perm_b32 assembles it from the
@@ -552,7 +553,7 @@ void scan_items_kernel(ScanArgs a)
     //    point value format for reducing shared memory bank conflict in ANN
     //    search", bank-conflict analysis: random 8-bit indices into one table
     //    collide in the banks; replication spreads them).
-    constexpr bool WIDE = M == 8 && !F16 && !QT && G == 2;
+    constexpr bool WIDE = M == 8 && !F16 && !PRE && G == 2;
 
     // Pieces (list, entry range) are handled in groups of PG: one barrier per
     // group, tables of the next group built while the current one is
@@ -623,11 +624,17 @@ void scan_items_kernel(ScanArgs a)
             const float cst = rs[0];
 #pragma unroll
             for (int jj = 0; jj < JG; ++jj) {
-                const int j = g * JG + jj;
-                Table<F16>::put(lut, j * 256 + v, j == 0 ? t2[jj] + cst : t2[jj]);
+                const int j = jsub(jj);
+                const float e = j == 0 ? t2[jj] + cst : t2[jj];
+                unsigned char *row = reinterpret_cast<unsigned char *>(lut) + (v << 8);
+                if (WIDE && wide)   // the four copies of (j, v): one 16-byte store
+                    *reinterpret_cast<float4 *>(row + 16 * j) = make_float4(e, e, e, e);
+                else if (WIDE)      // row table, one copy
+                    *reinterpret_cast<float *>(row + 4 * j) = e;
+                else
+                    Table<F16>::put(lut, j * 256 + v, e);
             }
             (void)list;
-            (void)wide;
         } else if constexpr (IP) {
             const float cst = rs[0];
             for (int j = 0; j < m; ++j) {
@@ -820,7 +827,7 @@ void scan_items_kernel(ScanArgs a)
             gfloat *cbk = reinterpret_cast<gfloat *>(cbase);
 #pragma unroll
             for (int jj = 0; jj < JG; ++jj) {
-                const int j = g * JG + jj;
+                const int j = jsub(jj);
                 gfloat *cw = cbk + ((size_t)j * 256 + v) * DSUB;
                 float acc = 0.f;
 #pragma unroll
