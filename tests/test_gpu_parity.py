@@ -233,8 +233,15 @@ def test_search_split_into_items(dev, chunk, shape):
     ix.close()
 
 
-@pytest.mark.parametrize("chunk", [0, 65536, 300000])
-def test_search_with_giant_lists(dev, chunk):
+@pytest.mark.parametrize("chunk,nprobe,k,metric,nq,d,m", [
+    (0, 6, 60, "l2", 400, 16, 4), (65536, 6, 60, "l2", 400, 16, 4),
+    (300000, 6, 60, "l2", 400, 16, 4),
+    # the 1B shape's scan (d 96, m 8: replicated row tables)
+    (0, 1, 1024, "l2", 64, 96, 8),     # one probe: some queries scan a giant list only
+    (65536, 6, 60, "ip", 300, 96, 8),  # inner product (row tables, negated scores)
+    (0, 6, 60, "l2", 1, 96, 8),        # a single query
+])
+def test_search_with_giant_lists(dev, chunk, nprobe, k, metric, nq, d, m):
     """Lists of 2^20 entries or more: each query's sequence is laid out with
     its giant lists on region boundaries (2^19 entries; padding that holds no
     entries), items are whole regions, and the items past a query's first
@@ -245,8 +252,8 @@ def test_search_with_giant_lists(dev, chunk):
     item targets of 64k and 300k entries (both rounded up to one region),
     one item per query, items mixing giant and small lists; the results must
     pass the checker and not depend on the item size."""
-    nlist, d, m, nq, nprobe, k = 48, 16, 4, 400, 6, 60
-    say("giant lists", chunk)
+    nlist = 48
+    say("giant lists", chunk, nprobe, k, metric, nq, d, m)
     rng = np.random.default_rng(2026 + chunk)
     sizes = rng.integers(50, 400, nlist).astype(np.int64)
     sizes[3], sizes[17] = 1_400_000, 1_100_000
@@ -257,16 +264,22 @@ def test_search_with_giant_lists(dev, chunk):
     q = (cent[rng.integers(0, nlist, nq)] + 0.5 * rng.standard_normal((nq, d))).astype(np.float32)
     ix = A.ivfpq_load_index_host(idx)
     qt = torch.from_numpy(q).to(dev)
-    d1, i1, p1 = A.ivfpq_search_ex(ix, qt, nprobe, k, chunk_len=chunk, return_probes=True)
-    d0, i0 = A.ivfpq_search_ex(ix, qt, nprobe, k, chunk_len=1 << 30)
+    d1, i1, p1 = A.ivfpq_search_ex(ix, qt, nprobe, k, chunk_len=chunk, return_probes=True,
+                                   metric=metric)
+    d0, i0 = A.ivfpq_search_ex(ix, qt, nprobe, k, chunk_len=1 << 30, metric=metric)
     torch.cuda.synchronize()
     p1 = p1.cpu().numpy()
-    assert np.mean(np.any(p1 == 3, axis=1)) > 0.8 and np.any(p1 == 17)
+    if nq >= 64 and metric == "l2":  # the case meets the giant lists
+        if nprobe > 1:
+            assert np.mean(np.any(p1 == 3, axis=1)) > 0.8
+        else:
+            assert np.any(np.isin(p1, [3, 17]))
     # one item per query (the largest chunk): the same distances
     assert np.array_equal(d1.cpu().numpy(), d0.cpu().numpy())
-    rows = np.sort(rng.choice(nq, 24, replace=False))
+    rows = np.sort(rng.choice(nq, min(nq, 24), replace=False))
     rep = check.compare_search(idx, q[rows], nprobe, k, d1.cpu().numpy()[rows],
-                               i1.cpu().numpy()[rows], p1[rows])
+                               i1.cpu().numpy()[rows], p1[rows],
+                               lut_mode=O.IP if metric == "ip" else O.LUT_F64)
     say("parity", rep.summary())
     assert rep.ok(), rep.failures[:5]
     ix.close()
