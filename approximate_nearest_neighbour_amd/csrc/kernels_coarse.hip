@@ -73,6 +73,20 @@ __global__ void centroid_blocks_kernel(const float *__restrict__ c, int d, int d
 // kernel then ends with wrong probes instead of hanging; never expected).
 constexpr int kRing = 4;
 
+// Lane `i` (a compile-time constant) of `vec` replaced by the wave-uniform
+// value `u`: a select under a constant lane mask, which the compiler
+// rematerialises instead of keeping sixteen masks live in registers.
+__device__ __forceinline__ float set_lane(float vec, int i, float u)
+{
+    return __builtin_amdgcn_inverse_ballot_w64(1ull << i) ? u : vec;
+}
+
+// The value of lane `i` (v_readlane).
+__device__ __forceinline__ float lane_value(float vec, int i)
+{
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(vec), i));
+}
+
 __device__ __forceinline__ void ring_wait(const uint32_t *ctr, uint32_t target, uint32_t *broken)
 {
     uint32_t n = 0;
@@ -285,9 +299,10 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
             u = u > o ? u : o;
             u = use_slots ? u : float_order_key(INFINITY);
             const uint32_t b = nb < u ? nb : u;
+            const float bf = float_from_order_key(b);
 #pragma unroll
             for (int i = 0; i < QS; ++i)
-                sel[i].bound(float_from_order_key((uint32_t)__builtin_amdgcn_readlane((int)b, i)));
+                sel[i].bound(lane_value(bf, i));
             pending = false;
         }
         // all reads first (one LDS round trip), then the selections
@@ -303,11 +318,12 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
         for (int i = 0; i < QS; ++i)
             sel[i].push(cand[i], (uint32_t)(t * 64 + lane));
         if (splits > 1 && ((t - t0) & 7) == 7) {
+            // lane i: query i's values (one select under a constant mask each)
             float mine = INFINITY, mpart = INFINITY;
 #pragma unroll
             for (int i = 0; i < QS; ++i) {
-                mine = lane == i ? sel[i].kth : mine;
-                mpart = lane == i ? sel[i].part : mpart;
+                mine = set_lane(mine, i, sel[i].kth);
+                mpart = set_lane(mpart, i, sel[i].part);
             }
             if (qvalid && mine < INFINITY)
                 atomicMin(qbound + ql, float_order_key(mine));
@@ -421,6 +437,21 @@ __global__ void centroid_x6_kernel(const float *__restrict__ c, int d, int nlist
     *reinterpret_cast<u16x8_t *>(o) = v0;
     *reinterpret_cast<u16x8_t *>(o + 512) = v1;
     *reinterpret_cast<u16x8_t *>(o + 1024) = v2;
+}
+
+// Tiles (counted from the start of a split's range) after which the
+// selection waves of the split-bfloat16 kernel exchange bounds: after tiles
+// 1 and 3, then every 4 tiles up to tile 31, then every 16.  Early on the
+// k-th values fall fastest and a split alone has seen few centroids, so the
+// shared bounds are worth most there; later each exchange (a global load
+// that the wave waits for) costs more than the few candidates it removes.
+// At the 1B coarse shape (8 splits of 512 tiles, k 128) a stream model of
+// the selection gives 423 candidates staged per query and split and 6.2
+// buffer merges, against 553 and 8.8 with an exchange every 8 tiles, from
+// 39 exchanges instead of 64.
+__device__ __forceinline__ bool exchange_after(int x)
+{
+    return x == 1 || (x < 32 ? (x & 3) == 3 : (x & 15) == 15);
 }
 
 // Workgroup of 8 waves, 64 queries, a range of 64-centroid tiles:
@@ -580,12 +611,16 @@ __global__ __launch_bounds__(512) void coarse_x6_kernel(
     }
 
     const int sw = wave - MW; // selection wave: queries 16 sw .. 16 sw + 15
+    // the selection is the slower role here: its waves issue first when both
+    // roles of a SIMD are ready (the matrix waves' MFMA chains fill the gaps)
+    __builtin_amdgcn_s_setprio(3);
     const int rk = splits > 1 ? (nprobe + splits - 1) / splits : nprobe;
     WaveTopK<NW> sel[QS];
 #pragma unroll
     for (int i = 0; i < QS; ++i)
         sel[i].init(nprobe, stage + (sw * QS + i) * 128, rk);
-    // shared bounds between the splits, as in the float32 kernel: lane i
+    // shared bounds between the splits, as in the float32 kernel (exchanged
+    // after the tiles exchange_after names): lane i
     // (< 16) publishes query i's k-th value and its slot value; the slots of
     // query i, split s, are loaded by lane i + 16 (s % 4), four loads for up
     // to 16 splits (more splits use the first bound only)
@@ -610,9 +645,10 @@ __global__ __launch_bounds__(512) void coarse_x6_kernel(
             u = u > o ? u : o;
             u = use_slots ? u : float_order_key(INFINITY);
             const uint32_t bnd = nb < u ? nb : u;
+            const float bf = float_from_order_key(bnd);
 #pragma unroll
             for (int i = 0; i < QS; ++i)
-                sel[i].bound(float_from_order_key((uint32_t)__builtin_amdgcn_readlane((int)bnd, i)));
+                sel[i].bound(lane_value(bf, i));
             pending = false;
         }
         const int rb = (t - t0) % kRing;
@@ -626,12 +662,13 @@ __global__ __launch_bounds__(512) void coarse_x6_kernel(
 #pragma unroll
         for (int i = 0; i < QS; ++i)
             sel[i].push(cand[i], (uint32_t)(t * 64 + lane));
-        if (splits > 1 && ((t - t0) & 7) == 7) {
+        if (splits > 1 && exchange_after(t - t0)) {
+            // lane i: query i's values (one select under a constant mask each)
             float mine = INFINITY, mpart = INFINITY;
 #pragma unroll
             for (int i = 0; i < QS; ++i) {
-                mine = lane == i ? sel[i].kth : mine;
-                mpart = lane == i ? sel[i].part : mpart;
+                mine = set_lane(mine, i, sel[i].kth);
+                mpart = set_lane(mpart, i, sel[i].part);
             }
             if (qvalid && mine < INFINITY)
                 atomicMin(qbound + ql, float_order_key(mine));
