@@ -73,6 +73,23 @@ __global__ void centroid_blocks_kernel(const float *__restrict__ c, int d, int d
 // kernel then ends with wrong probes instead of hanging; never expected).
 constexpr int kRing = 4;
 
+// Tiles (counted from the start of a split's range) after which the
+// selection waves of both top-nprobe kernels exchange bounds: after tiles
+// 1 and 3, then every 4 tiles up to tile 31, then every 16.  Early on the
+// k-th values fall fastest and a split alone has seen few centroids, so the
+// shared bounds are worth most there; later each exchange (a global load
+// that the wave waits for) costs more than the few candidates it removes.
+// At the 1B coarse shape (8 splits of 512 tiles, k 128) a stream model of
+// the selection gives 423 candidates staged per query and split and 6.2
+// buffer merges, against 553 and 8.8 with an exchange every 8 tiles, from
+// 39 exchanges instead of 64 (split-bfloat16 kernel alone 4.11 -> 3.85 ms; the
+// float32 kernel at that shape, with its selection waves also at raised
+// priority: 5.84 -> 5.36 ms).
+__device__ __forceinline__ bool exchange_after(int x)
+{
+    return x == 1 || (x < 32 ? (x & 3) == 3 : (x & 15) == 15);
+}
+
 // Lane `i` (a compile-time constant) of `vec` replaced by the wave-uniform
 // value `u`: a select under a constant lane mask, which the compiler
 // rematerialises instead of keeping sixteen masks live in registers.
@@ -264,12 +281,14 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
     //    own: every split has rk values at most its slot, so the union of the
     //    splits has >= k values at most the largest slot (+inf until every
     //    split has published), a far tighter bound early in the sweep.
-    // Every 8 tiles a wave publishes its queries' values and loads the shared
-    // ones, which it applies a tile later (the loads complete meanwhile).
+    // After the tiles exchange_after names a wave publishes its queries'
+    // values and loads the shared ones, which it applies a tile later.
     // Values only decrease, so a stale load is a weaker bound, never a wrong
     // one.  Lane i of a selection wave handles query i for the k-th value;
     // the slots of query i, split s are loaded by lane i + 8 (s % 8), two
     // loads for up to 16 splits (more splits use the first bound only).
+    // Selection waves issue first when both roles of a SIMD are ready.
+    __builtin_amdgcn_s_setprio(3);
     const int rk = splits > 1 ? (nprobe + splits - 1) / splits : nprobe;
     WaveTopK<NW> sel[QS];
 #pragma unroll
@@ -317,7 +336,7 @@ __global__ __launch_bounds__(1024) void coarse_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < QS; ++i)
             sel[i].push(cand[i], (uint32_t)(t * 64 + lane));
-        if (splits > 1 && ((t - t0) & 7) == 7) {
+        if (splits > 1 && exchange_after(t - t0)) {
             // lane i: query i's values (one select under a constant mask each)
             float mine = INFINITY, mpart = INFINITY;
 #pragma unroll
@@ -437,21 +456,6 @@ __global__ void centroid_x6_kernel(const float *__restrict__ c, int d, int nlist
     *reinterpret_cast<u16x8_t *>(o) = v0;
     *reinterpret_cast<u16x8_t *>(o + 512) = v1;
     *reinterpret_cast<u16x8_t *>(o + 1024) = v2;
-}
-
-// Tiles (counted from the start of a split's range) after which the
-// selection waves of the split-bfloat16 kernel exchange bounds: after tiles
-// 1 and 3, then every 4 tiles up to tile 31, then every 16.  Early on the
-// k-th values fall fastest and a split alone has seen few centroids, so the
-// shared bounds are worth most there; later each exchange (a global load
-// that the wave waits for) costs more than the few candidates it removes.
-// At the 1B coarse shape (8 splits of 512 tiles, k 128) a stream model of
-// the selection gives 423 candidates staged per query and split and 6.2
-// buffer merges, against 553 and 8.8 with an exchange every 8 tiles, from
-// 39 exchanges instead of 64.
-__device__ __forceinline__ bool exchange_after(int x)
-{
-    return x == 1 || (x < 32 ? (x & 3) == 3 : (x & 15) == 15);
 }
 
 // Workgroup of 8 waves, 64 queries, a range of 64-centroid tiles:
