@@ -60,49 +60,64 @@ __host__ __device__ inline uint64_t region_round(uint64_t n)
     return (n + kRegion - 1) / kRegion * kRegion;
 }
 
-__global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ probes, int nprobe,
-                                                   int64_t nq, int nlist,
-                                                   const uint32_t *__restrict__ list_off,
-                                                   uint32_t target, uint32_t imax,
-                                                   uint32_t *__restrict__ qtotal,
-                                                   uint32_t *__restrict__ qchunk,
-                                                   uint32_t *__restrict__ qcount,
-                                                   uint32_t *__restrict__ qbound,
-                                                   uint32_t *__restrict__ counter,
-                                                   unsigned long long *__restrict__ prof,
-                                                   const uint32_t *__restrict__ gbucket,
-                                                   uint32_t *__restrict__ bcur, uint32_t nbucket)
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ probes, int nprobe,
+                                                    int64_t nq, int nlist,
+                                                    const uint32_t *__restrict__ list_off,
+                                                    uint32_t target, uint32_t imax,
+                                                    uint32_t *__restrict__ qtotal,
+                                                    uint32_t *__restrict__ qchunk,
+                                                    uint32_t *__restrict__ qcount,
+                                                    uint32_t *__restrict__ qbound,
+                                                    uint32_t *__restrict__ counter,
+                                                    unsigned long long *__restrict__ prof,
+                                                    const uint32_t *__restrict__ gbucket,
+                                                    uint32_t *__restrict__ bcur, uint32_t nbucket)
 {
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q == 0)
+    // one wave per query (16 per workgroup): its lanes read the probes 64 at
+    // a time and the sums meet by shuffles
+    __shared__ unsigned long long wsum[16];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t gt = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+    const int64_t q = (int64_t)blockIdx.x * 16 + wave;
+    if (gt == 0)
         *counter = 0;
     if (bcur) // the giant-list buckets' counters (order_* kernels)
-        for (int64_t i = q; i <= (int64_t)nbucket; i += (int64_t)gridDim.x * 256)
+        for (int64_t i = gt; i <= (int64_t)nbucket; i += (int64_t)gridDim.x * 1024)
             bcur[i] = 0;
     uint64_t e = 0, small = 0, giant = 0;
-    if (q < nq) {
-        for (int p = 0; p < nprobe; ++p) {
-            const int l = probes[q * nprobe + p];
-            if ((unsigned)l < (unsigned)nlist) {
-                const uint32_t sz = list_off[l + 1] - list_off[l];
-                e += sz;
-                if (gbucket && gbucket[l] != kNoBucket)
-                    giant += region_round(sz);
-                else
-                    small += sz;
-            }
+    for (int p = lane; q < nq && p < nprobe; p += 64) {
+        const int l = probes[q * nprobe + p];
+        if ((unsigned)l < (unsigned)nlist) {
+            const uint32_t sz = list_off[l + 1] - list_off[l];
+            e += sz;
+            if (gbucket && gbucket[l] != kNoBucket)
+                giant += region_round(sz);
+            else
+                small += sz;
         }
     }
-    if (prof) {
-        // entries scanned, one atomic per wave
-        uint64_t w = e;
 #pragma unroll
-        for (int sh = 32; sh >= 1; sh >>= 1)
-            w += __shfl_xor(w, sh);
-        if ((threadIdx.x & 63) == 0 && w)
-            atomicAdd(prof, (unsigned long long)w);
+    for (int sh = 32; sh >= 1; sh >>= 1) {
+        e += __shfl_xor(e, sh);
+        small += __shfl_xor(small, sh);
+        giant += __shfl_xor(giant, sh);
     }
-    if (q >= nq)
+    if (prof) {
+        // entries scanned: one atomic per workgroup (a same-address atomic
+        // per query would queue behind each other)
+        if (lane == 0)
+            wsum[wave] = e;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long t = 0;
+            for (int w = 0; w < 16; ++w)
+                t += wsum[w];
+            if (t)
+                atomicAdd(prof, t);
+        }
+    }
+    if (lane != 0 || q >= nq)
         return;
     // the query's sequence: its entries (with giant lists, the region-aligned
     // layout of the scan order)
@@ -244,42 +259,79 @@ __global__ __launch_bounds__(256) void item_key_kernel(
     int nlist, const uint32_t *__restrict__ list_off, const uint32_t *__restrict__ gbucket,
     uint32_t *__restrict__ ikey, uint32_t *__restrict__ bcur)
 {
-    const uint32_t total = item_base[nq];
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)total)
-        return;
-    const int64_t q = rm_q[i];
-    const uint32_t r = rm_r[i];
-    uint32_t start, stop;
-    item_range(r, qchunk[q], qtotal[q], &start, &stop);
-    uint32_t best = 0, key = kNoBucket;
-    // a query's first item (its nearest lists) keeps its rank-major place:
-    // the bound it publishes is the one the query's other items start from
-    if (r > 0) {
-        // the giant lists' offsets in the region-aligned sequence
-        uint64_t acc = 0;
-        for (int p = 0; p < nprobe; ++p) {
-            const int l = probes[q * nprobe + p];
-            if ((unsigned)l < (unsigned)nlist && gbucket[l] == kNoBucket)
-                acc += list_off[l + 1] - list_off[l];
-        }
-        acc = region_round(acc);
-        for (int p = 0; p < nprobe && acc < stop; ++p) {
-            const int l = probes[q * nprobe + p];
-            if ((unsigned)l >= (unsigned)nlist || gbucket[l] == kNoBucket)
-                continue;
-            const uint32_t sz = list_off[l + 1] - list_off[l];
-            uint32_t b, e;
-            if (piece_of((uint32_t)acc, (uint32_t)acc + sz, start, stop, &b, &e) && e - b > best) {
-                best = e - b;
-                key = gbucket[l] + b / kRegion;
+    // one wave per item, the items of the rank-major order in turn: the
+    // lanes take the query's probes 64 at a time; the offsets of the giant
+    // lists in the region-aligned sequence come from a prefix sum over the
+    // lanes, the longest piece (the first probe among equals) from a maximum
+    const int lane = threadIdx.x & 63;
+    const int64_t total = item_base[nq];
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < total; i += nw) {
+        const int64_t q = rm_q[i];
+        const uint32_t r = rm_r[i];
+        uint32_t key = kNoBucket;
+        // a query's first item (its nearest lists) keeps its rank-major
+        // place: the bound it publishes is the one its other items start from
+        if (r > 0) {
+            uint32_t start, stop;
+            item_range(r, qchunk[q], qtotal[q], &start, &stop);
+            uint64_t small = 0;
+            for (int p = lane; p < nprobe; p += 64) {
+                const int l = probes[q * nprobe + p];
+                if ((unsigned)l < (unsigned)nlist && gbucket[l] == kNoBucket)
+                    small += list_off[l + 1] - list_off[l];
             }
-            acc += region_round(sz);
+#pragma unroll
+            for (int sh = 32; sh >= 1; sh >>= 1)
+                small += __shfl_xor(small, sh);
+            uint32_t acc = (uint32_t)region_round(small); // the giant lists start here
+            uint64_t best = 0; // (piece length, ~probe) of this lane's longest piece
+            uint32_t bkey = kNoBucket;
+            for (int p0 = 0; p0 < nprobe; p0 += 64) {
+                const int p = p0 + lane;
+                int l = 0;
+                uint32_t sz = 0;
+                bool g = false;
+                if (p < nprobe) {
+                    l = probes[q * nprobe + p];
+                    g = (unsigned)l < (unsigned)nlist && gbucket[l] != kNoBucket;
+                    sz = g ? list_off[l + 1] - list_off[l] : 0u;
+                }
+                const uint32_t w = (uint32_t)region_round(sz);
+                uint32_t x = w; // inclusive prefix over the lanes
+#pragma unroll
+                for (int dd = 1; dd < 64; dd <<= 1) {
+                    const uint32_t y = __shfl_up(x, dd);
+                    x += lane >= dd ? y : 0u;
+                }
+                const uint32_t lo = acc + x - w;
+                uint32_t b, e;
+                if (g && piece_of(lo, lo + sz, start, stop, &b, &e)) {
+                    const uint64_t c = ((uint64_t)(e - b) << 32) | (0xFFFFFFFFu - (uint32_t)p);
+                    if (c > best) {
+                        best = c;
+                        bkey = gbucket[l] + b / kRegion;
+                    }
+                }
+                acc += __shfl(x, 63);
+            }
+            uint64_t m = best;
+#pragma unroll
+            for (int sh = 32; sh >= 1; sh >>= 1) {
+                const uint64_t o = __shfl_xor(m, sh);
+                m = o > m ? o : m;
+            }
+            if (m != 0) {
+                const uint32_t pb = 0xFFFFFFFFu - (uint32_t)m;
+                key = (uint32_t)__shfl((int)bkey, (int)(pb & 63));
+            }
+        }
+        if (lane == 0) {
+            ikey[i] = key;
+            if (key != kNoBucket)
+                atomicAdd(&bcur[key + 1], 1u);
         }
     }
-    ikey[i] = key;
-    if (key != kNoBucket)
-        atomicAdd(&bcur[key + 1], 1u);
 }
 
 // One workgroup: the items without a bucket, compacted in rank-major order to
@@ -1302,9 +1354,9 @@ static bool giant_order(const DeviceIndex &ix, int nprobe)
 hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchPlan &pl,
                        hipStream_t stream)
 {
-    const unsigned blocks = (unsigned)((s.nq + 255) / 256);
+    const unsigned blocks = (unsigned)((s.nq + 15) / 16); // a wave per query
     const bool reorder = giant_order(ix, s.nprobe) && pl.bcur && pl.rm_q && pl.rm_r && pl.ikey;
-    hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(256), 0, stream, s.probes, s.nprobe, s.nq,
+    hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(1024), 0, stream, s.probes, s.nprobe, s.nq,
                        ix.nlist, ix.list_off, pl.target, pl.imax, pl.qtotal, pl.qchunk, pl.qcount,
                        pl.qbound, pl.counter, pl.prof, reorder ? ix.gbucket : nullptr,
                        reorder ? pl.bcur : nullptr, ix.nbucket);
@@ -1327,7 +1379,10 @@ hipError_t launch_plan(const DeviceIndex &ix, const SearchArgs &s, const SearchP
     if (e != hipSuccess || !reorder)
         return e;
     const unsigned iblocks = (unsigned)((pl.max_items + 255) / 256);
-    hipLaunchKernelGGL(item_key_kernel, dim3(iblocks), dim3(256), 0, stream, pl.item_base, s.nq,
+    // a wave per item, at most 8,192 waves looping over the items
+    const int64_t kb = (pl.max_items + 3) / 4;
+    const unsigned kblocks = (unsigned)(kb < 2048 ? kb : 2048);
+    hipLaunchKernelGGL(item_key_kernel, dim3(kblocks), dim3(256), 0, stream, pl.item_base, s.nq,
                        pl.rm_q, pl.rm_r, pl.qchunk, pl.qtotal, s.probes, s.nprobe, ix.nlist,
                        ix.list_off, ix.gbucket, pl.ikey, pl.bcur);
     e = hipGetLastError();
