@@ -75,19 +75,20 @@ constexpr int kRing = 4;
 
 // Tiles (counted from the start of a split's range) after which the
 // selection waves of both top-nprobe kernels exchange bounds: after tiles
-// 1 and 3, then every 4 tiles up to tile 31, then every 16.  Early on the
-// k-th values fall fastest and a split alone has seen few centroids, so the
-// shared bounds are worth most there; later each exchange (a global load
-// that the wave waits for) costs more than the few candidates it removes.
-// At the 1B coarse shape (8 splits of 512 tiles, k 128) a stream model of
-// the selection gives 423 candidates staged per query and split and 6.2
-// buffer merges, against 553 and 8.8 with an exchange every 8 tiles, from
-// 39 exchanges instead of 64 (split-bfloat16 kernel alone 4.11 -> 3.85 ms; the
-// float32 kernel at that shape, with its selection waves also at raised
-// priority: 5.84 -> 5.36 ms).
+// 1 and 3, every 4 tiles up to tile 31, every 16 up to tile 127, then every
+// 128.  Early on the k-th values fall fastest and a split alone has seen few
+// centroids, so the shared bounds are worth most there; later each exchange
+// (some 4,000-6,000 cycles of the selection wave, measured: the lane
+// selects, the global atomics and the loads of the shared values) costs more
+// than the few candidates it removes.  At the 1B coarse
+// shape (8 splits of 512 tiles, k 128) a stream model of the selection gives
+// 429 candidates staged per query and split and 6.2 buffer merges from 18
+// exchanges, against 553 and 8.8 from 64 with an exchange every 8 tiles
+// (split-bfloat16 kernel alone, with the raised priority and the
+// constant-mask selects below: 4.11 -> 3.52 ms).
 __device__ __forceinline__ bool exchange_after(int x)
 {
-    return x == 1 || (x < 32 ? (x & 3) == 3 : (x & 15) == 15);
+    return x == 1 || (x < 32 ? (x & 3) == 3 : x < 128 ? (x & 15) == 15 : (x & 127) == 127);
 }
 
 // Lane `i` (a compile-time constant) of `vec` replaced by the wave-uniform
